@@ -1,0 +1,461 @@
+"""Pins of the CPU oracle: each check ties an oracle function to something other
+than itself -- a closed form, an independent library routine, brute force, a
+textbook table or a worked example -- and raises AssertionError on a mismatch.
+
+The checks are plain functions so that ``test_oracle_pins`` can run them and
+``test_oracle_mutations`` can run them again against an oracle with a planted
+mistake and require that at least one check fails.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.spatial.transform import Rotation
+
+from oracle import codec, lloyd, pack, quant, rope, rotations
+from tests.conftest import read_golden
+
+RNG_SEED = 1234
+
+
+def _rng(k=0):
+    return np.random.default_rng(RNG_SEED + k)
+
+
+# --------------------------------------------------------------------------- #
+# RoPE
+# --------------------------------------------------------------------------- #
+def check_rope_theta_special_values():
+    """theta_0 = 1 and theta_{d/4} = base^(-1/2): 0.01 at base 10000 (closed form)."""
+    for d in (8, 64, 128, 256):
+        th = rope.thetas(d, 10000.0)
+        assert th.shape == (d // 2,)
+        assert th[0] == 1.0
+        assert abs(th[d // 4] - 0.01) < 1e-15
+        ratio = th[1:] / th[:-1]
+        assert np.allclose(ratio, 10000.0 ** (-2.0 / d), rtol=1e-12)
+
+
+def check_rope_basis_vectors():
+    """R_p e_{2i} = (cos p th_i) e_{2i} + (sin p th_i) e_{2i+1}; R_p e_{2i+1} = -sin e_{2i} + cos e_{2i+1}.
+
+    Pins the adjacent pairing and the sign of the sine (EliteKV page 2.1 matrix).
+    """
+    d = 16
+    th = rope.thetas(d)
+    for p in (1, 7, 1000):
+        for i in (0, 3, 7):
+            e = np.zeros((1, 1, 1, d))
+            e[..., 2 * i] = 1.0
+            y = rope.rope(e, np.array([p]))[0, 0, 0]
+            want = np.zeros(d)
+            want[2 * i] = np.cos(p * th[i])
+            want[2 * i + 1] = np.sin(p * th[i])
+            assert np.allclose(y, want, atol=1e-14), (p, i)
+            e = np.zeros((1, 1, 1, d))
+            e[..., 2 * i + 1] = 1.0
+            y = rope.rope(e, np.array([p]))[0, 0, 0]
+            want = np.zeros(d)
+            want[2 * i] = -np.sin(p * th[i])
+            want[2 * i + 1] = np.cos(p * th[i])
+            assert np.allclose(y, want, atol=1e-14), (p, i)
+
+
+def check_rope_composition():
+    """R(a) R(b) = R(a + b) (RoPE-KV page 7.1), to 1e-12."""
+    x = _rng(1).standard_normal((2, 5, 3, 32))
+    pa = np.array([0, 1, 17, 300, 4095])
+    pb = np.array([5, 0, 2, 1000, 28672])
+    two = rope.rope(rope.rope(x, pa), pb)
+    one = rope.rope(x, pa + pb)
+    assert np.allclose(two, one, atol=1e-12)
+    assert np.array_equal(rope.rope(x, np.zeros(5, dtype=np.int64)), x)
+
+
+def check_rope_relative_position():
+    """(R_m q).(R_n k) depends only on m - n, and equals the full expansion with the sine term."""
+    rng = _rng(2)
+    d = 64
+    q = rng.standard_normal(d)
+    k = rng.standard_normal(d)
+    th = rope.thetas(d)
+
+    def dot(m, n):
+        qm = rope.rope(q.reshape(1, 1, 1, d), np.array([m]))[0, 0, 0]
+        kn = rope.rope(k.reshape(1, 1, 1, d), np.array([n]))[0, 0, 0]
+        return qm @ kn
+
+    for m, n in ((5, 3), (100, 37), (32767, 1)):
+        base = dot(m, n)
+        assert abs(dot(m + 11, n + 11) - base) < 1e-9
+        delta = (m - n) * th
+        q0, q1, k0, k1 = q[0::2], q[1::2], k[0::2], k[1::2]
+        full = np.sum((q0 * k0 + q1 * k1) * np.cos(delta) + (q0 * k1 - q1 * k0) * np.sin(delta))
+        assert abs(full - base) < 1e-9
+
+
+def check_rope_complex_form():
+    """Pair (x_2i, x_2i+1) as the complex number x_2i + i x_2i+1 multiplied by exp(i p theta_i)."""
+    rng = _rng(3)
+    d = 128
+    x = rng.standard_normal((1, 6, 2, d))
+    pos = np.array([0, 1, 2, 77, 4096, 32767])
+    y = rope.rope(x, pos)
+    th = rope.thetas(d)
+    zc = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * pos[:, None, None] * th)[None]
+    assert np.allclose(y[..., 0::2], zc.real, atol=1e-12)
+    assert np.allclose(y[..., 1::2], zc.imag, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- #
+# Walsh-Hadamard
+# --------------------------------------------------------------------------- #
+def check_hadamard_definition():
+    """H[i, j] = (-1)^popcount(i & j) (Sylvester order) and H H^T = d I."""
+    for d in (2, 4, 16, 128, 256):
+        h = rotations.hadamard(d)
+        i = np.arange(d)
+        pc = np.array([[bin(a & b).count("1") for b in i] for a in i])
+        assert np.array_equal(h, (-1.0) ** pc)
+        assert np.array_equal(h @ h.T, d * np.eye(d))
+
+
+def _fwht_butterflies(u):
+    """Textbook in-place fast Walsh-Hadamard transform (natural order), unnormalised."""
+    a = np.array(u, dtype=np.float64).copy()
+    d = a.shape[-1]
+    hlen = 1
+    while hlen < d:
+        a = a.reshape(a.shape[:-1] + (d // (2 * hlen), 2, hlen))
+        top = a[..., 0, :] + a[..., 1, :]
+        bot = a[..., 0, :] - a[..., 1, :]
+        a = np.stack([top, bot], axis=-2).reshape(a.shape[:-3] + (d,))
+        hlen *= 2
+    return a
+
+
+def check_fwht_transform():
+    """fwht matches a butterfly FWHT / sqrt(d); e_0 -> constant 1/sqrt(d); involution; Parseval."""
+    rng = _rng(4)
+    for d in (128, 256):
+        u = rng.standard_normal((7, d))
+        z = rotations.fwht(u)
+        assert np.allclose(z, _fwht_butterflies(u) / np.sqrt(d), atol=1e-12)
+        e0 = np.zeros(d)
+        e0[0] = 1.0
+        assert np.allclose(rotations.fwht(e0), np.full(d, 1.0 / np.sqrt(d)), atol=1e-15)
+        ones = np.ones(d)
+        want = np.zeros(d)
+        want[0] = np.sqrt(d)
+        assert np.allclose(rotations.fwht(ones), want, atol=1e-12)
+        assert np.allclose(rotations.fwht(z), u, atol=1e-12)
+        assert np.allclose(np.sum(z * z, -1), np.sum(u * u, -1), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- #
+# quaternions / SO(4)
+# --------------------------------------------------------------------------- #
+ONE = np.array([1.0, 0, 0, 0])
+QI = np.array([0, 1.0, 0, 0])
+QJ = np.array([0, 0, 1.0, 0])
+QK = np.array([0, 0, 0, 1.0])
+
+
+def check_hamilton_rules():
+    """i j = k, j k = i, k i = j, j i = -k, i^2 = j^2 = k^2 = i j k = -1."""
+    m = rotations.quat_mul
+    assert np.array_equal(m(QI, QJ), QK)
+    assert np.array_equal(m(QJ, QK), QI)
+    assert np.array_equal(m(QK, QI), QJ)
+    assert np.array_equal(m(QJ, QI), -QK)
+    for q in (QI, QJ, QK):
+        assert np.array_equal(m(q, q), -ONE)
+    assert np.array_equal(m(m(QI, QJ), QK), -ONE)
+    assert np.array_equal(m(ONE, QJ), QJ) and np.array_equal(m(QJ, ONE), QJ)
+
+
+def _quat_params(ql, qr, nblocks=1):
+    q = np.zeros((nblocks, 2, 4))
+    q[:, 0] = ql
+    q[:, 1] = qr
+    return q
+
+
+def check_so4_product_order():
+    """T(v) = qL v qR: qL = i, qR = 1 maps j -> k; qL = 1, qR = i maps j -> -k."""
+    assert np.array_equal(rotations.so4_rotate(QJ, _quat_params(QI, ONE)), QK)
+    assert np.array_equal(rotations.so4_rotate(QJ, _quat_params(ONE, QI)), -QK)
+    assert np.array_equal(rotations.so4_rotate(QK, _quat_params(ONE, ONE)), QK)
+
+
+def _unit(rng, n):
+    g = rng.standard_normal((n, 4))
+    return g / np.linalg.norm(g, axis=1, keepdims=True)
+
+
+def check_so4_orthogonality():
+    """Unit (qL, qR) give an orthogonal map with det +1; norms kept; (-qL, -qR) identical; inverse exact."""
+    rng = _rng(5)
+    nb = 32
+    q = np.zeros((nb, 2, 4))
+    q[:, 0] = _unit(rng, nb)
+    q[:, 1] = _unit(rng, nb)
+    u = rng.standard_normal((9, 4 * nb))
+    z = rotations.so4_rotate(u, q)
+    assert np.allclose(np.sum(z * z, -1), np.sum(u * u, -1), rtol=1e-12)
+    assert np.allclose(rotations.so4_rotate(u, -q), z, atol=1e-13)
+    assert np.allclose(rotations.so4_inverse(z, q), u, atol=1e-12)
+    for b in range(4):
+        qb = q[b:b + 1]
+        m = np.stack([rotations.so4_rotate(e, qb) for e in np.eye(4)], axis=1)
+        assert np.allclose(m.T @ m, np.eye(4), atol=1e-13)
+        assert abs(np.linalg.det(m) - 1.0) < 1e-12
+
+
+def check_so4_reduces_to_3d_rotation():
+    """qR = qL*: v = (0, r) -> (0, R r) with R the rotation of unit quaternion qL (scipy, scalar-last)."""
+    rng = _rng(6)
+    for _ in range(5):
+        ql = _unit(rng, 1)[0]
+        r3 = rng.standard_normal(3)
+        v = np.concatenate(([0.0], r3))
+        out = rotations.so4_rotate(v, _quat_params(ql, ql * np.array([1, -1, -1, -1])))
+        want = Rotation.from_quat([ql[1], ql[2], ql[3], ql[0]]).apply(r3)
+        assert abs(out[0]) < 1e-13
+        assert np.allclose(out[1:], want, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- #
+# fp16 directed rounding and min-max quantization
+# --------------------------------------------------------------------------- #
+_ALL_F16 = np.arange(65536, dtype=np.uint16).view(np.float16)
+_FINITE_F16 = np.unique(_ALL_F16[np.isfinite(_ALL_F16)].astype(np.float64))
+
+
+def check_fp16_directed_rounding():
+    """Round-down/up agree with an exhaustive search over every finite float16."""
+    rng = _rng(7)
+    x = np.concatenate([rng.standard_normal(300) * 3, rng.standard_normal(50) * 1e-6,
+                        [0.0, -0.0, 1.0, -1.0, 65504.0, -65504.0, 5.9604645e-08, 1e-9, -1e-9]])
+    x = np.concatenate([x, _FINITE_F16[rng.integers(0, len(_FINITE_F16), 50)]])
+    dn = quant.fp16_round_down(x).astype(np.float64)
+    up = quant.fp16_round_up(x).astype(np.float64)
+    for xi, d_, u_ in zip(x, dn, up):
+        want_dn = _FINITE_F16[_FINITE_F16 <= xi].max()
+        want_up = _FINITE_F16[_FINITE_F16 >= xi].min()
+        assert d_ == want_dn, (xi, d_, want_dn)
+        assert u_ == want_up, (xi, u_, want_up)
+
+
+def check_minmax_properties():
+    """Grid covers [min, max]; |z - y| <= scale/2; codes in range; scale and zero are the tightest fp16."""
+    rng = _rng(8)
+    for bits in (2, 3, 4):
+        for g in (32, 128):
+            z = rng.standard_normal((40, 256)) * rng.uniform(0.1, 20, (40, 1)) + rng.uniform(-5, 5, (40, 1))
+            scale, zero = quant.minmax_params(z, bits, g)
+            q, t = quant.minmax_codes(z, scale, zero, bits, g)
+            y = quant.minmax_dequant(q, scale, zero, g)
+            levels = 2 ** bits - 1
+            zg = z.reshape(40, 256 // g, g)
+            s64, z64 = scale.astype(np.float64), zero.astype(np.float64)
+            assert np.all(z64 <= zg.min(-1))
+            assert np.all(np.nextafter(zero, np.float16(np.inf)).astype(np.float64) > zg.min(-1))
+            assert np.all(z64 + levels * s64 >= zg.max(-1))
+            prev = np.nextafter(scale, np.float16(-np.inf)).astype(np.float64)
+            assert np.all(z64 + levels * prev < zg.max(-1))
+            assert q.max() <= levels
+            err = np.abs(z - y).reshape(40, 256 // g, g)
+            assert np.all(err <= s64[..., None] / 2 * (1 + 1e-12))
+            # brute force: nearest grid point (ties excluded)
+            grid = z64[..., None] + np.arange(levels + 1) * s64[..., None]  # [40, ng, L]
+            dist = np.abs(zg[..., None] - grid[:, :, None, :])
+            best = np.argmin(dist, axis=-1).reshape(40, 256)
+            tie = np.abs(t - np.floor(t) - 0.5) < 1e-9
+            assert np.array_equal(best[~tie], q[~tie])
+
+
+def check_minmax_degenerate_group():
+    """A constant group that is an fp16 value: scale 0, codes 0, reconstruction exact."""
+    z = np.full((1, 128), 0.375)
+    scale, zero = quant.minmax_params(z, 2, 128)
+    q, _ = quant.minmax_codes(z, scale, zero, 2, 128)
+    assert scale[0, 0] == 0 and zero[0, 0] == np.float16(0.375)
+    assert np.all(q == 0)
+    assert np.all(quant.minmax_dequant(q, scale, zero, 128) == 0.375)
+
+
+def check_lloyd_codes_nearest():
+    """Threshold rule equals brute-force nearest centroid; a value on a threshold takes the lower code."""
+    rng = _rng(9)
+    cb = np.sort(rng.standard_normal(8))
+    u = rng.standard_normal(5000) * 1.5
+    q = quant.lloyd_codes(u, cb)
+    nearest = np.argmin(np.abs(u[:, None] - cb[None, :]), axis=1)
+    assert np.array_equal(q, nearest)
+    tau = 0.5 * (cb[:-1] + cb[1:])
+    assert np.array_equal(quant.lloyd_codes(tau, cb), np.arange(7))
+    assert np.array_equal(quant.lloyd_dequant(np.arange(8), cb), cb)
+
+
+# --------------------------------------------------------------------------- #
+# Lloyd-Max fitting
+# --------------------------------------------------------------------------- #
+def check_lloyd_max_table():
+    """Fitted N(0,1) quantizers match Max (1960), Table I, and the 1-bit closed form."""
+    rows = read_golden("lloyd_max_gaussian.txt")
+    fits = {b: lloyd.fit_gaussian(b, 1.0) for b in (1, 2, 3, 4)}
+    for bits, kind, vals in rows:
+        b = int(bits)
+        c = fits[b]
+        half = c[len(c) // 2:]
+        if kind == "levels":
+            want = np.array([float(v) for v in vals.split()])
+            assert np.allclose(half, want, atol=6e-4), (b, half, want)
+        elif kind == "thresholds":
+            want = np.array([float(v) for v in vals.split()])
+            tau = 0.5 * (c[:-1] + c[1:])
+            assert np.allclose(tau[len(tau) // 2:], want, atol=6e-4), (b, tau, want)
+        elif kind == "mse":
+            assert abs(lloyd.gaussian_mse(c) - float(vals)) < 6e-4 * float(vals) + 2e-6, b
+    assert abs(fits[1][1] - np.sqrt(2 / np.pi)) < 1e-12
+
+
+def check_lloyd_max_fixed_point():
+    """Converged: every centroid is its cell's conditional mean; symmetric; scales with sigma."""
+    from scipy.integrate import quad
+    from scipy.stats import norm
+    sigma = 1.0 / np.sqrt(128.0)
+    for b in (2, 3):
+        c = lloyd.fit_gaussian(b, sigma)
+        assert np.allclose(c, -c[::-1], atol=1e-15)
+        tau = np.concatenate(([-np.inf], 0.5 * (c[:-1] + c[1:]), [np.inf]))
+        for k in range(len(c)):
+            num = quad(lambda x: x * norm.pdf(x, scale=sigma), tau[k], tau[k + 1], epsabs=1e-14)[0]
+            den = quad(lambda x: norm.pdf(x, scale=sigma), tau[k], tau[k + 1], epsabs=1e-14)[0]
+            assert abs(num / den - c[k]) < 1e-9 * sigma * 100, (b, k)
+        assert np.allclose(c, lloyd.fit_gaussian(b, 1.0) * sigma, rtol=1e-12)
+
+
+def check_lloyd_max_brute_force():
+    """Brute force: 1-D Lloyd iterations on a fine weighted grid of N(0,1) reach the fitted
+    centroids (to the grid's discretisation error, well under 1e-3)."""
+    from scipy.stats import norm
+    x = np.linspace(-8.0, 8.0, 160_001)
+    w = np.exp(-0.5 * x * x)
+    for b in (2, 3):
+        c = norm.ppf((np.arange(2 ** b) + 0.5) / 2 ** b)
+        for _ in range(150):
+            tau = 0.5 * (c[:-1] + c[1:])
+            idx = np.searchsorted(tau, x)
+            c = np.bincount(idx, w * x, 2 ** b) / np.bincount(idx, w, 2 ** b)
+        assert np.allclose(c, lloyd.fit_gaussian(b, 1.0), atol=1e-3), (b, c)
+
+
+# --------------------------------------------------------------------------- #
+# packing
+# --------------------------------------------------------------------------- #
+def check_pack_worked_examples():
+    for bits, codes, hexbytes in read_golden("pack_examples.txt"):
+        b = int(bits)
+        q = np.array([int(v) for v in codes.split()], dtype=np.uint8)
+        want = np.array([int(h, 16) for h in hexbytes.split()], dtype=np.uint8)
+        got = pack.pack(q[None], b)[0]
+        assert np.array_equal(got, want), (b, got, want)
+        assert np.array_equal(pack.unpack(want[None], b, len(q))[0], q)
+
+
+def check_pack_matches_numpy_and_bigint():
+    """Agrees with np.packbits(bitorder='little') of the bit stream, and with a big-integer build."""
+    rng = _rng(11)
+    for b in (2, 3, 4):
+        q = rng.integers(0, 2 ** b, (6, 128)).astype(np.uint8)
+        got = pack.pack(q, b)
+        bitsarr = ((q[..., None] >> np.arange(b)) & 1).astype(np.uint8).reshape(6, -1)
+        assert np.array_equal(got, np.packbits(bitsarr, axis=-1, bitorder="little"))
+        for row in range(6):
+            big = sum(int(v) << (b * j) for j, v in enumerate(q[row]))
+            assert bytes(got[row]) == big.to_bytes(128 * b // 8, "little")
+        assert np.array_equal(pack.unpack(got, b, 128), q)
+
+
+# --------------------------------------------------------------------------- #
+# the whole pipeline
+# --------------------------------------------------------------------------- #
+def check_pipeline_error_bound():
+    """Post-RoPE x vs decode(encode(x)): per-vector L2 error <= sqrt(sum_g G (scale_g/2)^2) (Parseval)."""
+    rng = _rng(12)
+    d, g = 128, 32
+    x = rng.standard_normal((2, 9, 3, d))
+    x[..., [5, 77]] *= 15
+    perm = rng.permutation(d)
+    for bits in (2, 4):
+        p = codec.CodecParams(bits=bits, group_size=g, rope=True, perm=perm, n_sink=2, pos_offset=1)
+        out = codec.encode(x, p)
+        y = codec.decode(out, p, x.shape)
+        xr = rope.rope(x, 1 + np.arange(9))
+        err = np.sqrt(np.sum((y - xr) ** 2, axis=-1))[:, 1:]  # token 0 is a sink
+        s = out["scale"].astype(np.float64)[:, 1:]
+        bound = np.sqrt(np.sum(g * (s / 2) ** 2, axis=-1))
+        assert np.all(err <= bound * (1 + 1e-9))
+        assert out["sink_written"].tolist() == [False, True]
+        assert np.array_equal(out["sink"][:, 1], xr[:, 0].astype(np.float16))
+        assert np.array_equal(y[:, 0], xr[:, 0].astype(np.float16).astype(np.float64))
+        assert np.all(out["codes"][:, 0] == 0) and np.all(out["scale"][:, 0] == 0)
+
+
+def check_pipeline_sink_at_position_zero():
+    """Position 0: RoPE is the identity, so the sink is fp16(x) bit for bit."""
+    rng = _rng(13)
+    x = rng.standard_normal((3, 4, 2, 128)).astype(np.float16).astype(np.float64)
+    p = codec.CodecParams(bits=2, group_size=128, rope=True, n_sink=1)
+    out = codec.encode(x, p)
+    assert np.array_equal(out["sink"][:, 0], x[:, 0].astype(np.float16))
+
+
+def check_pipeline_permutation_is_a_gather():
+    """Encoding with perm equals encoding the gathered vector without it; decode scatters back."""
+    rng = _rng(14)
+    x = rng.standard_normal((1, 6, 2, 128))
+    perm = rng.permutation(128)
+    p1 = codec.CodecParams(bits=2, group_size=128, perm=perm)
+    p0 = codec.CodecParams(bits=2, group_size=128)
+    a = codec.encode(x, p1)
+    b = codec.encode(x[..., perm], p0)
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scale"], b["scale"])
+    ya = codec.decode(a, p1, x.shape)
+    yb = codec.decode(b, p0, x.shape)
+    assert np.allclose(ya[..., perm], yb, atol=1e-13)
+    e = np.zeros((1, 1, 1, 128))
+    e[..., perm[5]] = 1.0
+    assert np.argmax(codec.encode(e, codec.CodecParams(bits=4, group_size=128, perm=perm, rot="none"))["q"]) == 5
+
+
+def check_pipeline_norm_separation():
+    """Lloyd path: stored rho = |x|; |u| = rho/(rho+eps); codes are the nearest centroids of the
+    rotated direction (brute force); decoded / rho rotates onto codebook points; zero vector -> zero."""
+    rng = _rng(15)
+    d = 128
+    nb = d // 4
+    q = np.zeros((nb, 2, 4))
+    q[:, 0] = _unit(rng, nb)
+    q[:, 1] = _unit(rng, nb)
+    cb = lloyd.fit_gaussian(3, 1.0 / np.sqrt(d))
+    x = rng.standard_normal((2, 5, 1, d)) * 2.5
+    x[0, 0, 0] = 0.0
+    p = codec.CodecParams(bits=3, group_size=d, quant="lloyd", rot="so4", quat=q, codebook=cb)
+    out = codec.encode(x, p)
+    rho = np.sqrt(np.sum(x * x, axis=-1))
+    assert np.allclose(out["norm"], rho, rtol=1e-7)
+    un = x / (rho[..., None] + 1e-6)
+    assert np.allclose(np.linalg.norm(un, axis=-1), rho / (rho + 1e-6), rtol=1e-13)
+    zz = rotations.so4_rotate(un, q)
+    nearest = np.argmin(np.abs(zz[..., None] - cb), axis=-1)
+    assert np.array_equal(nearest, out["q"])
+    y = codec.decode(out, p, x.shape)
+    nz = out["norm"] > 0
+    w = rotations.so4_rotate(y[nz] / out["norm"][nz].astype(np.float64)[..., None], q)
+    assert np.min(np.abs(w[..., None] - cb), axis=-1).max() < 1e-12
+    assert np.all(y[0, 0, 0] == 0.0)
+
+
+ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -1,0 +1,172 @@
+"""Plant a plausible mistake in the oracle (CPU only, via monkeypatch) and require that
+at least one pin catches it.  This is what makes the pins evidence: a dropped term, a
+wrong sign or index, a transposed operand or a wrong rounding direction anywhere in
+the oracle turns at least one check red."""
+import numpy as np
+import pytest
+from scipy.stats import norm
+
+from oracle import codec, lloyd, pack, quant, rope, rotations
+from tests import oracle_pins
+
+
+def _rope_neg_sine(x, positions, base=10000.0):
+    x = np.asarray(x, dtype=np.float64)
+    th = rope.thetas(x.shape[-1], base)
+    phi = np.asarray(positions, dtype=np.float64)[:, None] * th[None, :]
+    c, s = np.cos(phi)[:, None, :], np.sin(phi)[:, None, :]
+    y = np.empty_like(x)
+    y[..., 0::2] = x[..., 0::2] * c + x[..., 1::2] * s
+    y[..., 1::2] = -x[..., 0::2] * s + x[..., 1::2] * c
+    return y
+
+
+def _rope_half_split(x, positions, base=10000.0):
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    th = rope.thetas(d, base)
+    phi = np.asarray(positions, dtype=np.float64)[:, None] * th[None, :]
+    c, s = np.cos(phi)[:, None, :], np.sin(phi)[:, None, :]
+    a, b = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def _thetas_wrong_exponent(head_dim, base=10000.0):
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(np.float64(base), -1.0 * i / head_dim)
+
+
+def _fwht_unnormalised(u):
+    u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    return (u.reshape(-1, d) @ rotations.hadamard(d).T).reshape(u.shape)
+
+
+def _quat_mul_sign_slip(a, b):
+    w1, x1, y1, z1 = [np.asarray(a, dtype=np.float64)[..., i] for i in range(4)]
+    w2, x2, y2, z2 = [np.asarray(b, dtype=np.float64)[..., i] for i in range(4)]
+    return np.stack([
+        w1 * w2 - x1 * x2 - y1 * y2 - z1 * z2,
+        w1 * x2 + x1 * w2 - y1 * z2 + z1 * y2,  # cross term with the wrong sign
+        w1 * y2 - x1 * z2 + y1 * w2 + z1 * x2,
+        w1 * z2 + x1 * y2 - y1 * x2 + z1 * w2,
+    ], axis=-1)
+
+
+def _so4_swapped(u, quat):
+    u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    q = np.asarray(quat, dtype=np.float64)
+    blocks = u.reshape(u.shape[:-1] + (d // 4, 4))
+    z = rotations.quat_mul(q[:, 1, :], rotations.quat_mul(blocks, q[:, 0, :]))
+    return z.reshape(u.shape)
+
+
+def _round_nearest(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
+def _minmax_params_range_from_min(z, bits, group):
+    z = np.asarray(z, dtype=np.float64)
+    g = z.reshape(z.shape[:-1] + (z.shape[-1] // group, group))
+    mn, mx = g.min(-1), g.max(-1)
+    zero = quant.fp16_round_down(mn)
+    return quant.fp16_round_up((mx - mn) / (2 ** bits - 1)), zero
+
+
+def _minmax_codes_floor(z, scale, zero, bits, group):
+    z = np.asarray(z, dtype=np.float64)
+    zg = z.reshape(z.shape[:-1] + (z.shape[-1] // group, group))
+    s = scale.astype(np.float64)[..., None]
+    t = np.where(s > 0, (zg - zero.astype(np.float64)[..., None]) / np.where(s > 0, s, 1), 0.0)
+    q = np.clip(np.floor(t), 0, 2 ** bits - 1).astype(np.uint8)
+    return q.reshape(z.shape), t.reshape(z.shape)
+
+
+def _lloyd_codes_ge(u, codebook):
+    tau = quant.lloyd_thresholds(codebook)
+    u = np.asarray(u, dtype=np.float64)
+    q = np.zeros(u.shape, dtype=np.uint8)
+    for t in tau:
+        q += (u >= t).astype(np.uint8)
+    return q
+
+
+def _fit_wrong_mean(bits, sigma=1.0, tol=1e-13, max_iter=2000):
+    n = 2 ** bits
+    c = norm.ppf((np.arange(n) + 0.5) / n)
+    for _ in range(max_iter):
+        tau = 0.5 * (c[:-1] + c[1:])
+        lo = np.concatenate(([-np.inf], tau))
+        hi = np.concatenate((tau, [np.inf]))
+        c = (norm.pdf(lo) - norm.pdf(hi)) / (norm.cdf(hi) - norm.cdf(lo)) * 0.5 + 0.5 * c  # damped, biased
+        c = c * 1.01
+    return c * sigma
+
+
+def _pack_msb_first(q, bits):
+    q = np.asarray(q, dtype=np.uint8)
+    d = q.shape[-1]
+    flat = q.reshape(-1, d)
+    stream = np.zeros((flat.shape[0], d * bits), dtype=np.uint8)
+    for m in range(bits):
+        stream[:, m::bits] = (flat >> m) & 1
+    return np.packbits(stream, axis=-1, bitorder="big").reshape(q.shape[:-1] + (d * bits // 8,))
+
+
+_orig_decode = codec.decode
+
+
+def _decode_gather_not_scatter(planes, p, shape):
+    if p.perm is None:
+        return _orig_decode(planes, p, shape)
+    inv = np.argsort(p.perm)
+    p2 = codec.CodecParams(**{**p.__dict__, "perm": inv.astype(np.uint16)})
+    return _orig_decode(planes, p2, shape)
+
+
+def _decode_rho_plus_eps(planes, p, shape):
+    y = _orig_decode(planes, p, shape)
+    if p.quant == "lloyd":
+        n = planes["norm"].astype(np.float64)[..., None]
+        y = np.where(n > 0, y / np.where(n > 0, n, 1) * (n + p.eps), y)
+    return y
+
+
+MUTATIONS = {
+    "rope_negative_sine": (rope, "rope", _rope_neg_sine),
+    "rope_half_split_pairs": (rope, "rope", _rope_half_split),
+    "rope_theta_exponent": (rope, "thetas", _thetas_wrong_exponent),
+    "fwht_missing_normalisation": (rotations, "fwht", _fwht_unnormalised),
+    "quat_mul_sign": (rotations, "quat_mul", _quat_mul_sign_slip),
+    "so4_operands_swapped": (rotations, "so4_rotate", _so4_swapped),
+    "fp16_round_down_to_nearest": (quant, "fp16_round_down", _round_nearest),
+    "fp16_round_up_to_nearest": (quant, "fp16_round_up", _round_nearest),
+    "minmax_range_from_min": (quant, "minmax_params", _minmax_params_range_from_min),
+    "minmax_floor_not_rint": (quant, "minmax_codes", _minmax_codes_floor),
+    "lloyd_threshold_ge": (quant, "lloyd_codes", _lloyd_codes_ge),
+    "lloyd_fit_biased": (lloyd, "fit_gaussian", _fit_wrong_mean),
+    "pack_msb_first": (pack, "pack", _pack_msb_first),
+    "decode_perm_gather": (codec, "decode", _decode_gather_not_scatter),
+    "decode_rho_plus_eps": (codec, "decode", _decode_rho_plus_eps),
+}
+
+
+def _patch(monkeypatch, module, name, fn):
+    monkeypatch.setattr(module, name, fn)
+    # codec imported rope() by name; every other step is looked up through its module
+    if module is rope and name == "rope":
+        monkeypatch.setattr(codec, "_rope", fn)
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(monkeypatch, mutation):
+    module, name, fn = MUTATIONS[mutation]
+    _patch(monkeypatch, module, name, fn)
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError, ZeroDivisionError, FloatingPointError) as e:
+            failed.append(check.__name__)
+    assert failed, f"no pin caught the planted mistake {mutation}"
