@@ -85,8 +85,8 @@ def encode(x: np.ndarray, p: CodecParams) -> Dict[str, np.ndarray]:
     Returns the stored planes -- ``codes`` u8 [R,T,H,D*b/8]; ``scale``/``zero`` f16
     [R,T,H,D/G] (min-max); ``norm`` f32 [R,T,H] (Lloyd-Max); ``sink`` f16
     [R,n_sink,H,D] with ``sink_written`` bool [n_sink] -- and, for the tests, the
-    unpacked codes ``q``, the pre-rounding values ``t`` (min-max: (z-zero)/scale;
-    Lloyd-Max: the rotated value z) and the mask ``quantized`` [T] of non-sink tokens.
+    unpacked codes ``q``, the rotated values ``z``, the pre-rounding values ``t``
+    (min-max: (z-zero)/scale; Lloyd-Max: z) and the mask ``quantized`` [T] of non-sink tokens.
     """
     x = np.asarray(x, dtype=np.float64)
     r, t, h, d = x.shape
@@ -100,6 +100,7 @@ def encode(x: np.ndarray, p: CodecParams) -> Dict[str, np.ndarray]:
         "sink_written": np.zeros(p.n_sink, dtype=bool),
         "q": np.zeros((r, t, h, d), dtype=np.uint8),
         "t": np.zeros((r, t, h, d), dtype=np.float64),
+        "z": np.zeros((r, t, h, d), dtype=np.float64),
     }
     if p.quant == "minmax":
         out["scale"] = np.zeros((r, t, h, d // g), dtype=np.float16)
@@ -132,6 +133,7 @@ def encode(x: np.ndarray, p: CodecParams) -> Dict[str, np.ndarray]:
         tt = z
     out["q"][:, keep] = q
     out["t"][:, keep] = tt
+    out["z"][:, keep] = z
     out["codes"][:, keep] = _pack.pack(q, b)
     return out
 

@@ -1,0 +1,292 @@
+"""GPU codec vs the CPU oracle, through the C ABI (via the thin Python binding).
+
+Small cases span several wave tiles and a ragged tail; the full-size workloads are
+checked on sampled vectors in the same launch configuration the bench uses.
+"""
+from __future__ import annotations
+
+import itertools
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import gpu_util as gu
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import rotate_then_bit_amd as kvq  # noqa: E402  (fails loudly if libkvq.so is missing)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(case, x_np, perm=None, quat=None, codebook=None, out_dtypes=("f32",), label="",
+             fraction=True):
+    """Encode x on the GPU and with the oracle; compare planes, then decode both from the GPU planes."""
+    say(f"[case] {label} shape={case.shape} dtype={case.dtype} bits={case.bits} G={case.group_size} "
+        f"{case.rot}/{case.quant} rope={case.rope} sink={case.n_sink} pos0={case.pos_offset}")
+    cfg = gu.make_config(case, perm, quat, codebook)
+    xt = gu.torch_input(x_np, case.dtype)
+    planes = kvq.encode(xt, cfg)
+    torch.cuda.synchronize()
+    g = gu.planes_numpy(planes)
+    x64 = oracle.widen(x_np, case.dtype)
+    p = parity.params_for(case, perm, quat, codebook)
+    ora = oracle.encode(x64, p)
+    if case.n_sink:
+        ora["sink_f64"] = parity.sink_f64(x64, p)
+    rep = parity.compare_encode(g, ora, p, case.shape, label, fraction=fraction)
+    ref = oracle.decode(g, p, case.shape)
+    for od in out_dtypes:
+        y = kvq.decode(planes, cfg, out_dtype=od)
+        torch.cuda.synchronize()
+        yn = y.float().cpu().numpy() if od != "f32" else y.cpu().numpy()
+        parity.compare_decode(yn, ref, od, f"{label} decode->{od}")
+    return rep, planes, cfg
+
+
+# --------------------------------------------------------------------------- #
+# the host-generated workloads, full size
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("key", ["tiny", "llama2", "isoquant"])
+def test_workload_full(key):
+    wl = workloads.WORKLOADS[key]
+    data = workloads.host_workload(key)
+    for case in wl.cases:
+        cb = gu.codebook_for(case)
+        rep, _, _ = run_case(case, data["inputs"][case.name], data["perm"], data["quat"], cb,
+                             out_dtypes=("f32", case.dtype), label=f"{key}.{case.name}")
+        say(f"  {dict(rep)}")
+
+
+# --------------------------------------------------------------------------- #
+# every (dtype, head_dim, bits, rotation, quantizer) at a small ragged shape
+# --------------------------------------------------------------------------- #
+COMBOS = list(itertools.product(["f16", "bf16", "f32"], [128, 256], [2, 3, 4], ["fwht", "so4", "none"],
+                                ["minmax", "lloyd"]))
+
+
+@pytest.mark.parametrize("dtype,d,bits,rot,quant", COMBOS,
+                         ids=["-".join(map(str, c)) for c in COMBOS])
+def test_combo_small(dtype, d, bits, rot, quant):
+    seed = zlib.crc32(f"{dtype}/{d}/{bits}/{rot}/{quant}".encode()) % 10000
+    g = {128: 64, 256: 32}[d] if bits != 3 else d
+    case = workloads.TensorCase(name="X", shape=(2, 37, 3, d), dtype=dtype, bits=bits, group_size=g,
+                                quant=quant, rot=rot, rope=(seed % 2 == 0), n_sink=2 if seed % 3 else 0,
+                                use_perm=(seed % 5 < 3), pos_offset=(seed % 7))
+    data = workloads.synth_case(case, seed)
+    cb = gu.codebook_for(case)
+    run_case(case, data["input"], data["perm"], data["quat"], cb, out_dtypes=("f32", "bf16"),
+             label=f"combo {dtype}/{d}/{bits}/{rot}/{quant}")
+
+
+@pytest.mark.parametrize("d,g", [(128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128), (256, 256)])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_group_sizes(d, g, bits):
+    case = workloads.TensorCase(name="X", shape=(3, 29, 5, d), dtype="bf16", bits=bits, group_size=g,
+                                quant="minmax", rot="fwht", rope=True, n_sink=3, use_perm=True)
+    data = workloads.synth_case(case, 100 + g + d + bits)
+    run_case(case, data["input"], data["perm"], None, None, label=f"group d={d} G={g} b={bits}")
+
+
+# --------------------------------------------------------------------------- #
+# shapes of the big workloads, reduced; edge cases
+# --------------------------------------------------------------------------- #
+def test_llama3_shape_small():
+    base = workloads.WORKLOADS["llama3"]
+    for name in ("K", "V"):
+        case = base.case(name).with_shape((3, 203, 8, 128))
+        data = workloads.synth_case(case, 7, outliers=(3, 15.0))
+        run_case(case, data["input"], data["perm"], None, None, out_dtypes=("f32", "bf16"),
+                 label=f"llama3-small.{name}")
+
+
+def test_widehead_shape_small():
+    base = workloads.WORKLOADS["widehead"]
+    for name in ("K", "V"):
+        case = base.case(name).with_shape((2, 77, 16, 256))
+        data = workloads.synth_case(case, 8, outliers=(13, 6.0))
+        run_case(case, data["input"], data["perm"], None, None, out_dtypes=("f32", "bf16"),
+                 label=f"widehead-small.{name}")
+
+
+@pytest.mark.parametrize("pos_offset,n_sink,t", [(0, 4, 3), (2, 4, 9), (3, 4, 1), (4, 4, 9), (0, 0, 5),
+                                                 (0, 64, 40), (30000, 4, 17)])
+def test_sinks_and_positions(pos_offset, n_sink, t):
+    case = workloads.TensorCase(name="K", shape=(2, t, 8, 128), dtype="bf16", bits=2, group_size=128,
+                                quant="minmax", rot="fwht", rope=True, n_sink=n_sink, use_perm=True,
+                                pos_offset=pos_offset)
+    data = workloads.synth_case(case, 11 + t, sink_token_scale=50.0)
+    run_case(case, data["input"], data["perm"], None, None, out_dtypes=("f32", "bf16"),
+             label=f"sinks p0={pos_offset} n={n_sink} T={t}")
+
+
+def test_large_positions_rope():
+    """RoPE angles at positions near 2^31 (fp64 angle reduction)."""
+    case = workloads.TensorCase(name="K", shape=(1, 40, 4, 128), dtype="f32", bits=4, group_size=32,
+                                quant="minmax", rot="fwht", rope=True, pos_offset=2 ** 31 - 40)
+    data = workloads.synth_case(case, 21)
+    run_case(case, data["input"], None, None, None, label="positions near 2^31")
+
+
+def test_degenerate_vectors():
+    """Zero and constant vectors (scale 0), fp16-exact constants, and a one-hot vector."""
+    d = 128
+    for quant, rot in (("minmax", "fwht"), ("minmax", "none"), ("lloyd", "so4"), ("lloyd", "fwht")):
+        case = workloads.TensorCase(name="X", shape=(1, 6, 4, d), dtype="f32", bits=3 if quant == "lloyd" else 2,
+                                    group_size=32, quant=quant, rot=rot, rope=False)
+        x = np.zeros(case.shape, dtype=np.float32)
+        x[0, 1] = 0.375
+        x[0, 2] = -2.0
+        x[0, 3, :, 5] = 1.0
+        x[0, 4] = np.arange(d, dtype=np.float32) / d
+        x[0, 5] = np.float32(1e-30)
+        rng = np.random.default_rng(3)
+        quat = workloads.unit_quaternions(d // 4, rng) if rot == "so4" else None
+        run_case(case, x, None, quat, gu.codebook_for(case), label=f"degenerate {quant}/{rot}", fraction=False)
+
+
+def test_empty_and_single():
+    for shape in ((0, 4, 4, 128), (1, 0, 8, 128), (1, 1, 1, 128), (1, 1, 1, 256)):
+        case = workloads.TensorCase(name="X", shape=shape, dtype="bf16", bits=2, group_size=128, quant="minmax",
+                                    rot="fwht", rope=True, n_sink=0)
+        data = workloads.synth_case(case, 1)
+        cfg = gu.make_config(case)
+        xt = gu.torch_input(data["input"], "bf16")
+        planes = kvq.encode(xt, cfg)
+        y = kvq.decode(planes, cfg)
+        torch.cuda.synchronize()
+        if np.prod(shape):
+            run_case(case, data["input"], label=f"single {shape}")
+        else:
+            assert y.numel() == 0
+
+
+def test_strided_head_shard():
+    """A tensor-parallel shard: one KV head of a [R, T, 8, D] cache, read through strides."""
+    d = 128
+    full = workloads.TensorCase(name="K", shape=(3, 45, 8, d), dtype="bf16", bits=2, group_size=128,
+                                quant="minmax", rot="fwht", rope=True, n_sink=4, use_perm=True)
+    data = workloads.synth_case(full, 31)
+    xt = gu.torch_input(data["input"], "bf16")
+    shard = xt[:, :, 5:6, :]
+    case = full.with_shape((3, 45, 1, d))
+    cfg = gu.make_config(case, data["perm"], strides=shard.stride()[:3])
+    planes = kvq.encode(shard, cfg)
+    torch.cuda.synchronize()
+    g = gu.planes_numpy(planes)
+    x_np = np.ascontiguousarray(data["input"][:, :, 5:6, :])
+    p = parity.params_for(case, data["perm"])
+    ora = oracle.encode(oracle.widen(x_np, "bf16"), p)
+    ora["sink_f64"] = parity.sink_f64(oracle.widen(x_np, "bf16"), p)
+    parity.compare_encode(g, ora, p, case.shape, "strided shard")
+
+
+def test_every_output_byte_written_and_deterministic():
+    """Planes prefilled with two different poison bytes come out identical (every byte,
+    including sink slots and code records, is written), and repeated runs are bit-identical."""
+    case = workloads.TensorCase(name="K", shape=(2, 50, 8, 128), dtype="bf16", bits=3, group_size=64,
+                                quant="minmax", rot="fwht", rope=True, n_sink=4, use_perm=True)
+    data = workloads.synth_case(case, 41, sink_token_scale=50.0)
+    cfg = gu.make_config(case, data["perm"])
+    xt = gu.torch_input(data["input"], "bf16")
+    outs = []
+    for poison in (0xAB, 0x00, 0xFF):
+        planes = gu.poison_planes(kvq.empty_planes(cfg), poison)
+        kvq.encode(xt, cfg, planes=planes)
+        torch.cuda.synchronize()
+        outs.append(gu.planes_numpy(planes))
+    for k in outs[0]:
+        if k == "sink":
+            continue  # slots of positions beyond T are not this call's to write
+        assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
+        assert np.array_equal(outs[0][k].view(np.uint8), outs[2][k].view(np.uint8)), k
+    # decode output fully written too
+    y1 = kvq.decode(kvq.encode(xt, cfg), cfg, out_dtype="bf16")
+    y2 = torch.full_like(y1, float("nan"))
+    kvq.decode(kvq.encode(xt, cfg), cfg, out_dtype="bf16", out=y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# --------------------------------------------------------------------------- #
+# full-size workloads on the GPU, sampled against the oracle
+# --------------------------------------------------------------------------- #
+def _sample_check(key, rows, tokens, out_dtype="bf16"):
+    wl = workloads.WORKLOADS[key]
+    say(f"[full] generating {key} on the GPU")
+    data = workloads.device_workload(key)
+    torch.cuda.synchronize()
+    for case in wl.cases:
+        x = data["inputs"][case.name]
+        cfg = gu.make_config(case, data["perm"])
+        say(f"[full] {key}.{case.name} encode/decode {tuple(case.shape)}")
+        planes = kvq.encode(x, cfg)
+        y = kvq.decode(planes, cfg, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        r_idx = torch.as_tensor(rows, device=x.device)
+        t_idx = torch.as_tensor(tokens, device=x.device)
+        xs = x.index_select(0, r_idx).index_select(1, t_idx)
+        sub = case.with_shape((len(rows), len(tokens), case.shape[2], case.shape[3]))
+        x_np = gu.raw_numpy(xs, case.dtype)
+        x64 = oracle.widen(x_np, case.dtype)
+        # oracle on the sampled vectors at their true positions: token blocks are contiguous
+        # runs, so encode each run with its own position offset
+        g_all = {k: v.index_select(0, r_idx).index_select(1, t_idx) if v.dim() == 4 and k != "sink" else v
+                 for k, v in planes.items()}
+        g = gu.planes_numpy(g_all)
+        if "sink" in planes:
+            g["sink"] = gu.planes_numpy({"s": planes["sink"].index_select(0, r_idx)})["s"]
+        runs = []
+        start = 0
+        for i in range(1, len(tokens) + 1):
+            if i == len(tokens) or tokens[i] != tokens[i - 1] + 1:
+                runs.append((start, i))
+                start = i
+        ys = y.index_select(0, r_idx).index_select(1, t_idx).float().cpu().numpy()
+        for a, b in runs:
+            c2 = workloads.TensorCase(**{**case.__dict__, "shape": (len(rows), b - a, case.shape[2], case.shape[3]),
+                                         "pos_offset": tokens[a]})
+            p = parity.params_for(c2, data["perm"])
+            ora = oracle.encode(x64[:, a:b], p)
+            if c2.n_sink:
+                ora["sink_f64"] = parity.sink_f64(x64[:, a:b], p)
+            gsub = {k: (v[:, a:b] if k != "sink" else v) for k, v in g.items()}
+            parity.compare_encode(gsub, ora, p, c2.shape, f"{key}.{case.name} tokens {tokens[a]}..{tokens[b-1]}")
+            ref = oracle.decode(gsub, p, c2.shape)
+            parity.compare_decode(ys[:, a:b], ref, out_dtype, f"{key}.{case.name} decode")
+        del planes, y
+        torch.cuda.empty_cache()
+    say(f"[full] {key} ok")
+
+
+def test_llama3_full_size_sampled():
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 1, 63, 127] + rng.integers(0, 128, 4).tolist()))
+    tokens = list(range(0, 40)) + list(range(16000, 16016)) + list(range(32760, 32768))
+    _sample_check("llama3", rows, tokens)
+
+
+def test_widehead_full_size_sampled():
+    rng = np.random.default_rng(6)
+    rows = sorted(set([0, 31] + rng.integers(0, 32, 3).tolist()))
+    tokens = list(range(0, 24)) + list(range(8190, 8200)) + list(range(16380, 16384))
+    _sample_check("widehead", rows, tokens)
+
+
+def test_zz_session_tie_fraction():
+    """Across every comparison above, code mismatches (all at rounding ties) stay <= 1e-5."""
+    s = parity.SESSION
+    say(f"[session] {s['tie_mismatches']} tie mismatches in {s['codes']} codes")
+    assert s["tie_mismatches"] <= parity.CODE_MISMATCH_MAX * max(s["codes"], 1)
