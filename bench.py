@@ -48,7 +48,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens per row in the CPU sample (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -70,36 +70,37 @@ def traffic_from_profile(kernel_name: str):
     return int(m.group(1)) if m else None
 
 
-def cpu_baseline(inputs, cases, perm, n_tokens):
-    """Time the CPU oracle (single thread) on rows 0..1, tokens 0..n_tokens-1, all heads, K and V."""
+def cpu_baseline(inputs, cases, perm, budget_s: float, max_rows: int):
+    """Time the CPU oracle (one thread) on whole rows of the cache -- all 32768 tokens x 8
+    heads of row r of K, then of V, for r = 0, 1, ... -- until ``budget_s`` of CPU time
+    has been spent or ``max_rows`` rows are done.  Returns (vectors, seconds, rows)."""
     import numpy as np
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+    import torch
+    from threadpoolctl import threadpool_limits
+
     import oracle
     from oracle.codec import CodecParams
 
     n_vec = 0
     t_total = 0.0
-    rows = 2
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
-        for case in cases:
-            x = inputs[case.name][:rows, :n_tokens]
-            raw = x.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
-            p = CodecParams(bits=case.bits, group_size=case.group_size, rope=case.rope, n_sink=case.n_sink,
-                            perm=perm if case.use_perm else None)
-            t0 = time.perf_counter()
-            x64 = oracle.widen(raw, "bf16")
-            planes = oracle.encode(x64, p)
-            oracle.decode(planes, p, x64.shape)
-            t_total += time.perf_counter() - t0
-            n_vec += int(np.prod(raw.shape[:3]))
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    return n_vec, t_total
+    rows_done = 0
+    with threadpool_limits(limits=1):
+        for r in range(max_rows):
+            for case in cases:
+                raw = inputs[case.name][r:r + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+                p = CodecParams(bits=case.bits, group_size=case.group_size, rope=case.rope, n_sink=case.n_sink,
+                                perm=perm if case.use_perm else None)
+                t0 = time.perf_counter()
+                x64 = oracle.widen(raw, "bf16")
+                planes = oracle.encode(x64, p)
+                oracle.decode(planes, p, x64.shape)
+                t_total += time.perf_counter() - t0
+                n_vec += int(np.prod(raw.shape[:3]))
+                del x64, planes
+            rows_done += 1
+            if t_total >= budget_s:
+                break
+    return n_vec, t_total, rows_done
 
 
 def main():
@@ -203,14 +204,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        n_tokens = args.cpu_tokens or 256
-        nv, tc = cpu_baseline(data["inputs"], wl.cases, perm, n_tokens)
-        if not args.cpu_tokens and tc < 8.0:  # scale the sample to ~10-20 s of CPU work
-            n_tokens = min(32768, int(n_tokens * max(1.0, 12.0 / max(tc, 1e-3))))
-            nv, tc = cpu_baseline(data["inputs"], wl.cases, perm, n_tokens)
+        nv, tc, nrows = cpu_baseline(data["inputs"], wl.cases, perm, args.cpu_seconds, 16)
         cpu = {"value": round(nv / tc, 1), "unit": "vectors/s", "cores": 1, "kind": "oracle",
-               "sample": f"{WORKLOAD} K and V, rows 0-1, tokens 0-{n_tokens - 1}, all 8 heads "
-                         f"({nv} vectors incl. sinks), encode+decode, float64 numpy, 1 thread",
+               "sample": f"{WORKLOAD} K and V rows 0-{nrows - 1}, all 32768 tokens x 8 heads ({nv} vectors, "
+                         f"sinks included), encode+decode, float64 numpy, 1 thread",
                "seconds": round(tc, 2)}
 
     out = {

@@ -76,7 +76,7 @@ typedef struct kvq_config {
   int32_t dtype;        /* kvq_dtype of the encode input x                            */
   int64_t rows;         /* R: batch rows (e.g. layers x batch folded together)        */
   int64_t tokens;       /* T: token positions                                         */
-  int64_t heads;        /* H: KV heads                                                */
+  int64_t heads;        /* H: KV heads, at most 32768                                 */
   int64_t head_dim;     /* D: 128 or 256                                              */
   int64_t stride_r;     /* encode-input strides in ELEMENTS; D is always contiguous.  */
   int64_t stride_t;     /*   all three 0 = contiguous [R,T,H,D].  Each must be a      */

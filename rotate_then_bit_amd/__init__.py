@@ -77,6 +77,15 @@ def library_path() -> str:
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m rotate_then_bit_amd.build`")
+    # The library must run on the same HIP runtime as the memory and streams it is
+    # handed.  PyTorch ships its own libamdhip64 under the system one's soname: with
+    # torch loaded first the dynamic linker binds libkvq.so to that copy; loaded the
+    # other way round, the process ends up with two HIP runtimes, and the library's
+    # calls go to one that owns no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(_LIB_PATH)
     lib.kvq_abi_version.restype = ctypes.c_int32
     lib.kvq_validate.argtypes = [ctypes.POINTER(_Config)]

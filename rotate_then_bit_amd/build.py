@@ -19,12 +19,14 @@ LIB = os.path.join(HERE, "libkvq.so")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 # Packed FP32 VALU ops are disabled for the device code: the compiler would
-# otherwise form v_pk_{add,mul,fma}_f32 from ordinary float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# otherwise form v_pk_{add,mul,fma}_f32 from ordinary float code.  The codec
+# requires finite inputs, so NaN semantics are relaxed (min/max then need no
+# operand canonicalisation).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
 
 # translation units: (source, extra defines)
-KERNEL_UNITS = [("kvq_kernels.hip", [f"-DKVQ_UNIT={i}"]) for i in range(6)]
+KERNEL_UNITS = [("kvq_kernels.hip", [f"-DKVQ_UNIT={i}"]) for i in range(12)]
 
 
 def _hipcc() -> str:

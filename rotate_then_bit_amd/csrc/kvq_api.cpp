@@ -80,6 +80,7 @@ kvq_status check_config(const kvq_config* cfg, Derived* dv) {
       n > (int64_t(1) << 50))
     return fail(KVQ_ERR_SHAPE, "tensor too large");
   if (th >= (int64_t(1) << 31)) return fail(KVQ_ERR_SHAPE, "tokens*heads must be below 2^31");
+  if (cfg->heads > 32768) return fail(KVQ_ERR_SHAPE, "heads %lld (at most 32768)", (long long)cfg->heads);
   if (cfg->rope != 0 && cfg->rope != 1) return fail(KVQ_ERR_PARAM, "rope must be 0 or 1");
   if (cfg->rope && !(isfinite(cfg->rope_base) && cfg->rope_base > 1.0))
     return fail(KVQ_ERR_PARAM, "rope_base must be finite and > 1");
@@ -107,6 +108,13 @@ kvq_status check_config(const kvq_config* cfg, Derived* dv) {
     dv->sr = cfg->stride_r;
     dv->st = cfg->stride_t;
     dv->sh = cfg->stride_h;
+  }
+  // the kernels address a wave's 16 (or 8) vectors of one row from a common base with
+  // 32-bit lane offsets: 16 token strides plus a head span must stay below 2^31 bytes
+  {
+    const double span = (16.0 * (double)dv->st + (double)std::max<int64_t>(cfg->heads - 1, 0) * (double)dv->sh +
+                         (double)d) * es;
+    if (span >= 2147483648.0) return fail(KVQ_ERR_SHAPE, "token/head strides too large (16 token strides must span < 2 GiB)");
   }
 
   // parameters
@@ -178,21 +186,15 @@ kvq_status check_planes(const kvq_config* cfg, const Derived& dv, const kvq_plan
   return KVQ_OK;
 }
 
-// Work decomposition: one wave per (tile of VPW columns, chunk of rows).
-void plan_work(const kvq_config* cfg, bool encode, kvq::CodecArgs* a) {
+// Work decomposition: an item is (row, tile of VPW consecutive (token, head) columns),
+// numbered row-major; the launcher sizes a persistent grid and each wave walks the
+// items w, w + n_waves, ...  The waves resident at any moment then cover one narrow,
+// advancing address window, which streams fastest on MI355X.
+void plan_work(const kvq_config* cfg, kvq::CodecArgs* a) {
   const int vpw = cfg->head_dim == 128 ? 16 : 8;
   const int64_t ncols = cfg->tokens * cfg->heads;
-  const int64_t n_tiles = (ncols + vpw - 1) / vpw;
-  const int64_t rows = std::max<int64_t>(cfg->rows, 1);
-  // enough waves to fill 256 CUs many times over; RoPE tiles amortise their
-  // angle set-up over more rows
-  const int64_t target_items = encode && cfg->rope ? 65536 : 262144;
-  int64_t rpi = (rows * n_tiles + target_items - 1) / target_items;
-  rpi = std::max<int64_t>(1, std::min<int64_t>(rpi, rows));
-  a->rows_per_item = (int32_t)rpi;
-  a->n_tiles = (int32_t)n_tiles;
-  a->n_row_chunks = (int32_t)((rows + rpi - 1) / rpi);
-  if (cfg->rows == 0) a->n_row_chunks = 0;
+  a->n_tiles = (ncols + vpw - 1) / vpw;
+  a->n_items = cfg->rows * a->n_tiles;
 }
 
 void fill_args(const kvq_config* cfg, const Derived& dv, kvq::CodecArgs* a) {
@@ -258,13 +260,19 @@ kvq_status kvq_encode(const kvq_config* cfg, const void* x, const kvq_planes* ou
   a.zero = static_cast<uint16_t*>(out->zero);
   a.norm = static_cast<float*>(out->norm);
   a.sink = static_cast<uint16_t*>(out->sink);
-  plan_work(cfg, true, &a);
-  const int d = (int)cfg->head_dim;
+  plan_work(cfg, &a);
+  const bool d128 = cfg->head_dim == 128;
   int err;
   switch (cfg->dtype) {
-    case KVQ_F16: err = kvq::launch_encode_f16(d, cfg->bits, cfg->rot, cfg->quant, a, stream); break;
-    case KVQ_BF16: err = kvq::launch_encode_bf16(d, cfg->bits, cfg->rot, cfg->quant, a, stream); break;
-    default: err = kvq::launch_encode_f32(d, cfg->bits, cfg->rot, cfg->quant, a, stream); break;
+    case KVQ_F16:
+      err = (d128 ? kvq::launch_encode_f16_d128 : kvq::launch_encode_f16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
+    case KVQ_BF16:
+      err = (d128 ? kvq::launch_encode_bf16_d128 : kvq::launch_encode_bf16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
+    default:
+      err = (d128 ? kvq::launch_encode_f32_d128 : kvq::launch_encode_f32_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
   }
   if (err != 0) return fail(KVQ_ERR_DEVICE, "encode launch failed: %s", kvq::device_error_string(err));
   return ok();
@@ -287,13 +295,19 @@ kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int3
   a.zero = static_cast<uint16_t*>(in->zero);
   a.norm = static_cast<float*>(in->norm);
   a.sink = static_cast<uint16_t*>(in->sink);
-  plan_work(cfg, false, &a);
-  const int d = (int)cfg->head_dim;
+  plan_work(cfg, &a);
+  const bool d128 = cfg->head_dim == 128;
   int err;
   switch (y_dtype) {
-    case KVQ_F16: err = kvq::launch_decode_f16(d, cfg->bits, cfg->rot, cfg->quant, a, stream); break;
-    case KVQ_BF16: err = kvq::launch_decode_bf16(d, cfg->bits, cfg->rot, cfg->quant, a, stream); break;
-    default: err = kvq::launch_decode_f32(d, cfg->bits, cfg->rot, cfg->quant, a, stream); break;
+    case KVQ_F16:
+      err = (d128 ? kvq::launch_decode_f16_d128 : kvq::launch_decode_f16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
+    case KVQ_BF16:
+      err = (d128 ? kvq::launch_decode_bf16_d128 : kvq::launch_decode_bf16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
+    default:
+      err = (d128 ? kvq::launch_decode_f32_d128 : kvq::launch_decode_f32_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
   }
   if (err != 0) return fail(KVQ_ERR_DEVICE, "decode launch failed: %s", kvq::device_error_string(err));
   return ok();

@@ -30,27 +30,40 @@ struct CodecArgs {
   int32_t n_sink;
   int32_t rope;
   int32_t use_perm;
-  // work decomposition: items = n_tiles * n_row_chunks, one wave per item
-  int32_t rows_per_item;
-  int32_t n_tiles;
-  int32_t n_row_chunks;
-  int32_t xcd_remap;
+  // work decomposition: an item is (row, tile of VPW consecutive (token, head)
+  // columns), items are numbered row-major, and wave w of the grid takes items
+  // w, w + n_waves, ...  The step constants advance a wave's cursor without division.
+  int64_t n_tiles;     // tiles per row
+  int64_t n_items;     // rows * n_tiles
+  int64_t n_waves;     // waves in the grid
+  int64_t step_rows;   // n_waves / n_tiles
+  int64_t step_tiles;  // n_waves % n_tiles
+  int64_t step_tok;    // step_tiles * VPW = step_tok * heads + step_head
+  int64_t step_head;
+  int64_t wrap_tok;    // n_tiles * VPW = wrap_tok * heads + wrap_head
+  int64_t wrap_head;
+  uint32_t heads_magic;  // ceil(2^32 / heads) for heads >= 2 (0 when heads == 1)
   // parameters
   uint8_t perm[kMaxHeadDim];
   float quat[kMaxHeadDim / 4 * 8];
   float codebook[kMaxCodebook];
 };
 
-// Launch helpers, one per (direction, dtype), defined in kvq_kernels.hip.
+// Launch helpers, one per (direction, dtype, head_dim), defined in kvq_kernels.hip.
 // Each returns a hipError_t as int (0 = success).
-#define KVQ_DECLARE_LAUNCH(NAME) \
-  int NAME(int head_dim, int bits, int rot, int quant, const CodecArgs& a, void* stream);
-KVQ_DECLARE_LAUNCH(launch_encode_f16)
-KVQ_DECLARE_LAUNCH(launch_encode_bf16)
-KVQ_DECLARE_LAUNCH(launch_encode_f32)
-KVQ_DECLARE_LAUNCH(launch_decode_f16)
-KVQ_DECLARE_LAUNCH(launch_decode_bf16)
-KVQ_DECLARE_LAUNCH(launch_decode_f32)
+#define KVQ_DECLARE_LAUNCH(NAME) int NAME(int bits, int rot, int quant, const CodecArgs& a, void* stream);
+KVQ_DECLARE_LAUNCH(launch_encode_f16_d128)
+KVQ_DECLARE_LAUNCH(launch_encode_f16_d256)
+KVQ_DECLARE_LAUNCH(launch_encode_bf16_d128)
+KVQ_DECLARE_LAUNCH(launch_encode_bf16_d256)
+KVQ_DECLARE_LAUNCH(launch_encode_f32_d128)
+KVQ_DECLARE_LAUNCH(launch_encode_f32_d256)
+KVQ_DECLARE_LAUNCH(launch_decode_f16_d128)
+KVQ_DECLARE_LAUNCH(launch_decode_f16_d256)
+KVQ_DECLARE_LAUNCH(launch_decode_bf16_d128)
+KVQ_DECLARE_LAUNCH(launch_decode_bf16_d256)
+KVQ_DECLARE_LAUNCH(launch_decode_f32_d128)
+KVQ_DECLARE_LAUNCH(launch_decode_f32_d256)
 #undef KVQ_DECLARE_LAUNCH
 const char* device_error_string(int err);
 

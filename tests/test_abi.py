@@ -159,3 +159,16 @@ def test_host_lloyd_max_rejects_bad_arguments():
         kvq.lloyd_max_gaussian(5, 1.0)
     with pytest.raises(kvq.KvqError):
         kvq.lloyd_max_gaussian(2, -1.0)
+
+
+def test_single_hip_runtime_when_binding_imported_first():
+    """Importing the binding before torch must still leave one HIP runtime in the process
+    (torch's copy, which owns the caller's memory and streams)."""
+    import subprocess
+    import sys
+    code = ("import rotate_then_bit_amd, torch\n"
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(libs))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
