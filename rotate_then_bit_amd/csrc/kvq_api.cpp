@@ -186,10 +186,10 @@ kvq_status check_planes(const kvq_config* cfg, const Derived& dv, const kvq_plan
   return KVQ_OK;
 }
 
-// Work decomposition: an item is (row, tile of VPW consecutive (token, head) columns),
-// numbered row-major; the launcher sizes a persistent grid and each wave walks the
-// items w, w + n_waves, ...  The waves resident at any moment then cover one narrow,
-// advancing address window, which streams fastest on MI355X.
+// Work decomposition: an item is (tile of VPW consecutive (token, head) columns, row),
+// numbered tile-major; the launcher sizes a persistent grid and gives each wave one
+// contiguous range of items, so a wave keeps the same columns (and RoPE angles) while it
+// walks down the rows.
 void plan_work(const kvq_config* cfg, kvq::CodecArgs* a) {
   const int vpw = cfg->head_dim == 128 ? 16 : 8;
   const int64_t ncols = cfg->tokens * cfg->heads;

@@ -30,19 +30,15 @@ struct CodecArgs {
   int32_t n_sink;
   int32_t rope;
   int32_t use_perm;
-  // work decomposition: an item is (row, tile of VPW consecutive (token, head)
-  // columns), items are numbered row-major, and wave w of the grid takes items
-  // w, w + n_waves, ...  The step constants advance a wave's cursor without division.
+  // work decomposition: an item is (tile of VPW consecutive (token, head) columns, row).
+  // With W waves in the grid, wave w first takes tiles w, w + W, ..., w + (K-1) W (all
+  // rows of each, K = n_tiles / W), so the waves in flight cover W adjacent tiles of one
+  // row at a time; the remaining n_tiles - K W tiles are split into equal contiguous runs
+  // of (tile, row) items, one per wave.
   int64_t n_tiles;     // tiles per row
   int64_t n_items;     // rows * n_tiles
-  int64_t n_waves;     // waves in the grid
-  int64_t step_rows;   // n_waves / n_tiles
-  int64_t step_tiles;  // n_waves % n_tiles
-  int64_t step_tok;    // step_tiles * VPW = step_tok * heads + step_head
-  int64_t step_head;
-  int64_t wrap_tok;    // n_tiles * VPW = wrap_tok * heads + wrap_head
-  int64_t wrap_head;
-  uint32_t heads_magic;  // ceil(2^32 / heads) for heads >= 2 (0 when heads == 1)
+  int64_t n_waves;     // waves in the grid (set by the launcher)
+  int32_t trig_rows;   // RoPE table rows per wave: tokens one tile can span (set by the launcher)
   // parameters
   uint8_t perm[kMaxHeadDim];
   float quat[kMaxHeadDim / 4 * 8];

@@ -1,26 +1,32 @@
 // HIP kernels of the rotation + low-bit KV-cache codec, written for gfx950 (CDNA4).
 //
-// Work layout.  A sub-wavefront of LV = D/32 lanes owns one token-head vector
-// (LV = 4 at d = 128, 8 at d = 256), so a wave64 holds VPW = 64/LV vectors.
-// Each lane holds 32 elements as 4 chunks of 8 consecutive channels; chunk k of
-// lane l covers channels e = (k*LV + l)*8 + s, s = 0..7.  This interleave makes
-// every 16-byte load or store of a 16-bit tensor coalesced across the wave
-// (VPW consecutive vectors are 16*VPW*LV contiguous bytes per instruction).
+// Lane layout.  A sub-wavefront of LV = D/32 lanes owns one token-head vector (LV = 4
+// at d = 128, 8 at d = 256), so a wave64 holds VPW = 64/LV vectors.  Lane l of a
+// vector holds the 32 consecutive channels 32l .. 32l + 31 in slots 0..31.  A lane's
+// packed codes are then one contiguous run of 4*bits bytes, so code planes move with a
+// single 8/12/16-byte access per lane and the wave covers whole records.
 //
-// A wave processes a tile of VPW consecutive (token, head) columns for a
-// range of rows; RoPE angles depend only on the column, so they are computed
-// once per tile and kept in registers across the rows.
+// Work.  An item is a tile of VPW consecutive (token, head) columns of one row.  Each
+// wave of a persistent grid of W waves takes tile w, then w + W, w + 2W, ..., and walks
+// all rows of each, with the next item's loads in flight while it computes the current
+// one; the tiles left over after the last full round of W are split evenly as runs of
+// (tile, row) items.  So the waves in flight read W adjacent tiles of one row at a time,
+// and a wave keeps the same columns -- and the same RoPE angles -- while it moves down
+// the rows.
 //
-// Walsh-Hadamard: the channel index bits split into in-lane bits (s and k) and
-// lane bits (l).  In-lane butterflies are plain VALU adds; lane-bit butterflies
-// use a DPP-fused v_fmac (partner * m + own) for lane xor 1/2 and ds_swizzle for
-// xor 4.  The fmac form leaves lanes with a set bit holding the negated value;
-// the sign after all lane stages is (-1)^popcount(l) and is folded into the
-// quantization scale (encode) or the output scale (decode).
+// Walsh-Hadamard.  The channel index splits into 5 in-lane bits (slots) and 2 or 3
+// lane bits.  In-lane butterflies are plain VALU adds; lane-bit butterflies are a
+// v_fmac with a DPP quad_perm operand (lane xor 1, xor 2) or a ds_swizzle partner
+// (xor 4): own + m * partner with m = +-1 per lane.  With m = -1 on the lane whose bit
+// is set, lane l ends up holding (-1)^popcount(l) times the true coefficient; that sign
+// is folded into the quantization scale.  With m = +1 there and inputs pre-multiplied
+// by (-1)^popcount(l), the lanes hold the true coefficients (used by the decoder).
 //
-// LDS holds only parameters (RoPE frequencies, SO(4) matrices, the Lloyd-Max
-// codebook) and, when a channel permutation is used, a per-wave scratch through
-// which the permutation is applied (a gather of 32 values per lane).
+// LDS holds parameters (RoPE frequencies, SO(4) matrices) and per-wave staging: the
+// cos/sin table of the tokens of the wave's current tile, the channel permutation (a
+// gather or scatter of 32 values per lane through one row per vector), and the
+// decoder's output, which is written per lane and read back so that every global store
+// of the wave covers 1 KiB of contiguous output.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -37,27 +43,45 @@ enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
 enum { ROT_NONE = 0, ROT_FWHT = 1, ROT_SO4 = 2 };
 enum { Q_MINMAX = 0, Q_LLOYD = 1 };
 
-constexpr int kNC = 4;  // 8-element chunks per lane (32 elements per lane)
-
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 template <int D>
 struct Geo {
-  static constexpr int LV = D / 32;                 // lanes per vector
-  static constexpr int LVB = (LV == 4) ? 2 : 3;      // log2(LV)
-  static constexpr int VPW = 64 / LV;                // vectors per wave
-  static constexpr int STRIDE = D + 4;               // floats per vector in the perm scratch
+  static constexpr int LV = D / 32;             // lanes per vector
+  static constexpr int LVB = (LV == 4) ? 2 : 3;  // log2(LV)
+  static constexpr int VPW = 64 / LV;            // vectors per wave
 };
 
-// Per-wave LDS scratch: VPW vectors of STRIDE floats for the permutation, which in the
-// encoder first holds the RoPE cos/sin table of the wave's current tile (at most VPW
-// tokens x D/2 pairs of float2 = VPW * D * 4 bytes, less than the permutation's need).
+// Per-wave LDS staging: one row per vector of the wave.  A row holds the vector as
+// floats (D * 4 bytes) plus 16 bytes of padding, which staggers the rows across banks.
 template <int D>
-constexpr int scratch_wave_bytes() {
-  return Geo<D>::VPW * Geo<D>::STRIDE * 4;
+constexpr int row_bytes() {
+  return D * 4 + 16;
 }
-static_assert(Geo<128>::VPW * 128 * 4 <= scratch_wave_bytes<128>(), "trig table fits");
-static_assert(Geo<256>::VPW * 256 * 4 <= scratch_wave_bytes<256>(), "trig table fits");
+template <int D>
+constexpr int stage_wave_bytes() {
+  return Geo<D>::VPW * row_bytes<D>();
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_f32*)p;
+}
+__device__ __forceinline__ float lds_ld(uint32_t addr) { return *(const lds_f32*)(uintptr_t)addr; }
+__device__ __forceinline__ void lds_st(uint32_t addr, float v) { *(lds_f32*)(uintptr_t)addr = v; }
+__device__ __forceinline__ u32x4_t lds_ld4(uint32_t addr) { return *(const lds_u32x4*)(uintptr_t)addr; }
+__device__ __forceinline__ void lds_st4(uint32_t addr, u32x4_t v) { *(lds_u32x4*)(uintptr_t)addr = v; }
+
+// Orders this wave's LDS accesses before and after the call (LDS ops of one wave are
+// executed in order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // ---------------------------------------------------------------------------
 // cross-lane primitives
@@ -65,10 +89,11 @@ static_assert(Geo<256>::VPW * 256 * 4 <= scratch_wave_bytes<256>(), "trig table 
 #define KVQ_QP1 " quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
 #define KVQ_QP2 " quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
 
-// v <- partner(v) * m + v for 8 values, partner = lane xor 1.  The leading
-// s_nop covers the VALU-write -> DPP-read hazard on the first operand.
+// v <- partner(v) * m + v for 8 values, partner = lane xor 1.  The leading s_nop gives
+// the 5 wait states a DPP read needs after an EXEC write (2 after a VALU write of its
+// operands), since the compiler does not look inside the asm.
 __device__ __forceinline__ void fmac_x1(float* v, float m) {
-  asm("s_nop 1\n\t"
+  asm("s_nop 4\n\t"
       "v_fmac_f32_dpp %0, %0, %8" KVQ_QP1 "\n\t"
       "v_fmac_f32_dpp %1, %1, %8" KVQ_QP1 "\n\t"
       "v_fmac_f32_dpp %2, %2, %8" KVQ_QP1 "\n\t"
@@ -83,7 +108,7 @@ __device__ __forceinline__ void fmac_x1(float* v, float m) {
 }
 
 __device__ __forceinline__ void fmac_x2(float* v, float m) {
-  asm("s_nop 1\n\t"
+  asm("s_nop 4\n\t"
       "v_fmac_f32_dpp %0, %0, %8" KVQ_QP2 "\n\t"
       "v_fmac_f32_dpp %1, %1, %8" KVQ_QP2 "\n\t"
       "v_fmac_f32_dpp %2, %2, %8" KVQ_QP2 "\n\t"
@@ -103,27 +128,27 @@ __device__ __forceinline__ float swz_x4(float v) {
 }
 
 __device__ __forceinline__ float min_x1(float v) {
-  asm("s_nop 1\n\tv_min_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
+  asm("s_nop 4\n\tv_min_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float min_x2(float v) {
-  asm("s_nop 1\n\tv_min_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
+  asm("s_nop 4\n\tv_min_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float max_x1(float v) {
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
+  asm("s_nop 4\n\tv_max_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float max_x2(float v) {
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
+  asm("s_nop 4\n\tv_max_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float add_x1(float v) {
-  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
+  asm("s_nop 4\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float add_x2(float v) {
-  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
+  asm("s_nop 4\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
   return v;
 }
 
@@ -143,140 +168,52 @@ __device__ __forceinline__ float vec_max(float v) {
   return v;
 }
 
-// ---------------------------------------------------------------------------
-// Walsh-Hadamard, unnormalised, on the 32 values of a lane plus the lane bits.
-// On return lane l holds (-1)^popcount(l) times the true coefficients.
-// ---------------------------------------------------------------------------
-template <int LV, bool FIRST_DONE = false>
-__device__ __forceinline__ void fwht_lane(float* v, int l) {
-  // slot bits (s = 0..7 within each chunk); the bit-0 stage may already have been
-  // applied while widening 16-bit input pairs
-#pragma unroll
-  for (int hb = FIRST_DONE ? 2 : 1; hb < 8; hb <<= 1) {
-#pragma unroll
-    for (int k = 0; k < kNC; ++k) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (s & hb) continue;
-        float a = v[8 * k + s], b = v[8 * k + s + hb];
-        v[8 * k + s] = a + b;
-        v[8 * k + s + hb] = a - b;
-      }
-    }
-  }
-  // chunk bits (k = 0..3)
-#pragma unroll
-  for (int hk = 1; hk < kNC; hk <<= 1) {
-#pragma unroll
-    for (int k = 0; k < kNC; ++k) {
-      if (k & hk) continue;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        float a = v[8 * k + s], b = v[8 * (k + hk) + s];
-        v[8 * k + s] = a + b;
-        v[8 * (k + hk) + s] = a - b;
-      }
-    }
-  }
-  // lane bits
-  const float m1 = (l & 1) ? -1.0f : 1.0f;
-  const float m2 = (l & 2) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int k = 0; k < kNC; ++k) fmac_x1(v + 8 * k, m1);
-#pragma unroll
-  for (int k = 0; k < kNC; ++k) fmac_x2(v + 8 * k, m2);
-  if constexpr (LV == 8) {
-    const float m4 = (l & 4) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(swz_x4(v[i]), m4, v[i]);
-  }
-}
-
 __device__ __forceinline__ float lane_sign(int l) {
   return (__builtin_popcount(l) & 1) ? -1.0f : 1.0f;
 }
 
 // ---------------------------------------------------------------------------
-// dtype conversions
+// Walsh-Hadamard, unnormalised, on the 32 slots of a lane (from slot bit FIRST on)
+// plus the lane bits, with per-lane multipliers m1, m2, m4 for the lane stages.
 // ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ void load_chunk(const void* base, int64_t off, float* v) {
-  if constexpr (DT == DT_F32) {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+template <int LV, int FIRST = 0>
+__device__ __forceinline__ void fwht_lane(float* v, float m1, float m2, float m4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == DT_BF16) {
-        v[2 * i] = __uint_as_float(ws[i] << 16);
-        v[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
-      } else {
-        v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[i] & 0xffffu));
-        v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[i] >> 16));
-      }
+  for (int hb = 1 << FIRST; hb < 32; hb <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i & hb) continue;
+      const float a = v[i], b = v[i + hb];
+      v[i] = a + b;
+      v[i + hb] = a - b;
     }
   }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) fmac_x1(v + 8 * k, m1);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) fmac_x2(v + 8 * k, m2);
+  if constexpr (LV == 8) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(swz_x4(v[i]), m4, v[i]);
+  }
 }
+
+// ---------------------------------------------------------------------------
+// dtype conversions
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2_t f = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
-
-template <int DT>
-__device__ __forceinline__ void store_chunk(void* base, int64_t off, const float* v) {
-  if constexpr (DT == DT_F32) {
-    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off);
-    p[0] = make_float4(v[0], v[1], v[2], v[3]);
-    p[1] = make_float4(v[4], v[5], v[6], v[7]);
-  } else {
-    uint32_t ws[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == DT_BF16)
-        ws[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-      else
-        ws[i] = f16_bits(v[2 * i]) | (f16_bits(v[2 * i + 1]) << 16);
-    }
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + off) =
-        make_uint4(ws[0], ws[1], ws[2], ws[3]);
-  }
-}
-
-// 8 elements to ``p``.  Plain stores: with this kernel's store pattern (each wave64
-// store covers a 64-byte run in each of 16 vector records) non-temporal stores were
-// measured at about half the bandwidth of ordinary ones on MI355X.
-template <int DT>
-__device__ __forceinline__ void store_chunk_at(char* p, const float* v) {
-  if constexpr (DT == DT_F32) {
-    u32x4_t a, b;
-    a.x = __float_as_uint(v[0]); a.y = __float_as_uint(v[1]); a.z = __float_as_uint(v[2]); a.w = __float_as_uint(v[3]);
-    b.x = __float_as_uint(v[4]); b.y = __float_as_uint(v[5]); b.z = __float_as_uint(v[6]); b.w = __float_as_uint(v[7]);
-    reinterpret_cast<u32x4_t*>(p)[0] = a;
-    reinterpret_cast<u32x4_t*>(p)[1] = b;
-  } else {
-    u32x4_t w;
-    if constexpr (DT == DT_BF16) {
-      w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
-      w.z = pack_bf16x2(v[4], v[5]); w.w = pack_bf16x2(v[6], v[7]);
-    } else {
-      w.x = f16_bits(v[0]) | (f16_bits(v[1]) << 16); w.y = f16_bits(v[2]) | (f16_bits(v[3]) << 16);
-      w.z = f16_bits(v[4]) | (f16_bits(v[5]) << 16); w.w = f16_bits(v[6]) | (f16_bits(v[7]) << 16);
-    }
-    *reinterpret_cast<u32x4_t*>(p) = w;
-  }
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) { return f16_bits(a) | (f16_bits(b) << 16); }
+__device__ __forceinline__ float f16_value(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
 // fp16 with directed rounding, from the IEEE bit pattern of the nearest value.
@@ -292,78 +229,107 @@ __device__ __forceinline__ uint32_t f16_round_up(float x) {
   if ((float)h < x) b = (b & 0x8000u) ? (b == 0x8000u ? 0x0001u : b - 1u) : b + 1u;
   return b;
 }
-__device__ __forceinline__ float f16_value(uint32_t b) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+
+// One lane's 32 channels of one vector as stored: 4 x 16 bytes for 16-bit types,
+// 8 x 16 bytes for float.
+template <int DT>
+struct RawRow {
+  static constexpr int NW = (DT == DT_F32) ? 8 : 4;
+  u32x4_t w[NW];
+};
+
+// Plain (temporal) loads: the four 16-byte loads of a lane hit the same cache lines as
+// its neighbours' (each wave instruction covers a 16-byte slice of every 64-byte lane
+// run), and with non-temporal hints the lines were fetched from HBM more than once.
+template <int DT>
+__device__ __forceinline__ void load_row(RawRow<DT>& raw, const char* p) {
+#pragma unroll
+  for (int k = 0; k < RawRow<DT>::NW; ++k) raw.w[k] = reinterpret_cast<const u32x4_t*>(p)[k];
 }
 
-// ---------------------------------------------------------------------------
-// bit-packing of one chunk (8 codes, 8*BITS bits, byte offset chunk*BITS)
-// ---------------------------------------------------------------------------
-template <int BITS>
-__device__ __forceinline__ void store_codes(uint8_t* rec, int chunk, uint32_t word) {
-  if constexpr (BITS == 2) {
-    *reinterpret_cast<uint16_t*>(rec + 2 * chunk) = (uint16_t)word;
-  } else if constexpr (BITS == 4) {
-    *reinterpret_cast<uint32_t*>(rec + 4 * chunk) = word;
-  } else {
-    uint8_t* p = rec + 3 * chunk;
-    if ((chunk & 1) == 0) {
-      *reinterpret_cast<uint16_t*>(p) = (uint16_t)word;
-      p[2] = (uint8_t)(word >> 16);
-    } else {
-      p[0] = (uint8_t)word;
-      *reinterpret_cast<uint16_t*>(p + 1) = (uint16_t)(word >> 8);
+template <int DT>
+__device__ __forceinline__ void widen_row(const RawRow<DT>& raw, float* v) {
+#pragma unroll
+  for (int k = 0; k < RawRow<DT>::NW; ++k) {
+    const uint32_t ws[4] = {raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == DT_F32) {
+        v[4 * k + i] = __uint_as_float(ws[i]);
+      } else if constexpr (DT == DT_BF16) {
+        v[8 * k + 2 * i] = __uint_as_float(ws[i] << 16);
+        v[8 * k + 2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
+      } else {
+        v[8 * k + 2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[i] & 0xffffu));
+        v[8 * k + 2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[i] >> 16));
+      }
     }
   }
 }
 
-// Same layout, with ``p`` already pointing at chunk ``chunk``'s first byte.
-template <int BITS>
-__device__ __forceinline__ void store_codes_at(uint8_t* p, int chunk, uint32_t word) {
-  if constexpr (BITS == 2) {
-    *reinterpret_cast<uint16_t*>(p) = (uint16_t)word;
-  } else if constexpr (BITS == 4) {
-    *reinterpret_cast<uint32_t*>(p) = word;
+// Slots 8c .. 8c + 7 of a raw row, widened.
+template <int DT>
+__device__ __forceinline__ void widen_chunk(const RawRow<DT>& raw, int c, float* t) {
+  if constexpr (DT == DT_F32) {
+    const u32x4_t a = raw.w[2 * c], b = raw.w[2 * c + 1];
+    t[0] = __uint_as_float(a.x); t[1] = __uint_as_float(a.y); t[2] = __uint_as_float(a.z); t[3] = __uint_as_float(a.w);
+    t[4] = __uint_as_float(b.x); t[5] = __uint_as_float(b.y); t[6] = __uint_as_float(b.z); t[7] = __uint_as_float(b.w);
   } else {
-    if ((chunk & 1) == 0) {
-      *reinterpret_cast<uint16_t*>(p) = (uint16_t)word;
-      p[2] = (uint8_t)(word >> 16);
-    } else {
-      p[0] = (uint8_t)word;
-      *reinterpret_cast<uint16_t*>(p + 1) = (uint16_t)(word >> 8);
+    const uint32_t ws[4] = {raw.w[c].x, raw.w[c].y, raw.w[c].z, raw.w[c].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == DT_BF16) {
+        t[2 * i] = __uint_as_float(ws[i] << 16);
+        t[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
+      } else {
+        t[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[i] & 0xffffu));
+        t[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[i] >> 16));
+      }
     }
   }
 }
 
-template <int BITS>
-__device__ __forceinline__ uint32_t load_codes_at(const uint8_t* p, int chunk) {
-  if constexpr (BITS == 2) {
-    return *reinterpret_cast<const uint16_t*>(p);
-  } else if constexpr (BITS == 4) {
-    return *reinterpret_cast<const uint32_t*>(p);
+// v_dot2 of a 16-bit pair with (+-1, +-1) and a float addend: x0 * s0 + x1 * s1 + acc
+// (products exact, one float sum).  Through the compiler builtin, so that the compiler
+// sees a dot instruction and schedules its result hazards.
+template <int DT, int S0, int S1>
+__device__ __forceinline__ float dot2pm(uint32_t pair, float acc) {
+  if constexpr (DT == DT_BF16) {
+    const bf16x2_t c = {(__bf16)(float)S0, (__bf16)(float)S1};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), c, acc, false);
   } else {
-    if ((chunk & 1) == 0)
-      return (uint32_t)*reinterpret_cast<const uint16_t*>(p) | ((uint32_t)p[2] << 16);
-    return (uint32_t)p[0] | ((uint32_t)*reinterpret_cast<const uint16_t*>(p + 1) << 8);
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const h2_t c = {(_Float16)(float)S0, (_Float16)(float)S1};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, pair), c, acc, false);
   }
 }
 
-template <int BITS>
-__device__ __forceinline__ uint32_t load_codes(const uint8_t* rec, int chunk) {
-  if constexpr (BITS == 2) {
-    return *reinterpret_cast<const uint16_t*>(rec + 2 * chunk);
-  } else if constexpr (BITS == 4) {
-    return *reinterpret_cast<const uint32_t*>(rec + 4 * chunk);
-  } else {
-    const uint8_t* p = rec + 3 * chunk;
-    if ((chunk & 1) == 0)
-      return (uint32_t)*reinterpret_cast<const uint16_t*>(p) | ((uint32_t)p[2] << 16);
-    return (uint32_t)p[0] | ((uint32_t)*reinterpret_cast<const uint16_t*>(p + 1) << 8);
+// Widen a 16-bit row and apply the first two Walsh-Hadamard stages (slot bits 0 and 1)
+// at once: each group of 4 channels (two dwords p, r) gives
+//   x0+x1+x2+x3, x0-x1+x2-x3, x0+x1-x2-x3, x0-x1-x2+x3
+// from two v_dot2 of p (x0+x1, x0-x1) and four v_dot2 of r with those as addends.
+template <int DT>
+__device__ __forceinline__ void widen_row_h4(const RawRow<DT>& raw, float* v) {
+  static_assert(DT != DT_F32, "16-bit inputs only");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t ws[4] = {raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w};
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t p = ws[2 * g], r = ws[2 * g + 1];
+      const float s = dot2pm<DT, 1, 1>(p, 0.0f);
+      const float d = dot2pm<DT, 1, -1>(p, 0.0f);
+      float* o = v + 8 * k + 4 * g;
+      o[0] = dot2pm<DT, 1, 1>(r, s);
+      o[1] = dot2pm<DT, 1, -1>(r, d);
+      o[2] = dot2pm<DT, -1, -1>(r, s);
+      o[3] = dot2pm<DT, -1, 1>(r, d);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// parameter staging shared by both kernels
+// parameter staging
 // ---------------------------------------------------------------------------
 // SO(4) block matrix M = L(qL) R(qR): M v = qL * v * qR (Hamilton product, real first).
 __device__ void build_so4(const float* q, float* m) {
@@ -428,140 +394,164 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, double theta, float* c
 }
 
 // ---------------------------------------------------------------------------
-// per-lane row storage and the work item shared by both kernels
+// work walk shared by both kernels
 // ---------------------------------------------------------------------------
-// Raw input of one lane for one row: 4 chunks of 8 elements (16 bytes per chunk
-// for 16-bit types, 32 bytes for float).
-template <int DT>
-struct RawRow {
-  static constexpr int NW = (DT == DT_F32) ? 8 : 4;
-  u32x4_t w[NW];
-};
-
-// Loads of one row: ``rowbase`` is wave-uniform, ``loff`` the lane's byte offset from it
-// (32-bit), so the loads use a scalar base with a vector offset.
-template <int DT, int LV>
-__device__ __forceinline__ void load_row(RawRow<DT>& raw, const char* rowbase, uint32_t loff) {
-  constexpr int ES = (DT == DT_F32) ? 4 : 2;
-  const char* b = rowbase + loff;
-#pragma unroll
-  for (int k = 0; k < kNC; ++k) {
-    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(b + k * LV * 8 * ES);
-    if constexpr (DT == DT_F32) {
-      raw.w[2 * k] = __builtin_nontemporal_load(p);
-      raw.w[2 * k + 1] = __builtin_nontemporal_load(p + 1);
-    } else {
-      raw.w[k] = __builtin_nontemporal_load(p);
-    }
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ void widen_row(const RawRow<DT>& raw, float* v) {
-#pragma unroll
-  for (int k = 0; k < kNC; ++k) {
-    if constexpr (DT == DT_F32) {
-      const u32x4_t a = raw.w[2 * k], b = raw.w[2 * k + 1];
-      v[8 * k + 0] = __uint_as_float(a.x); v[8 * k + 1] = __uint_as_float(a.y);
-      v[8 * k + 2] = __uint_as_float(a.z); v[8 * k + 3] = __uint_as_float(a.w);
-      v[8 * k + 4] = __uint_as_float(b.x); v[8 * k + 5] = __uint_as_float(b.y);
-      v[8 * k + 6] = __uint_as_float(b.z); v[8 * k + 7] = __uint_as_float(b.w);
-    } else {
-      const uint32_t ws[4] = {raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (DT == DT_BF16) {
-          v[8 * k + 2 * i] = __uint_as_float(ws[i] << 16);
-          v[8 * k + 2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
-        } else {
-          v[8 * k + 2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[i] & 0xffffu));
-          v[8 * k + 2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[i] >> 16));
-        }
-      }
-    }
-  }
-}
-
-// Widen a 16-bit row and apply the first Walsh-Hadamard stage (channel pairs 2i, 2i+1,
-// which share a dword) in one step: dot2(pair, (1, 1)) and dot2(pair, (1, -1)) form
-// x0 + x1 and x0 - x1 in float with a single rounding, like the float adds they replace.
-template <int DT>
-__device__ __forceinline__ void widen_row_butterfly(const RawRow<DT>& raw, float* v) {
-  static_assert(DT != DT_F32, "16-bit inputs only");
-#pragma unroll
-  for (int k = 0; k < kNC; ++k) {
-    const uint32_t ws[4] = {raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == DT_BF16) {
-        const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, ws[i]);
-        const bf16x2_t pp = {(__bf16)1.0f, (__bf16)1.0f};
-        const bf16x2_t pm = {(__bf16)1.0f, (__bf16)-1.0f};
-        v[8 * k + 2 * i] = __builtin_amdgcn_fdot2_f32_bf16(pr, pp, 0.0f, false);
-        v[8 * k + 2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, pm, 0.0f, false);
-      } else {
-        const f16x2_t pr = __builtin_bit_cast(f16x2_t, ws[i]);
-        const f16x2_t pp = {(_Float16)1.0f, (_Float16)1.0f};
-        const f16x2_t pm = {(_Float16)1.0f, (_Float16)-1.0f};
-        v[8 * k + 2 * i] = __builtin_amdgcn_fdot2(pr, pp, 0.0f, false);
-        v[8 * k + 2 * i + 1] = __builtin_amdgcn_fdot2(pr, pm, 0.0f, false);
-      }
-    }
-  }
-}
-
-// A wave's position in the row-major item sequence: row r, tile (VPW consecutive
-// (token, head) columns starting at col0 = tile * VPW = t0 * heads + h0).  All fields
-// are wave-uniform; the step from one of the wave's items to the next is a fixed
-// (rows, tiles) increment, so no division is needed after the first item.
-struct Cursor {
-  int64_t r, tile, t0, h0;
+// The lane's vector in a tile: column col = tile*VPW + q = (t0 + dtok) * heads + h.
+// The encoder's input address is a wave-uniform base (row, t0) plus a 32-bit lane
+// offset; the host bounds 16 token strides plus a head span below 2^31 bytes.
+struct LaneTile {
+  int64_t tile, t0;
+  int64_t pos;     // pos_offset + token of the lane's vector
+  int32_t h;       // head of the lane's vector
+  int32_t dtok;    // token - t0
+  int32_t valid;   // col < tokens * heads (0 / 1; a full word keeps the struct in registers)
+  int32_t pad;
 };
 
 template <int VPW>
-__device__ __forceinline__ Cursor first_cursor(const CodecArgs& a, int64_t wid) {
-  Cursor c;
-  c.r = wid / a.n_tiles;
-  c.tile = wid - c.r * a.n_tiles;
-  const int64_t col0 = c.tile * VPW;
-  c.t0 = col0 / a.heads;
-  c.h0 = col0 - c.t0 * a.heads;
-  return c;
+__device__ __forceinline__ LaneTile lane_tile(const CodecArgs& a, int64_t tile, int q) {
+  LaneTile lt;
+  lt.tile = tile;
+  const int64_t col0 = tile * VPW;
+  lt.t0 = col0 / a.heads;
+  const int64_t h0 = col0 - lt.t0 * a.heads;
+  const int64_t hq = h0 + q;               // < heads + 64
+  const int64_t dt = hq / a.heads;
+  lt.dtok = (int32_t)dt;
+  lt.h = (int32_t)(hq - dt * a.heads);
+  lt.pos = a.pos_offset + lt.t0 + dt;
+  lt.valid = (col0 + q < a.tokens * a.heads) ? 1 : 0;
+  lt.pad = 0;
+  return lt;
 }
 
-__device__ __forceinline__ void advance(const CodecArgs& a, Cursor& c) {
-  c.tile += a.step_tiles;
-  c.r += a.step_rows;
-  c.h0 += a.step_head;
-  c.t0 += a.step_tok;
-  if (c.h0 >= a.heads) { c.h0 -= a.heads; c.t0 += 1; }
-  if (c.tile >= a.n_tiles) {
-    c.tile -= a.n_tiles;
-    c.r += 1;
-    c.h0 -= a.wrap_head;
-    c.t0 -= a.wrap_tok;
-    if (c.h0 < 0) { c.h0 += a.heads; c.t0 -= 1; }
+// A wave's walk over its items: first rounds j = 0..K-1 of whole tiles (tile j*W + wid,
+// rows 0..R-1), then its share [t, t1) of the leftover (tile, row) items, numbered
+// tile-major from tile K*W on.
+struct Walk {
+  int64_t tile, r;  // current item
+  int64_t j;        // current round, or -1 in the leftover part
+  int64_t t, t1;    // leftover part: current index and end
+};
+
+__device__ __forceinline__ bool walk_leftover(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
+  const int64_t base = K * a.n_waves;
+  const int64_t n = (a.n_tiles - base) * a.rows;
+  const int64_t t0 = wid * n / a.n_waves, t1 = (wid + 1) * n / a.n_waves;
+  if (t0 >= t1) return false;
+  w.j = -1;
+  w.t = t0;
+  w.t1 = t1;
+  w.tile = base + t0 / a.rows;
+  w.r = t0 - (w.tile - base) * a.rows;
+  return true;
+}
+
+__device__ __forceinline__ bool walk_first(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
+  if (K > 0) {
+    w.j = 0;
+    w.tile = wid;
+    w.r = 0;
+    return true;
+  }
+  return walk_leftover(a, wid, K, w);
+}
+
+__device__ __forceinline__ bool walk_next(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
+  if (w.j >= 0) {
+    if (++w.r < a.rows) return true;
+    if (++w.j < K) {
+      w.tile += a.n_waves;
+      w.r = 0;
+      return true;
+    }
+    return walk_leftover(a, wid, K, w);
+  }
+  if (++w.t >= w.t1) return false;
+  if (++w.r == a.rows) {
+    w.r = 0;
+    ++w.tile;
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// bit-packing of a lane's 32 codes (4*BITS bytes, code i at bits BITS*i)
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct LaneCodes {
+  static constexpr int NW = BITS;  // 32-bit words: 32 codes * BITS bits / 32
+  uint32_t w[NW];
+};
+
+template <int BITS>
+__device__ __forceinline__ void store_lane_codes(uint8_t* p, const LaneCodes<BITS>& c) {
+  if constexpr (BITS == 2) {
+    u32x2_t v = {c.w[0], c.w[1]};
+    *reinterpret_cast<u32x2_t*>(p) = v;
+  } else if constexpr (BITS == 4) {
+    u32x4_t v = {c.w[0], c.w[1], c.w[2], c.w[3]};
+    *reinterpret_cast<u32x4_t*>(p) = v;
+  } else {
+    uint32_t* d = reinterpret_cast<uint32_t*>(p);
+    d[0] = c.w[0];
+    d[1] = c.w[1];
+    d[2] = c.w[2];
   }
 }
 
-// Token offset from t0 and head of the lane's vector q in the tile: (h0 + q) / heads by
-// a multiply-high with ceil(2^32 / heads), exact for h0 + q < heads + 64 <= 2^16 + 64.
-__device__ __forceinline__ void lane_token_head(const CodecArgs& a, const Cursor& c, int q, int& dtok, int& head) {
-  const uint32_t hq = (uint32_t)(c.h0 + q);
-  const uint32_t d = (a.heads == 1) ? hq : __umulhi(hq, a.heads_magic);
-  dtok = (int)d;
-  head = (int)(hq - d * (uint32_t)a.heads);
+template <int BITS>
+__device__ __forceinline__ void load_lane_codes(const uint8_t* p, LaneCodes<BITS>& c) {
+  if constexpr (BITS == 2) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    c.w[0] = v.x;
+    c.w[1] = v.y;
+  } else if constexpr (BITS == 4) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    c.w[0] = v.x;
+    c.w[1] = v.y;
+    c.w[2] = v.z;
+    c.w[3] = v.w;
+  } else {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+    c.w[0] = __builtin_nontemporal_load(s);
+    c.w[1] = __builtin_nontemporal_load(s + 1);
+    c.w[2] = __builtin_nontemporal_load(s + 2);
+  }
 }
 
-// Permutation gather offsets (bytes) for lane-in-vector l and slot i = 8k + s:
-// perm[(k*LV + l)*8 + s] * 4, staged in LDS once per block.
+// Code i of a lane (0 <= i < 32).
+template <int BITS>
+__device__ __forceinline__ uint32_t code_at(const LaneCodes<BITS>& c, int i) {
+  if constexpr (BITS == 3) {
+    const int bit = 3 * i, w = bit >> 5, sh = bit & 31;
+    if (sh <= 29) return (c.w[w] >> sh) & 7u;
+    return ((c.w[w] >> sh) | (c.w[w + 1] << (32 - sh))) & 7u;
+  } else {
+    const int bit = BITS * i;
+    return (c.w[bit >> 5] >> (bit & 31)) & ((1u << BITS) - 1u);
+  }
+}
+
+// acc + sum of pat[S] << BITS*S, as a chain of (a << sh) + b (one v_lshl_add each)
+template <int BITS, int S>
+__device__ __forceinline__ uint32_t pack_word(const uint32_t* pat, uint32_t acc) {
+  if constexpr (S == 32 / BITS) {
+    return acc;
+  } else {
+    return pack_word<BITS, S + 1>(pat, (pat[S] << (BITS * S)) + acc);
+  }
+}
+
+// Per-wave encoder staging: permutation rows (when a permutation is used), then the
+// RoPE table of the wave's tile: trig_rows rows of D/2 (cos, sin) float pairs.
 template <int D>
-__device__ __forceinline__ void stage_perm_offsets(const CodecArgs& a, int* s_poff) {
-  constexpr int LV = Geo<D>::LV;
-  for (int i = threadIdx.x; i < LV * 32; i += blockDim.x) {
-    const int l = i / 32, slot = i % 32, k = slot / 8, s = slot % 8;
-    s_poff[i] = 4 * (int)a.perm[(k * LV + l) * 8 + s];
-  }
+__device__ __forceinline__ uint32_t enc_perm_bytes(bool perm) {
+  return perm ? (uint32_t)stage_wave_bytes<D>() : 0u;
+}
+template <int D>
+__device__ __host__ inline size_t enc_wave_bytes(bool perm, bool rope, int trig_rows) {
+  return (perm ? (size_t)stage_wave_bytes<D>() : 0) + (rope ? (size_t)trig_rows * D * 4 : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -577,10 +567,9 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   constexpr bool ROPE_ANY = RT != 0, PERM_ANY = PT != 0;
   const bool ROPE = (RT < 0) ? (a.rope != 0) : (RT == 1);
   const bool PERM = (PT < 0) ? (a.use_perm != 0) : (PT == 1);
-  extern __shared__ float s_scratch[];
+  extern __shared__ float s_stage[];
   __shared__ double s_theta[ROPE_ANY ? D / 2 : 1];
   __shared__ float s_mat[ROT == ROT_SO4 ? (D / 4) * 16 : 1];
-  __shared__ int s_poff[PERM_ANY ? LV * 32 : 1];
 
   const int tid = threadIdx.x;
   if constexpr (ROPE_ANY) {
@@ -591,120 +580,132 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   if constexpr (ROT == ROT_SO4) {
     for (int b = tid; b < D / 4; b += blockDim.x) build_so4(&a.quat[8 * b], &s_mat[16 * b]);
   }
-  if constexpr (PERM_ANY) {
-    if (PERM) stage_perm_offsets<D>(a, s_poff);
-  }
   __syncthreads();
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  if (wid >= a.n_items) return;  // wave-uniform; no barrier follows
+  const int64_t K = a.n_tiles / a.n_waves;  // rounds of whole tiles
+  Walk wk;
+  if (!walk_first(a, wid, K, wk)) return;  // wave-uniform; no barrier follows
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
   constexpr int ES = (DT == DT_F32) ? 4 : 2;
-  constexpr int CBYTES = D * BITS / 8;  // code bytes per vector
-  const uint32_t clane = (uint32_t)(q * CBYTES + l * BITS);
+  constexpr int CB = D * BITS / 8;  // code bytes per vector
 
-  // per-wave LDS: the permutation scratch, which also holds the RoPE cos/sin table of
-  // the current item until the rotation has consumed it
-  char* wscratch = reinterpret_cast<char*>(s_scratch) + wave * scratch_wave_bytes<D>();
-  char* vscratch = wscratch + q * G::STRIDE * 4;
-  const int* poff = s_poff + l * 32;
+  // 16-bit input straight into the transform: widen fused with two butterfly stages
+  constexpr bool FUSED = (DT != DT_F32) && RT == 0 && PT == 0 && (QUANT == Q_MINMAX) && (ROT == ROT_FWHT);
+
+  // per-wave staging: permutation rows, then the RoPE table
+  const uint32_t wave_addr =
+      lds_addr(s_stage) + (uint32_t)(wave * enc_wave_bytes<D>(PERM, ROPE, a.trig_rows));
+  const uint32_t trig_addr = wave_addr + enc_perm_bytes<D>(PERM);
+  // permutation: this vector's LDS row and the lane's 32 gather addresses
+  const uint32_t row_addr = wave_addr + (uint32_t)(q * row_bytes<D>());
+  uint32_t gaddr[PERM_ANY ? 32 : 1];
+  if constexpr (PERM_ANY) {
+    if (PERM) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) gaddr[i] = row_addr + 4u * (uint32_t)a.perm[32 * l + i];
+    }
+  }
 
   const float norm_c = (ROT == ROT_FWHT) ? (float)(1.0 / __builtin_sqrt((double)D)) : 1.0f;
   const float sgn = (ROT == ROT_FWHT) ? lane_sign(l) : 1.0f;
   const float A = sgn * norm_c;  // true rotated coefficient = A * (value held by this lane)
+  const float m1 = (l & 1) ? -1.0f : 1.0f, m2 = (l & 2) ? -1.0f : 1.0f, m4 = (l & 4) ? -1.0f : 1.0f;
   const int gb = (GBT > 0) ? GBT : a.group_log2;
-  const int LB = (QUANT == Q_MINMAX) ? min(G::LVB, gb - 3) : 0;     // lane bits inside a group
-  const int CB = (QUANT == Q_MINMAX) ? max(0, gb - 3 - G::LVB) : 0; // chunk bits inside a group
+  const int LB = (QUANT == Q_MINMAX) ? gb - 5 : 0;  // lane bits inside a group (G >= 32)
   const int64_t ngroups = (QUANT == Q_MINMAX) ? (D >> gb) : 0;
 
-  // 16-bit input straight into the transform: widen and first butterfly stage fused
-  constexpr bool FUSED = (DT != DT_F32) && RT == 0 && PT == 0 && (QUANT == Q_MINMAX) && (ROT == ROT_FWHT);
-
-  // input address of the lane's vector for an item: wave-uniform base, 32-bit lane offset
-  auto input_of = [&](const Cursor& c, const char*& base, uint32_t& loff, bool& valid) {
-    int dtok, head;
-    lane_token_head(a, c, q, dtok, head);
-    valid = c.tile * VPW + q < ncols;
-    base = reinterpret_cast<const char*>(a.x) + (c.r * a.sr + c.t0 * a.st) * ES;
-    loff = (uint32_t)(((int64_t)dtok * a.st + (int64_t)head * a.sh + (int64_t)l * 8) * ES);
+  // lane state of the current tile; the wave's RoPE table holds cos/sin of (token, pair)
+  // for the tokens t0 .. t0 + ntok - 1 the tile spans
+  LaneTile cur = lane_tile<VPW>(a, wk.tile, q);
+  auto set_trig = [&](const LaneTile& lt) __attribute__((always_inline)) {
+    if constexpr (ROPE_ANY) {
+      if (ROPE) {
+        const int64_t last = min(lt.tile * VPW + VPW, ncols) - 1;
+        const int ntok = (int)(last / a.heads - lt.t0) + 1;
+        const int64_t p0 = a.pos_offset + lt.t0;
+        wave_lds_sync();  // the previous tile's table has been read
+        for (int m = lane; m < ntok * (D / 2); m += 64) {
+          const int tok = m / (D / 2), i = m % (D / 2);
+          float c, sn;
+          rope_cos_sin(p0 + tok, s_theta[i], &c, &sn);
+          u32x2_t w = {__float_as_uint(c), __float_as_uint(sn)};
+          *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)(trig_addr + 8u * (uint32_t)m) = w;
+        }
+        wave_lds_sync();
+      }
+    }
+  };
+  auto lane_in = [&](const LaneTile& lt, int64_t row) __attribute__((always_inline)) -> const char* {
+    const char* base = reinterpret_cast<const char*>(a.x) + (row * a.sr + lt.t0 * a.st) * ES;
+    const uint32_t loff = (uint32_t)(((int64_t)lt.dtok * a.st + (int64_t)lt.h * a.sh + 32 * l) * ES);
+    return base + loff;
   };
 
-  auto process = [&](const RawRow<DT>& raw, const Cursor& c) {
-    const int64_t r = c.r;
-    const int64_t col0 = c.tile * VPW;
-    int dtok, h;
-    lane_token_head(a, c, q, dtok, h);
-    const int64_t col = col0 + q;
-    const bool valid = col < ncols;
-    const int64_t pos = a.pos_offset + c.t0 + dtok;
-    const bool is_sink = valid && pos < a.n_sink;
-    const bool work = valid && !is_sink;
-    const int64_t vec = r * ncols + col;  // index into the packed planes
-    const int64_t vec0 = r * ncols + col0;  // wave-uniform
-    uint8_t* rec = a.codes + vec0 * CBYTES + clane;  // chunk c of this lane at rec + (c - l) * BITS
+  auto process = [&](const RawRow<DT>& raw, const LaneTile& lt, int64_t row) __attribute__((always_inline)) {
+    if (!lt.valid) return;
+    const int64_t vec = row * ncols + lt.tile * VPW + q;  // index into the packed planes
+    uint8_t* rec = a.codes + vec * CB + l * (4 * BITS);
     float v[32];
-    if constexpr (FUSED) {
-      if (is_sink) widen_row<DT>(raw, v);  // sinks store the unrotated values
-      else widen_row_butterfly<DT>(raw, v);
-    } else {
-      widen_row<DT>(raw, v);
-    }
-    if (ROPE_ANY && ROPE) {
-      // cos/sin of (position, pair) for the tokens of this tile, computed once per item
-      // by the whole wave into LDS (about 2 angles per lane when heads = 8)
-      const int ntok = (int)((c.h0 + VPW - 1) / a.heads) + 1;
-      float2* trig = reinterpret_cast<float2*>(wscratch);
-      for (int m = lane; m < ntok * (D / 2); m += 64) {
-        const int tok = m / (D / 2), i = m % (D / 2);
-        float cs, sn;
-        rope_cos_sin(a.pos_offset + c.t0 + tok, s_theta[i], &cs, &sn);
-        trig[m] = make_float2(cs, sn);
+    // RoPE of the 4 channel pairs of 8 consecutive slots 8c .. 8c + 7
+    auto rope8 = [&](float* u, int c) __attribute__((always_inline)) {
+      const uint32_t tp = trig_addr + (uint32_t)(lt.dtok * (D * 4) + 128 * l + 32 * c);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t cs = lds_ld4(tp + 16u * h);
+        const float c0 = __uint_as_float(cs.x), s0 = __uint_as_float(cs.y);
+        const float c1 = __uint_as_float(cs.z), s1 = __uint_as_float(cs.w);
+        float* w = u + 4 * h;
+        const float x0 = w[0], x1 = w[1], x2 = w[2], x3 = w[3];
+        w[0] = __builtin_fmaf(x0, c0, -x1 * s0);
+        w[1] = __builtin_fmaf(x0, s0, x1 * c0);
+        w[2] = __builtin_fmaf(x2, c1, -x3 * s1);
+        w[3] = __builtin_fmaf(x2, s1, x3 * c1);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (valid) {
-        const float4* tl = reinterpret_cast<const float4*>(trig + dtok * (D / 2));
+    };
+    bool staged = false;
+    if constexpr (PERM_ANY) {
+      if (PERM) {
+        // widen (and rotate by RoPE) 8 slots at a time straight into the vector's staging
+        // row in natural order, then gather u'[j] = u[perm[j]]
 #pragma unroll
-        for (int k = 0; k < kNC; ++k) {
-          const float4 p01 = tl[(k * LV + l) * 2], p23 = tl[(k * LV + l) * 2 + 1];
-          const float cc[4] = {p01.x, p01.z, p23.x, p23.z};
-          const float ss[4] = {p01.y, p01.w, p23.y, p23.w};
+        for (int c = 0; c < 4; ++c) {
+          float t[8];
+          widen_chunk<DT>(raw, c, t);
+          if constexpr (ROPE_ANY) {
+            if (ROPE) rope8(t, c);
+          }
+          const u32x4_t w0 = {__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]), __float_as_uint(t[3])};
+          const u32x4_t w1 = {__float_as_uint(t[4]), __float_as_uint(t[5]), __float_as_uint(t[6]), __float_as_uint(t[7])};
+          lds_st4(row_addr + 128u * l + 32u * c, w0);
+          lds_st4(row_addr + 128u * l + 32u * c + 16u, w1);
+        }
+        wave_lds_sync();
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x0 = v[8 * k + 2 * j], x1 = v[8 * k + 2 * j + 1];
-            v[8 * k + 2 * j] = __builtin_fmaf(x0, cc[j], -x1 * ss[j]);
-            v[8 * k + 2 * j + 1] = __builtin_fmaf(x0, ss[j], x1 * cc[j]);
+        for (int i = 0; i < 32; ++i) v[i] = lds_ld(gaddr[i]);
+        wave_lds_sync();
+        staged = true;
+      }
+    }
+    if (!staged) {
+      if constexpr (FUSED) {
+        widen_row_h4<DT>(raw, v);  // 16-bit input with the first two butterfly stages
+      } else {
+        widen_row<DT>(raw, v);
+        if constexpr (ROPE_ANY) {
+          if (ROPE) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) rope8(v + 8 * c, c);
           }
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (!valid) return;
-    if (is_sink) {
-      const int64_t srow = (r * a.n_sink + pos) * a.heads + h;
-#pragma unroll
-      for (int k = 0; k < kNC; ++k) store_chunk<DT_F16>(a.sink, srow * D + (k * LV + l) * 8, v + 8 * k);
-#pragma unroll
-      for (int k = 0; k < kNC; ++k) store_codes_at<BITS>(rec + k * LV * BITS, k * LV + l, 0u);
-      if constexpr (QUANT == Q_MINMAX) {
-        for (int g = l; g < ngroups; g += LV) {
-          a.scale[vec * ngroups + g] = 0;
-          a.zero[vec * ngroups + g] = 0;
-        }
-      } else {
-        if (l == 0) a.norm[vec] = 0.0f;
-      }
-    }
-    if (!work) return;
     if constexpr (QUANT == Q_LLOYD) {
-      // |x| with an exact power-of-two pre-scale by the largest |x_i|, so that the
-      // sum of squares neither underflows nor overflows in float
+      // |u| (the permutation does not change it) with an exact power-of-two pre-scale by
+      // the largest |u_i|, so that the sum of squares neither underflows nor overflows
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -723,148 +724,94 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       for (int i = 0; i < 32; ++i) v[i] *= inv;
       if (l == 0) a.norm[vec] = rho;
     }
-    if (PERM_ANY && PERM) {
-      // natural order in, gathered order out: u'[j] = u[perm[j]] (one wave, in-order LDS)
-#pragma unroll
-      for (int k = 0; k < kNC; ++k) {
-        float4* dst = reinterpret_cast<float4*>(vscratch + 32 * (k * LV + l));
-        dst[0] = make_float4(v[8 * k], v[8 * k + 1], v[8 * k + 2], v[8 * k + 3]);
-        dst[1] = make_float4(v[8 * k + 4], v[8 * k + 5], v[8 * k + 6], v[8 * k + 7]);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        const int4 o = *reinterpret_cast<const int4*>(poff + i);
-        v[i] = *reinterpret_cast<const float*>(vscratch + o.x);
-        v[i + 1] = *reinterpret_cast<const float*>(vscratch + o.y);
-        v[i + 2] = *reinterpret_cast<const float*>(vscratch + o.z);
-        v[i + 3] = *reinterpret_cast<const float*>(vscratch + o.w);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
     if constexpr (ROT == ROT_FWHT) {
-      fwht_lane<LV, FUSED>(v, l);
+      fwht_lane<LV, FUSED ? 2 : 0>(v, m1, m2, m4);
     } else if constexpr (ROT == ROT_SO4) {
 #pragma unroll
-      for (int k = 0; k < kNC; ++k)
+      for (int b = 0; b < 8; ++b) {
+        const float* m = &s_mat[16 * (8 * l + b)];
+        float* u = v + 4 * b;
+        const float u0 = u[0], u1 = u[1], u2 = u[2], u3 = u[3];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int blk = (k * LV + l) * 2 + half;
-          const float* m = &s_mat[16 * blk];
-          float* u = v + 8 * k + 4 * half;
-          const float u0 = u[0], u1 = u[1], u2 = u[2], u3 = u[3];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            u[i] = __builtin_fmaf(m[4 * i], u0,
-                   __builtin_fmaf(m[4 * i + 1], u1, __builtin_fmaf(m[4 * i + 2], u2, m[4 * i + 3] * u3)));
-        }
+        for (int i = 0; i < 4; ++i)
+          u[i] = __builtin_fmaf(m[4 * i], u0,
+                 __builtin_fmaf(m[4 * i + 1], u1, __builtin_fmaf(m[4 * i + 2], u2, m[4 * i + 3] * u3)));
+      }
     }
+    LaneCodes<BITS> cw;
     if constexpr (QUANT == Q_MINMAX) {
-      // min/max of the lane's values of each group (a group covers 1, 2 or 4 of the
-      // lane's chunks); the true coefficients are A * v, so for A < 0 min and max swap
-      float cmn[kNC], cmx[kNC];
-      auto mm8 = [&](int k, float& lo, float& hi) {
-        const float* c = v + 8 * k;
-        lo = fminf(fminf(fminf(c[0], c[1]), fminf(c[2], c[3])), fminf(fminf(c[4], c[5]), fminf(c[6], c[7])));
-        hi = fmaxf(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])), fmaxf(fmaxf(c[4], c[5]), fmaxf(c[6], c[7])));
-      };
-      auto orient = [&](float lo, float hi, float& mn, float& mx) {
-        mn = (A > 0.0f) ? lo * A : hi * A;
-        mx = (A > 0.0f) ? hi * A : lo * A;
-      };
-      if (CB == 2) {
-        float lo, hi, lo1, hi1, lo2, hi2, lo3, hi3;
-        mm8(0, lo, hi); mm8(1, lo1, hi1); mm8(2, lo2, hi2); mm8(3, lo3, hi3);
-        lo = fminf(fminf(lo, lo1), fminf(lo2, lo3));
-        hi = fmaxf(fmaxf(hi, hi1), fmaxf(hi2, hi3));
-        orient(lo, hi, cmn[0], cmx[0]);
-      } else if (CB == 1) {
-        float lo, hi, lo1, hi1;
-        mm8(0, lo, hi); mm8(1, lo1, hi1);
-        orient(fminf(lo, lo1), fmaxf(hi, hi1), cmn[0], cmx[0]);
-        mm8(2, lo, hi); mm8(3, lo1, hi1);
-        orient(fminf(lo, lo1), fmaxf(hi, hi1), cmn[2], cmx[2]);
-      } else {
+      // min/max of the lane's 32 values (one group covers 1, 2, 4 or 8 whole lanes); the
+      // true coefficients are A * v, so for A < 0 min and max swap
+      float lo = fminf(fminf(v[0], v[1]), v[2]), hi = fmaxf(fmaxf(v[0], v[1]), v[2]);
 #pragma unroll
-        for (int k = 0; k < kNC; ++k) {
-          float lo, hi;
-          mm8(k, lo, hi);
-          orient(lo, hi, cmn[k], cmx[k]);
-        }
+      for (int i = 3; i < 31; i += 2) {
+        lo = fminf(fminf(lo, v[i]), v[i + 1]);
+        hi = fmaxf(fmaxf(hi, v[i]), v[i + 1]);
       }
-      // per-group zero/scale: reduce over the group's lanes, round to fp16
-      // (zero down, scale up), store from the group's first lane
-      auto group = [&](float mn, float mx, int k, float& zo, float& so, float& io) {
-        if (LB >= 1) { mn = min_x1(mn); mx = max_x1(mx); }
-        if (LB >= 2) { mn = min_x2(mn); mx = max_x2(mx); }
-        if (LB >= 3) { mn = fminf(mn, swz_x4(mn)); mx = fmaxf(mx, swz_x4(mx)); }
-        // "+ 0.0f" turns a -0 (all-zero group, negated lanes) into +0
-        const uint32_t zb = f16_round_down(mn + 0.0f);
-        const float z = f16_value(zb);
-        // (max - zero) / (2^b - 1) to within an ulp, then rounded up to fp16
-        constexpr float kInvLevels = 1.0f / (float)((1 << BITS) - 1);
-        const uint32_t sb = f16_round_up((mx - z) * kInvLevels + 0.0f);
-        const float sc = f16_value(sb);
-        if ((l & ((1 << LB) - 1)) == 0) {
-          const int64_t gi = ((int64_t)((k * LV + l) * 8)) >> gb;
-          a.scale[vec * ngroups + gi] = (uint16_t)sb;
-          a.zero[vec * ngroups + gi] = (uint16_t)zb;
-        }
-        zo = z;
-        so = sc;
-        io = (sc > 0.0f) ? __builtin_amdgcn_rcpf(sc) : 0.0f;
-      };
-      float zf[kNC], inv[kNC], scf[kNC];
-      group(cmn[0], cmx[0], 0, zf[0], scf[0], inv[0]);
-      if (CB == 0) {
-        group(cmn[1], cmx[1], 1, zf[1], scf[1], inv[1]);
-        group(cmn[2], cmx[2], 2, zf[2], scf[2], inv[2]);
-        group(cmn[3], cmx[3], 3, zf[3], scf[3], inv[3]);
-      } else if (CB == 1) {
-        group(cmn[2], cmx[2], 2, zf[2], scf[2], inv[2]);
-        zf[1] = zf[0]; inv[1] = inv[0]; scf[1] = scf[0];
-        zf[3] = zf[2]; inv[3] = inv[2]; scf[3] = scf[2];
-      } else {
-        zf[1] = zf[2] = zf[3] = zf[0];
-        inv[1] = inv[2] = inv[3] = inv[0];
-        scf[1] = scf[2] = scf[3] = scf[0];
+      lo = fminf(lo, v[31]);
+      hi = fmaxf(hi, v[31]);
+      float mn = (A > 0.0f) ? lo * A : hi * A;
+      float mx = (A > 0.0f) ? hi * A : lo * A;
+      if (LB >= 1) { mn = min_x1(mn); mx = max_x1(mx); }
+      if (LB >= 2) { mn = min_x2(mn); mx = max_x2(mx); }
+      if (LB >= 3) { mn = fminf(mn, swz_x4(mn)); mx = fmaxf(mx, swz_x4(mx)); }
+      // zero rounded down, scale = (max - zero)/(2^b - 1) rounded up, both to fp16;
+      // "+ 0.0f" turns a -0 (all-zero group, negated lanes) into +0
+      const uint32_t zb = f16_round_down(mn + 0.0f);
+      const float z = f16_value(zb);
+      constexpr float kInvLevels = 1.0f / (float)((1 << BITS) - 1);
+      const uint32_t sb = f16_round_up((mx - z) * kInvLevels + 0.0f);
+      const float sc = f16_value(sb);
+      if ((l & ((1 << LB) - 1)) == 0) {
+        a.scale[vec * ngroups + (l >> LB)] = (uint16_t)sb;
+        a.zero[vec * ngroups + (l >> LB)] = (uint16_t)zb;
       }
+      const float iv = (sc > 0.0f) ? __builtin_amdgcn_rcpf(sc) : 0.0f;
       // q = rint((A v - zero) / scale), nearest-even: adding 1.5 * 2^23 inside the fma
       // rounds the exact product to an integer, which then sits in the low mantissa bits
-      // (bit pattern 0x4B400000 + q, since -eps <= t <= 2^b - 1 + eps).  The codes are
-      // accumulated as (pattern << BITS*s) sums and the constant part subtracted once.
+      // (bit pattern 0x4B400000 + q, since -eps <= t <= 2^b - 1 + eps).
       constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-      constexpr uint32_t kMagicSum = [] {
-        uint32_t c = 0;
-        for (int s = 0; s < 8; ++s) c += 0x4B400000u << (BITS * s);
-        return c;
-      }();
-#pragma unroll
-      for (int k = 0; k < kNC; ++k) {
-        const float z = zf[k], iv = inv[k], sc = scf[k];
-        uint32_t word = 0;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const float d = __builtin_fmaf(v[8 * k + s], A, -z);
-          float tq;
-          if constexpr (ROT == ROT_NONE) {
-            // unrotated fp16/bf16 data sit on the same grid as zero/scale, so exact
-            // half-way quotients are common: one residual step makes d/scale correctly
-            // rounded before the integer rounding
-            const float t0 = d * iv;
-            const float t1 = __builtin_fmaf(__builtin_fmaf(-t0, sc, d), iv, t0);
-            tq = (sc > 0.0f ? t1 : 0.0f) + kMagic;
-          } else {
-            (void)sc;
-            tq = __builtin_fmaf(d, iv, kMagic);
-          }
-          word += __float_as_uint(tq) << (BITS * s);
+      auto code_of = [&](float x) -> uint32_t {
+        const float d = __builtin_fmaf(x, A, -z);
+        float tq;
+        if constexpr (ROT == ROT_NONE) {
+          // unrotated fp16/bf16 data sit on the same grid as zero/scale, so exact
+          // half-way quotients are common: one residual step makes d/scale correctly
+          // rounded before the integer rounding
+          const float t0 = d * iv;
+          const float t1 = __builtin_fmaf(__builtin_fmaf(-t0, sc, d), iv, t0);
+          tq = (sc > 0.0f ? t1 : 0.0f) + kMagic;
+        } else {
+          tq = __builtin_fmaf(d, iv, kMagic);
         }
-        store_codes_at<BITS>(rec + k * LV * BITS, k * LV + l, word - kMagicSum);
+        return __float_as_uint(tq);
+      };
+      if constexpr (BITS == 3) {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) cw.w[w] = 0u;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t cq = code_of(v[i]) - 0x4B400000u;
+          const int bit = 3 * i, w = bit >> 5, sh = bit & 31;
+          cw.w[w] |= cq << sh;
+          if (sh > 29) cw.w[w + 1] |= cq >> (32 - sh);
+        }
+      } else {
+        // the codes are accumulated as (pattern << BITS*s) sums and the constant part
+        // subtracted once per word
+        constexpr int PER = 32 / BITS;
+        constexpr uint32_t kMagicSum = [] {
+          uint32_t c = 0;
+          for (int s = 0; s < 32 / BITS; ++s) c += 0x4B400000u << (BITS * s);
+          return c;
+        }();
+#pragma unroll
+        for (int w = 0; w < BITS; ++w) {
+          uint32_t pat[PER];
+#pragma unroll
+          for (int s = 0; s < PER; ++s) pat[s] = code_of(v[PER * w + s]);
+          cw.w[w] = pack_word<BITS, 0>(pat, 0u - kMagicSum);
+        }
       }
     } else {
       // Lloyd-Max: q = #{k : z > tau_k}
@@ -873,46 +820,43 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
 #pragma unroll
       for (int i = 0; i < NT; ++i) tau[i] = 0.5f * (a.codebook[i] + a.codebook[i + 1]);
 #pragma unroll
-      for (int k = 0; k < kNC; ++k) {
-        uint32_t word = 0;
+      for (int w = 0; w < BITS; ++w) cw.w[w] = 0u;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const float z = v[8 * k + s] * A;
-          uint32_t c = 0;
+      for (int i = 0; i < 32; ++i) {
+        const float z = v[i] * A;
+        uint32_t c = 0;
 #pragma unroll
-          for (int i = 0; i < NT; ++i) c += (z > tau[i]) ? 1u : 0u;
-          word |= c << (BITS * s);
-        }
-        store_codes_at<BITS>(rec + k * LV * BITS, k * LV + l, word);
+        for (int k = 0; k < NT; ++k) c += (z > tau[k]) ? 1u : 0u;
+        const int bit = BITS * i, w = bit >> 5, sh = bit & 31;
+        cw.w[w] |= c << sh;
+        if (BITS == 3 && sh > 29) cw.w[w + 1] |= c >> (32 - sh);
       }
     }
+    store_lane_codes<BITS>(rec, cw);
   };
 
-  // persistent loop over the wave's items with the next item's loads in flight
-  Cursor ca = first_cursor<VPW>(a, wid);
+  // persistent walk over the wave's items with the next item's loads in flight
+  set_trig(cur);
   RawRow<DT> ra, rb;
-  const char* xb;
-  uint32_t xl;
-  bool ok;
-  input_of(ca, xb, xl, ok);
-  if (ok) load_row<DT, LV>(ra, xb, xl);
-  for (int64_t it = wid; it < a.n_items; it += 2 * a.n_waves) {
-    Cursor cb = ca;
-    advance(a, cb);
-    const bool has_b = it + a.n_waves < a.n_items;
-    if (has_b) {
-      input_of(cb, xb, xl, ok);
-      if (ok) load_row<DT, LV>(rb, xb, xl);
+  if (cur.valid) load_row<DT>(ra, lane_in(cur, wk.r));
+  LaneTile nxt = cur;
+  auto step = [&](RawRow<DT>& now, RawRow<DT>& later) __attribute__((always_inline)) -> bool {
+    Walk nw = wk;
+    const bool more = walk_next(a, wid, K, nw);
+    if (more) {
+      if (nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
+      if (nxt.valid) load_row<DT>(later, lane_in(nxt, nw.r));
     }
-    process(ra, ca);
-    if (!has_b) break;
-    ca = cb;
-    advance(a, ca);
-    if (it + 2 * a.n_waves < a.n_items) {
-      input_of(ca, xb, xl, ok);
-      if (ok) load_row<DT, LV>(ra, xb, xl);
+    process(now, cur, wk.r);
+    if (!more) return false;
+    wk = nw;
+    if (nxt.tile != cur.tile) {
+      cur = nxt;
+      set_trig(cur);
     }
-    process(rb, cb);
+    return true;
+  };
+  while (step(ra, rb) && step(rb, ra)) {
   }
 }
 
@@ -920,16 +864,19 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
 // DECODE
 // ---------------------------------------------------------------------------
 // PT: permutation off (0), on (1) or read from the arguments (-1).
+// FWHT + min-max runs the in-lane Walsh-Hadamard stages on the integer codes (packed
+// 16-bit pairs, exact), then scales once per element and finishes the lane stages in
+// float; other rotations and quantizers dequantize first and rotate in float.
 template <int ODT, int D, int BITS, int ROT, int QUANT, int PT>
 __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const CodecArgs a) {
   using G = Geo<D>;
   constexpr int LV = G::LV, VPW = G::VPW;
   constexpr bool PERM_ANY = PT != 0;
+  constexpr bool INTPATH = (ROT == ROT_FWHT) && (QUANT == Q_MINMAX);
   const bool PERM = (PT < 0) ? (a.use_perm != 0) : (PT == 1);
-  extern __shared__ float s_scratch[];
+  extern __shared__ float s_stage[];
   __shared__ float s_mat[ROT == ROT_SO4 ? (D / 4) * 16 : 1];
   __shared__ float s_cb[kMaxCodebook];
-  __shared__ int s_poff[PERM_ANY ? LV * 32 : 1];
 
   const int tid = threadIdx.x;
   if constexpr (ROT == ROT_SO4) {
@@ -938,180 +885,394 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   if constexpr (QUANT == Q_LLOYD) {
     if (tid < (1 << BITS)) s_cb[tid] = a.codebook[tid];
   }
-  if constexpr (PERM_ANY) {
-    if (PERM) stage_perm_offsets<D>(a, s_poff);
-  }
   __syncthreads();
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  if (wid >= a.n_items) return;  // wave-uniform; no barrier follows
+  const int64_t K = a.n_tiles / a.n_waves;  // rounds of whole tiles
+  Walk wk;
+  if (!walk_first(a, wid, K, wk)) return;  // wave-uniform; no barrier follows
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
-
-  char* vscratch = reinterpret_cast<char*>(s_scratch) + wave * scratch_wave_bytes<D>() + q * G::STRIDE * 4;
-  const int* poff = s_poff + l * 32;
+  constexpr int CB = D * BITS / 8;
+  constexpr int OES = (ODT == DT_F32) ? 4 : 2;
   const float norm_c = (ROT == ROT_FWHT) ? (float)(1.0 / __builtin_sqrt((double)D)) : 1.0f;
   const float sgn = (ROT == ROT_FWHT) ? lane_sign(l) : 1.0f;
   const int gb = a.group_log2;
+  const int LB = (QUANT == Q_MINMAX) ? gb - 5 : 0;
   const int64_t ngroups = (QUANT == Q_MINMAX) ? (D >> gb) : 0;
 
-  // packed inputs of one vector for this lane: code words of its 4 chunks, plus the
-  // scale/zero of each chunk's group (min-max) or rho (Lloyd-Max)
+  // staging rows: vector q's row; in the permuted case the lane scatters its 32 floats
+  // to out[perm[j]], otherwise it writes its 32 outputs (in the output type) in order
+  const uint32_t wave_addr = lds_addr(s_stage) + (uint32_t)(wave * stage_wave_bytes<D>());
+  const uint32_t row_addr = wave_addr + (uint32_t)(q * row_bytes<D>());
+  uint32_t saddr[PERM_ANY ? 32 : 1];
+  if constexpr (PERM_ANY) {
+    if (PERM) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) saddr[i] = row_addr + 4u * (uint32_t)a.perm[32 * l + i];
+    }
+  }
+
   struct Packed {
-    uint32_t word[kNC];
-    uint32_t sz[kNC];  // scale | zero << 16
-    float rho;
+    LaneCodes<BITS> c;
+    uint32_t sz;  // scale | zero << 16 (min-max)
+    float rho;    // Lloyd-Max
   };
-  constexpr int CBYTES = D * BITS / 8;
-  const uint32_t clane = (uint32_t)(q * CBYTES + l * BITS);
-  // a lane's vector of an item: validity, sink test and (for sinks) the sink record
-  auto lane_state = [&](const Cursor& c, bool& valid, bool& is_sink, int64_t& srow) {
-    int dtok, h;
-    lane_token_head(a, c, q, dtok, h);
-    valid = c.tile * VPW + q < ncols;
-    const int64_t pos = a.pos_offset + c.t0 + dtok;
-    is_sink = valid && pos < a.n_sink;
-    srow = (c.r * a.n_sink + pos) * a.heads + h;
-  };
-  auto load_packed = [&](Packed& pk, const Cursor& c) {
-    const int64_t vec0 = c.r * ncols + c.tile * VPW;  // wave-uniform
-    const uint8_t* rec = a.codes + vec0 * CBYTES + clane;
-#pragma unroll
-    for (int k = 0; k < kNC; ++k) pk.word[k] = load_codes_at<BITS>(rec + k * LV * BITS, k * LV + l);
+  auto fetch = [&](Packed& pk, const LaneTile& lt, int64_t row) __attribute__((always_inline)) {
+    if (!lt.valid) return;
+    const int64_t vec = row * ncols + lt.tile * VPW + q;
+    load_lane_codes<BITS>(a.codes + vec * CB + l * (4 * BITS), pk.c);
     if constexpr (QUANT == Q_MINMAX) {
-      const uint16_t* sp = a.scale + vec0 * ngroups + q * ngroups;
-      const uint16_t* zp = a.zero + vec0 * ngroups + q * ngroups;
-#pragma unroll
-      for (int k = 0; k < kNC; ++k) {
-        const int gi = ((k * LV + l) * 8) >> gb;
-        pk.sz[k] = (uint32_t)sp[gi] | ((uint32_t)zp[gi] << 16);
-      }
+      const int64_t gi = vec * ngroups + (l >> LB);
+      pk.sz = (uint32_t)a.scale[gi] | ((uint32_t)a.zero[gi] << 16);
     } else {
-      pk.rho = a.norm[vec0 + q];
+      pk.rho = a.norm[vec];
     }
   };
 
-  auto process = [&](const Packed& pk, const Cursor& c) {
-    bool valid, is_sink;
-    int64_t srow;
-    lane_state(c, valid, is_sink, srow);
-    if (!valid) return;
-    float v[32];
-    if (is_sink) {
+  // a lane's 32 output values, true coefficients in natural slot order
+  auto reconstruct = [&](const Packed& pk, float* v) __attribute__((always_inline)) {
+    if constexpr (INTPATH) {
+      // packed pairs: word s holds codes (s, s + 16) as 16-bit integers
+      uint32_t w[16];
+      if constexpr (BITS == 2) {
+        // bytes of c.w[0] hold codes 0-3, 4-7, 8-11, 12-15; c.w[1] codes 16-31
+        const uint32_t plo = __builtin_amdgcn_perm(pk.c.w[1], pk.c.w[0], 0x05040100u);  // codes 0-7 | 16-23
+        const uint32_t phi = __builtin_amdgcn_perm(pk.c.w[1], pk.c.w[0], 0x07060302u);  // codes 8-15 | 24-31
 #pragma unroll
-      for (int k = 0; k < kNC; ++k) load_chunk<DT_F16>(a.sink, srow * D + (k * LV + l) * 8, v + 8 * k);
-    } else {
-      if constexpr (QUANT == Q_MINMAX) {
+        for (int s = 0; s < 8; ++s) {
+          w[s] = (plo >> (2 * s)) & 0x00030003u;
+          w[s + 8] = (phi >> (2 * s)) & 0x00030003u;
+        }
+      } else if constexpr (BITS == 4) {
+        // c.w[0]: codes 0-7, c.w[1]: 8-15, c.w[2]: 16-23, c.w[3]: 24-31
 #pragma unroll
-        for (int k = 0; k < kNC; ++k) {
-          const float sc = f16_value(pk.sz[k] & 0xffffu);
-          const float z = f16_value(pk.sz[k] >> 16);
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t plo = __builtin_amdgcn_perm(pk.c.w[2 + h], pk.c.w[h], 0x05040100u);
+          const uint32_t phi = __builtin_amdgcn_perm(pk.c.w[2 + h], pk.c.w[h], 0x07060302u);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const float qv = (float)((pk.word[k] >> (BITS * s)) & ((1u << BITS) - 1u));
-            v[8 * k + s] = __builtin_fmaf(qv, sc, z);
+          for (int s = 0; s < 4; ++s) {
+            w[8 * h + s] = (plo >> (4 * s)) & 0x000F000Fu;
+            w[8 * h + s + 4] = (phi >> (4 * s)) & 0x000F000Fu;
           }
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < kNC; ++k)
+        for (int s = 0; s < 16; ++s) w[s] = code_at<3>(pk.c, s) | (code_at<3>(pk.c, s + 16) << 16);
+      }
+      // Walsh-Hadamard over slot bits 0..3 between words, exact in 16-bit lanes
 #pragma unroll
-          for (int s = 0; s < 8; ++s) v[8 * k + s] = s_cb[(pk.word[k] >> (BITS * s)) & ((1u << BITS) - 1u)];
+      for (int hb = 1; hb < 16; hb <<= 1) {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          if (s & hb) continue;
+          const i16x2_t x = __builtin_bit_cast(i16x2_t, w[s]), y = __builtin_bit_cast(i16x2_t, w[s + hb]);
+          w[s] = __builtin_bit_cast(uint32_t, (i16x2_t)(x + y));
+          w[s + hb] = __builtin_bit_cast(uint32_t, (i16x2_t)(x - y));
+        }
+      }
+      // slot bit 4, inside each word: (lo, hi) -> (lo + hi, lo - hi), one v_pk_mad_u16
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const i16x2_t x = __builtin_bit_cast(i16x2_t, w[s]);
+        const i16x2_t pm = {1, -1};
+        w[s] = __builtin_bit_cast(uint32_t, (i16x2_t)(x.yy * pm + x.xx));
+      }
+      // value = zero + q * scale per group: H_32 of (zero * ones) puts 32 * zero on slot 0.
+      // The lane's inputs to the lane stages carry (-1)^popcount(l) so that the stages
+      // below (m = +1 on a set bit) yield the true coefficients, times 1/sqrt(D).
+      const float sc = f16_value(pk.sz & 0xffffu), z = f16_value(pk.sz >> 16);
+      const float S = sgn * norm_c * sc;
+      const float Z0 = sgn * norm_c * 32.0f * z;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        v[s] = (float)(short)(w[s] & 0xffffu) * S;
+        v[s + 16] = (float)((int)w[s] >> 16) * S;
+      }
+      v[0] = __builtin_fmaf((float)(short)(w[0] & 0xffffu), S, Z0);
+      const float p1 = (l & 1) ? 1.0f : -1.0f, p2 = (l & 2) ? 1.0f : -1.0f, p4 = (l & 4) ? 1.0f : -1.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fmac_x1(v + 8 * k, p1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fmac_x2(v + 8 * k, p2);
+      if constexpr (LV == 8) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(swz_x4(v[i]), p4, v[i]);
+      }
+    } else {
+      if constexpr (QUANT == Q_MINMAX) {
+        const float sc = f16_value(pk.sz & 0xffffu), z = f16_value(pk.sz >> 16);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf((float)code_at<BITS>(pk.c, i), sc, z);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = s_cb[code_at<BITS>(pk.c, i)];
       }
       float outscale = 1.0f;
       if constexpr (ROT == ROT_FWHT) {
-        fwht_lane<LV>(v, l);
+        const float m1 = (l & 1) ? -1.0f : 1.0f, m2 = (l & 2) ? -1.0f : 1.0f, m4 = (l & 4) ? -1.0f : 1.0f;
+        fwht_lane<LV>(v, m1, m2, m4);
         outscale = sgn * norm_c;
       } else if constexpr (ROT == ROT_SO4) {
         // inverse: M^T z (M orthogonal for unit quaternions)
 #pragma unroll
-        for (int k = 0; k < kNC; ++k)
+        for (int b = 0; b < 8; ++b) {
+          const float* m = &s_mat[16 * (8 * l + b)];
+          float* u = v + 4 * b;
+          const float u0 = u[0], u1 = u[1], u2 = u[2], u3 = u[3];
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int blk = (k * LV + l) * 2 + half;
-            const float* m = &s_mat[16 * blk];
-            float* u = v + 8 * k + 4 * half;
-            const float u0 = u[0], u1 = u[1], u2 = u[2], u3 = u[3];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              u[i] = __builtin_fmaf(m[i], u0,
-                     __builtin_fmaf(m[4 + i], u1, __builtin_fmaf(m[8 + i], u2, m[12 + i] * u3)));
-          }
+          for (int i = 0; i < 4; ++i)
+            u[i] = __builtin_fmaf(m[i], u0, __builtin_fmaf(m[4 + i], u1, __builtin_fmaf(m[8 + i], u2, m[12 + i] * u3)));
+        }
       }
       if constexpr (QUANT == Q_LLOYD) outscale *= pk.rho;
+      if (ROT == ROT_FWHT || QUANT == Q_LLOYD) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] *= outscale;
-      if (PERM_ANY && PERM) {
-        // scatter: out[perm[j]] = v[j], then read back in natural order
-#pragma unroll
-        for (int i = 0; i < 32; i += 4) {
-          const int4 o = *reinterpret_cast<const int4*>(poff + i);
-          *reinterpret_cast<float*>(vscratch + o.x) = v[i];
-          *reinterpret_cast<float*>(vscratch + o.y) = v[i + 1];
-          *reinterpret_cast<float*>(vscratch + o.z) = v[i + 2];
-          *reinterpret_cast<float*>(vscratch + o.w) = v[i + 3];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int k = 0; k < kNC; ++k) {
-          const float4* src = reinterpret_cast<const float4*>(vscratch + 32 * (k * LV + l));
-          const float4 p0 = src[0], p1 = src[1];
-          v[8 * k] = p0.x; v[8 * k + 1] = p0.y; v[8 * k + 2] = p0.z; v[8 * k + 3] = p0.w;
-          v[8 * k + 4] = p1.x; v[8 * k + 5] = p1.y; v[8 * k + 6] = p1.z; v[8 * k + 7] = p1.w;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int i = 0; i < 32; ++i) v[i] *= outscale;
       }
     }
-    constexpr int OES = (ODT == DT_F32) ? 4 : 2;
-    char* yrow = reinterpret_cast<char*>(a.y) + (c.r * ncols + c.tile * VPW) * D * OES;  // wave-uniform
-    const uint32_t ylane = (uint32_t)((q * D + l * 8) * OES);
-#pragma unroll
-    for (int k = 0; k < kNC; ++k) store_chunk_at<ODT>(yrow + ylane + k * LV * 8 * OES, v + 8 * k);
   };
 
-  // persistent loop over the wave's items with the next item's loads in flight
-  auto fetch = [&](Packed& pk, const Cursor& c) {
-    bool valid, is_sink;
-    int64_t srow;
-    lane_state(c, valid, is_sink, srow);
-    if (valid && !is_sink) load_packed(pk, c);
+  // One item: every valid lane puts its 32 outputs into its vector's staging row, then
+  // the wave stores the tile's output as contiguous 1 KiB runs (16 bytes per lane).
+  constexpr int ITEM_BYTES = VPW * D * OES;   // contiguous output bytes of a full tile
+  constexpr int NCHUNK = ITEM_BYTES / 1024;
+  constexpr int VBYTES = D * OES;             // output bytes per vector
+  auto process = [&](const Packed& pk, const LaneTile& lt, int64_t row) __attribute__((always_inline)) {
+    if (lt.valid) {
+      float v[32];
+      reconstruct(pk, v);
+      if constexpr (PERM_ANY) {
+        if (PERM) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) lds_st(saddr[i], v[i]);
+        }
+      }
+      if (!(PERM_ANY && PERM)) {
+        // the lane's 32 outputs in the output type, in order
+        if constexpr (ODT == DT_F32) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            u32x4_t w = {__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]), __float_as_uint(v[4 * k + 2]),
+                         __float_as_uint(v[4 * k + 3])};
+            lds_st4(row_addr + 128u * l + 16u * k, w);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            u32x4_t w;
+            if constexpr (ODT == DT_BF16) {
+              w.x = pack_bf16x2(v[8 * k + 0], v[8 * k + 1]);
+              w.y = pack_bf16x2(v[8 * k + 2], v[8 * k + 3]);
+              w.z = pack_bf16x2(v[8 * k + 4], v[8 * k + 5]);
+              w.w = pack_bf16x2(v[8 * k + 6], v[8 * k + 7]);
+            } else {
+              w.x = pack_f16x2(v[8 * k + 0], v[8 * k + 1]);
+              w.y = pack_f16x2(v[8 * k + 2], v[8 * k + 3]);
+              w.z = pack_f16x2(v[8 * k + 4], v[8 * k + 5]);
+              w.w = pack_f16x2(v[8 * k + 6], v[8 * k + 7]);
+            }
+            lds_st4(row_addr + 64u * l + 16u * k, w);
+          }
+        }
+      }
+    }
+    wave_lds_sync();
+    // contiguous stores: chunk c, lane L covers output bytes c*1024 + L*16 of the tile
+    const int64_t nvalid = ncols - lt.tile * VPW;  // vectors of this tile that exist (wave-uniform)
+    char* ybase = reinterpret_cast<char*>(a.y) + (row * ncols + lt.tile * VPW) * (int64_t)VBYTES;
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) {
+      const int off = c * 1024 + lane * 16;
+      const int vq = off / VBYTES, inner = off % VBYTES;
+      if (vq < nvalid) {
+        u32x4_t w;
+        if (PERM_ANY && PERM) {
+          // rows hold floats: 16 output bytes = 16/OES floats
+          const uint32_t src = wave_addr + (uint32_t)(vq * row_bytes<D>() + inner * (4 / OES));
+          if constexpr (ODT == DT_F32) {
+            w = lds_ld4(src);
+          } else {
+            const u32x4_t f0 = lds_ld4(src), f1 = lds_ld4(src + 16u);
+            const float f[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
+                                __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
+                                __uint_as_float(f1.z), __uint_as_float(f1.w)};
+            if constexpr (ODT == DT_BF16) {
+              w.x = pack_bf16x2(f[0], f[1]); w.y = pack_bf16x2(f[2], f[3]);
+              w.z = pack_bf16x2(f[4], f[5]); w.w = pack_bf16x2(f[6], f[7]);
+            } else {
+              w.x = pack_f16x2(f[0], f[1]); w.y = pack_f16x2(f[2], f[3]);
+              w.z = pack_f16x2(f[4], f[5]); w.w = pack_f16x2(f[6], f[7]);
+            }
+          }
+        } else {
+          w = lds_ld4(wave_addr + (uint32_t)(vq * row_bytes<D>() + inner));
+        }
+        *reinterpret_cast<u32x4_t*>(ybase + off) = w;
+      }
+    }
+    wave_lds_sync();
   };
-  Cursor ca = first_cursor<VPW>(a, wid);
+
+  // persistent walk over the wave's items with the next item's packed planes in flight
+  LaneTile cur = lane_tile<VPW>(a, wk.tile, q);
   Packed pa, pb;
-  fetch(pa, ca);
-  for (int64_t it = wid; it < a.n_items; it += 2 * a.n_waves) {
-    Cursor cb = ca;
-    advance(a, cb);
-    const bool has_b = it + a.n_waves < a.n_items;
-    if (has_b) fetch(pb, cb);
-    process(pa, ca);
-    if (!has_b) break;
-    ca = cb;
-    advance(a, ca);
-    if (it + 2 * a.n_waves < a.n_items) fetch(pa, ca);
-    process(pb, cb);
+  fetch(pa, cur, wk.r);
+  LaneTile nxt = cur;
+  auto step = [&](Packed& now, Packed& later) __attribute__((always_inline)) -> bool {
+    Walk nw = wk;
+    const bool more = walk_next(a, wid, K, nw);
+    if (more) {
+      if (nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
+      fetch(later, nxt, nw.r);
+    }
+    process(now, cur, wk.r);
+    if (!more) return false;
+    wk = nw;
+    cur = nxt;
+    return true;
+  };
+  while (step(pa, pb) && step(pb, pa)) {
   }
+}
+
+// ---------------------------------------------------------------------------
+// ATTENTION SINKS
+// ---------------------------------------------------------------------------
+// Positions p < n_sink are kept as fp16 of the post-RoPE, unrotated vector.  The main
+// kernels treat every vector alike; these small kernels run after them on the same
+// stream and cover only the sink positions of the call: the encoder's writes the sink
+// plane and zeroes the vector's code, scale, zero and norm slots, the decoder's copies
+// the sink plane to the output.  One sub-wavefront per vector, as in the main kernels.
+__device__ __forceinline__ int64_t sink_tokens(const CodecArgs& a) {
+  const int64_t n = (int64_t)a.n_sink - a.pos_offset;
+  return n <= 0 ? 0 : (n < a.tokens ? n : a.tokens);
+}
+
+template <int DT, int D, int BITS, int QUANT>
+__global__ void __launch_bounds__(64 * kWavesPerBlock) encode_sink_kernel(const CodecArgs a) {
+  constexpr int LV = Geo<D>::LV;
+  constexpr int ES = (DT == DT_F32) ? 4 : 2;
+  constexpr int CB = D * BITS / 8;
+  const int64_t nt = sink_tokens(a);
+  const int64_t g = (int64_t)blockIdx.x * (blockDim.x / LV) + threadIdx.x / LV;  // (row, token, head)
+  const int l = threadIdx.x % LV;
+  if (g >= a.rows * nt * a.heads) return;
+  const int64_t h = g % a.heads, rt = g / a.heads, t = rt % nt, r = rt / nt;
+  const int64_t pos = a.pos_offset + t;
+  RawRow<DT> raw;
+  load_row<DT>(raw, reinterpret_cast<const char*>(a.x) + (r * a.sr + t * a.st + h * a.sh + 32 * l) * ES);
+  float v[32];
+  widen_row<DT>(raw, v);
+  if (a.rope) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int i = 16 * l + m;  // pair index
+      const double theta = exp2(-(2.0 * (double)i / (double)D) * a.rope_log2_base);
+      float c, sn;
+      rope_cos_sin(pos, theta, &c, &sn);
+      const float x0 = v[2 * m], x1 = v[2 * m + 1];
+      v[2 * m] = __builtin_fmaf(x0, c, -x1 * sn);
+      v[2 * m + 1] = __builtin_fmaf(x0, sn, x1 * c);
+    }
+  }
+  const int64_t srow = (r * a.n_sink + pos) * a.heads + h;
+  u32x4_t* sp = reinterpret_cast<u32x4_t*>(a.sink + srow * D + 32 * l);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u32x4_t w;
+    w.x = pack_f16x2(v[8 * k + 0], v[8 * k + 1]);
+    w.y = pack_f16x2(v[8 * k + 2], v[8 * k + 3]);
+    w.z = pack_f16x2(v[8 * k + 4], v[8 * k + 5]);
+    w.w = pack_f16x2(v[8 * k + 6], v[8 * k + 7]);
+    sp[k] = w;
+  }
+  const int64_t vec = (r * a.tokens + t) * a.heads + h;
+  LaneCodes<BITS> zc;
+#pragma unroll
+  for (int w = 0; w < BITS; ++w) zc.w[w] = 0u;
+  store_lane_codes<BITS>(a.codes + vec * CB + l * (4 * BITS), zc);
+  if constexpr (QUANT == Q_MINMAX) {
+    const int LB = a.group_log2 - 5;
+    const int64_t ngroups = D >> a.group_log2;
+    if ((l & ((1 << LB) - 1)) == 0) {
+      a.scale[vec * ngroups + (l >> LB)] = 0;
+      a.zero[vec * ngroups + (l >> LB)] = 0;
+    }
+  } else {
+    if (l == 0) a.norm[vec] = 0.0f;
+  }
+}
+
+template <int ODT, int D>
+__global__ void __launch_bounds__(64 * kWavesPerBlock) decode_sink_kernel(const CodecArgs a) {
+  constexpr int LV = Geo<D>::LV;
+  const int64_t nt = sink_tokens(a);
+  const int64_t g = (int64_t)blockIdx.x * (blockDim.x / LV) + threadIdx.x / LV;
+  const int l = threadIdx.x % LV;
+  if (g >= a.rows * nt * a.heads) return;
+  const int64_t h = g % a.heads, rt = g / a.heads, t = rt % nt, r = rt / nt;
+  const int64_t pos = a.pos_offset + t;
+  const int64_t srow = (r * a.n_sink + pos) * a.heads + h;
+  const u32x4_t* sp = reinterpret_cast<const u32x4_t*>(a.sink + srow * D + 32 * l);
+  const int64_t vec = (r * a.tokens + t) * a.heads + h;
+  if constexpr (ODT == DT_F16) {
+    u32x4_t* yp = reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(a.y) + vec * D + 32 * l);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) yp[k] = sp[k];
+  } else {
+    float v[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4_t w = sp[k];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * k + 2 * i] = f16_value(ws[i] & 0xffffu);
+        v[8 * k + 2 * i + 1] = f16_value(ws[i] >> 16);
+      }
+    }
+    if constexpr (ODT == DT_F32) {
+      u32x4_t* yp = reinterpret_cast<u32x4_t*>(reinterpret_cast<float*>(a.y) + vec * D + 32 * l);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        u32x4_t w = {__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]), __float_as_uint(v[4 * k + 2]),
+                     __float_as_uint(v[4 * k + 3])};
+        yp[k] = w;
+      }
+    } else {
+      u32x4_t* yp = reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(a.y) + vec * D + 32 * l);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u32x4_t w;
+        w.x = pack_bf16x2(v[8 * k + 0], v[8 * k + 1]);
+        w.y = pack_bf16x2(v[8 * k + 2], v[8 * k + 3]);
+        w.z = pack_bf16x2(v[8 * k + 4], v[8 * k + 5]);
+        w.w = pack_bf16x2(v[8 * k + 6], v[8 * k + 7]);
+        yp[k] = w;
+      }
+    }
+  }
+}
+
+// Grid of a sink pass: one sub-wavefront per sink vector of the call.
+inline unsigned sink_blocks(const CodecArgs& a, int lv) {
+  const int64_t n = (int64_t)a.n_sink - a.pos_offset;
+  const int64_t nt = n <= 0 ? 0 : (n < a.tokens ? n : a.tokens);
+  const int64_t nvec = a.rows * nt * a.heads;
+  const int64_t per_block = 64 * kWavesPerBlock / lv;
+  return (unsigned)((nvec + per_block - 1) / per_block);
 }
 
 // ---------------------------------------------------------------------------
 // launch dispatch
 // ---------------------------------------------------------------------------
 // Grid of a persistent launch: as many blocks as can be resident at once (occupancy
-// of this kernel instance x compute units), but no more than there are items.  The
-// cursor step constants follow from the wave count.
-// Grid of a persistent launch: as many blocks as can be resident at once (occupancy
-// of the kernel instance x compute units), but no more than there are items.  The
-// cursor step constants follow from the wave count.  ``per_cu`` caches the occupancy
-// of the instance (a property of the kernel and the gfx950 target, 0 = not yet known).
-template <int D>
+// of the kernel instance x compute units), but no more than there are items.
+// ``per_cu`` caches the occupancy of the instance (0 = not yet known).
 int plan_grid(const void* kernel, size_t lds, int& per_cu, CodecArgs& b, unsigned& nb) {
-  constexpr int VPW = Geo<D>::VPW;
   static thread_local int cached_dev = -1, cu = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1131,51 +1292,56 @@ int plan_grid(const void* kernel, size_t lds, int& per_cu, CodecArgs& b, unsigne
   const int64_t blocks = std::min<int64_t>(need, (int64_t)per_cu * cu);
   nb = (unsigned)blocks;
   b.n_waves = blocks * kWavesPerBlock;
-  b.step_rows = b.n_waves / b.n_tiles;
-  b.step_tiles = b.n_waves % b.n_tiles;
-  b.step_tok = b.step_tiles * VPW / b.heads;
-  b.step_head = b.step_tiles * VPW % b.heads;
-  b.wrap_tok = b.n_tiles * VPW / b.heads;
-  b.wrap_head = b.n_tiles * VPW % b.heads;
-  b.heads_magic = (b.heads >= 2) ? (uint32_t)(((1ull << 32) + (uint64_t)b.heads - 1) / (uint64_t)b.heads) : 0u;
   return 0;
-}
-
-template <int D>
-inline size_t scratch_bytes(bool needed) {
-  return needed ? (size_t)kWavesPerBlock * scratch_wave_bytes<D>() : 0;
 }
 
 template <int DT, int D, int BITS, int ROT, int QUANT, int RT, int PT, int GBT>
 int launch_enc_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
   const void* k = reinterpret_cast<const void*>(&encode_kernel<DT, D, BITS, ROT, QUANT, RT, PT, GBT>);
-  const size_t lds = scratch_bytes<D>(a.use_perm || a.rope);
-  static std::atomic<int> occ[2];  // by whether the LDS scratch is allocated
-  int per_cu = occ[lds > 0].load(std::memory_order_relaxed);
+  constexpr int VPW = Geo<D>::VPW;
   CodecArgs b = a;
+  // tokens a tile of VPW columns can span: floor((h0 + VPW - 1) / heads) + 1, h0 < heads
+  b.trig_rows = (int32_t)std::min<int64_t>(VPW, (a.heads - 1 + VPW - 1) / a.heads + 1);
+  const size_t lds = (size_t)kWavesPerBlock * enc_wave_bytes<D>(a.use_perm != 0, a.rope != 0, b.trig_rows);
+  // occupancy cache by staging size (it depends on the LDS the launch asks for)
+  static std::atomic<int> occ[4];
+  static std::atomic<size_t> occ_lds[4];
+  const int slot = (a.use_perm ? 1 : 0) + (a.rope ? 2 : 0);
+  int per_cu = occ_lds[slot].load(std::memory_order_relaxed) == lds ? occ[slot].load(std::memory_order_relaxed) : 0;
   unsigned nb = 0;
-  if (int e = plan_grid<D>(k, lds, per_cu, b, nb)) return e;
-  occ[lds > 0].store(per_cu, std::memory_order_relaxed);
+  if (int e = plan_grid(k, lds, per_cu, b, nb)) return e;
+  occ[slot].store(per_cu, std::memory_order_relaxed);
+  occ_lds[slot].store(lds, std::memory_order_relaxed);
   hipLaunchKernelGGL((encode_kernel<DT, D, BITS, ROT, QUANT, RT, PT, GBT>), dim3(nb), dim3(64 * kWavesPerBlock),
                      lds, s, b);
-  return (int)hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  if (const unsigned ns = sink_blocks(a, Geo<D>::LV)) {
+    hipLaunchKernelGGL((encode_sink_kernel<DT, D, BITS, QUANT>), dim3(ns), dim3(64 * kWavesPerBlock), 0, s, b);
+    return (int)hipGetLastError();
+  }
+  return 0;
 }
 
 template <int ODT, int D, int BITS, int ROT, int QUANT, int PT>
 int launch_dec_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
   const void* k = reinterpret_cast<const void*>(&decode_kernel<ODT, D, BITS, ROT, QUANT, PT>);
-  const size_t lds = scratch_bytes<D>(a.use_perm);
-  static std::atomic<int> occ[2];  // by whether the LDS scratch is allocated
-  int per_cu = occ[lds > 0].load(std::memory_order_relaxed);
+  const size_t lds = (size_t)kWavesPerBlock * stage_wave_bytes<D>();
+  static std::atomic<int> occ{0};
+  int per_cu = occ.load(std::memory_order_relaxed);
   CodecArgs b = a;
   unsigned nb = 0;
-  if (int e = plan_grid<D>(k, lds, per_cu, b, nb)) return e;
-  occ[lds > 0].store(per_cu, std::memory_order_relaxed);
-  hipLaunchKernelGGL((decode_kernel<ODT, D, BITS, ROT, QUANT, PT>), dim3(nb), dim3(64 * kWavesPerBlock),
-                     lds, s, b);
-  return (int)hipGetLastError();
+  if (int e = plan_grid(k, lds, per_cu, b, nb)) return e;
+  occ.store(per_cu, std::memory_order_relaxed);
+  hipLaunchKernelGGL((decode_kernel<ODT, D, BITS, ROT, QUANT, PT>), dim3(nb), dim3(64 * kWavesPerBlock), lds, s,
+                     b);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  if (const unsigned ns = sink_blocks(a, Geo<D>::LV)) {
+    hipLaunchKernelGGL((decode_sink_kernel<ODT, D>), dim3(ns), dim3(64 * kWavesPerBlock), 0, s, b);
+    return (int)hipGetLastError();
+  }
+  return 0;
 }
 
 // FWHT + min-max, the hot configurations: RoPE, permutation and group size fixed at
