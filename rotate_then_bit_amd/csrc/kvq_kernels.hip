@@ -533,16 +533,6 @@ __device__ __forceinline__ uint32_t code_at(const LaneCodes<BITS>& c, int i) {
   }
 }
 
-// acc + sum of pat[S] << BITS*S, as a chain of (a << sh) + b (one v_lshl_add each)
-template <int BITS, int S>
-__device__ __forceinline__ uint32_t pack_word(const uint32_t* pat, uint32_t acc) {
-  if constexpr (S == 32 / BITS) {
-    return acc;
-  } else {
-    return pack_word<BITS, S + 1>(pat, (pat[S] << (BITS * S)) + acc);
-  }
-}
-
 // Per-wave encoder staging: permutation rows (when a permutation is used), then the
 // RoPE table of the wave's tile: trig_rows rows of D/2 (cos, sin) float pairs.
 template <int D>
@@ -606,7 +596,10 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   if constexpr (PERM_ANY) {
     if (PERM) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) gaddr[i] = row_addr + 4u * (uint32_t)a.perm[32 * l + i];
+      for (int i = 0; i < 32; ++i) {
+        gaddr[i] = row_addr + 4u * (uint32_t)a.perm[32 * l + i];
+        asm volatile("" : "+v"(gaddr[i]));  // keep the sums (not offsets re-added per item)
+      }
     }
   }
 
@@ -767,50 +760,53 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
         a.zero[vec * ngroups + (l >> LB)] = (uint16_t)zb;
       }
       const float iv = (sc > 0.0f) ? __builtin_amdgcn_rcpf(sc) : 0.0f;
-      // q = rint((A v - zero) / scale), nearest-even: adding 1.5 * 2^23 inside the fma
-      // rounds the exact product to an integer, which then sits in the low mantissa bits
-      // (bit pattern 0x4B400000 + q, since -eps <= t <= 2^b - 1 + eps).
-      constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-      auto code_of = [&](float x) -> uint32_t {
-        const float d = __builtin_fmaf(x, A, -z);
-        float tq;
-        if constexpr (ROT == ROT_NONE) {
-          // unrotated fp16/bf16 data sit on the same grid as zero/scale, so exact
-          // half-way quotients are common: one residual step makes d/scale correctly
-          // rounded before the integer rounding
+      // q = rint(t), nearest-even, with t = (A v - zero) / scale for the 32 slots
+      float tv[32];
+      if constexpr (ROT == ROT_NONE) {
+        // q = rint(t): unrotated fp16/bf16 data sit on the same grid as zero/scale, so
+        // exact half-way quotients are common; one residual step makes d / scale
+        // correctly rounded before the integer rounding
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float d = __builtin_fmaf(v[i], A, -z);
           const float t0 = d * iv;
-          const float t1 = __builtin_fmaf(__builtin_fmaf(-t0, sc, d), iv, t0);
-          tq = (sc > 0.0f ? t1 : 0.0f) + kMagic;
-        } else {
-          tq = __builtin_fmaf(d, iv, kMagic);
+          tv[i] = (sc > 0.0f) ? __builtin_fmaf(__builtin_fmaf(-t0, sc, d), iv, t0) : 0.0f;
         }
-        return __float_as_uint(tq);
-      };
+      } else {
+        const float Ai = A * iv, c0 = -z * iv;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) tv[i] = __builtin_fmaf(v[i], Ai, c0);
+      }
       if constexpr (BITS == 3) {
+        // q = rint(t) via 1.5 * 2^23: the sum rounds t to an integer in the low mantissa
+        // bits (bit pattern 0x4B400000 + q, since -eps <= t <= 2^b - 1 + eps)
+        constexpr float kMagic = 12582912.0f;
 #pragma unroll
         for (int w = 0; w < 3; ++w) cw.w[w] = 0u;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const uint32_t cq = code_of(v[i]) - 0x4B400000u;
+          const uint32_t cq = __float_as_uint(tv[i] + kMagic) - 0x4B400000u;
           const int bit = 3 * i, w = bit >> 5, sh = bit & 31;
           cw.w[w] |= cq << sh;
           if (sh > 29) cw.w[w + 1] |= cq >> (32 - sh);
         }
       } else {
-        // the codes are accumulated as (pattern << BITS*s) sums and the constant part
-        // subtracted once per word
-        constexpr int PER = 32 / BITS;
-        constexpr uint32_t kMagicSum = [] {
-          uint32_t c = 0;
-          for (int s = 0; s < 32 / BITS; ++s) c += 0x4B400000u << (BITS * s);
-          return c;
-        }();
+        // v_cvt_pk_u8_f32 (round to nearest even, clamped at 0) writes code k + ND j into
+        // byte j of dword D_k; the word is D_0 + D_1 << BITS + ... (each byte's code
+        // lands on its own BITS-bit field)
+        constexpr int PER = 32 / BITS;  // codes per word
+        constexpr int ND = PER / 4;     // dwords D_k per word
 #pragma unroll
         for (int w = 0; w < BITS; ++w) {
-          uint32_t pat[PER];
+          uint32_t word = 0;
 #pragma unroll
-          for (int s = 0; s < PER; ++s) pat[s] = code_of(v[PER * w + s]);
-          cw.w[w] = pack_word<BITS, 0>(pat, 0u - kMagicSum);
+          for (int k = ND - 1; k >= 0; --k) {
+            uint32_t d = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_cvt_pk_u8_f32(tv[PER * w + k + ND * j], j, d);
+            word = (word << BITS) + d;
+          }
+          cw.w[w] = word;
         }
       }
     } else {
