@@ -31,14 +31,18 @@ struct CodecArgs {
   int32_t rope;
   int32_t use_perm;
   // work decomposition: an item is (tile of VPW consecutive (token, head) columns, row).
-  // With W waves in the grid, wave w first takes tiles w, w + W, ..., w + (K-1) W (all
-  // rows of each, K = n_tiles / W), so the waves in flight cover W adjacent tiles of one
-  // row at a time; the remaining n_tiles - K W tiles are split into equal contiguous runs
-  // of (tile, row) items, one per wave.
-  int64_t n_tiles;     // tiles per row
-  int64_t n_items;     // rows * n_tiles
-  int64_t n_waves;     // waves in the grid (set by the launcher)
-  int32_t trig_rows;   // RoPE table rows per wave: tokens one tile can span (set by the launcher)
+  // Two walks (set by the launcher):
+  //  - tasks (rows_per_task = k > 0): one wave per (tile, run of k consecutive rows), wave
+  //    w taking tile w % n_tiles and rows k * (w / n_tiles) ...; the grid holds every task.
+  //  - persistent (rows_per_task = 0): W waves, as many as fit; wave w first takes tiles
+  //    w, w + W, ..., w + (K-1) W (all rows of each, K = n_tiles / W), so the waves in
+  //    flight cover W adjacent tiles of one row at a time; the remaining n_tiles - K W
+  //    tiles are split into equal contiguous runs of (tile, row) items, one per wave.
+  int64_t n_tiles;        // tiles per row
+  int64_t n_items;        // rows * n_tiles
+  int64_t n_waves;        // waves in the grid (set by the launcher)
+  int32_t rows_per_task;  // 0: persistent walk (set by the launcher)
+  int32_t trig_rows;      // RoPE table rows per wave: tokens one tile can span (set by the launcher)
   // parameters
   uint8_t perm[kMaxHeadDim];
   float quat[kMaxHeadDim / 4 * 8];

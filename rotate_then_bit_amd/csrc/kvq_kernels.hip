@@ -44,6 +44,7 @@ enum { ROT_NONE = 0, ROT_FWHT = 1, ROT_SO4 = 2 };
 enum { Q_MINMAX = 0, Q_LLOYD = 1 };
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x3_t __attribute__((ext_vector_type(3)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) float lds_f32;
@@ -74,6 +75,23 @@ __device__ __forceinline__ float lds_ld(uint32_t addr) { return *(const lds_f32*
 __device__ __forceinline__ void lds_st(uint32_t addr, float v) { *(lds_f32*)(uintptr_t)addr = v; }
 __device__ __forceinline__ u32x4_t lds_ld4(uint32_t addr) { return *(const lds_u32x4*)(uintptr_t)addr; }
 __device__ __forceinline__ void lds_st4(uint32_t addr, u32x4_t v) { *(lds_u32x4*)(uintptr_t)addr = v; }
+
+// Raw buffer accesses: a wave-uniform descriptor (base address and size in bytes, in
+// SGPRs) plus a per-lane byte offset.  A lane whose access starts at or beyond the size
+// reads zeros and its store is dropped.  Sizing each descriptor to the part of the tensor
+// an item may touch makes lanes past the end of a tensor (and the prefetch after a wave's
+// last item, with size 0) harmless without any branch or per-lane select, so the hot
+// loops stay straight-line and the next item's loads stay in flight while the current
+// item is computed.  The sizes are whole vectors (or a whole row of the input, whose
+// strides are multiples of 16 bytes), so each lane's access lies wholly inside or wholly
+// outside its descriptor.
+typedef __amdgpu_buffer_rsrc_t buf_t;
+constexpr int kBufWord3 = 0x00020000;  // descriptor word 3 for untyped access on gfx9
+constexpr int kNT = 2;                 // cache-policy bit: non-temporal
+__device__ __forceinline__ buf_t make_buf(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufWord3);
+}
 
 // Orders this wave's LDS accesses before and after the call (LDS ops of one wave are
 // executed in order; this keeps the compiler from moving them across).
@@ -245,6 +263,11 @@ template <int DT>
 __device__ __forceinline__ void load_row(RawRow<DT>& raw, const char* p) {
 #pragma unroll
   for (int k = 0; k < RawRow<DT>::NW; ++k) raw.w[k] = reinterpret_cast<const u32x4_t*>(p)[k];
+}
+template <int DT>
+__device__ __forceinline__ void load_row(RawRow<DT>& raw, buf_t b, uint32_t off) {
+#pragma unroll
+  for (int k = 0; k < RawRow<DT>::NW; ++k) raw.w[k] = __builtin_amdgcn_raw_buffer_load_b128(b, off + 16u * k, 0, 0);
 }
 
 template <int DT>
@@ -425,13 +448,13 @@ __device__ __forceinline__ LaneTile lane_tile(const CodecArgs& a, int64_t tile, 
   return lt;
 }
 
-// A wave's walk over its items: first rounds j = 0..K-1 of whole tiles (tile j*W + wid,
-// rows 0..R-1), then its share [t, t1) of the leftover (tile, row) items, numbered
-// tile-major from tile K*W on.
+// A wave's walk over its items.  Task walk: tile wid % n_tiles, rows [r, t1).  Persistent
+// walk: first rounds j = 0..K-1 of whole tiles (tile j*W + wid, rows 0..R-1), then its
+// share [t, t1) of the leftover (tile, row) items, numbered tile-major from tile K*W on.
 struct Walk {
   int64_t tile, r;  // current item
-  int64_t j;        // current round, or -1 in the leftover part
-  int64_t t, t1;    // leftover part: current index and end
+  int64_t j;        // current round, or -1 in the leftover part (persistent walk)
+  int64_t t, t1;    // leftover part: current index and end; task walk: t1 = end row
 };
 
 __device__ __forceinline__ bool walk_leftover(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
@@ -448,6 +471,12 @@ __device__ __forceinline__ bool walk_leftover(const CodecArgs& a, int64_t wid, i
 }
 
 __device__ __forceinline__ bool walk_first(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
+  if (a.rows_per_task > 0) {
+    w.tile = wid % a.n_tiles;
+    w.r = (wid / a.n_tiles) * a.rows_per_task;
+    w.t1 = min(w.r + a.rows_per_task, a.rows);
+    return w.r < a.rows;
+  }
   if (K > 0) {
     w.j = 0;
     w.tile = wid;
@@ -458,6 +487,7 @@ __device__ __forceinline__ bool walk_first(const CodecArgs& a, int64_t wid, int6
 }
 
 __device__ __forceinline__ bool walk_next(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
+  if (a.rows_per_task > 0) return ++w.r < w.t1;
   if (w.j >= 0) {
     if (++w.r < a.rows) return true;
     if (++w.j < K) {
@@ -475,6 +505,38 @@ __device__ __forceinline__ bool walk_next(const CodecArgs& a, int64_t wid, int64
   return true;
 }
 
+// Persistent walk: all waves start with the same number of items, but the SIMD arbiter
+// favours older waves, so without help some waves finish long before others and the
+// launch ends with a thinly occupied tail.  Each wave lowers its priority (3 .. 0) as it
+// gets through its items, which lets the waves behind catch up.
+struct Prio {
+  int64_t total, done;
+  int lvl;
+};
+__device__ __forceinline__ void prio_init(const CodecArgs& a, int64_t wid, int64_t K, Prio& p) {
+  p.total = 0;
+  p.done = 0;
+  p.lvl = 3;
+  if (a.rows_per_task > 0) return;
+  const int64_t n = (a.n_tiles - K * a.n_waves) * a.rows;
+  p.total = K * a.rows + ((wid + 1) * n / a.n_waves - wid * n / a.n_waves);
+  __builtin_amdgcn_s_setprio(3);
+}
+__device__ __forceinline__ void prio_step(Prio& p) {
+  if (p.total == 0) return;
+  ++p.done;
+  const int lvl = 3 - (int)((4 * p.done) / (p.total + 1));
+  if (lvl != p.lvl) {
+    p.lvl = lvl;
+    switch (lvl) {
+      case 3: __builtin_amdgcn_s_setprio(3); break;
+      case 2: __builtin_amdgcn_s_setprio(2); break;
+      case 1: __builtin_amdgcn_s_setprio(1); break;
+      default: __builtin_amdgcn_s_setprio(0); break;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bit-packing of a lane's 32 codes (4*BITS bytes, code i at bits BITS*i)
 // ---------------------------------------------------------------------------
@@ -484,6 +546,16 @@ struct LaneCodes {
   uint32_t w[NW];
 };
 
+template <int BITS>
+__device__ __forceinline__ void store_lane_codes(buf_t b, uint32_t off, const LaneCodes<BITS>& c) {
+  if constexpr (BITS == 2) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{c.w[0], c.w[1]}, b, off, 0, 0);
+  } else if constexpr (BITS == 4) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{c.w[0], c.w[1], c.w[2], c.w[3]}, b, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b96(u32x3_t{c.w[0], c.w[1], c.w[2]}, b, off, 0, 0);
+  }
+}
 template <int BITS>
 __device__ __forceinline__ void store_lane_codes(uint8_t* p, const LaneCodes<BITS>& c) {
   if constexpr (BITS == 2) {
@@ -501,22 +573,22 @@ __device__ __forceinline__ void store_lane_codes(uint8_t* p, const LaneCodes<BIT
 }
 
 template <int BITS>
-__device__ __forceinline__ void load_lane_codes(const uint8_t* p, LaneCodes<BITS>& c) {
+__device__ __forceinline__ void load_lane_codes(buf_t b, uint32_t off, LaneCodes<BITS>& c) {
   if constexpr (BITS == 2) {
-    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(b, off, 0, kNT);
     c.w[0] = v.x;
     c.w[1] = v.y;
   } else if constexpr (BITS == 4) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, kNT);
     c.w[0] = v.x;
     c.w[1] = v.y;
     c.w[2] = v.z;
     c.w[3] = v.w;
   } else {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
-    c.w[0] = __builtin_nontemporal_load(s);
-    c.w[1] = __builtin_nontemporal_load(s + 1);
-    c.w[2] = __builtin_nontemporal_load(s + 2);
+    const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(b, off, 0, kNT);
+    c.w[0] = v.x;
+    c.w[1] = v.y;
+    c.w[2] = v.z;
   }
 }
 
@@ -577,6 +649,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   const int64_t K = a.n_tiles / a.n_waves;  // rounds of whole tiles
   Walk wk;
   if (!walk_first(a, wid, K, wk)) return;  // wave-uniform; no barrier follows
+  Prio pr;
+  prio_init(a, wid, K, pr);
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
@@ -596,8 +670,10 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   if constexpr (PERM_ANY) {
     if (PERM) {
 #pragma unroll
+      for (int i = 0; i < 32; ++i) gaddr[i] = a.perm[32 * l + i];
+#pragma unroll
       for (int i = 0; i < 32; ++i) {
-        gaddr[i] = row_addr + 4u * (uint32_t)a.perm[32 * l + i];
+        gaddr[i] = row_addr + 4u * gaddr[i];
         asm volatile("" : "+v"(gaddr[i]));  // keep the sums (not offsets re-added per item)
       }
     }
@@ -632,16 +708,22 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       }
     }
   };
-  auto lane_in = [&](const LaneTile& lt, int64_t row) __attribute__((always_inline)) -> const char* {
-    const char* base = reinterpret_cast<const char*>(a.x) + (row * a.sr + lt.t0 * a.st) * ES;
-    const uint32_t loff = (uint32_t)(((int64_t)lt.dtok * a.st + (int64_t)lt.h * a.sh + 32 * l) * ES);
-    return base + loff;
+  // input of an item: from the tile's first token of the row (wave-uniform) up to the
+  // row's last element; lanes of columns past the end start beyond it.  The lane's offset
+  // fits in 31 bits (checked on the host).
+  auto in_buf = [&](const LaneTile& lt, int64_t row, bool on) __attribute__((always_inline)) -> buf_t {
+    const int64_t span = ((a.tokens - 1 - lt.t0) * a.st + (a.heads - 1) * a.sh + D) * ES;
+    return make_buf(reinterpret_cast<const char*>(a.x) + (on ? (row * a.sr + lt.t0 * a.st) * ES : 0),
+                    on ? span : 0);
+  };
+  auto in_off = [&](const LaneTile& lt) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)(((int64_t)lt.dtok * a.st + (int64_t)lt.h * a.sh + 32 * l) * ES);
   };
 
+  // Every lane computes; the stores of lanes past the end of the tensor are dropped.
   auto process = [&](const RawRow<DT>& raw, const LaneTile& lt, int64_t row) __attribute__((always_inline)) {
-    if (!lt.valid) return;
-    const int64_t vec = row * ncols + lt.tile * VPW + q;  // index into the packed planes
-    uint8_t* rec = a.codes + vec * CB + l * (4 * BITS);
+    const int64_t vec0 = row * ncols + lt.tile * VPW;        // first vector of the item in the planes
+    const int64_t nvalid = min(ncols - lt.tile * VPW, (int64_t)VPW);  // vectors of the item that exist
     float v[32];
     // RoPE of the 4 channel pairs of 8 consecutive slots 8c .. 8c + 7
     auto rope8 = [&](float* u, int c) __attribute__((always_inline)) {
@@ -715,7 +797,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       const float inv = 1.0f / (rho + 1e-6f);
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] *= inv;
-      if (l == 0) a.norm[vec] = rho;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rho), make_buf(a.norm + vec0, 4 * nvalid),
+                                            4u * (uint32_t)q, 0, 0);
     }
     if constexpr (ROT == ROT_FWHT) {
       fwht_lane<LV, FUSED ? 2 : 0>(v, m1, m2, m4);
@@ -755,9 +838,12 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       constexpr float kInvLevels = 1.0f / (float)((1 << BITS) - 1);
       const uint32_t sb = f16_round_up((mx - z) * kInvLevels + 0.0f);
       const float sc = f16_value(sb);
-      if ((l & ((1 << LB) - 1)) == 0) {
-        a.scale[vec * ngroups + (l >> LB)] = (uint16_t)sb;
-        a.zero[vec * ngroups + (l >> LB)] = (uint16_t)zb;
+      {
+        // every lane of a group holds the same values and stores them
+        const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
+        const int64_t gbytes = 2 * nvalid * ngroups;
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sb, make_buf(a.scale + vec0 * ngroups, gbytes), go, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)zb, make_buf(a.zero + vec0 * ngroups, gbytes), go, 0, 0);
       }
       const float iv = (sc > 0.0f) ? __builtin_amdgcn_rcpf(sc) : 0.0f;
       // q = rint(t), nearest-even, with t = (A v - zero) / scale for the 32 slots
@@ -828,22 +914,24 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
         if (BITS == 3 && sh > 29) cw.w[w + 1] |= c >> (32 - sh);
       }
     }
-    store_lane_codes<BITS>(rec, cw);
+    store_lane_codes<BITS>(make_buf(a.codes + vec0 * CB, CB * nvalid), (uint32_t)(q * CB + l * (4 * BITS)), cw);
   };
 
   // persistent walk over the wave's items with the next item's loads in flight
   set_trig(cur);
   RawRow<DT> ra, rb;
-  if (cur.valid) load_row<DT>(ra, lane_in(cur, wk.r));
+  load_row<DT>(ra, in_buf(cur, wk.r, true), in_off(cur));
   LaneTile nxt = cur;
   auto step = [&](RawRow<DT>& now, RawRow<DT>& later) __attribute__((always_inline)) -> bool {
     Walk nw = wk;
     const bool more = walk_next(a, wid, K, nw);
-    if (more) {
-      if (nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
-      if (nxt.valid) load_row<DT>(later, lane_in(nxt, nw.r));
-    }
+    if (more && nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
+    // the next item's loads go out before this item's work (after the last item they
+    // fall outside the buffer and move nothing)
+    load_row<DT>(later, in_buf(nxt, nw.r, more), in_off(nxt));
+    __builtin_amdgcn_sched_barrier(0);
     process(now, cur, wk.r);
+    prio_step(pr);
     if (!more) return false;
     wk = nw;
     if (nxt.tile != cur.tile) {
@@ -888,6 +976,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   const int64_t K = a.n_tiles / a.n_waves;  // rounds of whole tiles
   Walk wk;
   if (!walk_first(a, wid, K, wk)) return;  // wave-uniform; no barrier follows
+  Prio pr;
+  prio_init(a, wid, K, pr);
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
@@ -916,15 +1006,20 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     uint32_t sz;  // scale | zero << 16 (min-max)
     float rho;    // Lloyd-Max
   };
-  auto fetch = [&](Packed& pk, const LaneTile& lt, int64_t row) __attribute__((always_inline)) {
-    if (!lt.valid) return;
-    const int64_t vec = row * ncols + lt.tile * VPW + q;
-    load_lane_codes<BITS>(a.codes + vec * CB + l * (4 * BITS), pk.c);
+  // the packed planes of item (tile, row); with on == false (wave-uniform) nothing is read
+  auto fetch = [&](Packed& pk, const LaneTile& lt, int64_t row, bool on) __attribute__((always_inline)) {
+    const int64_t vec0 = on ? row * ncols + lt.tile * VPW : 0;  // first vector of the item
+    const int64_t nvalid = on ? min(ncols - lt.tile * VPW, (int64_t)VPW) : 0;  // its vectors that exist
+    load_lane_codes<BITS>(make_buf(a.codes + vec0 * CB, CB * nvalid), (uint32_t)(q * CB + l * (4 * BITS)), pk.c);
     if constexpr (QUANT == Q_MINMAX) {
-      const int64_t gi = vec * ngroups + (l >> LB);
-      pk.sz = (uint32_t)a.scale[gi] | ((uint32_t)a.zero[gi] << 16);
+      const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
+      const int64_t gbytes = 2 * nvalid * ngroups;
+      const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.scale + vec0 * ngroups, gbytes), go, 0, kNT);
+      const uint32_t zr = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.zero + vec0 * ngroups, gbytes), go, 0, kNT);
+      pk.sz = sc | (zr << 16);
     } else {
-      pk.rho = a.norm[vec];
+      pk.rho = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(make_buf(a.norm + vec0, 4 * nvalid), 4u * (uint32_t)q, 0, kNT));
     }
   };
 
@@ -1031,13 +1126,14 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     }
   };
 
-  // One item: every valid lane puts its 32 outputs into its vector's staging row, then
-  // the wave stores the tile's output as contiguous 1 KiB runs (16 bytes per lane).
+  // One item: every lane puts its 32 outputs into its vector's staging row, then the wave
+  // stores the tile's output as contiguous 1 KiB runs (16 bytes per lane); the runs of
+  // vectors past the end of the tensor fall outside the store descriptor.
   constexpr int ITEM_BYTES = VPW * D * OES;   // contiguous output bytes of a full tile
   constexpr int NCHUNK = ITEM_BYTES / 1024;
   constexpr int VBYTES = D * OES;             // output bytes per vector
   auto process = [&](const Packed& pk, const LaneTile& lt, int64_t row) __attribute__((always_inline)) {
-    if (lt.valid) {
+    {
       float v[32];
       reconstruct(pk, v);
       if constexpr (PERM_ANY) {
@@ -1077,13 +1173,14 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     }
     wave_lds_sync();
     // contiguous stores: chunk c, lane L covers output bytes c*1024 + L*16 of the tile
-    const int64_t nvalid = ncols - lt.tile * VPW;  // vectors of this tile that exist (wave-uniform)
-    char* ybase = reinterpret_cast<char*>(a.y) + (row * ncols + lt.tile * VPW) * (int64_t)VBYTES;
+    const int64_t nvalid = min(ncols - lt.tile * VPW, (int64_t)VPW);  // vectors of this tile that exist
+    const buf_t yb = make_buf(reinterpret_cast<char*>(a.y) + (row * ncols + lt.tile * VPW) * (int64_t)VBYTES,
+                              nvalid * VBYTES);
 #pragma unroll
     for (int c = 0; c < NCHUNK; ++c) {
       const int off = c * 1024 + lane * 16;
       const int vq = off / VBYTES, inner = off % VBYTES;
-      if (vq < nvalid) {
+      {
         u32x4_t w;
         if (PERM_ANY && PERM) {
           // rows hold floats: 16 output bytes = 16/OES floats
@@ -1106,7 +1203,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
         } else {
           w = lds_ld4(wave_addr + (uint32_t)(vq * row_bytes<D>() + inner));
         }
-        *reinterpret_cast<u32x4_t*>(ybase + off) = w;
+        __builtin_amdgcn_raw_buffer_store_b128(w, yb, (uint32_t)off, 0, 0);
       }
     }
     wave_lds_sync();
@@ -1115,16 +1212,16 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   // persistent walk over the wave's items with the next item's packed planes in flight
   LaneTile cur = lane_tile<VPW>(a, wk.tile, q);
   Packed pa, pb;
-  fetch(pa, cur, wk.r);
+  fetch(pa, cur, wk.r, true);
   LaneTile nxt = cur;
   auto step = [&](Packed& now, Packed& later) __attribute__((always_inline)) -> bool {
     Walk nw = wk;
     const bool more = walk_next(a, wid, K, nw);
-    if (more) {
-      if (nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
-      fetch(later, nxt, nw.r);
-    }
+    if (more && nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
+    fetch(later, nxt, nw.r, more);  // in flight during this item's work
+    __builtin_amdgcn_sched_barrier(0);
     process(now, cur, wk.r);
+    prio_step(pr);
     if (!more) return false;
     wk = nw;
     cur = nxt;
@@ -1265,9 +1362,10 @@ inline unsigned sink_blocks(const CodecArgs& a, int lv) {
 // ---------------------------------------------------------------------------
 // launch dispatch
 // ---------------------------------------------------------------------------
-// Grid of a persistent launch: as many blocks as can be resident at once (occupancy
-// of the kernel instance x compute units), but no more than there are items.
-// ``per_cu`` caches the occupancy of the instance (0 = not yet known).
+// Grid of a launch.  Task walk: one wave per task.  Persistent walk: as many blocks as
+// can be resident at once (occupancy of the kernel instance x compute units), but no
+// more than there are items.  ``per_cu`` caches the occupancy of the instance (0 = not
+// yet known).
 int plan_grid(const void* kernel, size_t lds, int& per_cu, CodecArgs& b, unsigned& nb) {
   static thread_local int cached_dev = -1, cu = 0;
   int dev = 0;
@@ -1284,8 +1382,15 @@ int plan_grid(const void* kernel, size_t lds, int& per_cu, CodecArgs& b, unsigne
     if (e != hipSuccess) return (int)e;
     per_cu = n < 1 ? 1 : n;
   }
-  const int64_t need = (b.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t blocks = std::min<int64_t>(need, (int64_t)per_cu * cu);
+  int64_t blocks;
+  if (b.rows_per_task > 0) {
+    const int64_t tasks = b.n_tiles * ((b.rows + b.rows_per_task - 1) / b.rows_per_task);
+    blocks = (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
+  } else {
+    const int64_t need = (b.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
+    blocks = std::min<int64_t>(need, (int64_t)per_cu * cu);
+  }
+  if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
   nb = (unsigned)blocks;
   b.n_waves = blocks * kWavesPerBlock;
   return 0;
@@ -1299,6 +1404,10 @@ int launch_enc_t(const CodecArgs& a, hipStream_t s) {
   CodecArgs b = a;
   // tokens a tile of VPW columns can span: floor((h0 + VPW - 1) / heads) + 1, h0 < heads
   b.trig_rows = (int32_t)std::min<int64_t>(VPW, (a.heads - 1 + VPW - 1) / a.heads + 1);
+  // With RoPE a wave keeps its tile's cos/sin table over all rows (persistent walk);
+  // otherwise short tasks, which streamed fastest on MI355X (one item per wave, two
+  // with a permutation, whose gather addresses each wave sets up once).
+  b.rows_per_task = a.rope ? 0 : (a.use_perm ? 2 : 1);
   const size_t lds = (size_t)kWavesPerBlock * enc_wave_bytes<D>(a.use_perm != 0, a.rope != 0, b.trig_rows);
   // occupancy cache by staging size (it depends on the LDS the launch asks for)
   static std::atomic<int> occ[4];
@@ -1327,6 +1436,7 @@ int launch_dec_t(const CodecArgs& a, hipStream_t s) {
   static std::atomic<int> occ{0};
   int per_cu = occ.load(std::memory_order_relaxed);
   CodecArgs b = a;
+  b.rows_per_task = 2;  // tasks of two rows streamed fastest on MI355X
   unsigned nb = 0;
   if (int e = plan_grid(k, lds, per_cu, b, nb)) return e;
   occ.store(per_cu, std::memory_order_relaxed);
