@@ -10,6 +10,22 @@ constexpr int kMaxHeadDim = 256;
 constexpr int kMaxCodebook = 16;
 constexpr int kWavesPerBlock = 4;
 
+// n / d for 0 <= n < 2^31 as (n * mul) >> shift, the round-up method of Granlund and
+// Montgomery ("Division by invariant integers using multiplication", 1994): with
+// l = ceil(log2 d), mul = floor(2^(31+l) / d) + 1 < 2^32 and shift = 31 + l.  The error
+// of the product is below n * d / (d * 2^(31+l)) < 1/d, so the floor is exact.
+struct FastDiv {
+  uint32_t mul, shift;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while (l < 31 && (1u << l) < d) ++l;
+  FastDiv f;
+  f.mul = (uint32_t)((uint64_t(1) << (31 + l)) / d + 1);
+  f.shift = 31 + l;
+  return f;
+}
+
 // Everything a kernel needs, passed by value in the kernel-argument segment
 // (about 2.6 KB), so no device allocation is ever made for parameters.
 struct CodecArgs {
@@ -30,18 +46,14 @@ struct CodecArgs {
   int32_t n_sink;
   int32_t rope;
   int32_t use_perm;
-  // work decomposition: an item is (tile of VPW consecutive (token, head) columns, row).
-  // Two walks (set by the launcher):
-  //  - tasks (rows_per_task = k > 0): one wave per (tile, run of k consecutive rows), wave
-  //    w taking tile w % n_tiles and rows k * (w / n_tiles) ...; the grid holds every task.
-  //  - persistent (rows_per_task = 0): W waves, as many as fit; wave w first takes tiles
-  //    w, w + W, ..., w + (K-1) W (all rows of each, K = n_tiles / W), so the waves in
-  //    flight cover W adjacent tiles of one row at a time; the remaining n_tiles - K W
-  //    tiles are split into equal contiguous runs of (tile, row) items, one per wave.
-  int64_t n_tiles;        // tiles per row
+  // work decomposition: an item is (tile of VPW consecutive (token, head) columns, row);
+  // a task is one tile over rows_per_task consecutive rows, one wave per task: wave w
+  // takes tile w % n_tiles and rows rows_per_task * (w / n_tiles) onwards.
+  int64_t n_tiles;        // tiles per row (below 2^31)
   int64_t n_items;        // rows * n_tiles
-  int64_t n_waves;        // waves in the grid (set by the launcher)
-  int32_t rows_per_task;  // 0: persistent walk (set by the launcher)
+  int32_t rows_per_task;  // set by the launcher
+  FastDiv div_tiles;      // division by n_tiles (wave id -> run of rows)
+  FastDiv div_heads;      // division by heads (column -> token)
   int32_t trig_rows;      // RoPE table rows per wave: tokens one tile can span (set by the launcher)
   // parameters
   uint8_t perm[kMaxHeadDim];

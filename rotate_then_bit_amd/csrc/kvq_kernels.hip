@@ -6,13 +6,12 @@
 // packed codes are then one contiguous run of 4*bits bytes, so code planes move with a
 // single 8/12/16-byte access per lane and the wave covers whole records.
 //
-// Work.  An item is a tile of VPW consecutive (token, head) columns of one row.  Each
-// wave of a persistent grid of W waves takes tile w, then w + W, w + 2W, ..., and walks
-// all rows of each, with the next item's loads in flight while it computes the current
-// one; the tiles left over after the last full round of W are split evenly as runs of
-// (tile, row) items.  So the waves in flight read W adjacent tiles of one row at a time,
-// and a wave keeps the same columns -- and the same RoPE angles -- while it moves down
-// the rows.
+// Work.  An item is a tile of VPW consecutive (token, head) columns of one row; a task
+// is one tile over a few consecutive rows, and the grid has one wave per task (the
+// dispatcher keeps the SIMDs full to the end).  A wave keeps the same columns -- and the
+// same RoPE table -- over its rows, with the next item's loads in flight while it
+// computes the current one.  Global memory is accessed through buffer descriptors sized
+// to what an item may touch, so lanes past the end of a tensor need no branches.
 //
 // Walsh-Hadamard.  The channel index splits into 5 in-lane bits (slots) and 2 or 3
 // lane bits.  In-lane butterflies are plain VALU adds; lane-bit butterflies are a
@@ -32,7 +31,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <atomic>
 
 #include "kvq_internal.h"
 
@@ -371,49 +369,37 @@ __device__ void build_so4(const float* q, float* m) {
     }
 }
 
-// cos/sin of the RoPE angle phi = pos * theta, evaluated in double precision:
-// quadrant reduction phi = k*pi/2 + r, |r| <= pi/4 (two-term Cody-Waite split of
-// pi/2, exact products for k < 2^31), then the Taylor series of sin and cos in r
-// (terms up to r^17 / r^16, truncation error < 1e-17), rounded once to float.
+// cos and sin of phi = pos * theta.  The angle (up to ~1e5 rad) and its quadrant
+// reduction phi = k*pi/2 + r, |r| <= pi/4, are evaluated in float64 (two-term Cody-Waite
+// split of pi/2, exact products for k < 2^31); sin r and cos r then come from their
+// Taylor polynomials in float32 (terms up to r^9 / r^10; truncation below 2e-9 for
+// |r| <= pi/4), within about 2 ulp of the correctly rounded float.
 __device__ __forceinline__ void rope_cos_sin(int64_t pos, double theta, float* c, float* s) {
   constexpr double kTwoOverPi = 0.63661977236758138;
   constexpr double kPio2Hi = 1.570796012878418;       // pi/2 truncated to 22 bits
   constexpr double kPio2Lo = 3.139164786504813e-07;   // pi/2 - kPio2Hi (rounded)
   const double phi = (double)pos * theta;
   const double k = rint(phi * kTwoOverPi);
-  double r = fma(-k, kPio2Hi, phi);
-  r = fma(-k, kPio2Lo, r);
-  const double r2 = r * r;
+  double rd = fma(-k, kPio2Hi, phi);
+  rd = fma(-k, kPio2Lo, rd);
+  const float r = (float)rd, r2 = r * r;
   // sin r = r (1 - r2/3! + r2^2/5! - ...), cos r = 1 - r2/2! + r2^2/4! - ...
-  double sn = 1.0 / 355687428096000.0;                   // 1/17!
-  sn = fma(sn, -r2, 1.0 / 1307674368000.0);              // 1/15!
-  sn = fma(sn, -r2, 1.0 / 6227020800.0);
-  sn = fma(sn, -r2, 1.0 / 39916800.0);
-  sn = fma(sn, -r2, 1.0 / 362880.0);
-  sn = fma(sn, -r2, 1.0 / 5040.0);
-  sn = fma(sn, -r2, 1.0 / 120.0);
-  sn = fma(sn, -r2, 1.0 / 6.0);
-  sn = fma(sn, -r2, 1.0);
+  float sn = 1.0f / 362880.0f;                     // 1/9!
+  sn = __builtin_fmaf(sn, -r2, 1.0f / 5040.0f);
+  sn = __builtin_fmaf(sn, -r2, 1.0f / 120.0f);
+  sn = __builtin_fmaf(sn, -r2, 1.0f / 6.0f);
+  sn = __builtin_fmaf(sn, -r2, 1.0f);
   sn *= r;
-  double cs = 1.0 / 20922789888000.0;                    // 1/16!
-  cs = fma(cs, -r2, 1.0 / 87178291200.0);                // 1/14!
-  cs = fma(cs, -r2, 1.0 / 479001600.0);                  // 1/12!
-  cs = fma(cs, -r2, 1.0 / 3628800.0);                    // 1/10!
-  cs = fma(cs, -r2, 1.0 / 40320.0);                      // 1/8!
-  cs = fma(cs, -r2, 1.0 / 720.0);                        // 1/6!
-  cs = fma(cs, -r2, 1.0 / 24.0);                         // 1/4!
-  cs = fma(cs, -r2, 0.5);                                // 1/2!
-  cs = fma(cs, -r2, 1.0);
+  float cs = 1.0f / 3628800.0f;                    // 1/10!
+  cs = __builtin_fmaf(cs, -r2, 1.0f / 40320.0f);
+  cs = __builtin_fmaf(cs, -r2, 1.0f / 720.0f);
+  cs = __builtin_fmaf(cs, -r2, 1.0f / 24.0f);
+  cs = __builtin_fmaf(cs, -r2, 0.5f);
+  cs = __builtin_fmaf(cs, -r2, 1.0f);
   const int quad = (int)((int64_t)k & 3);
-  double oc, os;
-  switch (quad) {
-    case 0: oc = cs; os = sn; break;
-    case 1: oc = -sn; os = cs; break;
-    case 2: oc = -cs; os = -sn; break;
-    default: oc = sn; os = -cs; break;
-  }
-  *c = (float)oc;
-  *s = (float)os;
+  const float oc = (quad & 1) ? sn : cs, os = (quad & 1) ? cs : sn;
+  *c = (quad == 1 || quad == 2) ? -oc : oc;
+  *s = (quad >= 2) ? -os : os;
 }
 
 // ---------------------------------------------------------------------------
@@ -431,111 +417,48 @@ struct LaneTile {
   int32_t pad;
 };
 
+// n / d for 0 <= n < 2^31 with the host's constants for d
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.mul) >> f.shift);
+}
+
+// (columns stay below 2^31: tokens * heads is checked on the host)
 template <int VPW>
 __device__ __forceinline__ LaneTile lane_tile(const CodecArgs& a, int64_t tile, int q) {
   LaneTile lt;
   lt.tile = tile;
-  const int64_t col0 = tile * VPW;
-  lt.t0 = col0 / a.heads;
-  const int64_t h0 = col0 - lt.t0 * a.heads;
-  const int64_t hq = h0 + q;               // < heads + 64
-  const int64_t dt = hq / a.heads;
+  const uint32_t heads = (uint32_t)a.heads;
+  const uint32_t col0 = (uint32_t)tile * VPW;
+  const uint32_t t0 = fdiv(col0, a.div_heads);
+  const uint32_t hq = col0 - t0 * heads + (uint32_t)q;  // < heads + 64
+  const uint32_t dt = fdiv(hq, a.div_heads);
+  lt.t0 = t0;
   lt.dtok = (int32_t)dt;
-  lt.h = (int32_t)(hq - dt * a.heads);
-  lt.pos = a.pos_offset + lt.t0 + dt;
-  lt.valid = (col0 + q < a.tokens * a.heads) ? 1 : 0;
+  lt.h = (int32_t)(hq - dt * heads);
+  lt.pos = a.pos_offset + (int64_t)(t0 + dt);
+  lt.valid = ((int64_t)col0 + q < a.tokens * a.heads) ? 1 : 0;
   lt.pad = 0;
   return lt;
 }
 
-// A wave's walk over its items.  Task walk: tile wid % n_tiles, rows [r, t1).  Persistent
-// walk: first rounds j = 0..K-1 of whole tiles (tile j*W + wid, rows 0..R-1), then its
-// share [t, t1) of the leftover (tile, row) items, numbered tile-major from tile K*W on.
+// A wave's walk over its items: one task, tile wid % n_tiles over the rows
+// [k * (wid / n_tiles), min(k * (wid / n_tiles + 1), rows)), k = rows_per_task.  The grid
+// holds every task, so the hardware dispatcher keeps the SIMDs full until the end.
 struct Walk {
   int64_t tile, r;  // current item
-  int64_t j;        // current round, or -1 in the leftover part (persistent walk)
-  int64_t t, t1;    // leftover part: current index and end; task walk: t1 = end row
+  int64_t end;      // one past the task's last row
 };
 
-__device__ __forceinline__ bool walk_leftover(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
-  const int64_t base = K * a.n_waves;
-  const int64_t n = (a.n_tiles - base) * a.rows;
-  const int64_t t0 = wid * n / a.n_waves, t1 = (wid + 1) * n / a.n_waves;
-  if (t0 >= t1) return false;
-  w.j = -1;
-  w.t = t0;
-  w.t1 = t1;
-  w.tile = base + t0 / a.rows;
-  w.r = t0 - (w.tile - base) * a.rows;
-  return true;
+// (wave ids stay below 2^31: the launcher checks the number of tasks)
+__device__ __forceinline__ bool walk_first(const CodecArgs& a, uint32_t wid, Walk& w) {
+  const uint32_t run = fdiv(wid, a.div_tiles);
+  w.tile = wid - run * (uint32_t)a.n_tiles;
+  w.r = (int64_t)run * a.rows_per_task;
+  w.end = min(w.r + a.rows_per_task, a.rows);
+  return w.r < a.rows;
 }
 
-__device__ __forceinline__ bool walk_first(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
-  if (a.rows_per_task > 0) {
-    w.tile = wid % a.n_tiles;
-    w.r = (wid / a.n_tiles) * a.rows_per_task;
-    w.t1 = min(w.r + a.rows_per_task, a.rows);
-    return w.r < a.rows;
-  }
-  if (K > 0) {
-    w.j = 0;
-    w.tile = wid;
-    w.r = 0;
-    return true;
-  }
-  return walk_leftover(a, wid, K, w);
-}
-
-__device__ __forceinline__ bool walk_next(const CodecArgs& a, int64_t wid, int64_t K, Walk& w) {
-  if (a.rows_per_task > 0) return ++w.r < w.t1;
-  if (w.j >= 0) {
-    if (++w.r < a.rows) return true;
-    if (++w.j < K) {
-      w.tile += a.n_waves;
-      w.r = 0;
-      return true;
-    }
-    return walk_leftover(a, wid, K, w);
-  }
-  if (++w.t >= w.t1) return false;
-  if (++w.r == a.rows) {
-    w.r = 0;
-    ++w.tile;
-  }
-  return true;
-}
-
-// Persistent walk: all waves start with the same number of items, but the SIMD arbiter
-// favours older waves, so without help some waves finish long before others and the
-// launch ends with a thinly occupied tail.  Each wave lowers its priority (3 .. 0) as it
-// gets through its items, which lets the waves behind catch up.
-struct Prio {
-  int64_t total, done;
-  int lvl;
-};
-__device__ __forceinline__ void prio_init(const CodecArgs& a, int64_t wid, int64_t K, Prio& p) {
-  p.total = 0;
-  p.done = 0;
-  p.lvl = 3;
-  if (a.rows_per_task > 0) return;
-  const int64_t n = (a.n_tiles - K * a.n_waves) * a.rows;
-  p.total = K * a.rows + ((wid + 1) * n / a.n_waves - wid * n / a.n_waves);
-  __builtin_amdgcn_s_setprio(3);
-}
-__device__ __forceinline__ void prio_step(Prio& p) {
-  if (p.total == 0) return;
-  ++p.done;
-  const int lvl = 3 - (int)((4 * p.done) / (p.total + 1));
-  if (lvl != p.lvl) {
-    p.lvl = lvl;
-    switch (lvl) {
-      case 3: __builtin_amdgcn_s_setprio(3); break;
-      case 2: __builtin_amdgcn_s_setprio(2); break;
-      case 1: __builtin_amdgcn_s_setprio(1); break;
-      default: __builtin_amdgcn_s_setprio(0); break;
-    }
-  }
-}
+__device__ __forceinline__ bool walk_next(Walk& w) { return ++w.r < w.end; }
 
 // ---------------------------------------------------------------------------
 // bit-packing of a lane's 32 codes (4*BITS bytes, code i at bits BITS*i)
@@ -642,15 +565,12 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   if constexpr (ROT == ROT_SO4) {
     for (int b = tid; b < D / 4; b += blockDim.x) build_so4(&a.quat[8 * b], &s_mat[16 * b]);
   }
-  __syncthreads();
+  if constexpr (ROPE_ANY || ROT == ROT_SO4) __syncthreads();  // block-shared parameters ready
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  const int64_t K = a.n_tiles / a.n_waves;  // rounds of whole tiles
+  const uint32_t wid = blockIdx.x * kWavesPerBlock + (uint32_t)wave;
   Walk wk;
-  if (!walk_first(a, wid, K, wk)) return;  // wave-uniform; no barrier follows
-  Prio pr;
-  prio_init(a, wid, K, pr);
+  if (!walk_first(a, wid, wk)) return;  // wave-uniform; no barrier follows
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
@@ -917,21 +837,34 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
     store_lane_codes<BITS>(make_buf(a.codes + vec0 * CB, CB * nvalid), (uint32_t)(q * CB + l * (4 * BITS)), cw);
   };
 
-  // persistent walk over the wave's items with the next item's loads in flight
-  set_trig(cur);
+  // the task's items, with the next item's loads in flight
   RawRow<DT> ra, rb;
   load_row<DT>(ra, in_buf(cur, wk.r, true), in_off(cur));
+  {
+    // the stores of an item, on size-0 descriptors (nothing is written): the loop is then
+    // entered with the same outstanding memory instructions on every path, and the
+    // compiler's wait for an item's loads does not also wait for earlier stores
+    const buf_t nb = make_buf(a.codes, 0);
+    if constexpr (QUANT == Q_MINMAX) {
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, nb, 0, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, nb, 16, 0, 0);  // distinct, so none is merged
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(0u, nb, 0, 0, 0);
+    }
+    LaneCodes<BITS> z{};
+    store_lane_codes<BITS>(nb, 32, z);
+  }
+  set_trig(cur);  // while the first loads are in flight
   LaneTile nxt = cur;
   auto step = [&](RawRow<DT>& now, RawRow<DT>& later) __attribute__((always_inline)) -> bool {
     Walk nw = wk;
-    const bool more = walk_next(a, wid, K, nw);
+    const bool more = walk_next(nw);
     if (more && nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
     // the next item's loads go out before this item's work (after the last item they
     // fall outside the buffer and move nothing)
     load_row<DT>(later, in_buf(nxt, nw.r, more), in_off(nxt));
     __builtin_amdgcn_sched_barrier(0);
     process(now, cur, wk.r);
-    prio_step(pr);
     if (!more) return false;
     wk = nw;
     if (nxt.tile != cur.tile) {
@@ -969,15 +902,12 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   if constexpr (QUANT == Q_LLOYD) {
     if (tid < (1 << BITS)) s_cb[tid] = a.codebook[tid];
   }
-  __syncthreads();
+  if constexpr (ROT == ROT_SO4 || QUANT == Q_LLOYD) __syncthreads();  // block-shared parameters ready
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  const int64_t K = a.n_tiles / a.n_waves;  // rounds of whole tiles
+  const uint32_t wid = blockIdx.x * kWavesPerBlock + (uint32_t)wave;
   Walk wk;
-  if (!walk_first(a, wid, K, wk)) return;  // wave-uniform; no barrier follows
-  Prio pr;
-  prio_init(a, wid, K, pr);
+  if (!walk_first(a, wid, wk)) return;  // wave-uniform; no barrier follows
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
@@ -1003,7 +933,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
 
   struct Packed {
     LaneCodes<BITS> c;
-    uint32_t sz;  // scale | zero << 16 (min-max)
+    uint32_t sc, zr;  // fp16 bits of scale and zero (min-max), combined only where used,
+                      // so that nothing waits for the prefetch before the current item
     float rho;    // Lloyd-Max
   };
   // the packed planes of item (tile, row); with on == false (wave-uniform) nothing is read
@@ -1014,9 +945,10 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     if constexpr (QUANT == Q_MINMAX) {
       const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
       const int64_t gbytes = 2 * nvalid * ngroups;
-      const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.scale + vec0 * ngroups, gbytes), go, 0, kNT);
-      const uint32_t zr = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.zero + vec0 * ngroups, gbytes), go, 0, kNT);
-      pk.sz = sc | (zr << 16);
+      const uint16_t sc = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.scale + vec0 * ngroups, gbytes), go, 0, kNT);
+      const uint16_t zr = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.zero + vec0 * ngroups, gbytes), go, 0, kNT);
+      pk.sc = sc;
+      pk.zr = zr;
     } else {
       pk.rho = __uint_as_float(
           __builtin_amdgcn_raw_buffer_load_b32(make_buf(a.norm + vec0, 4 * nvalid), 4u * (uint32_t)q, 0, kNT));
@@ -1074,7 +1006,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
       // value = zero + q * scale per group: H_32 of (zero * ones) puts 32 * zero on slot 0.
       // The lane's inputs to the lane stages carry (-1)^popcount(l) so that the stages
       // below (m = +1 on a set bit) yield the true coefficients, times 1/sqrt(D).
-      const float sc = f16_value(pk.sz & 0xffffu), z = f16_value(pk.sz >> 16);
+      const float sc = f16_value(pk.sc), z = f16_value(pk.zr);
       const float S = sgn * norm_c * sc;
       const float Z0 = sgn * norm_c * 32.0f * z;
 #pragma unroll
@@ -1094,7 +1026,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
       }
     } else {
       if constexpr (QUANT == Q_MINMAX) {
-        const float sc = f16_value(pk.sz & 0xffffu), z = f16_value(pk.sz >> 16);
+        const float sc = f16_value(pk.sc), z = f16_value(pk.zr);
 #pragma unroll
         for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf((float)code_at<BITS>(pk.c, i), sc, z);
       } else {
@@ -1209,19 +1141,24 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     wave_lds_sync();
   };
 
-  // persistent walk over the wave's items with the next item's packed planes in flight
+  // the task's items, with the next item's packed planes in flight
   LaneTile cur = lane_tile<VPW>(a, wk.tile, q);
   Packed pa, pb;
   fetch(pa, cur, wk.r, true);
+  // the stores of an item, on a size-0 descriptor (nothing is written): the loop is then
+  // entered with the same outstanding memory instructions on every path, and the
+  // compiler's wait for an item's loads does not also wait for earlier stores
+#pragma unroll
+  for (int c = 0; c < NCHUNK; ++c)  // distinct offsets, so none is merged
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, make_buf(a.y, 0), 16u * c, 0, 0);
   LaneTile nxt = cur;
   auto step = [&](Packed& now, Packed& later) __attribute__((always_inline)) -> bool {
     Walk nw = wk;
-    const bool more = walk_next(a, wid, K, nw);
+    const bool more = walk_next(nw);
     if (more && nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
     fetch(later, nxt, nw.r, more);  // in flight during this item's work
     __builtin_amdgcn_sched_barrier(0);
     process(now, cur, wk.r);
-    prio_step(pr);
     if (!more) return false;
     wk = nw;
     cur = nxt;
@@ -1362,62 +1299,29 @@ inline unsigned sink_blocks(const CodecArgs& a, int lv) {
 // ---------------------------------------------------------------------------
 // launch dispatch
 // ---------------------------------------------------------------------------
-// Grid of a launch.  Task walk: one wave per task.  Persistent walk: as many blocks as
-// can be resident at once (occupancy of the kernel instance x compute units), but no
-// more than there are items.  ``per_cu`` caches the occupancy of the instance (0 = not
-// yet known).
-int plan_grid(const void* kernel, size_t lds, int& per_cu, CodecArgs& b, unsigned& nb) {
-  static thread_local int cached_dev = -1, cu = 0;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return (int)e;
-  if (dev != cached_dev) {
-    e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return (int)e;
-    cached_dev = dev;
-  }
-  if (per_cu <= 0) {
-    int n = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 64 * kWavesPerBlock, lds);
-    if (e != hipSuccess) return (int)e;
-    per_cu = n < 1 ? 1 : n;
-  }
-  int64_t blocks;
-  if (b.rows_per_task > 0) {
-    const int64_t tasks = b.n_tiles * ((b.rows + b.rows_per_task - 1) / b.rows_per_task);
-    blocks = (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
-  } else {
-    const int64_t need = (b.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
-    blocks = std::min<int64_t>(need, (int64_t)per_cu * cu);
-  }
-  if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+// Grid of a launch: one wave per task (a tile over rows_per_task consecutive rows).
+int plan_grid(const CodecArgs& b, unsigned& nb) {
+  const int64_t tasks = b.n_tiles * ((b.rows + b.rows_per_task - 1) / b.rows_per_task);
+  const int64_t blocks = (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks * kWavesPerBlock > 0x7fffffff) return (int)hipErrorInvalidConfiguration;  // wave ids < 2^31
   nb = (unsigned)blocks;
-  b.n_waves = blocks * kWavesPerBlock;
   return 0;
 }
 
 template <int DT, int D, int BITS, int ROT, int QUANT, int RT, int PT, int GBT>
 int launch_enc_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
-  const void* k = reinterpret_cast<const void*>(&encode_kernel<DT, D, BITS, ROT, QUANT, RT, PT, GBT>);
   constexpr int VPW = Geo<D>::VPW;
   CodecArgs b = a;
   // tokens a tile of VPW columns can span: floor((h0 + VPW - 1) / heads) + 1, h0 < heads
   b.trig_rows = (int32_t)std::min<int64_t>(VPW, (a.heads - 1 + VPW - 1) / a.heads + 1);
-  // With RoPE a wave keeps its tile's cos/sin table over all rows (persistent walk);
-  // otherwise short tasks, which streamed fastest on MI355X (one item per wave, two
-  // with a permutation, whose gather addresses each wave sets up once).
-  b.rows_per_task = a.rope ? 0 : (a.use_perm ? 2 : 1);
+  // Rows per task, the fastest measured on MI355X at the Llama-3 cache shape: with RoPE a
+  // wave's cos/sin table serves 16 rows; with only a permutation its gather addresses
+  // serve 2; otherwise one item per wave.
+  b.rows_per_task = a.rope ? 16 : (a.use_perm ? 2 : 1);
   const size_t lds = (size_t)kWavesPerBlock * enc_wave_bytes<D>(a.use_perm != 0, a.rope != 0, b.trig_rows);
-  // occupancy cache by staging size (it depends on the LDS the launch asks for)
-  static std::atomic<int> occ[4];
-  static std::atomic<size_t> occ_lds[4];
-  const int slot = (a.use_perm ? 1 : 0) + (a.rope ? 2 : 0);
-  int per_cu = occ_lds[slot].load(std::memory_order_relaxed) == lds ? occ[slot].load(std::memory_order_relaxed) : 0;
   unsigned nb = 0;
-  if (int e = plan_grid(k, lds, per_cu, b, nb)) return e;
-  occ[slot].store(per_cu, std::memory_order_relaxed);
-  occ_lds[slot].store(lds, std::memory_order_relaxed);
+  if (int e = plan_grid(b, nb)) return e;
   hipLaunchKernelGGL((encode_kernel<DT, D, BITS, ROT, QUANT, RT, PT, GBT>), dim3(nb), dim3(64 * kWavesPerBlock),
                      lds, s, b);
   if (hipError_t e = hipGetLastError()) return (int)e;
@@ -1431,15 +1335,11 @@ int launch_enc_t(const CodecArgs& a, hipStream_t s) {
 template <int ODT, int D, int BITS, int ROT, int QUANT, int PT>
 int launch_dec_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
-  const void* k = reinterpret_cast<const void*>(&decode_kernel<ODT, D, BITS, ROT, QUANT, PT>);
   const size_t lds = (size_t)kWavesPerBlock * stage_wave_bytes<D>();
-  static std::atomic<int> occ{0};
-  int per_cu = occ.load(std::memory_order_relaxed);
   CodecArgs b = a;
-  b.rows_per_task = 2;  // tasks of two rows streamed fastest on MI355X
+  b.rows_per_task = 2;  // measured fastest on MI355X (1, 3 and 4 rows streamed far slower)
   unsigned nb = 0;
-  if (int e = plan_grid(k, lds, per_cu, b, nb)) return e;
-  occ.store(per_cu, std::memory_order_relaxed);
+  if (int e = plan_grid(b, nb)) return e;
   hipLaunchKernelGGL((decode_kernel<ODT, D, BITS, ROT, QUANT, PT>), dim3(nb), dim3(64 * kWavesPerBlock), lds, s,
                      b);
   if (hipError_t e = hipGetLastError()) return (int)e;
