@@ -187,14 +187,13 @@ kvq_status check_planes(const kvq_config* cfg, const Derived& dv, const kvq_plan
 }
 
 // Work decomposition: an item is (tile of VPW consecutive (token, head) columns, row);
-// the launcher groups the items of a tile into tasks of consecutive rows, one wave each,
-// so a wave keeps the same columns (and RoPE angles) while it walks down its rows.
+// the launcher groups items into tasks, one wave each (runs of rows of one tile in the
+// encoder, runs of tiles of one row in the decoder).
 void plan_work(const kvq_config* cfg, kvq::CodecArgs* a) {
   const int vpw = cfg->head_dim == 128 ? 16 : 8;
   const int64_t ncols = cfg->tokens * cfg->heads;
   a->n_tiles = (ncols + vpw - 1) / vpw;
   a->n_items = cfg->rows * a->n_tiles;
-  a->div_tiles = kvq::make_fastdiv((uint32_t)std::max<int64_t>(a->n_tiles, 1));
   a->div_heads = kvq::make_fastdiv((uint32_t)std::max<int64_t>(cfg->heads, 1));
 }
 

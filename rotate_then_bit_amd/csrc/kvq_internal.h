@@ -47,13 +47,16 @@ struct CodecArgs {
   int32_t rope;
   int32_t use_perm;
   // work decomposition: an item is (tile of VPW consecutive (token, head) columns, row);
-  // a task is one tile over rows_per_task consecutive rows, one wave per task: wave w
-  // takes tile w % n_tiles and rows rows_per_task * (w / n_tiles) onwards.
-  int64_t n_tiles;        // tiles per row (below 2^31)
-  int64_t n_items;        // rows * n_tiles
-  int32_t rows_per_task;  // set by the launcher
-  FastDiv div_tiles;      // division by n_tiles (wave id -> run of rows)
-  FastDiv div_heads;      // division by heads (column -> token)
+  // one wave per task.  Encoder task: one tile over task_len consecutive rows (wave w
+  // takes tile w % n_tiles, rows from task_len * (w / n_tiles)).  Decoder task: task_len
+  // consecutive tiles of one row (wave w takes tiles from task_len * (w % n_tblk), row
+  // w / n_tblk).
+  int64_t n_tiles;   // tiles per row (below 2^31)
+  int64_t n_items;   // rows * n_tiles
+  int64_t n_tblk;    // decoder: tile blocks per row (set by the launcher)
+  int32_t task_len;  // set by the launcher
+  FastDiv div_task;  // division by n_tiles (encoder) or n_tblk (decoder), set by the launcher
+  FastDiv div_heads; // division by heads (column -> token)
   int32_t trig_rows;      // RoPE table rows per wave: tokens one tile can span (set by the launcher)
   // parameters
   uint8_t perm[kMaxHeadDim];

@@ -444,24 +444,34 @@ __device__ __forceinline__ LaneTile lane_tile(const CodecArgs& a, int64_t tile, 
   return lt;
 }
 
-// A wave's walk over its items: one task, tile wid % n_tiles over the rows
-// [k * (wid / n_tiles), min(k * (wid / n_tiles + 1), rows)), k = rows_per_task.  The grid
-// holds every task, so the hardware dispatcher keeps the SIMDs full until the end.
+// A wave's walk over its task.  Encoder: tile wid % n_tiles over the rows
+// [k * (wid / n_tiles), min(k * (wid / n_tiles + 1), rows)), so a wave keeps its tile (and
+// RoPE table) down its rows.  Decoder: tiles [k * (wid % n_tblk), ...) of row
+// wid / n_tblk, so a wave's output is one contiguous run.  k = task_len.  The grid holds
+// every task, so the hardware dispatcher keeps the SIMDs full until the end.
 struct Walk {
   int64_t tile, r;  // current item
-  int64_t end;      // one past the task's last row
+  int64_t end;      // one past the task's last row (encoder) or tile (decoder)
 };
 
 // (wave ids stay below 2^31: the launcher checks the number of tasks)
-__device__ __forceinline__ bool walk_first(const CodecArgs& a, uint32_t wid, Walk& w) {
-  const uint32_t run = fdiv(wid, a.div_tiles);
+__device__ __forceinline__ bool walk_first_rows(const CodecArgs& a, uint32_t wid, Walk& w) {
+  const uint32_t run = fdiv(wid, a.div_task);
   w.tile = wid - run * (uint32_t)a.n_tiles;
-  w.r = (int64_t)run * a.rows_per_task;
-  w.end = min(w.r + a.rows_per_task, a.rows);
+  w.r = (int64_t)run * a.task_len;
+  w.end = min(w.r + a.task_len, a.rows);
   return w.r < a.rows;
 }
+__device__ __forceinline__ bool walk_next_rows(Walk& w) { return ++w.r < w.end; }
 
-__device__ __forceinline__ bool walk_next(Walk& w) { return ++w.r < w.end; }
+__device__ __forceinline__ bool walk_first_tiles(const CodecArgs& a, uint32_t wid, Walk& w) {
+  const uint32_t row = fdiv(wid, a.div_task);
+  w.r = row;
+  w.tile = (int64_t)(wid - row * (uint32_t)a.n_tblk) * a.task_len;
+  w.end = min(w.tile + a.task_len, a.n_tiles);
+  return w.r < a.rows;
+}
+__device__ __forceinline__ bool walk_next_tiles(Walk& w) { return ++w.tile < w.end; }
 
 // ---------------------------------------------------------------------------
 // bit-packing of a lane's 32 codes (4*BITS bytes, code i at bits BITS*i)
@@ -587,7 +597,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const uint32_t wid = blockIdx.x * kWavesPerBlock + (uint32_t)wave;
   Walk wk;
-  if (!walk_first(a, wid, wk)) return;  // wave-uniform; no barrier follows
+  if (!walk_first_rows(a, wid, wk)) return;  // wave-uniform; no barrier follows
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
@@ -875,7 +885,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   LaneTile nxt = cur;
   auto step = [&](RawRow<DT>& now, RawRow<DT>& later) __attribute__((always_inline)) -> bool {
     Walk nw = wk;
-    const bool more = walk_next(nw);
+    const bool more = walk_next_rows(nw);
     if (more && nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
     // the next item's loads go out before this item's work (after the last item they
     // fall outside the buffer and move nothing)
@@ -926,7 +936,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const uint32_t wid = blockIdx.x * kWavesPerBlock + (uint32_t)wave;
   Walk wk;
-  if (!walk_first(a, wid, wk)) return;  // wave-uniform; no barrier follows
+  if (!walk_first_tiles(a, wid, wk)) return;  // wave-uniform; no barrier follows
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
@@ -1173,7 +1183,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   LaneTile nxt = cur;
   auto step = [&](Packed& now, Packed& later) __attribute__((always_inline)) -> bool {
     Walk nw = wk;
-    const bool more = walk_next(nw);
+    const bool more = walk_next_tiles(nw);
     if (more && nw.tile != cur.tile) nxt = lane_tile<VPW>(a, nw.tile, q);
     fetch(later, nxt, nw.r, more);  // in flight during this item's work
     __builtin_amdgcn_sched_barrier(0);
@@ -1318,9 +1328,12 @@ inline unsigned sink_blocks(const CodecArgs& a, int lv) {
 // ---------------------------------------------------------------------------
 // launch dispatch
 // ---------------------------------------------------------------------------
-// Grid of a launch: one wave per task (a tile over rows_per_task consecutive rows).
-int plan_grid(const CodecArgs& b, unsigned& nb) {
-  const int64_t tasks = b.n_tiles * ((b.rows + b.rows_per_task - 1) / b.rows_per_task);
+// Grid of a launch: one wave per task (len rows of one tile, or len tiles of one row).
+int plan_grid(CodecArgs& b, bool tiles_of_a_row, int len, unsigned& nb) {
+  b.task_len = len;
+  b.n_tblk = (b.n_tiles + len - 1) / len;
+  b.div_task = make_fastdiv((uint32_t)(tiles_of_a_row ? b.n_tblk : b.n_tiles));
+  const int64_t tasks = tiles_of_a_row ? b.rows * b.n_tblk : b.n_tiles * ((b.rows + len - 1) / len);
   const int64_t blocks = (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks * kWavesPerBlock > 0x7fffffff) return (int)hipErrorInvalidConfiguration;  // wave ids < 2^31
   nb = (unsigned)blocks;
@@ -1337,10 +1350,9 @@ int launch_enc_t(const CodecArgs& a, hipStream_t s) {
   // Rows per task, the fastest measured on MI355X at the Llama-3 cache shape: with RoPE a
   // wave's cos/sin table serves 8 rows; with only a permutation its gather addresses
   // serve 2; otherwise one item per wave.
-  b.rows_per_task = a.rope ? 8 : (a.use_perm ? 2 : 1);
   const size_t lds = (size_t)kWavesPerBlock * enc_wave_bytes<D>(a.use_perm != 0, a.rope != 0, b.trig_rows);
   unsigned nb = 0;
-  if (int e = plan_grid(b, nb)) return e;
+  if (int e = plan_grid(b, false, a.rope ? 8 : (a.use_perm ? 2 : 1), nb)) return e;
   hipLaunchKernelGGL((encode_kernel<DT, D, BITS, ROT, QUANT, RT, PT, GBT>), dim3(nb), dim3(64 * kWavesPerBlock),
                      lds, s, b);
   if (hipError_t e = hipGetLastError()) return (int)e;
@@ -1356,9 +1368,13 @@ int launch_dec_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
   const size_t lds = (size_t)kWavesPerBlock * stage_wave_bytes<D>();
   CodecArgs b = a;
-  b.rows_per_task = 3;  // measured fastest on MI355X at the Llama-3 cache shape
+#ifndef KVQ_DEC_TILES
+#define KVQ_DEC_TILES 4
+#endif
   unsigned nb = 0;
-  if (int e = plan_grid(b, nb)) return e;
+  // tasks of 4 consecutive tiles of a row (a 16 KiB output run per wave at d = 128, bf16):
+  // the fastest measured on MI355X at the Llama-3 cache shape
+  if (int e = plan_grid(b, true, KVQ_DEC_TILES, nb)) return e;
   hipLaunchKernelGGL((decode_kernel<ODT, D, BITS, ROT, QUANT, PT>), dim3(nb), dim3(64 * kWavesPerBlock), lds, s,
                      b);
   if (hipError_t e = hipGetLastError()) return (int)e;
