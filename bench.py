@@ -202,6 +202,23 @@ def main():
     dk = kern[dominant]
     traffic = traffic_from_profile(dominant)
 
+    # context, outside the timed region: a plain device-to-device copy that moves the same
+    # number of bytes as one launch (half read, half written)
+    half = dk["bytes"] // 2
+    src = data["inputs"]["K"].view(-1).view(torch.uint8)[:half]
+    dst = torch.empty(half, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(3):
+            dst.copy_(src)
+        b.record(stream)
+        stream.synchronize()
+    copy_gbps = 2 * half * 3 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del dst
+
     cpu = None
     if not args.no_cpu_baseline:
         nv, tc, nrows = cpu_baseline(data["inputs"], wl.cases, perm, args.cpu_seconds, 16)
@@ -233,6 +250,7 @@ def main():
         "decode_vectors_per_s": round(n_kv / (t_dec * 1e-3), 1),
         "compression_ratio": round(in_bytes["K"] / (pl_bytes["K"] - sink_bytes["K"]), 3),
         "kernels": kern,
+        "copy_GBps_same_bytes": round(copy_gbps, 1),
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dk["GBps"] / HBM_PEAK_GBPS, 4),
                      "traffic": (round(traffic / (dk["avg_ms"] * 1e-3) / 1e9, 1) if traffic else None),
