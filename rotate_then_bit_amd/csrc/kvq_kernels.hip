@@ -974,8 +974,10 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     if constexpr (QUANT == Q_MINMAX) {
       const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
       const int64_t gbytes = 2 * nvalid * ngroups;
-      const uint16_t sc = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.scale + vec0 * ngroups, gbytes), go, 0, kNT);
-      const uint16_t zr = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.zero + vec0 * ngroups, gbytes), go, 0, kNT);
+      // temporal: lanes share the lines of these 2-byte values (with the non-temporal hint
+      // the decoders fetched 16 % more than the planes hold)
+      const uint16_t sc = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.scale + vec0 * ngroups, gbytes), go, 0, 0);
+      const uint16_t zr = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.zero + vec0 * ngroups, gbytes), go, 0, 0);
       pk.sc = sc;
       pk.zr = zr;
     } else {
