@@ -65,12 +65,20 @@ template <int D>
 constexpr int stage_wave_bytes() {
   return Geo<D>::VPW * row_bytes<D>();
 }
+// Decoder staging rows hold a vector in the output type (D * bytes + 16 of padding).
+template <int D, int ODT>
+constexpr int dec_row_bytes() {
+  return D * (ODT == DT_F32 ? 4 : 2) + 16;
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_f32*)p;
 }
 __device__ __forceinline__ float lds_ld(uint32_t addr) { return *(const lds_f32*)(uintptr_t)addr; }
 __device__ __forceinline__ void lds_st(uint32_t addr, float v) { *(lds_f32*)(uintptr_t)addr = v; }
+__device__ __forceinline__ void lds_st16(uint32_t addr, uint16_t v) {
+  *(__attribute__((address_space(3))) uint16_t*)(uintptr_t)addr = v;
+}
 __device__ __forceinline__ u32x4_t lds_ld4(uint32_t addr) { return *(const lds_u32x4*)(uintptr_t)addr; }
 __device__ __forceinline__ void lds_st4(uint32_t addr, u32x4_t v) { *(lds_u32x4*)(uintptr_t)addr = v; }
 
@@ -952,13 +960,14 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
 
   // staging rows: vector q's row; in the permuted case the lane scatters its 32 floats
   // to out[perm[j]], otherwise it writes its 32 outputs (in the output type) in order
-  const uint32_t wave_addr = lds_addr(s_stage) + (uint32_t)(wave * stage_wave_bytes<D>());
-  const uint32_t row_addr = wave_addr + (uint32_t)(q * row_bytes<D>());
+  constexpr int ROWB = dec_row_bytes<D, ODT>();
+  const uint32_t wave_addr = lds_addr(s_stage) + (uint32_t)(wave * Geo<D>::VPW * ROWB);
+  const uint32_t row_addr = wave_addr + (uint32_t)(q * ROWB);
   uint32_t saddr[PERM_ANY ? 32 : 1];
   if constexpr (PERM_ANY) {
     if (PERM) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) saddr[i] = row_addr + 4u * (uint32_t)a.perm[32 * l + i];
+      for (int i = 0; i < 32; ++i) saddr[i] = row_addr + (uint32_t)OES * (uint32_t)a.perm[32 * l + i];
     }
   }
 
@@ -1103,8 +1112,18 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
       reconstruct(pk, v);
       if constexpr (PERM_ANY) {
         if (PERM) {
+          // scatter out[perm[j]] = v[j] in the output type
+          if constexpr (ODT == DT_F32) {
 #pragma unroll
-          for (int i = 0; i < 32; ++i) lds_st(saddr[i], v[i]);
+            for (int i = 0; i < 32; ++i) lds_st(saddr[i], v[i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t h2 = (ODT == DT_BF16) ? pack_bf16x2(v[2 * i], v[2 * i + 1]) : pack_f16x2(v[2 * i], v[2 * i + 1]);
+              lds_st16(saddr[2 * i], (uint16_t)h2);
+              lds_st16(saddr[2 * i + 1], (uint16_t)(h2 >> 16));
+            }
+          }
         }
       }
       if (!(PERM_ANY && PERM)) {
@@ -1146,28 +1165,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
       const int off = c * 1024 + lane * 16;
       const int vq = off / VBYTES, inner = off % VBYTES;
       {
-        u32x4_t w;
-        if (PERM_ANY && PERM) {
-          // rows hold floats: 16 output bytes = 16/OES floats
-          const uint32_t src = wave_addr + (uint32_t)(vq * row_bytes<D>() + inner * (4 / OES));
-          if constexpr (ODT == DT_F32) {
-            w = lds_ld4(src);
-          } else {
-            const u32x4_t f0 = lds_ld4(src), f1 = lds_ld4(src + 16u);
-            const float f[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
-                                __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
-                                __uint_as_float(f1.z), __uint_as_float(f1.w)};
-            if constexpr (ODT == DT_BF16) {
-              w.x = pack_bf16x2(f[0], f[1]); w.y = pack_bf16x2(f[2], f[3]);
-              w.z = pack_bf16x2(f[4], f[5]); w.w = pack_bf16x2(f[6], f[7]);
-            } else {
-              w.x = pack_f16x2(f[0], f[1]); w.y = pack_f16x2(f[2], f[3]);
-              w.z = pack_f16x2(f[4], f[5]); w.w = pack_f16x2(f[6], f[7]);
-            }
-          }
-        } else {
-          w = lds_ld4(wave_addr + (uint32_t)(vq * row_bytes<D>() + inner));
-        }
+        // rows hold the vectors in the output type, in channel order
+        const u32x4_t w = lds_ld4(wave_addr + (uint32_t)(vq * ROWB + inner));
         __builtin_amdgcn_raw_buffer_store_b128(w, yb, (uint32_t)off, 0, kNT | kSC1);
       }
     }
@@ -1370,7 +1369,7 @@ int launch_enc_t(const CodecArgs& a, hipStream_t s) {
 template <int ODT, int D, int BITS, int ROT, int QUANT, int PT>
 int launch_dec_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
-  const size_t lds = (size_t)kWavesPerBlock * stage_wave_bytes<D>();
+  const size_t lds = (size_t)kWavesPerBlock * Geo<D>::VPW * dec_row_bytes<D, ODT>();
   CodecArgs b = a;
 #ifndef KVQ_DEC_TILES
 #define KVQ_DEC_TILES 4
