@@ -1371,13 +1371,11 @@ int launch_dec_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
   const size_t lds = (size_t)kWavesPerBlock * Geo<D>::VPW * dec_row_bytes<D, ODT>();
   CodecArgs b = a;
-#ifndef KVQ_DEC_TILES
-#define KVQ_DEC_TILES 4
-#endif
   unsigned nb = 0;
-  // tasks of 4 consecutive tiles of a row (a 16 KiB output run per wave at d = 128, bf16):
-  // the fastest measured on MI355X at the Llama-3 cache shape
-  if (int e = plan_grid(b, true, KVQ_DEC_TILES, nb)) return e;
+  // tasks of 4 consecutive tiles of a row (a 16 KiB output run per wave at d = 128, bf16),
+  // 8 with the permutation (whose scatter addresses each wave sets up once): the fastest
+  // measured on MI355X at the Llama-3 cache shape
+  if (int e = plan_grid(b, true, PT != 0 ? 8 : 4, nb)) return e;
   hipLaunchKernelGGL((decode_kernel<ODT, D, BITS, ROT, QUANT, PT>), dim3(nb), dim3(64 * kWavesPerBlock), lds, s,
                      b);
   if (hipError_t e = hipGetLastError()) return (int)e;
