@@ -342,9 +342,47 @@ __device__ __forceinline__ float dot2pm(uint32_t pair, float acc) {
 // at once: each group of 4 channels (two dwords p, r) gives
 //   x0+x1+x2+x3, x0-x1+x2-x3, x0+x1-x2-x3, x0-x1-x2+x3
 // from two v_dot2 of p (x0+x1, x0-x1) and four v_dot2 of r with those as addends.
+#ifndef KVQ_DOT_ASM
+#define KVQ_DOT_ASM 1
+#endif
+// Eight outputs (two groups of 4 channels, dwords X Y and Z W) with the three-address
+// dot instruction OP: the builtins select the accumulating two-address form, which costs
+// a copy of every partial sum used twice and a zeroed register for every zero addend.
+// The 4 zero-addend dots go first, so every dependent dot reads a result at least 3
+// instructions old; the closing s_nop 2 gives the 3 wait states a dot result needs
+// before other VALU instructions read it.
+#define KVQ_H4_BLOCK(OP, o, X, Y, Z, W)                                                           \
+  {                                                                                               \
+    float s0, d0, s1, d1;                                                                         \
+    asm volatile(OP " %8, %12, %16, 0\n\t" OP " %9, %12, %17, 0\n\t" OP " %10, %14, %16, 0\n\t"  \
+                 OP " %11, %14, %17, 0\n\t" OP " %0, %13, %16, %8\n\t" OP " %1, %13, %17, %9\n\t" \
+                 OP " %2, %13, %18, %8\n\t" OP " %3, %13, %19, %9\n\t" OP " %4, %15, %16, %10\n\t"\
+                 OP " %5, %15, %17, %11\n\t" OP " %6, %15, %18, %10\n\t" OP " %7, %15, %19, %11\n\t" \
+                 "s_nop 2"                                                                        \
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),  \
+                   "=&v"(o[6]), "=&v"(o[7]), "=&v"(s0), "=&v"(d0), "=&v"(s1), "=&v"(d1)           \
+                 : "v"(X), "v"(Y), "v"(Z), "v"(W), "s"(c11), "s"(c1m), "s"(cmm), "s"(cm1));      \
+  }
 template <int DT>
 __device__ __forceinline__ void widen_row_h4(const RawRow<DT>& raw, float* v) {
   static_assert(DT != DT_F32, "16-bit inputs only");
+#if KVQ_DOT_ASM
+  {
+    // packed (+-1, +-1) pairs: low half multiplies the even channel
+    constexpr uint32_t P1 = (DT == DT_BF16) ? 0x3F80u : 0x3C00u, M1 = P1 | 0x8000u;
+    const uint32_t c11 = P1 | P1 << 16, c1m = P1 | M1 << 16, cmm = M1 | M1 << 16, cm1 = M1 | P1 << 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float* o = v + 8 * k;
+      if constexpr (DT == DT_BF16) {
+        KVQ_H4_BLOCK("v_dot2_f32_bf16", o, raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w)
+      } else {
+        KVQ_H4_BLOCK("v_dot2_f32_f16", o, raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w)
+      }
+    }
+    return;
+  }
+#endif
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t ws[4] = {raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w};
@@ -569,9 +607,20 @@ template <int D>
 __device__ __forceinline__ uint32_t enc_perm_bytes(bool perm) {
   return perm ? (uint32_t)(Geo<D>::VPW * enc_row<D>()) : 0u;
 }
+// RoPE table: a token's D/2 (cos, sin) pairs, the 16 pairs lane l reads at byte l * kTrigLane
+// (128 bytes of pairs + 16 of padding: 16-byte LDS reads are served 16 lanes at a time on
+// 64 banks of 4 bytes, and with the padding the lanes of a vector read different banks).
+#ifndef KVQ_TRIG_PAD
+#define KVQ_TRIG_PAD 1
+#endif
+constexpr int kTrigLane = KVQ_TRIG_PAD ? 144 : 128;
+template <int D>
+constexpr int trig_row() {
+  return Geo<D>::LV * kTrigLane;
+}
 template <int D>
 __device__ __host__ inline size_t enc_wave_bytes(bool perm, bool rope, int trig_rows) {
-  return (perm ? (size_t)(Geo<D>::VPW * enc_row<D>()) : 0) + (rope ? (size_t)trig_rows * D * 4 : 0);
+  return (perm ? (size_t)(Geo<D>::VPW * enc_row<D>()) : 0) + (rope ? (size_t)trig_rows * trig_row<D>() : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -659,7 +708,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
           float c, sn;
           rope_cos_sin(p0 + tok, s_theta[i], &c, &sn);
           u32x2_t w = {__float_as_uint(c), __float_as_uint(sn)};
-          *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)(trig_addr + 8u * (uint32_t)m) = w;
+          const uint32_t ta = trig_addr + (uint32_t)(tok * trig_row<D>() + (i >> 4) * kTrigLane + 8 * (i & 15));
+          *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)ta = w;
         }
         wave_lds_sync();
       }
@@ -684,7 +734,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
     float v[32];
     // RoPE of the 4 channel pairs of 8 consecutive slots 8c .. 8c + 7
     auto rope8 = [&](float* u, int c) __attribute__((always_inline)) {
-      const uint32_t tp = trig_addr + (uint32_t)(lt.dtok * (D * 4) + 128 * l + 32 * c);
+      const uint32_t tp = trig_addr + (uint32_t)(lt.dtok * trig_row<D>() + kTrigLane * l + 32 * c);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const u32x4_t cs = lds_ld4(tp + 16u * h);
