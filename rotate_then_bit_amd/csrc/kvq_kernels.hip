@@ -103,6 +103,10 @@ __device__ __forceinline__ buf_t make_buf(const void* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufWord3);
 }
+// The same for the planes and output of one item (at most 16 KiB, so no clamp).
+__device__ __forceinline__ buf_t make_buf_item(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
 
 // Orders this wave's LDS accesses before and after the call (LDS ops of one wave are
 // executed in order; this keeps the compiler from moving them across).
@@ -639,8 +643,17 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   extern __shared__ float s_stage[];
   __shared__ double s_theta[ROPE_ANY ? D / 2 : 1];
   __shared__ float s_mat[ROT == ROT_SO4 ? (D / 4) * 16 : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t s_goff[PERM_ANY ? D : 8];
 
   const int tid = threadIdx.x;
+  if constexpr (PERM_ANY) {
+    // byte offset of channel perm[j] in a staging row, for the gather
+    if (PERM)
+      for (int j = tid; j < D; j += blockDim.x) {
+        const uint32_t p = a.perm[j];
+        s_goff[j] = (uint16_t)((p >> 5) * (uint32_t)enc_pitch<D>() + 4u * (p & 31u));
+      }
+  }
   if constexpr (ROPE_ANY) {
     if (ROPE)
       for (int i = tid; i < D / 2; i += blockDim.x)
@@ -675,13 +688,19 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   uint32_t gaddr[PERM_ANY ? 32 : 1];
   if constexpr (PERM_ANY) {
     if (PERM) {
+      // the lane's 32 offsets (64 bytes of the block's table), two per word
 #pragma unroll
-      for (int i = 0; i < 32; ++i) gaddr[i] = a.perm[32 * l + i];
+      for (int k = 0; k < 4; ++k) {
+        const u32x4_t w = lds_ld4(lds_addr(s_goff) + 64u * l + 16u * k);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        gaddr[i] = row_addr + (gaddr[i] >> 5) * (uint32_t)enc_pitch<D>() + 4u * (gaddr[i] & 31u);
-        asm volatile("" : "+v"(gaddr[i]));  // keep the sums (not offsets re-added per item)
+        for (int e = 0; e < 4; ++e) {
+          gaddr[8 * k + 2 * e] = row_addr + (ws[e] & 0xffffu);
+          gaddr[8 * k + 2 * e + 1] = row_addr + (ws[e] >> 16);
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(gaddr[i]));  // keep the sums (not offsets re-added per item)
     }
   }
 
@@ -699,8 +718,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   auto set_trig = [&](const LaneTile& lt) __attribute__((always_inline)) {
     if constexpr (ROPE_ANY) {
       if (ROPE) {
-        const int64_t last = min(lt.tile * VPW + VPW, ncols) - 1;
-        const int ntok = (int)(last / a.heads - lt.t0) + 1;
+        const uint32_t last = (uint32_t)(min(lt.tile * VPW + VPW, ncols) - 1);  // < 2^31
+        const int ntok = (int)(fdiv(last, a.div_heads) - (uint32_t)lt.t0) + 1;
         const int64_t p0 = a.pos_offset + lt.t0;
         wave_lds_sync();  // the previous tile's table has been read
         for (int m = lane; m < ntok * (D / 2); m += 64) {
@@ -804,7 +823,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       const float inv = 1.0f / (rho + 1e-6f);
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] *= inv;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rho), make_buf(a.norm + vec0, 4 * nvalid),
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rho), make_buf_item(a.norm + vec0, (uint32_t)(4 * nvalid)),
                                             4u * (uint32_t)q, 0, 0);
     }
     if constexpr (ROT == ROT_FWHT) {
@@ -848,9 +867,9 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       {
         // every lane of a group holds the same values and stores them
         const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
-        const int64_t gbytes = 2 * nvalid * ngroups;
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sb, make_buf(a.scale + vec0 * ngroups, gbytes), go, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)zb, make_buf(a.zero + vec0 * ngroups, gbytes), go, 0, 0);
+        const uint32_t gbytes = (uint32_t)(2 * nvalid * ngroups);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sb, make_buf_item(a.scale + vec0 * ngroups, gbytes), go, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)zb, make_buf_item(a.zero + vec0 * ngroups, gbytes), go, 0, 0);
       }
       const float iv = (sc > 0.0f) ? __builtin_amdgcn_rcpf(sc) : 0.0f;
       // q = rint(t), nearest-even, with t = (A v - zero) / scale for the 32 slots
@@ -921,7 +940,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
         if (BITS == 3 && sh > 29) cw.w[w + 1] |= c >> (32 - sh);
       }
     }
-    store_lane_codes<BITS>(make_buf(a.codes + vec0 * CB, CB * nvalid), (uint32_t)(q * CB + l * (4 * BITS)), cw);
+    store_lane_codes<BITS>(make_buf_item(a.codes + vec0 * CB, (uint32_t)(CB * nvalid)),
+                           (uint32_t)(q * CB + l * (4 * BITS)), cw);
   };
 
   // the task's items, with the next item's loads in flight
@@ -931,7 +951,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
     // the stores of an item, on size-0 descriptors (nothing is written): the loop is then
     // entered with the same outstanding memory instructions on every path, and the
     // compiler's wait for an item's loads does not also wait for earlier stores
-    const buf_t nb = make_buf(a.codes, 0);
+    const buf_t nb = make_buf_item(a.codes, 0);
     if constexpr (QUANT == Q_MINMAX) {
       __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, nb, 0, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, nb, 16, 0, 0);  // distinct, so none is merged
