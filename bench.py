@@ -28,6 +28,18 @@ if ROOT not in sys.path:
 
 METRIC = "KV vectors encoded+decoded/sec and achieved HBM GB/s (% peak), d=128 2-bit"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+# 32-bit VALU peak in lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one add, mul,
+# fma, min, max or convert per lane per cycle; packed two-wide FP32 is not used by these
+# kernels, so the published 157.3 TFLOP/s -- FMA = 2 flops, two lanes per packed op -- is
+# 4x this figure in flops and 2x in operations)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Algorithmic operations per vector element at 2-bit, one per element per step of the
+# method: encode = widen 16-bit to fp32, 7 butterfly stages (log2 128), min and max,
+# affine + round to an integer, merge the code into its word (+ 2 for the RoPE pair
+# rotation on K: one mul and one fma per output); decode = unpack, dequantize (fma),
+# 7 butterfly stages, narrow to the output type.  The permutation is data movement.
+OPS_PER_ELEMENT = {("encode", "K"): 1 + 7 + 2 + 2 + 1 + 2, ("encode", "V"): 1 + 7 + 2 + 2 + 1,
+                   ("decode", "K"): 1 + 1 + 7 + 1, ("decode", "V"): 1 + 1 + 7 + 1}
 WORKLOAD = "llama3"
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "llama3_cache_hbm_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "rotate_then_bit_amd", "csrc", f)
@@ -190,8 +202,14 @@ def main():
         durs = [a.elapsed_time(b) for a, b in ev[key]]
         avg = sum(durs) / len(durs)
         gbps = algo[key] / (avg * 1e-3) / 1e9
+        ops = OPS_PER_ELEMENT[key] * cases[key[1]].n_vectors * cases[key[1]].shape[-1]
+        tops = ops / (avg * 1e-3) / 1e12
+        # the binding roofline: the resource whose peak would take longer for this launch
+        alu_bound = ops / (VALU_PEAK_TOPS * 1e12) > algo[key] / (HBM_PEAK_GBPS * 1e9)
         kern[f"{key[0]}_{key[1]}"] = {"avg_ms": round(avg, 4), "GBps": round(gbps, 1),
-                                      "frac_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": algo[key]}
+                                      "frac_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": algo[key],
+                                      "valu_Tops": round(tops, 2), "valu_frac": round(tops / VALU_PEAK_TOPS, 4),
+                                      "ops": ops, "bound": "alu" if alu_bound else "hbm"}
     n_vec = cases["K"].n_vectors  # K and V vectors each
     n_kv = 2 * n_vec
     t_enc = sum(kern[f"encode_{n}"]["avg_ms"] for n in cases)
@@ -251,10 +269,15 @@ def main():
         "compression_ratio": round(in_bytes["K"] / (pl_bytes["K"] - sink_bytes["K"]), 3),
         "kernels": kern,
         "copy_GBps_same_bytes": round(copy_gbps, 1),
-        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dk["GBps"] / HBM_PEAK_GBPS, 4),
-                     "traffic": (round(traffic / (dk["avg_ms"] * 1e-3) / 1e9, 1) if traffic else None),
-                     "algorithmic_bytes": dk["bytes"], "traffic_bytes": traffic},
+        "roofline": dict(
+            {"kernel": dominant, "bound": dk["bound"]},
+            **({"achieved": dk["valu_Tops"], "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s (32-bit VALU lane ops)",
+                "frac": dk["valu_frac"], "algorithmic_ops": dk["ops"]}
+               if dk["bound"] == "alu" else
+               {"achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dk["frac_peak"]}),
+            **{"hbm_achieved_GBps": dk["GBps"], "hbm_frac": dk["frac_peak"],
+               "traffic": (round(traffic / (dk["avg_ms"] * 1e-3) / 1e9, 1) if traffic else None),
+               "algorithmic_bytes": dk["bytes"], "traffic_bytes": traffic}),
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
