@@ -237,6 +237,31 @@ def main():
     copy_gbps = 2 * half * 3 / (a.elapsed_time(b) * 1e-3) / 1e9
     del dst
 
+    # context, outside the timed region: one decode step's cache update -- every row's new K
+    # and V token (its first token's values, here) appended at a random position of the
+    # cache (a few thousand vectors per launch: launch-latency bound, reported in us)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    r0, t_cap = cases["K"].shape[0], cases["K"].shape[1]
+    positions = torch.randint(0, t_cap, (r0,), generator=gen, device=dev, dtype=torch.int64)
+    x_new = {n: data["inputs"][n][:, 0].contiguous() for n in cases}
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            for n in cases:
+                kvq.append(x_new[n], positions, planes[n], cfgs[n], stream=stream)
+        stream.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        n_rep = 50
+        a.record(stream)
+        for _ in range(n_rep):
+            for n in cases:
+                kvq.append(x_new[n], positions, planes[n], cfgs[n], stream=stream)
+        b.record(stream)
+        stream.synchronize()
+    append_us = a.elapsed_time(b) * 1e3 / n_rep
+    append_vec = sum(int(x_new[n].shape[0] * x_new[n].shape[1]) for n in cases)
+
     cpu = None
     if not args.no_cpu_baseline:
         nv, tc, nrows = cpu_baseline(data["inputs"], wl.cases, perm, args.cpu_seconds, 16)
@@ -269,6 +294,9 @@ def main():
         "compression_ratio": round(in_bytes["K"] / (pl_bytes["K"] - sink_bytes["K"]), 3),
         "kernels": kern,
         "copy_GBps_same_bytes": round(copy_gbps, 1),
+        "append": {"us_per_step": round(append_us, 2), "vectors_per_step": append_vec,
+                   "what": "decode-step cache update: K and V of every row appended at per-row positions "
+                           "(kvq_append, K with RoPE + perm), launch-latency bound"},
         "roofline": dict(
             {"kernel": dominant, "bound": dk["bound"]},
             **({"achieved": dk["valu_Tops"], "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s (32-bit VALU lane ops)",

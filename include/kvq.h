@@ -129,6 +129,29 @@ kvq_status kvq_packed_sizes(const kvq_config* cfg, size_t* codes_bytes, size_t* 
  * left untouched. */
 kvq_status kvq_encode(const kvq_config* cfg, const void* x, const kvq_planes* out, void* stream);
 
+/* Decode-step append: encode one new token per row into an encoded cache, as the
+ * cache update of single-token decoding does (EliteKV page, section 7.1: each step's
+ * post-RoPE key and value are appended at the sequence's current length).
+ *   cfg        describes the CACHE: rows R, tokens = T slots per row (slot s holds
+ *              position pos_offset + s), heads, head_dim, dtype of x, bits, rotation,
+ *              quantizer, RoPE, sinks and parameters exactly as for kvq_encode.
+ *   x          DEVICE, dtype cfg->dtype: one vector per (row, head), element (r, h, c) at
+ *              x + r*stride_r + h*stride_h + c (stride_t is not used; all strides 0 =
+ *              contiguous [R, H, D]).
+ *   positions  DEVICE int64 [R]: the position of row r's new token.  The token is encoded
+ *              exactly as kvq_encode encodes a token at that position (its RoPE angle; a
+ *              sink, i.e. fp16 into sink slot positions[r] with zeroed code, scale, zero
+ *              and norm slots, when positions[r] < n_sink) and written to slot
+ *              positions[r] - pos_offset of every plane of that row.  A row whose position
+ *              lies outside [pos_offset, pos_offset + T) writes nothing.
+ *   cache      DEVICE planes of the [R, T, H] cache, laid out as for kvq_encode.  Slots
+ *              other than the written ones are not touched.
+ * Asynchronous; x must not alias any plane.  The positions are read on the device, so
+ * they are not checked on the host beyond the pointer (a row with an out-of-range
+ * position is skipped, as above). */
+kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* positions, const kvq_planes* cache,
+                      void* stream);
+
 /* Decode in's planes into y (DEVICE, contiguous [R,T,H,D] of y_dtype).  Asynchronous.
  * y must not alias any plane. */
 kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int32_t y_dtype,

@@ -23,5 +23,5 @@ Parity pins: every function is pinned by a CPU test against something other
 than itself (closed forms, library routines, brute force, textbook values);
 see the tests named ``test_oracle_*``.
 """
-from .codec import CodecParams, decode, encode, widen  # noqa: F401
+from .codec import CodecParams, append, decode, encode, widen  # noqa: F401
 from .lloyd import fit_gaussian  # noqa: F401

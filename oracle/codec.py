@@ -25,7 +25,7 @@ applies RoPE to k before the cache update).
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Dict, Optional
 
 import numpy as np
@@ -159,3 +159,36 @@ def decode(planes: Dict[str, np.ndarray], p: CodecParams, shape) -> np.ndarray:
     for ti in np.nonzero(pos < p.n_sink)[0]:
         v[:, ti] = planes["sink"][:, pos[ti]].astype(np.float64)
     return v
+
+
+PLANE_NAMES = ("codes", "scale", "zero", "norm", "sink")
+
+
+def append(cache: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, p: CodecParams) -> Dict[str, np.ndarray]:
+    """Decode-step append: one new token per row written into an encoded cache.
+
+    EliteKV page, section 7.1 (core implementation): during single-token decoding the
+    attention forward applies RoPE to the new key and the cache's update appends the
+    token at the sequence's current length.  Reading: row r's vector ``x[r]`` ([R, H, D],
+    float64) is the token at position ``positions[r]``, encoded exactly as ``encode``
+    encodes a token at that position (same RoPE angle; a sink when the position is below
+    ``n_sink``), and stored in slot ``positions[r] - pos_offset`` of a cache whose planes
+    hold ``T`` slots per row (slot s = position pos_offset + s).  A row whose position has
+    no slot is left unchanged.  Returns updated copies of the cache planes.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = {k: np.array(v, copy=True) for k, v in cache.items() if k in PLANE_NAMES}
+    rows, slots = out["codes"].shape[:2]
+    for r in range(rows):
+        pos = int(positions[r])
+        slot = pos - p.pos_offset
+        if not 0 <= slot < slots:
+            continue
+        one = encode(x[r][None, None], replace(p, pos_offset=pos))
+        for name in ("codes", "scale", "zero", "norm"):
+            if name in out and name in one:
+                out[name][r, slot] = one[name][0, 0]
+        if pos < p.n_sink:
+            out["sink"][r, pos] = one["sink"][0, pos]
+    return out
+

@@ -21,7 +21,7 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
-__all__ = ["Config", "KvqError", "encode", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
+__all__ = ["Config", "KvqError", "encode", "append", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
            "library_path", "abi_version", "DTYPES", "ROTATIONS", "QUANTIZERS", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,8 +31,8 @@ ABI_VERSION = 1
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 ROTATIONS = {"none": 0, "fwht": 1, "so4": 2}
 QUANTIZERS = {"minmax": 0, "lloyd": 1}
-EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_decode",
-                    "kvq_lloyd_max_gaussian", "kvq_status_string", "kvq_last_error_message")
+EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append",
+                    "kvq_decode", "kvq_lloyd_max_gaussian", "kvq_status_string", "kvq_last_error_message")
 
 
 class _Config(ctypes.Structure):
@@ -91,13 +91,15 @@ def _load():
     lib.kvq_validate.argtypes = [ctypes.POINTER(_Config)]
     lib.kvq_packed_sizes.argtypes = [ctypes.POINTER(_Config)] + [ctypes.POINTER(ctypes.c_size_t)] * 5
     lib.kvq_encode.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.POINTER(_Planes), ctypes.c_void_p]
+    lib.kvq_append.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Planes),
+                               ctypes.c_void_p]
     lib.kvq_decode.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Planes), ctypes.c_void_p, ctypes.c_int32,
                                ctypes.c_void_p]
     lib.kvq_lloyd_max_gaussian.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_last_error_message.restype = ctypes.c_char_p
-    for fn in ("kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_decode", "kvq_lloyd_max_gaussian"):
+    for fn in ("kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append", "kvq_decode", "kvq_lloyd_max_gaussian"):
         getattr(lib, fn).restype = ctypes.c_int
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -220,6 +222,22 @@ def encode(x, cfg: Config, planes=None, stream=None):
     p = _planes_struct(planes)
     _check(_lib.kvq_encode(ctypes.byref(c), _ptr(x), ctypes.byref(p), _stream_handle(stream)))
     return planes
+
+
+def append(x, positions, cache, cfg: Config, stream=None):
+    """Decode-step append: encode row r's new token ``x[r]`` ([R,H,D] of cfg.dtype, strided
+    as cfg.strides' row and head strides) at position ``positions[r]`` (int64 device tensor
+    [R]) into slot ``positions[r] - cfg.pos_offset`` of the ``cache`` planes, which hold
+    cfg.shape = (R, slots, H, D).  Rows whose position is outside the cache's slots write
+    nothing.  Returns ``cache``."""
+    import torch
+    r = int(cfg.shape[0])
+    if positions.dtype != torch.int64 or positions.numel() != r or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous int64 tensor with one entry per row")
+    c = cfg.c_struct()
+    p = _planes_struct(cache)
+    _check(_lib.kvq_append(ctypes.byref(c), _ptr(x), _ptr(positions), ctypes.byref(p), _stream_handle(stream)))
+    return cache
 
 
 _TORCH_DT = {"f16": "float16", "bf16": "bfloat16", "f32": "float32"}

@@ -278,6 +278,58 @@ kvq_status kvq_encode(const kvq_config* cfg, const void* x, const kvq_planes* ou
   return ok();
 }
 
+kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* positions, const kvq_planes* cache,
+                      void* stream) {
+  Derived dv;
+  kvq_status st = check_config(cfg, &dv);  // cfg describes the cache: tokens = slots per row
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_ERR_NULL, "cache planes is NULL");
+  if (dv.n_vec == 0) return ok();
+  if ((st = check_planes(cfg, dv, cache)) != KVQ_OK) return st;
+  // a sink plane is needed whenever some slot of the cache is a sink position
+  if (cfg->n_sink > 0 && cfg->pos_offset < cfg->n_sink && !cache->sink)
+    return fail(KVQ_ERR_NULL, "sink plane is NULL");
+  if (!x) return fail(KVQ_ERR_NULL, "x is NULL");
+  if (!positions) return fail(KVQ_ERR_NULL, "positions is NULL");
+  if (!aligned16(x)) return fail(KVQ_ERR_ALIGN, "x not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(positions) & 7u) != 0) return fail(KVQ_ERR_ALIGN, "positions not 8-byte aligned");
+  kvq::CodecArgs a;
+  fill_args(cfg, dv, &a);
+  // the input is one vector per (row, head): [R, H, D] with the row and head strides
+  const bool contiguous = cfg->stride_r == 0 && cfg->stride_t == 0 && cfg->stride_h == 0;
+  a.tokens = 1;
+  a.sr = contiguous ? cfg->heads * cfg->head_dim : cfg->stride_r;
+  a.st = 0;
+  a.sh = contiguous ? cfg->head_dim : cfg->stride_h;
+  a.cap = cfg->tokens;
+  a.row_pos = positions;
+  a.x = x;
+  a.codes = static_cast<uint8_t*>(cache->codes);
+  a.scale = static_cast<uint16_t*>(cache->scale);
+  a.zero = static_cast<uint16_t*>(cache->zero);
+  a.norm = static_cast<float*>(cache->norm);
+  a.sink = static_cast<uint16_t*>(cache->sink);
+  const int vpw = cfg->head_dim == 128 ? 16 : 8;
+  a.n_tiles = (cfg->heads + vpw - 1) / vpw;
+  a.n_items = cfg->rows * a.n_tiles;
+  a.div_heads = kvq::make_fastdiv((uint32_t)std::max<int64_t>(cfg->heads, 1));
+  const bool d128 = cfg->head_dim == 128;
+  int err;
+  switch (cfg->dtype) {
+    case KVQ_F16:
+      err = (d128 ? kvq::launch_encode_f16_d128 : kvq::launch_encode_f16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
+    case KVQ_BF16:
+      err = (d128 ? kvq::launch_encode_bf16_d128 : kvq::launch_encode_bf16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
+    default:
+      err = (d128 ? kvq::launch_encode_f32_d128 : kvq::launch_encode_f32_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+      break;
+  }
+  if (err != 0) return fail(KVQ_ERR_DEVICE, "append launch failed: %s", kvq::device_error_string(err));
+  return ok();
+}
+
 kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int32_t y_dtype, void* stream) {
   Derived dv;
   kvq_status st = check_config(cfg, &dv);

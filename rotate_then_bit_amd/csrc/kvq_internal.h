@@ -58,6 +58,11 @@ struct CodecArgs {
   FastDiv div_task;  // division by n_tiles (encoder) or n_tblk (decoder), set by the launcher
   FastDiv div_heads; // division by heads (column -> token)
   int32_t trig_rows;      // RoPE table rows per wave: tokens one tile can span (set by the launcher)
+  // append (decode-step update): the input is one token per row, row r's position is
+  // row_pos[r] (DEVICE), and it is written to slot row_pos[r] - pos_offset of planes with
+  // cap token slots per row; NULL for a plain encode
+  const int64_t* row_pos;
+  int64_t cap;
   // parameters
   uint8_t perm[kMaxHeadDim];
   float quat[kMaxHeadDim / 4 * 8];

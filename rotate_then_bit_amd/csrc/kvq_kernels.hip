@@ -633,7 +633,9 @@ __device__ __host__ inline size_t enc_wave_bytes(bool perm, bool rope, int trig_
 // RT / PT: RoPE / permutation off (0), on (1) or read from the arguments (-1).
 // GBT: log2 of the min-max group size, or -1 to read it from the arguments.  The hot
 // configurations get compile-time values; the rest share run-time variants.
-template <int DT, int D, int BITS, int ROT, int QUANT, int RT, int PT, int GBT>
+// AP: append mode (one token per row at the row's own position, into a cache of cap
+// slots per row); one item per wave, so each wave builds its RoPE table for its row.
+template <int DT, int D, int BITS, int ROT, int QUANT, int RT, int PT, int GBT, int AP = 0>
 __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const CodecArgs a) {
   using G = Geo<D>;
   constexpr int LV = G::LV, VPW = G::VPW;
@@ -670,6 +672,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   const uint32_t wid = blockIdx.x * kWavesPerBlock + (uint32_t)wave;
   Walk wk;
   if (!walk_first_rows(a, wid, wk)) return;  // wave-uniform; no barrier follows
+  // append: the position of the wave's row (its only item)
+  const int64_t prow = AP ? a.row_pos[wk.r] : 0;
 
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
@@ -720,7 +724,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       if (ROPE) {
         const uint32_t last = (uint32_t)(min(lt.tile * VPW + VPW, ncols) - 1);  // < 2^31
         const int ntok = (int)(fdiv(last, a.div_heads) - (uint32_t)lt.t0) + 1;
-        const int64_t p0 = a.pos_offset + lt.t0;
+        const int64_t p0 = (AP ? prow : a.pos_offset) + lt.t0;
         wave_lds_sync();  // the previous tile's table has been read
         for (int m = lane; m < ntok * (D / 2); m += 64) {
           const int tok = m / (D / 2), i = m % (D / 2);
@@ -748,8 +752,61 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
 
   // Every lane computes; the stores of lanes past the end of the tensor are dropped.
   auto process = [&](const RawRow<DT>& raw, const LaneTile& lt, int64_t row) __attribute__((always_inline)) {
-    const int64_t vec0 = row * ncols + lt.tile * VPW;        // first vector of the item in the planes
-    const int64_t nvalid = min(ncols - lt.tile * VPW, (int64_t)VPW);  // vectors of the item that exist
+    int64_t vec0 = row * ncols + lt.tile * VPW;                // first vector of the item in the planes
+    int64_t nvalid = min(ncols - lt.tile * VPW, (int64_t)VPW);  // vectors of the item that exist
+    if constexpr (AP) {
+      // the row's slot in the cache; a position outside the cache's slots writes nothing
+      const int64_t slot = prow - a.pos_offset;
+      const bool in = slot >= 0 && slot < a.cap;
+      vec0 = in ? (row * a.cap + slot) * a.heads + lt.tile * VPW : 0;
+      nvalid = in ? nvalid : 0;
+      if (prow < a.n_sink) {
+        // a sink position (wave-uniform: the item is one row at one position): fp16 of the
+        // post-RoPE vector into the sink plane, zeros into the vector's other slots
+        float v[32];
+        widen_row<DT>(raw, v);
+        if constexpr (ROPE_ANY) {
+          if (ROPE) {
+            const uint32_t tp0 = trig_addr + (uint32_t)(lt.dtok * trig_row<D>() + kTrigLane * l);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const u32x4_t cs = lds_ld4(tp0 + 32u * c + 16u * hh);
+                float* w = v + 8 * c + 4 * hh;
+                const float x0 = w[0], x1 = w[1], x2 = w[2], x3 = w[3];
+                w[0] = __builtin_fmaf(x0, __uint_as_float(cs.x), -x1 * __uint_as_float(cs.y));
+                w[1] = __builtin_fmaf(x0, __uint_as_float(cs.y), x1 * __uint_as_float(cs.x));
+                w[2] = __builtin_fmaf(x2, __uint_as_float(cs.z), -x3 * __uint_as_float(cs.w));
+                w[3] = __builtin_fmaf(x2, __uint_as_float(cs.w), x3 * __uint_as_float(cs.z));
+              }
+          }
+        }
+        const buf_t sb = make_buf_item(a.sink + ((row * a.n_sink + prow) * a.heads + lt.tile * VPW) * D,
+                                       (uint32_t)(nvalid * D * 2));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4_t w = {pack_f16x2(v[8 * k + 0], v[8 * k + 1]), pack_f16x2(v[8 * k + 2], v[8 * k + 3]),
+                             pack_f16x2(v[8 * k + 4], v[8 * k + 5]), pack_f16x2(v[8 * k + 6], v[8 * k + 7])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, sb, (uint32_t)((q * D + 32 * l) * 2 + 16 * k), 0, 0);
+        }
+        LaneCodes<BITS> zc;
+#pragma unroll
+        for (int w = 0; w < BITS; ++w) zc.w[w] = 0u;
+        store_lane_codes<BITS>(make_buf_item(a.codes + vec0 * CB, (uint32_t)(CB * nvalid)),
+                               (uint32_t)(q * CB + l * (4 * BITS)), zc);
+        if constexpr (QUANT == Q_MINMAX) {
+          const uint32_t gbytes = (uint32_t)(2 * nvalid * ngroups);
+          const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, make_buf_item(a.scale + vec0 * ngroups, gbytes), go, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, make_buf_item(a.zero + vec0 * ngroups, gbytes), go, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(0u, make_buf_item(a.norm + vec0, (uint32_t)(4 * nvalid)),
+                                                4u * (uint32_t)q, 0, 0);
+        }
+        return;
+      }
+    }
     float v[32];
     // RoPE of the 4 channel pairs of 8 consecutive slots 8c .. 8c + 7
     auto rope8 = [&](float* u, int c) __attribute__((always_inline)) {
@@ -1413,7 +1470,7 @@ int plan_grid(CodecArgs& b, bool tiles_of_a_row, int len, unsigned& nb) {
   return 0;
 }
 
-template <int DT, int D, int BITS, int ROT, int QUANT, int RT, int PT, int GBT>
+template <int DT, int D, int BITS, int ROT, int QUANT, int RT, int PT, int GBT, int AP = 0>
 int launch_enc_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
   constexpr int VPW = Geo<D>::VPW;
@@ -1425,10 +1482,11 @@ int launch_enc_t(const CodecArgs& a, hipStream_t s) {
   // serve 2; otherwise one item per wave.
   const size_t lds = (size_t)kWavesPerBlock * enc_wave_bytes<D>(a.use_perm != 0, a.rope != 0, b.trig_rows);
   unsigned nb = 0;
-  if (int e = plan_grid(b, false, a.rope ? 8 : (a.use_perm ? 2 : 1), nb)) return e;
-  hipLaunchKernelGGL((encode_kernel<DT, D, BITS, ROT, QUANT, RT, PT, GBT>), dim3(nb), dim3(64 * kWavesPerBlock),
+  if (int e = plan_grid(b, false, AP ? 1 : (a.rope ? 8 : (a.use_perm ? 2 : 1)), nb)) return e;
+  hipLaunchKernelGGL((encode_kernel<DT, D, BITS, ROT, QUANT, RT, PT, GBT, AP>), dim3(nb), dim3(64 * kWavesPerBlock),
                      lds, s, b);
   if (hipError_t e = hipGetLastError()) return (int)e;
+  if constexpr (AP) return 0;  // the append kernel writes sink positions itself
   if (const unsigned ns = sink_blocks(a, Geo<D>::LV)) {
     hipLaunchKernelGGL((encode_sink_kernel<DT, D, BITS, QUANT>), dim3(ns), dim3(64 * kWavesPerBlock), 0, s, b);
     return (int)hipGetLastError();
@@ -1473,6 +1531,8 @@ int pick_group(const CodecArgs& a, hipStream_t s) {
 template <bool ENC, int DT, int D, int BITS, int ROT, int QUANT>
 int pick_feat(const CodecArgs& a, hipStream_t s) {
   if constexpr (ENC) {
+    // append: features read from the arguments (a launch of a few thousand vectors)
+    if (a.row_pos) return launch_enc_t<DT, D, BITS, ROT, QUANT, -1, -1, -1, 1>(a, s);
     if constexpr (ROT == ROT_FWHT && QUANT == Q_MINMAX) {
       if (a.rope) return a.use_perm ? pick_group<DT, D, BITS, 1, 1>(a, s) : pick_group<DT, D, BITS, 1, 0>(a, s);
       return a.use_perm ? pick_group<DT, D, BITS, 0, 1>(a, s) : pick_group<DT, D, BITS, 0, 0>(a, s);

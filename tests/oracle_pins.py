@@ -458,4 +458,52 @@ def check_pipeline_norm_separation():
     assert np.all(y[0, 0, 0] == 0.0)
 
 
+# --------------------------------------------------------------------------- #
+# decode-step append
+# --------------------------------------------------------------------------- #
+def check_append_matches_batch_encode():
+    """Appending the tokens of a tensor one position at a time (in any order) into an empty
+    cache reproduces the batch encode of the whole tensor, plane for plane; positions
+    without a slot leave the cache untouched; rows are independent."""
+    rng = _rng(16)
+    r, t, h, d = 3, 7, 2, 128
+    x = rng.standard_normal((r, t, h, d))
+    x[..., [3, 90]] *= 15
+    perm = rng.permutation(d)
+    for quant_kind in ("minmax", "lloyd"):
+        if quant_kind == "minmax":
+            p = codec.CodecParams(bits=2, group_size=64, rope=True, perm=perm, n_sink=3, pos_offset=2)
+        else:
+            cb = lloyd.fit_gaussian(3, 1.0 / np.sqrt(d))
+            p = codec.CodecParams(bits=3, group_size=d, quant="lloyd", rope=True, n_sink=3, pos_offset=2,
+                                  codebook=cb)
+        full = codec.encode(x, p)
+        names = [n for n in ("codes", "scale", "zero", "norm", "sink") if n in full]
+        cache = {n: np.zeros_like(full[n]) for n in names}
+        for ti in rng.permutation(t):
+            cache = codec.append(cache, x[:, ti], np.full(r, p.pos_offset + ti), p)
+        for n in names:
+            assert np.array_equal(cache[n], full[n]), n
+        # no slot: below pos_offset, at pos_offset + t, far beyond
+        for pos in (p.pos_offset - 1, p.pos_offset + t, 10 ** 6):
+            again = codec.append(cache, x[:, 0] + 1.0, np.full(r, pos), p)
+            for n in names:
+                assert np.array_equal(again[n], cache[n]), n
+        # one row at a time, each at its own position
+        empty = {n: np.zeros_like(full[n]) for n in names}
+        pos = np.array([p.pos_offset + 4, p.pos_offset, p.pos_offset + 6])
+        xs = np.stack([x[i, pos[i] - p.pos_offset] for i in range(r)])
+        one = codec.append(empty, xs, pos, p)
+        for i in range(r):
+            s = pos[i] - p.pos_offset
+            for n in names:
+                if n == "sink":
+                    if pos[i] < p.n_sink:
+                        assert np.array_equal(one[n][i, pos[i]], full[n][i, pos[i]])
+                else:
+                    assert np.array_equal(one[n][i, s], full[n][i, s]), n
+                    other = np.delete(one[n][i], s, axis=0)
+                    assert not np.any(other), n
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -133,6 +133,14 @@ def _decode_rho_plus_eps(planes, p, shape):
     return y
 
 
+_orig_append = codec.append
+
+
+def _append_slot_is_position(cache, x, positions, p):
+    # the slot taken as the position itself, ignoring the cache's first position
+    return _orig_append(cache, x, positions, codec.CodecParams(**{**p.__dict__, "pos_offset": 0}))
+
+
 MUTATIONS = {
     "rope_negative_sine": (rope, "rope", _rope_neg_sine),
     "rope_half_split_pairs": (rope, "rope", _rope_half_split),
@@ -149,6 +157,7 @@ MUTATIONS = {
     "pack_msb_first": (pack, "pack", _pack_msb_first),
     "decode_perm_gather": (codec, "decode", _decode_gather_not_scatter),
     "decode_rho_plus_eps": (codec, "decode", _decode_rho_plus_eps),
+    "append_slot_is_position": (codec, "append", _append_slot_is_position),
 }
 
 
