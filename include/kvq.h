@@ -152,6 +152,34 @@ kvq_status kvq_encode(const kvq_config* cfg, const void* x, const kvq_planes* ou
 kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* positions, const kvq_planes* cache,
                       void* stream);
 
+/* Decode-step attention over an encoded K/V cache: for every row r and query head m,
+ *   out[r, m] = sum_t softmax_t(scale * q[r, m] . k_t) v_t   over slots t < lengths[r],
+ * where k_t, v_t are the cache's decoded vectors (what kvq_decode returns) of KV head
+ * m / (q_heads / heads) -- the attention of the EliteKV page, section 7.1 (query scaled,
+ * scored against the cached post-RoPE keys, softmax over positions, weighted sum of the
+ * cached values).  The keys are never decoded: with the orthonormal Hadamard rotation M and
+ * the keys' permutation P, q . k_t = (M P q) . y_t for the stored y_t = zero + code * scale,
+ * and the values are summed in the rotated domain and rotated back once per output (the
+ * rotation of the RotateKV page, whose decode-stage speed-up this serves).  Sink slots are
+ * read from the fp16 sink planes.
+ *   cfg_k, cfg_v  the K and V caches: same rows R, slots T, heads H, head_dim 128, bits
+ *                 (2 or 4), group (32, 64 or 128), n_sink (at most 64), Walsh-Hadamard and
+ *                 min-max, pos_offset 0 (slot t holds position t); each its own permutation
+ *                 and RoPE flag (keys hold post-RoPE values; q must be rotated by RoPE at its
+ *                 own position by the caller).  Otherwise KVQ_ERR_UNSUPPORTED / KVQ_ERR_SHAPE.
+ *   k, v          DEVICE planes of the two caches (as written by kvq_encode / kvq_append).
+ *   q, out        DEVICE float32 [R, q_heads, 128], contiguous; q_heads = H * g, g in {1, 2, 4}.
+ *   lengths       DEVICE int32 [R]: slots each row attends over (clamped to [0, T]); NULL = T.
+ *                 A row with no slot gets zeros.
+ *   scale         score multiplier (head_dim^-1/2 in the page's code); finite.
+ *   workspace     DEVICE, 16-byte aligned, at least kvq_attend_workspace_size(cfg_k, q_heads)
+ *                 bytes, owned by the caller; its contents are scratch between calls.
+ * Asynchronous; calls that share a workspace must not overlap. */
+kvq_status kvq_attend_workspace_size(const kvq_config* cfg_k, int64_t q_heads, size_t* bytes);
+kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v, const kvq_planes* v,
+                      const float* q, int64_t q_heads, const int32_t* lengths, float scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Decode in's planes into y (DEVICE, contiguous [R,T,H,D] of y_dtype).  Asynchronous.
  * y must not alias any plane. */
 kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int32_t y_dtype,

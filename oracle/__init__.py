@@ -24,4 +24,5 @@ than itself (closed forms, library routines, brute force, textbook values);
 see the tests named ``test_oracle_*``.
 """
 from .codec import CodecParams, append, decode, encode, widen  # noqa: F401
+from .attention import attend, attend_decoded  # noqa: F401
 from .lloyd import fit_gaussian  # noqa: F401

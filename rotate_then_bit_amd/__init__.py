@@ -21,7 +21,7 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
-__all__ = ["Config", "KvqError", "encode", "append", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
+__all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_workspace_size", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
            "library_path", "abi_version", "DTYPES", "ROTATIONS", "QUANTIZERS", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,8 @@ DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 ROTATIONS = {"none": 0, "fwht": 1, "so4": 2}
 QUANTIZERS = {"minmax": 0, "lloyd": 1}
 EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append",
-                    "kvq_decode", "kvq_lloyd_max_gaussian", "kvq_status_string", "kvq_last_error_message")
+                    "kvq_attend_workspace_size", "kvq_attend", "kvq_decode", "kvq_lloyd_max_gaussian",
+                    "kvq_status_string", "kvq_last_error_message")
 
 
 class _Config(ctypes.Structure):
@@ -95,11 +96,16 @@ def _load():
                                ctypes.c_void_p]
     lib.kvq_decode.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Planes), ctypes.c_void_p, ctypes.c_int32,
                                ctypes.c_void_p]
+    lib.kvq_attend_workspace_size.argtypes = [ctypes.POINTER(_Config), ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_attend.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Planes), ctypes.POINTER(_Config),
+                               ctypes.POINTER(_Planes), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                               ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.kvq_lloyd_max_gaussian.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_last_error_message.restype = ctypes.c_char_p
-    for fn in ("kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append", "kvq_decode", "kvq_lloyd_max_gaussian"):
+    for fn in ("kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append", "kvq_decode", "kvq_lloyd_max_gaussian",
+               "kvq_attend_workspace_size", "kvq_attend"):
         getattr(lib, fn).restype = ctypes.c_int
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -238,6 +244,40 @@ def append(x, positions, cache, cfg: Config, stream=None):
     p = _planes_struct(cache)
     _check(_lib.kvq_append(ctypes.byref(c), _ptr(x), _ptr(positions), ctypes.byref(p), _stream_handle(stream)))
     return cache
+
+
+def attend_workspace_size(k_cfg: Config, q_heads: int) -> int:
+    """Bytes of device workspace ``attend`` needs for this cache shape and query-head count."""
+    c = k_cfg.c_struct()
+    n = ctypes.c_size_t()
+    _check(_lib.kvq_attend_workspace_size(ctypes.byref(c), int(q_heads), ctypes.byref(n)))
+    return int(n.value)
+
+
+def attend(q, k_planes, k_cfg: Config, v_planes, v_cfg: Config, lengths=None, scale=None, out=None,
+           workspace=None, stream=None):
+    """Decode-step attention of ``q`` (float32 device tensor [R, q_heads, 128]) over the encoded
+    K/V cache; ``lengths`` (int32 device tensor [R]) limits each row to its first slots.
+    Returns ``out`` (float32 [R, q_heads, 128])."""
+    import torch
+    r, q_heads = int(q.shape[0]), int(q.shape[1])
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float32 tensor [rows, q_heads, 128]")
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() != r or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous int32 tensor with one entry per row")
+    if scale is None:
+        scale = float(k_cfg.shape[-1]) ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    need = attend_workspace_size(k_cfg, q_heads)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ck, cv = k_cfg.c_struct(), v_cfg.c_struct()
+    pk, pv = _planes_struct(k_planes), _planes_struct(v_planes)
+    _check(_lib.kvq_attend(ctypes.byref(ck), ctypes.byref(pk), ctypes.byref(cv), ctypes.byref(pv), _ptr(q), q_heads,
+                           _ptr(lengths), float(scale), _ptr(out), int(workspace.data_ptr()),
+                           int(workspace.numel() * workspace.element_size()), _stream_handle(stream)))
+    return out
 
 
 _TORCH_DT = {"f16": "float16", "bf16": "bfloat16", "f32": "float32"}

@@ -365,6 +365,113 @@ kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int3
   return ok();
 }
 
+namespace {
+// the configurations decode-step attention supports, and the workspace it needs
+kvq_status check_attend(const kvq_config* cfg_k, const kvq_config* cfg_v, int64_t q_heads, size_t* ws_bytes,
+                        kvq::AttendArgs* a) {
+  Derived dk, dv;
+  kvq_status st = check_config(cfg_k, &dk);
+  if (st != KVQ_OK) return st;
+  if (cfg_v) {
+    if ((st = check_config(cfg_v, &dv)) != KVQ_OK) return st;
+    if (cfg_v->rows != cfg_k->rows || cfg_v->tokens != cfg_k->tokens || cfg_v->heads != cfg_k->heads ||
+        cfg_v->head_dim != cfg_k->head_dim || cfg_v->bits != cfg_k->bits || cfg_v->group_size != cfg_k->group_size ||
+        cfg_v->n_sink != cfg_k->n_sink || cfg_v->pos_offset != cfg_k->pos_offset || cfg_v->rot != cfg_k->rot ||
+        cfg_v->quant != cfg_k->quant)
+      return fail(KVQ_ERR_SHAPE, "the K and V caches must share rows, slots, heads, head_dim, bits, group, "
+                                 "sinks, pos_offset, rotation and quantizer");
+  }
+  if (cfg_k->head_dim != 128 || cfg_k->rot != KVQ_ROT_FWHT || cfg_k->quant != KVQ_Q_MINMAX ||
+      (cfg_k->bits != 2 && cfg_k->bits != 4) || cfg_k->group_size < 32 || cfg_k->group_size > 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "attention supports head_dim 128, Walsh-Hadamard, min-max, 2 or 4 bits, "
+                                     "groups of 32, 64 or 128");
+  if (cfg_k->pos_offset != 0) return fail(KVQ_ERR_UNSUPPORTED, "attention needs pos_offset 0 (slot = position)");
+  if (cfg_k->n_sink > 64) return fail(KVQ_ERR_UNSUPPORTED, "attention supports at most 64 sink slots");
+  if (cfg_k->heads <= 0 || q_heads <= 0 || q_heads % cfg_k->heads != 0)
+    return fail(KVQ_ERR_SHAPE, "q_heads must be a positive multiple of heads");
+  const int64_t qg = q_heads / cfg_k->heads;
+  if (qg != 1 && qg != 2 && qg != 4)
+    return fail(KVQ_ERR_UNSUPPORTED, "attention supports 1, 2 or 4 query heads per KV head");
+  int32_t nc = 1, ct = 8;
+  kvq::attend_chunks(cfg_k->rows, cfg_k->heads, cfg_k->tokens, &nc, &ct);
+  int64_t nq = 0, tmp = 0;
+  if (!mul_ok(cfg_k->rows, q_heads, &nq) || !mul_ok(nq, (int64_t)nc * kvq::kAttendPart + 128, &tmp) ||
+      tmp > (int64_t(1) << 40))
+    return fail(KVQ_ERR_SHAPE, "attention workspace too large");
+  const size_t q_bytes = (size_t)(nq * 128 * 4 + 255) / 256 * 256;
+  *ws_bytes = q_bytes + (size_t)nq * (size_t)nc * kvq::kAttendPart * 4;
+  if (a) {
+    memset(a, 0, sizeof *a);
+    a->rows = cfg_k->rows;
+    a->tokens = cfg_k->tokens;
+    a->heads = cfg_k->heads;
+    a->q_heads = q_heads;
+    a->group_log2 = ilog2(cfg_k->group_size);
+    a->n_sink = cfg_k->n_sink;
+    a->n_chunks = nc;
+    a->chunk = ct;
+    a->use_perm_k = cfg_k->perm ? 1 : 0;
+    if (cfg_k->perm)
+      for (int i = 0; i < 128; ++i) a->perm_k[i] = (uint8_t)cfg_k->perm[i];
+    if (cfg_v) {
+      a->use_perm_v = cfg_v->perm ? 1 : 0;
+      if (cfg_v->perm)
+        for (int i = 0; i < 128; ++i) a->perm_v[i] = (uint8_t)cfg_v->perm[i];
+    }
+  }
+  return KVQ_OK;
+}
+}  // namespace
+
+kvq_status kvq_attend_workspace_size(const kvq_config* cfg_k, int64_t q_heads, size_t* bytes) {
+  if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+  kvq_status st = check_attend(cfg_k, nullptr, q_heads, bytes, nullptr);
+  return st == KVQ_OK ? ok() : st;
+}
+
+kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v, const kvq_planes* v,
+                      const float* q, int64_t q_heads, const int32_t* lengths, float scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cfg_v) return fail(KVQ_ERR_NULL, "cfg_v is NULL");
+  size_t need = 0;
+  kvq::AttendArgs a;
+  kvq_status st = check_attend(cfg_k, cfg_v, q_heads, &need, &a);
+  if (st != KVQ_OK) return st;
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(KVQ_ERR_PARAM, "scale must be finite");
+  Derived dk, dv;
+  (void)check_config(cfg_k, &dk);  // both already accepted above; this fills the derived sizes
+  (void)check_config(cfg_v, &dv);
+  if (!k || !v) return fail(KVQ_ERR_NULL, "planes is NULL");
+  if (cfg_k->rows == 0) return ok();
+  // (a cache with no slot still runs: every output row is then zero)
+  if ((st = check_planes(cfg_k, dk, k)) != KVQ_OK) return st;
+  if ((st = check_planes(cfg_v, dv, v)) != KVQ_OK) return st;
+  if (cfg_k->n_sink > 0 && (!k->sink || !v->sink)) return fail(KVQ_ERR_NULL, "sink plane is NULL");
+  if (!q || !out || !workspace) return fail(KVQ_ERR_NULL, "q, out or workspace is NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
+    return fail(KVQ_ERR_ALIGN, "q, out and workspace must be 16-byte aligned");
+  if (lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) return fail(KVQ_ERR_ALIGN, "lengths not 4-byte aligned");
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  a.k_codes = static_cast<const uint8_t*>(k->codes);
+  a.k_scale = static_cast<const uint16_t*>(k->scale);
+  a.k_zero = static_cast<const uint16_t*>(k->zero);
+  a.k_sink = static_cast<const uint16_t*>(k->sink);
+  a.v_codes = static_cast<const uint8_t*>(v->codes);
+  a.v_scale = static_cast<const uint16_t*>(v->scale);
+  a.v_zero = static_cast<const uint16_t*>(v->zero);
+  a.v_sink = static_cast<const uint16_t*>(v->sink);
+  a.q = q;
+  a.out = out;
+  a.qrot = static_cast<float*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)(a.rows * q_heads * 128 * 4 + 255) / 256 * 256);
+  a.lengths = lengths;
+  a.scale = scale;
+  const int err = kvq::launch_attend(cfg_k->bits, (int)(q_heads / cfg_k->heads), a, stream);
+  if (err != 0) return fail(KVQ_ERR_DEVICE, "attention launch failed: %s", kvq::device_error_string(err));
+  return ok();
+}
+
 kvq_status kvq_lloyd_max_gaussian(int32_t bits, double sigma, float* codebook_out) {
   if (!codebook_out) return fail(KVQ_ERR_NULL, "codebook_out is NULL");
   if (bits < 1 || bits > 4) return fail(KVQ_ERR_BITS, "bits %d (1..4)", bits);

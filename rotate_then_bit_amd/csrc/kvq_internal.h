@@ -69,6 +69,47 @@ struct CodecArgs {
   float codebook[kMaxCodebook];
 };
 
+// Decode-step attention over an encoded cache (d = 128, Walsh-Hadamard + min-max).  The
+// workspace holds the rotated queries [rows, q_heads, 128] and, per (row, query head,
+// chunk of slots), a partial result: 128 rotated-domain sums, the running maximum and
+// the softmax denominator.
+constexpr int kAttendPart = 128 + 2;  // floats per partial
+struct AttendArgs {
+  const uint8_t* k_codes;
+  const uint16_t* k_scale;
+  const uint16_t* k_zero;
+  const uint16_t* k_sink;
+  const uint8_t* v_codes;
+  const uint16_t* v_scale;
+  const uint16_t* v_zero;
+  const uint16_t* v_sink;
+  const float* q;        // [rows, q_heads, 128]
+  float* out;            // [rows, q_heads, 128]
+  float* qrot;           // workspace: rotated queries
+  float* part;           // workspace: partials [rows, q_heads, n_chunks, kAttendPart]
+  const int32_t* lengths;  // DEVICE [rows] or NULL (every slot)
+  int64_t rows, tokens, heads, q_heads;
+  int32_t group_log2, n_sink, n_chunks, chunk;  // chunk: slots per chunk (multiple of 8)
+  float scale;
+  int32_t use_perm_k, use_perm_v;
+  uint8_t perm_k[128];
+  uint8_t perm_v[128];
+};
+// the chunking of the slot axis for a cache shape (same rule on both sides of the ABI)
+inline void attend_chunks(int64_t rows, int64_t heads, int64_t tokens, int32_t* n_chunks, int32_t* chunk) {
+  const int64_t target = 16384;  // waves in flight for the partial pass
+  int64_t nc = (target + rows * heads - 1) / (rows * heads > 0 ? rows * heads : 1);
+  const int64_t max_nc = (tokens + 63) / 64;
+  if (nc > max_nc) nc = max_nc;
+  if (nc < 1) nc = 1;
+  int64_t ct = (tokens + nc - 1) / nc;
+  ct = (ct + 7) / 8 * 8;
+  if (ct < 8) ct = 8;
+  *n_chunks = (int32_t)((tokens + ct - 1) / ct > 0 ? (tokens + ct - 1) / ct : 1);
+  *chunk = (int32_t)ct;
+}
+int launch_attend(int bits, int qg, const AttendArgs& a, void* stream);
+
 // Launch helpers, one per (direction, dtype, head_dim), defined in kvq_kernels.hip.
 // Each returns a hipError_t as int (0 = success).
 #define KVQ_DECLARE_LAUNCH(NAME) int NAME(int bits, int rot, int quant, const CodecArgs& a, void* stream);

@@ -1456,6 +1456,270 @@ inline unsigned sink_blocks(const CodecArgs& a, int lv) {
 }
 
 // ---------------------------------------------------------------------------
+// DECODE-STEP ATTENTION OVER THE ENCODED CACHE (d = 128, Walsh-Hadamard + min-max)
+// ---------------------------------------------------------------------------
+// A decoded key is P^T M y with the orthonormal Hadamard M = H / sqrt(128), the keys'
+// permutation P and y = zero + code * scale per group, so q . k = (M P q) . y: each query
+// is rotated once and scored against the stored codes, scale and zero directly.  Values
+// are summed in the rotated domain, sum_t p_t P^T M y_t = P^T M sum_t p_t y_t, and rotated
+// back once per output.  Sink slots hold fp16 of the unrotated vectors and are scored and
+// summed unrotated.  Three passes: rotate the queries; per (row, KV head, chunk of slots)
+// a partial softmax-weighted sum; per (row, query head) the merge of the chunks, the
+// rotation back, the sinks and the normalisation.
+__device__ __forceinline__ float hsign(uint32_t a, uint32_t b) {
+  return (__builtin_popcount(a & b) & 1) ? -1.0f : 1.0f;
+}
+constexpr float kInvSqrt128 = 0.08838834764831845f;
+
+// rotated queries M P q: one wave per (row, query head), lane i computes channels i, i + 64
+__global__ void __launch_bounds__(256) attend_rotate_q(const AttendArgs a) {
+  __shared__ float s_q[4][128];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.q_heads) return;  // wave-uniform; no block barrier in this kernel
+  const float* q = a.q + w * 128;
+  float* sq = s_q[wave];
+  for (int k = lane; k < 128; k += 64) sq[k] = q[a.use_perm_k ? a.perm_k[k] : k];  // (P q)[k] = q[perm[k]]
+  wave_lds_sync();
+  float z0 = 0.0f, z1 = 0.0f;
+  for (int k = 0; k < 128; ++k) {
+    const float v = sq[k];
+    z0 = __builtin_fmaf(hsign((uint32_t)lane, (uint32_t)k), v, z0);
+    z1 = __builtin_fmaf(hsign((uint32_t)lane + 64u, (uint32_t)k), v, z1);
+  }
+  a.qrot[w * 128 + lane] = z0 * kInvSqrt128;
+  a.qrot[w * 128 + lane + 64] = z1 * kInvSqrt128;
+}
+
+template <int BITS>
+struct AttSlot {
+  uint32_t kw[BITS / 2], vw[BITS / 2];  // the lane's 16 codes of the key and of the value
+  uint32_t ks, kz, vs, vz;              // fp16 bits of the lane's group scale and zero
+};
+
+// Partial attention: one wave per (row, KV head, chunk of slots).  Lane (tk, l) =
+// (lane / 8, lane % 8) holds channels 16 l .. 16 l + 15 of the token slot tk of each step of
+// 8 slots; the 8 lanes of a slot reduce its scores, and each slot keeps its own running
+// maximum, denominator and rotated-domain sums until the wave merges them at the end.
+template <int BITS, int QG>
+__global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
+  const int64_t c = w % a.n_chunks, rh = w / a.n_chunks, h = rh % a.heads, r = rh / a.heads;
+  const int tk = lane >> 3, l = lane & 7;
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.n_sink);
+  const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
+  const int64_t ngroups = 128 >> a.group_log2;
+  const int g = (16 * l) >> a.group_log2;  // the lane's 16 channels lie in one group (G >= 32)
+  constexpr int CB = 128 * BITS / 8;       // code bytes per vector
+  constexpr int LB = 2 * BITS;             // code bytes per lane (16 codes)
+
+  float qv[QG][16], sl[QG];
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    const float* src = a.qrot + ((r * a.q_heads + h * QG + m) * 128 + 16 * l);
+    sl[m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      qv[m][i] = src[i];
+      sl[m] += qv[m][i];
+    }
+  }
+  float mx[QG], ls[QG], zs[QG], acc[QG][16];
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    mx[m] = -INFINITY;
+    ls[m] = 0.0f;
+    zs[m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
+  }
+
+  // the lane's slot of step t0 (clamped into the chunk for the loads; masked afterwards)
+  auto load = [&](int64_t t0, AttSlot<BITS>& s) __attribute__((always_inline)) {
+    int64_t t = t0 + tk;
+    if (t >= t_end) t = t_end - 1;
+    const int64_t vec = (r * a.tokens + t) * a.heads + h;
+    const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.k_codes + vec * CB + l * LB);
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_codes + vec * CB + l * LB);
+#pragma unroll
+    for (int i = 0; i < BITS / 2; ++i) {
+      s.kw[i] = kp[i];
+      s.vw[i] = vp[i];
+    }
+    s.ks = a.k_scale[vec * ngroups + g];
+    s.kz = a.k_zero[vec * ngroups + g];
+    s.vs = a.v_scale[vec * ngroups + g];
+    s.vz = a.v_zero[vec * ngroups + g];
+  };
+  auto unpack = [&](const uint32_t* wd, float* code) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      constexpr int PER = 32 / BITS;
+      code[i] = (float)((wd[i / PER] >> (BITS * (i % PER))) & ((1u << BITS) - 1u));
+    }
+  };
+
+  if (t_begin < t_end) {
+    AttSlot<BITS> cur, nxt;
+    load(t_begin, cur);
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += 8) {
+      if (t0 + 8 < t_end) load(t0 + 8, nxt);  // wave-uniform: the next step's loads in flight
+      const bool valid = t0 + tk < t_end;
+      float code[16];
+      unpack(cur.kw, code);
+      const float ks = f16_value(cur.ks), kz = f16_value(cur.kz);
+      float s[QG];
+#pragma unroll
+      for (int m = 0; m < QG; ++m) {
+        float d = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d = __builtin_fmaf(qv[m][i], code[i], d);
+        float part = __builtin_fmaf(ks, d, kz * sl[m]);  // q~ . (zero + code * scale) over 16 channels
+        part = add_x1(part);
+        part = add_x2(part);
+        part += swz_x4(part);
+        s[m] = valid ? part * a.scale : -INFINITY;
+      }
+      // online softmax: rescale the slot's sums when its maximum grows
+      bool grow = false;
+      float mn[QG];
+#pragma unroll
+      for (int m = 0; m < QG; ++m) {
+        mn[m] = fmaxf(mx[m], s[m]);
+        grow |= mn[m] > mx[m];
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int m = 0; m < QG; ++m) {
+          const float corr = (mn[m] > mx[m]) ? __expf(mx[m] - mn[m]) : 1.0f;
+          ls[m] *= corr;
+          zs[m] *= corr;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[m][i] *= corr;
+          mx[m] = mn[m];
+        }
+      }
+      unpack(cur.vw, code);
+      const float vs = f16_value(cur.vs), vz = f16_value(cur.vz);
+#pragma unroll
+      for (int m = 0; m < QG; ++m) {
+        const float p = valid ? __expf(s[m] - mx[m]) : 0.0f;
+        ls[m] += p;
+        zs[m] = __builtin_fmaf(p, vz, zs[m]);  // sum_t p_t zero_t, applies to every channel of the group
+        const float ps = p * vs;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][i] = __builtin_fmaf(ps, code[i], acc[m][i]);
+      }
+      cur = nxt;
+    }
+  }
+  // merge the wave's 8 slots and write the chunk's partial
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    float M = mx[m];
+    M = fmaxf(M, __shfl_xor(M, 8));
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float f = (mx[m] == -INFINITY) ? 0.0f : __expf(mx[m] - M);
+    float L = ls[m] * f;
+    L += __shfl_xor(L, 8);
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    float* pb = a.part + ((r * a.q_heads + h * QG + m) * a.n_chunks + c) * kAttendPart;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = (acc[m][i] + zs[m]) * f;
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (tk == 0) pb[16 * l + i] = v;
+    }
+    if (lane == 0) {
+      pb[128] = M;
+      pb[129] = L;
+    }
+  }
+}
+
+// Merge the chunks of each (row, query head), rotate back, add the sink slots, normalise.
+__global__ void __launch_bounds__(256) attend_combine(const AttendArgs a) {
+  __shared__ float s_acc[4][128];
+  __shared__ float s_out[4][128];
+  __shared__ float s_sc[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.q_heads) return;  // wave-uniform; no block barrier in this kernel
+  const int64_t r = w / a.q_heads, m = w % a.q_heads;
+  const int64_t h = m / (a.q_heads / a.heads);
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  const float* pb = a.part + w * (int64_t)a.n_chunks * kAttendPart;
+  float M = -INFINITY;
+  for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, pb[c * kAttendPart + 128]);
+  float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const float mc = pb[c * kAttendPart + 128];
+    const float f = (mc == -INFINITY) ? 0.0f : __expf(mc - M);
+    L = __builtin_fmaf(f, pb[c * kAttendPart + 129], L);
+    a0 = __builtin_fmaf(f, pb[c * kAttendPart + lane], a0);
+    a1 = __builtin_fmaf(f, pb[c * kAttendPart + lane + 64], a1);
+  }
+  // back from the rotated domain: z = M acc, then out[perm[j]] = z[j]
+  float* sa = s_acc[wave];
+  float* so = s_out[wave];
+  sa[lane] = a0;
+  sa[lane + 64] = a1;
+  wave_lds_sync();
+  float z0 = 0.0f, z1 = 0.0f;
+  for (int k = 0; k < 128; ++k) {
+    const float v = sa[k];
+    z0 = __builtin_fmaf(hsign((uint32_t)lane, (uint32_t)k), v, z0);
+    z1 = __builtin_fmaf(hsign((uint32_t)lane + 64u, (uint32_t)k), v, z1);
+  }
+  so[a.use_perm_v ? a.perm_v[lane] : lane] = z0 * kInvSqrt128;
+  so[a.use_perm_v ? a.perm_v[lane + 64] : lane + 64] = z1 * kInvSqrt128;
+  wave_lds_sync();
+  const float y0 = so[lane], y1 = so[lane + 64];
+  // sink slots: raw query against the fp16 keys, fp16 values, unrotated
+  const int nsk = (int)min((int64_t)a.n_sink, len);
+  const float* qr = a.q + w * 128;
+  const float q0 = qr[lane], q1 = qr[lane + 64];
+  float Mp = M;
+  for (int t = 0; t < nsk; ++t) {
+    const uint16_t* kk = a.k_sink + ((r * a.n_sink + t) * a.heads + h) * 128;
+    float d = __builtin_fmaf(q0, f16_value(kk[lane]), q1 * f16_value(kk[lane + 64]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) d += __shfl_xor(d, o);
+    const float st = d * a.scale;
+    if (lane == 0) s_sc[wave][t] = st;
+    Mp = fmaxf(Mp, st);
+  }
+  wave_lds_sync();
+  const float f = (M == -INFINITY) ? 0.0f : __expf(M - Mp);
+  float n0 = f * y0, n1 = f * y1, den = f * L;
+  for (int t = 0; t < nsk; ++t) {
+    const float e = __expf(s_sc[wave][t] - Mp);
+    const uint16_t* vv = a.v_sink + ((r * a.n_sink + t) * a.heads + h) * 128;
+    n0 = __builtin_fmaf(e, f16_value(vv[lane]), n0);
+    n1 = __builtin_fmaf(e, f16_value(vv[lane + 64]), n1);
+    den += e;
+  }
+  float* out = a.out + w * 128;
+  out[lane] = den > 0.0f ? n0 / den : 0.0f;
+  out[lane + 64] = den > 0.0f ? n1 / den : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
 // launch dispatch
 // ---------------------------------------------------------------------------
 // Grid of a launch: one wave per task (len rows of one tile, or len tiles of one row).
@@ -1629,6 +1893,34 @@ KVQ_DEFINE_LAUNCH(launch_decode_f32_d128, 10, false, DT_F32, 128)
 #endif
 #if KVQ_UNIT == 11 || KVQ_UNIT == -1
 KVQ_DEFINE_LAUNCH(launch_decode_f32_d256, 11, false, DT_F32, 256)
+#endif
+#if KVQ_UNIT == 12 || KVQ_UNIT == -1
+namespace {
+template <int BITS, int QG>
+int launch_attend_t(const AttendArgs& a, hipStream_t s) {
+  const int64_t nq = a.rows * a.q_heads;
+  const int64_t np = a.rows * a.heads * a.n_chunks;
+  if (nq == 0) return 0;
+  if ((np + 3) / 4 > 0x7fffffff || (nq + 3) / 4 > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(attend_rotate_q, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  hipLaunchKernelGGL((attend_partial<BITS, QG>), dim3((unsigned)((np + 3) / 4)), dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  hipLaunchKernelGGL(attend_combine, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+}  // namespace
+int launch_attend(int bits, int qg, const AttendArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (bits == 2) {
+    if (qg == 1) return launch_attend_t<2, 1>(a, s);
+    if (qg == 2) return launch_attend_t<2, 2>(a, s);
+    return launch_attend_t<2, 4>(a, s);
+  }
+  if (qg == 1) return launch_attend_t<4, 1>(a, s);
+  if (qg == 2) return launch_attend_t<4, 2>(a, s);
+  return launch_attend_t<4, 4>(a, s);
+}
 #endif
 
 }  // namespace kvq

@@ -506,4 +506,111 @@ def check_append_matches_batch_encode():
                     assert not np.any(other), n
 
 
+# --------------------------------------------------------------------------- #
+# decode-step attention over the encoded cache
+# --------------------------------------------------------------------------- #
+def check_attention_closed_forms():
+    """One slot returns its value; identical keys (or scale 0) give the mean of the values;
+    two slots weigh as a logistic of their score difference; query head m reads KV head
+    m // group; slots at or past a row's length do not matter."""
+    from oracle import attention
+    rng = _rng(17)
+    r, t, h, d, hq = 2, 6, 2, 8, 4
+    k = rng.standard_normal((r, t, h, d))
+    v = rng.standard_normal((r, t, h, d))
+    q = rng.standard_normal((r, hq, d))
+    one = attention.attend_decoded(q, k, v, np.array([1, 1]), 0.7)
+    for m in range(hq):
+        assert np.allclose(one[:, m], v[:, 0, m // 2], atol=1e-15)
+    same = np.repeat(k[:, :1], t, axis=1)
+    out = attention.attend_decoded(q, same, v, None, 0.7)
+    assert np.allclose(out[:, 1], v[:, :, 0].mean(axis=1), atol=1e-13)
+    assert np.allclose(out[:, 3], v[:, :, 1].mean(axis=1), atol=1e-13)
+    assert np.allclose(attention.attend_decoded(q, k, v, None, 0.0)[:, 2], v[:, :, 1].mean(axis=1), atol=1e-13)
+    # two slots: weights 1 / (1 + e^(s0 - s1)) on the second
+    k2 = np.zeros((1, 2, 1, d))
+    k2[0, 0, 0, 0], k2[0, 1, 0, 0] = 0.5, 2.0
+    q2 = np.zeros((1, 1, d))
+    q2[0, 0, 0] = 1.5
+    v2 = rng.standard_normal((1, 2, 1, d))
+    w1 = 1.0 / (1.0 + np.exp(0.3 * 1.5 * (0.5 - 2.0)))
+    out2 = attention.attend_decoded(q2, k2, v2, None, 0.3)
+    assert np.allclose(out2[0, 0], (1 - w1) * v2[0, 0, 0] + w1 * v2[0, 1, 0], atol=1e-14)
+    # slots past the length are ignored; length 0 gives zeros
+    lens = np.array([3, 0])
+    a = attention.attend_decoded(q, k, v, lens, 0.7)
+    k3, v3 = k.copy(), v.copy()
+    k3[:, 3:] += 5.0
+    v3[:, 3:] -= 7.0
+    assert np.array_equal(a, attention.attend_decoded(q, k3, v3, lens, 0.7))
+    assert not np.any(a[1])
+
+
+def check_attention_matches_library_softmax():
+    """The oracle equals the same attention written with scipy's softmax and einsum."""
+    from scipy.special import softmax
+    from oracle import attention
+    rng = _rng(18)
+    r, t, h, d, hq = 3, 11, 2, 16, 6
+    k = rng.standard_normal((r, t, h, d)) * 3
+    v = rng.standard_normal((r, t, h, d))
+    q = rng.standard_normal((r, hq, d))
+    kq = np.repeat(k, hq // h, axis=2)  # [r, t, hq, d]
+    vq = np.repeat(v, hq // h, axis=2)
+    w = softmax(0.25 * np.einsum("rmd,rtmd->rmt", q, kq), axis=-1)
+    ref = np.einsum("rmt,rtmd->rmd", w, vq)
+    assert np.allclose(attention.attend_decoded(q, k, v, None, 0.25), ref, atol=1e-12)
+
+
+def check_attention_rotated_domain():
+    """Attention over the encoded planes equals the rotated-domain evaluation: scores from
+    the rotated query and the stored codes, scale and zero (q.k = (M P q).y with the
+    orthonormal Hadamard M), values summed in the rotated domain and rotated back once,
+    sink slots taken unrotated from the fp16 plane.  M comes from scipy's hadamard."""
+    from scipy.linalg import hadamard
+    from oracle import attention
+    rng = _rng(19)
+    r, t, h, d, hq, g, n_sink = 2, 9, 2, 128, 4, 64, 2
+    x_k = rng.standard_normal((r, t, h, d))
+    x_v = rng.standard_normal((r, t, h, d))
+    perm = rng.permutation(d)
+    pk = codec.CodecParams(bits=2, group_size=g, rope=True, perm=perm, n_sink=n_sink)
+    pv = codec.CodecParams(bits=2, group_size=g, n_sink=n_sink)
+    ek = codec.encode(x_k, pk)
+    ev = codec.encode(x_v, pv)
+    q = rng.standard_normal((r, hq, d))
+    lens = np.array([t, 5])
+    scale = d ** -0.5
+    got = attention.attend(q, ek, pk, ev, pv, (r, t, h, d), lens, scale)
+    mh = hadamard(d) / np.sqrt(d)
+    qk = pack.unpack(ek["codes"], 2, d).astype(np.float64)
+    qv = pack.unpack(ev["codes"], 2, d).astype(np.float64)
+    ref = np.zeros((r, hq, d))
+    for i in range(r):
+        for m in range(hq):
+            kv = m // (hq // h)
+            qt = mh @ q[i, m][perm]  # rotated query
+            s = np.empty(lens[i])
+            for tt in range(lens[i]):
+                if tt < n_sink:
+                    s[tt] = q[i, m] @ ek["sink"][i, tt, kv].astype(np.float64)
+                else:
+                    sc = np.repeat(ek["scale"][i, tt, kv].astype(np.float64), g)
+                    ze = np.repeat(ek["zero"][i, tt, kv].astype(np.float64), g)
+                    s[tt] = qt @ (ze + qk[i, tt, kv] * sc)
+            w = np.exp(scale * s - np.max(scale * s))
+            w /= w.sum()
+            acc = np.zeros(d)
+            out = np.zeros(d)
+            for tt in range(lens[i]):
+                if tt < n_sink:
+                    out += w[tt] * ev["sink"][i, tt, kv].astype(np.float64)
+                else:
+                    sc = np.repeat(ev["scale"][i, tt, kv].astype(np.float64), g)
+                    ze = np.repeat(ev["zero"][i, tt, kv].astype(np.float64), g)
+                    acc += w[tt] * (ze + qv[i, tt, kv] * sc)
+            ref[i, m] = out + mh @ acc  # the V cache has no permutation
+    assert np.allclose(got, ref, atol=1e-11)
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

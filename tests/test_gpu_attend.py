@@ -1,0 +1,120 @@
+"""Decode-step attention over the encoded cache on the GPU vs the CPU oracle.
+
+Both sides read the same GPU-encoded planes; the oracle decodes them in float64 and
+applies plain softmax attention, while the GPU never decodes a key (rotated-domain
+scores) and sums the values in the rotated domain.  Tolerance: 1e-4 of the largest
+decoded value a row attends over (fp32 scores and sums over up to 32768 slots).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import gpu_util as gu
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import rotate_then_bit_amd as kvq  # noqa: E402  (fails loudly if libkvq.so is missing)
+
+ATT_REL = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _compare(out_gpu, ref, vmax, label):
+    err = np.abs(out_gpu.astype(np.float64) - ref)
+    tol = ATT_REL * vmax[:, None, None] + 1e-6
+    bad = err > tol
+    assert not bad.any(), (f"{label}: attention differs by up to {err.max():.3g} "
+                           f"(tolerance {tol.min():.3g}; {int(bad.sum())} elements)")
+    return float(err.max())
+
+
+def _case(r, t, h, bits, g, rope, use_perm, n_sink, name):
+    return workloads.TensorCase(name=name, shape=(r, t, h, 128), dtype="bf16", bits=bits, group_size=g,
+                                quant="minmax", rot="fwht", rope=rope, n_sink=n_sink, use_perm=use_perm)
+
+
+@pytest.mark.parametrize("qg,bits,g,n_sink,perm_v", [
+    (4, 2, 128, 4, False),   # Llama-3 shape of K and V, reduced
+    (1, 2, 64, 0, True),
+    (2, 4, 32, 3, False),
+    (4, 4, 64, 0, True),
+    (2, 2, 32, 4, True),
+])
+def test_attend_small(qg, bits, g, n_sink, perm_v):
+    r, t, h = 5, 203, 3
+    seed = 500 + 10 * qg + bits + g + n_sink + (7 if perm_v else 0)
+    ck = _case(r, t, h, bits, g, True, True, n_sink, "K")
+    cv = _case(r, t, h, bits, g, False, perm_v, n_sink, "V")
+    dk = workloads.synth_case(ck, seed)
+    dv = workloads.synth_case(cv, seed + 1)
+    cfg_k = gu.make_config(ck, dk["perm"])
+    cfg_v = gu.make_config(cv, dv["perm"])
+    say(f"[case] attend qg={qg} bits={bits} G={g} sinks={n_sink} perm_v={perm_v} cache={ck.shape}")
+    pk_t = kvq.encode(gu.torch_input(dk["input"], "bf16"), cfg_k)
+    pv_t = kvq.encode(gu.torch_input(dv["input"], "bf16"), cfg_v)
+    rng = np.random.default_rng(seed + 2)
+    q = rng.standard_normal((r, h * qg, 128)).astype(np.float32)
+    lengths = np.array([t, 1, 0, min(n_sink, 2), 117], dtype=np.int32)
+    out = kvq.attend(torch.from_numpy(q).cuda(), pk_t, cfg_k, pv_t, cfg_v,
+                     lengths=torch.from_numpy(lengths).cuda())
+    torch.cuda.synchronize()
+    gk, gv = gu.planes_numpy(pk_t), gu.planes_numpy(pv_t)
+    pk = parity.params_for(ck, dk["perm"])
+    pv = parity.params_for(cv, dv["perm"])
+    kdec = oracle.decode(gk, pk, ck.shape)
+    vdec = oracle.decode(gv, pv, cv.shape)
+    ref = oracle.attend_decoded(q.astype(np.float64), kdec, vdec, lengths, 128 ** -0.5)
+    vmax = np.array([np.abs(vdec[i, :max(int(lengths[i]), 1)]).max() for i in range(r)])
+    e = _compare(out.cpu().numpy(), ref, vmax, f"attend qg={qg} b={bits} G={g}")
+    assert not out.cpu().numpy()[2].any()  # length 0: zeros
+    say(f"  max |err| {e:.3g}")
+
+
+def test_attend_llama3_cache_full_size():
+    """The Llama-3 cache shape (128 rows x 32768 slots x 8 KV heads, 32 query heads): every
+    row attended at its own length on the GPU, sampled rows checked against the oracle."""
+    base = workloads.WORKLOADS["llama3"]
+    data = workloads.device_workload("llama3", device=torch.device("cuda:0"))
+    torch.cuda.synchronize()
+    cases = {c.name: c for c in base.cases}
+    cfgs = {n: kvq.Config(shape=c.shape, dtype=c.dtype, bits=c.bits, group_size=c.group_size, rope=c.rope,
+                          rope_base=c.rope_base, n_sink=c.n_sink, perm=data["perm"] if c.use_perm else None)
+            for n, c in cases.items()}
+    planes = {n: kvq.encode(data["inputs"][n], cfgs[n]) for n in cases}
+    del data["inputs"]
+    r, t, h, d = cases["K"].shape
+    rng = np.random.default_rng(91)
+    q = rng.standard_normal((r, 4 * h, d)).astype(np.float32)
+    lengths = rng.integers(1, t + 1, size=r).astype(np.int32)
+    lengths[:3] = [t, 5, 4000]
+    say(f"[case] attend llama3 full size: {r} rows x {t} slots x {h} KV heads, {4 * h} query heads")
+    out = kvq.attend(torch.from_numpy(q).cuda(), planes["K"], cfgs["K"], planes["V"], cfgs["V"],
+                     lengths=torch.from_numpy(lengths).cuda())
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    pk = parity.params_for(cases["K"], data["perm"])
+    pv = parity.params_for(cases["V"], data["perm"])
+    for row in (0, 1, 2, 77):
+        one = lambda n: {k: gu.planes_numpy({k: v[row:row + 1]})[k] for k, v in planes[n].items()}
+        shape1 = (1, t, h, d)
+        kdec = oracle.decode(one("K"), pk, shape1)
+        vdec = oracle.decode(one("V"), pv, shape1)
+        ln = lengths[row:row + 1]
+        ref = oracle.attend_decoded(q[row:row + 1].astype(np.float64), kdec, vdec, ln, d ** -0.5)
+        vmax = np.array([np.abs(vdec[0, :int(ln[0])]).max()])
+        e = _compare(out[row:row + 1], ref, vmax, f"llama3 row {row} len {int(ln[0])}")
+        say(f"  row {row} len {int(ln[0])}: max |err| {e:.3g}")

@@ -141,6 +141,21 @@ def _append_slot_is_position(cache, x, positions, p):
     return _orig_append(cache, x, positions, codec.CodecParams(**{**p.__dict__, "pos_offset": 0}))
 
 
+from oracle import attention as _attention
+
+_orig_attend_decoded = _attention.attend_decoded
+
+
+def _attend_heads_interleaved(q, k, v, lengths, scale):
+    # query head m reading KV head m % heads instead of m // group
+    hq, h = q.shape[1], k.shape[2]
+    order = np.array([(m % h) * (hq // h) + m // h for m in range(hq)])
+    out = _orig_attend_decoded(q[:, order], k, v, lengths, scale)
+    res = np.empty_like(out)
+    res[:, order] = out
+    return res
+
+
 MUTATIONS = {
     "rope_negative_sine": (rope, "rope", _rope_neg_sine),
     "rope_half_split_pairs": (rope, "rope", _rope_half_split),
@@ -158,6 +173,7 @@ MUTATIONS = {
     "decode_perm_gather": (codec, "decode", _decode_gather_not_scatter),
     "decode_rho_plus_eps": (codec, "decode", _decode_rho_plus_eps),
     "append_slot_is_position": (codec, "append", _append_slot_is_position),
+    "attention_heads_interleaved": (_attention, "attend_decoded", _attend_heads_interleaved),
 }
 
 
