@@ -1501,8 +1501,13 @@ struct AttSlot {
 // (lane / 8, lane % 8) holds channels 16 l .. 16 l + 15 of the token slot tk of each step of
 // 8 slots; the 8 lanes of a slot reduce its scores, and each slot keeps its own running
 // maximum, denominator and rotated-domain sums until the wave merges them at the end.
+#ifndef KVQ_ATT_LDSQ
+#define KVQ_ATT_LDSQ 1
+#endif
 template <int BITS, int QG>
 __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
+  // the rotated query slices live in LDS (read every step) instead of 16 * QG registers
+  __shared__ __attribute__((aligned(16))) float s_qv[KVQ_ATT_LDSQ ? 4 : 1][KVQ_ATT_LDSQ ? QG * 128 : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
@@ -1520,7 +1525,25 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
   constexpr int CB = 128 * BITS / 8;       // code bytes per vector
   constexpr int LB = 2 * BITS;             // code bytes per lane (16 codes)
 
-  float qv[QG][16], sl[QG];
+  float sl[QG];
+#if KVQ_ATT_LDSQ
+  {
+    const float* src = a.qrot + (r * a.q_heads + h * QG) * 128;
+    for (int i = lane; i < QG * 128; i += 64) s_qv[wave][i] = src[i];
+    wave_lds_sync();
+  }
+  const uint32_t qaddr = lds_addr(&s_qv[wave][16 * l]);
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    sl[m] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4_t v = lds_ld4(qaddr + 512u * m + 16u * k);
+      sl[m] += (__uint_as_float(v.x) + __uint_as_float(v.y)) + (__uint_as_float(v.z) + __uint_as_float(v.w));
+    }
+  }
+#else
+  float qv[QG][16];
 #pragma unroll
   for (int m = 0; m < QG; ++m) {
     const float* src = a.qrot + ((r * a.q_heads + h * QG + m) * 128 + 16 * l);
@@ -1531,6 +1554,7 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
       sl[m] += qv[m][i];
     }
   }
+#endif
   float mx[QG], ls[QG], zs[QG], acc[QG][16];
 #pragma unroll
   for (int m = 0; m < QG; ++m) {
@@ -1558,12 +1582,21 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
     s.vs = a.v_scale[vec * ngroups + g];
     s.vz = a.v_zero[vec * ngroups + g];
   };
+  // codes to floats: spread each word's codes over bytes, then one byte-to-float conversion
+  // per code (v_cvt_f32_ubyteN)
   auto unpack = [&](const uint32_t* wd, float* code) __attribute__((always_inline)) {
+    constexpr int PER = 32 / BITS;         // codes per word
+    constexpr int SPR = 8 / BITS;          // byte-spread words per word
+    constexpr uint32_t BM = (BITS == 2) ? 0x03030303u : 0x0F0F0F0Fu;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      constexpr int PER = 32 / BITS;
-      code[i] = (float)((wd[i / PER] >> (BITS * (i % PER))) & ((1u << BITS) - 1u));
-    }
+    for (int j = 0; j < BITS / 2; ++j)
+#pragma unroll
+      for (int k = 0; k < SPR; ++k) {
+        uint32_t e = (wd[j] >> (BITS * k)) & BM;  // byte b holds code SPR * b + k of word j
+        asm volatile("" : "+v"(e));                // (kept whole, so each byte converts directly)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) code[PER * j + SPR * b + k] = (float)((e >> (8 * b)) & 0xffu);
+      }
   };
 
   if (t_begin < t_end) {
@@ -1576,11 +1609,26 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
       unpack(cur.kw, code);
       const float ks = f16_value(cur.ks), kz = f16_value(cur.kz);
       float s[QG];
+#if KVQ_ATT_LDSQ
+      uint32_t qa = qaddr;
+      asm volatile("" : "+v"(qa));  // read the slices here, each step (not hoisted into registers)
+#endif
 #pragma unroll
       for (int m = 0; m < QG; ++m) {
         float d = 0.0f;
+#if KVQ_ATT_LDSQ
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4_t v = lds_ld4(qa + 512u * m + 16u * k);
+          d = __builtin_fmaf(__uint_as_float(v.x), code[4 * k + 0], d);
+          d = __builtin_fmaf(__uint_as_float(v.y), code[4 * k + 1], d);
+          d = __builtin_fmaf(__uint_as_float(v.z), code[4 * k + 2], d);
+          d = __builtin_fmaf(__uint_as_float(v.w), code[4 * k + 3], d);
+        }
+#else
 #pragma unroll
         for (int i = 0; i < 16; ++i) d = __builtin_fmaf(qv[m][i], code[i], d);
+#endif
         float part = __builtin_fmaf(ks, d, kz * sl[m]);  // q~ . (zero + code * scale) over 16 channels
         part = add_x1(part);
         part = add_x2(part);
