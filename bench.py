@@ -262,6 +262,31 @@ def main():
     append_us = a.elapsed_time(b) * 1e3 / n_rep
     append_vec = sum(int(x_new[n].shape[0] * x_new[n].shape[1]) for n in cases)
 
+    # context, outside the timed region: one decode step of attention over the whole encoded
+    # cache (every row at full length; Llama-3-8B's 32 query heads over its 8 KV heads), scored
+    # and summed in the rotated domain without decoding a key
+    r0, t0_, h0, d0 = cases["K"].shape
+    q_heads = 4 * h0
+    qa = torch.randn((r0, q_heads, d0), generator=gen, device=dev, dtype=torch.float32)
+    oa = torch.empty_like(qa)
+    wsa = torch.empty(kvq.attend_workspace_size(cfgs["K"], q_heads), dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            kvq.attend(qa, planes["K"], cfgs["K"], planes["V"], cfgs["V"], out=oa, workspace=wsa, stream=stream)
+        stream.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        n_rep = 10
+        a.record(stream)
+        for _ in range(n_rep):
+            kvq.attend(qa, planes["K"], cfgs["K"], planes["V"], cfgs["V"], out=oa, workspace=wsa, stream=stream)
+        b.record(stream)
+        stream.synchronize()
+    attend_ms = a.elapsed_time(b) / n_rep
+    attend_bytes = pl_bytes["K"] + pl_bytes["V"]  # the encoded cache, read once
+    bf16_bytes = in_bytes["K"] + in_bytes["V"]  # what the same attention reads from a bf16 cache
+    attend_fma = r0 * t0_ * h0 * (q_heads // h0) * d0 * 2  # score and value multiply-adds
+
     cpu = None
     if not args.no_cpu_baseline:
         nv, tc, nrows = cpu_baseline(data["inputs"], wl.cases, perm, args.cpu_seconds, 16)
@@ -294,6 +319,15 @@ def main():
         "compression_ratio": round(in_bytes["K"] / (pl_bytes["K"] - sink_bytes["K"]), 3),
         "kernels": kern,
         "copy_GBps_same_bytes": round(copy_gbps, 1),
+        "attend": {"ms_per_step": round(attend_ms, 4), "rows": r0, "slots": t0_, "kv_heads": h0, "q_heads": q_heads,
+                   "encoded_cache_bytes": attend_bytes,
+                   "GBps": round(attend_bytes / (attend_ms * 1e-3) / 1e9, 1),
+                   "bf16_cache_bytes": bf16_bytes,
+                   "bf16_cache_read_at_hbm_peak_ms": round(bf16_bytes / (HBM_PEAK_GBPS * 1e9) * 1e3, 4),
+                   "valu_fma": attend_fma,
+                   "valu_frac": round(attend_fma / (attend_ms * 1e-3) / (VALU_PEAK_TOPS * 1e12), 4),
+                   "what": "decode-step attention over the encoded K/V cache in the rotated domain "
+                           "(kvq_attend), VALU-bound"},
         "append": {"us_per_step": round(append_us, 2), "vectors_per_step": append_vec,
                    "what": "decode-step cache update: K and V of every row appended at per-row positions "
                            "(kvq_append, K with RoPE + perm), launch-latency bound"},
