@@ -172,3 +172,68 @@ def test_single_hip_runtime_when_binding_imported_first():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+# --------------------------------------------------------------------------- #
+# append and attention: host-side refusals (nothing reaches the device)
+# --------------------------------------------------------------------------- #
+def _lib_new_entry_points():
+    lib = ctypes.CDLL(kvq.library_path())
+    lib.kvq_append.argtypes = [ctypes.c_void_p] * 5
+    lib.kvq_attend.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_size_t, ctypes.c_void_p]
+    lib.kvq_attend_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    return lib
+
+
+def _planes(codes=4096, scale=8192, zero=12288, sink=None):
+    p = kvq._Planes()
+    p.codes, p.scale, p.zero, p.sink = codes, scale, zero, sink
+    return p
+
+
+def test_append_refuses_bad_arguments_on_the_host():
+    lib = _lib_new_entry_points()
+    c = _cfg().c_struct()
+    pl = _planes()
+    assert lib.kvq_append(ctypes.byref(c), 4096, None, ctypes.byref(pl), None) == 1    # positions NULL
+    assert lib.kvq_append(ctypes.byref(c), None, 4096, ctypes.byref(pl), None) == 1    # x NULL
+    assert lib.kvq_append(ctypes.byref(c), 4100, 4096, ctypes.byref(pl), None) == 7    # x misaligned
+    assert lib.kvq_append(ctypes.byref(c), 4096, 4100, ctypes.byref(pl), None) == 7    # positions misaligned
+    assert lib.kvq_append(ctypes.byref(c), 4096, 4096, None, None) == 1                # planes NULL
+    cs = _cfg(n_sink=4).c_struct()
+    assert lib.kvq_append(ctypes.byref(cs), 4096, 4096, ctypes.byref(pl), None) == 1   # sink plane NULL
+    cb = _cfg(bits=7).c_struct()
+    assert lib.kvq_append(ctypes.byref(cb), 4096, 4096, ctypes.byref(pl), None) == 3
+
+
+def test_attend_workspace_size_and_refusals_on_the_host():
+    lib = _lib_new_entry_points()
+    c = _cfg(shape=(2, 100, 4, 128)).c_struct()
+    n = ctypes.c_size_t()
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), 16, ctypes.byref(n)) == 0
+    assert n.value >= 2 * 16 * 128 * 4 + 2 * 16 * 130 * 4
+    assert kvq.attend_workspace_size(kvq.Config(shape=(2, 100, 4, 128), dtype="bf16", bits=2, group_size=128), 16) == n.value
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), 6, ctypes.byref(n)) == 2     # not a multiple of heads
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), 32, ctypes.byref(n)) == 8    # 8 query heads per KV head
+    for kw, status in ((dict(rot="none"), 8), (dict(bits=3), 8), (dict(group_size=32, shape=(1, 4, 2, 256)), 8),
+                       (dict(quant="lloyd", codebook=np.linspace(-1, 1, 4).astype(np.float32)), 8),
+                       (dict(pos_offset=3), 8), (dict(n_sink=65), 8)):
+        ck = _cfg(**kw).c_struct()
+        assert lib.kvq_attend_workspace_size(ctypes.byref(ck), 8, ctypes.byref(n)) == status, kw
+    ck, cv = _cfg().c_struct(), _cfg(bits=4).c_struct()
+    pk, pv = _planes(), _planes()
+    ws = 1 << 20
+    # the K and V caches must agree
+    assert lib.kvq_attend(ctypes.byref(ck), ctypes.byref(pk), ctypes.byref(cv), ctypes.byref(pv), 4096, 8, None,
+                          0.1, 4096, 4096, ws, None) == 2
+    cv = _cfg().c_struct()
+    args = lambda q=4096, out=4096, wsp=4096, wsz=ws, sc=0.1: (ctypes.byref(ck), ctypes.byref(pk), ctypes.byref(cv),
+                                                               ctypes.byref(pv), q, 8, None, sc, out, wsp, wsz, None)
+    assert lib.kvq_attend(*args(q=None)) == 1
+    assert lib.kvq_attend(*args(q=4100)) == 7
+    assert lib.kvq_attend(*args(wsz=16)) == 2        # workspace too small
+    assert lib.kvq_attend(*args(sc=float("nan"))) == 6
+    assert lib.kvq_attend(ctypes.byref(ck), ctypes.byref(pk), None, ctypes.byref(pv), 4096, 8, None, 0.1, 4096,
+                          4096, ws, None) == 1        # cfg_v NULL

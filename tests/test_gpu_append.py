@@ -149,3 +149,25 @@ def test_append_rejects_bad_arguments():
         kvq.append(x, torch.zeros(3, dtype=torch.int64, device="cuda"), cache, cfg)
     with pytest.raises(kvq.KvqError):
         kvq.append(x[:, :, 1:], torch.zeros(2, dtype=torch.int64, device="cuda"), cache, cfg)  # misaligned x
+
+
+def test_append_strided_input():
+    """x given as a view with its own row and head strides (every other token of a wider tensor)."""
+    r, slots, h, d = 6, 9, 3, 128
+    case = workloads.TensorCase(name="K", shape=(r, slots, h, d), dtype="bf16", bits=2, group_size=128,
+                                quant="minmax", rot="fwht", rope=True, n_sink=2, use_perm=True)
+    data = workloads.synth_case(case.with_shape((r, 2, h, d)), 404)
+    wide = gu.torch_input(data["input"], "bf16")          # [r, 2, h, d] contiguous
+    x_view = wide[:, 1]                                    # row stride 2*h*d, head stride d
+    cfg = gu.make_config(case, data["perm"], strides=(2 * h * d, 0, d))
+    cache = _filled_planes(cfg)
+    pos = torch.tensor([0, 1, 2, 8, 9, 4], dtype=torch.int64, device="cuda")
+    kvq.append(x_view, pos, cache, cfg)
+    # the same rows appended from a contiguous copy
+    cfg_c = gu.make_config(case, data["perm"])
+    cache_c = _filled_planes(cfg_c)
+    kvq.append(x_view.contiguous(), pos, cache_c, cfg_c)
+    torch.cuda.synchronize()
+    for n in cache:
+        assert torch.equal(cache[n].view(torch.uint8), cache_c[n].view(torch.uint8)), n
+    _check_append(case, data["input"][:, 1], pos.cpu().numpy(), data["perm"], label="strided")

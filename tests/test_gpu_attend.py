@@ -118,3 +118,34 @@ def test_attend_llama3_cache_full_size():
         vmax = np.array([np.abs(vdec[0, :int(ln[0])]).max()])
         e = _compare(out[row:row + 1], ref, vmax, f"llama3 row {row} len {int(ln[0])}")
         say(f"  row {row} len {int(ln[0])}: max |err| {e:.3g}")
+
+
+@pytest.mark.parametrize("t,h,qg,n_sink,lengths", [
+    (5, 1, 1, 0, [7, -3, 5, 2]),      # fewer slots than one step; lengths past the cache and negative
+    (5, 2, 2, 6, [5, 3, 0, 9]),       # every slot a sink
+    (9, 1, 4, 1, [9, 8, 1, 2]),       # one step plus one slot
+])
+def test_attend_edge_shapes(t, h, qg, n_sink, lengths):
+    r = len(lengths)
+    seed = 900 + 13 * t + h + qg + n_sink
+    ck = _case(r, t, h, 2, 128, True, True, n_sink, "K")
+    cv = _case(r, t, h, 2, 128, False, False, n_sink, "V")
+    dk = workloads.synth_case(ck, seed)
+    dv = workloads.synth_case(cv, seed + 1)
+    cfg_k, cfg_v = gu.make_config(ck, dk["perm"]), gu.make_config(cv, None)
+    say(f"[case] attend edge T={t} H={h} qg={qg} sinks={n_sink} lengths={lengths}")
+    pk_t = kvq.encode(gu.torch_input(dk["input"], "bf16"), cfg_k)
+    pv_t = kvq.encode(gu.torch_input(dv["input"], "bf16"), cfg_v)
+    q = np.random.default_rng(seed + 2).standard_normal((r, h * qg, 128)).astype(np.float32)
+    ln = np.array(lengths, dtype=np.int32)
+    out = kvq.attend(torch.from_numpy(q).cuda(), pk_t, cfg_k, pv_t, cfg_v, lengths=torch.from_numpy(ln).cuda(),
+                     scale=0.2)
+    torch.cuda.synchronize()
+    kdec = oracle.decode(gu.planes_numpy(pk_t), parity.params_for(ck, dk["perm"]), ck.shape)
+    vdec = oracle.decode(gu.planes_numpy(pv_t), parity.params_for(cv, None), cv.shape)
+    ref = oracle.attend_decoded(q.astype(np.float64), kdec, vdec, ln, 0.2)
+    vmax = np.array([np.abs(vdec[i]).max() for i in range(r)])
+    _compare(out.cpu().numpy(), ref, vmax, f"attend edge T={t}")
+    for i, n in enumerate(lengths):
+        if n <= 0:
+            assert not out.cpu().numpy()[i].any()
