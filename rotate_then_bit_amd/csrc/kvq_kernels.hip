@@ -1501,6 +1501,9 @@ struct AttSlot {
 // (lane / 8, lane % 8) holds channels 16 l .. 16 l + 15 of the token slot tk of each step of
 // 8 slots; the 8 lanes of a slot reduce its scores, and each slot keeps its own running
 // maximum, denominator and rotated-domain sums until the wave merges them at the end.
+#ifndef KVQ_ATT_MMA
+#define KVQ_ATT_MMA 1
+#endif
 #ifndef KVQ_ATT_LDSQ
 #define KVQ_ATT_LDSQ 1
 #endif
@@ -1692,6 +1695,281 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
     if (lane == 0) {
       pb[128] = M;
       pb[129] = L;
+    }
+  }
+}
+
+// Partial attention on the int8 matrix cores, for 2-bit codes with one group of 128 channels
+// (scale and zero per vector).  Every product is exact integer arithmetic:
+//  * keys: a code byte is spread into the bytes of four words by masks, so byte e holds
+//    code(e) * mul(e) with mul in {1, 4, 16, 16}; the rotated query of each head is scaled by
+//    a power of two, divided by mul and rounded to a 31-bit integer, cut into four signed
+//    8-bit digits (rows 4 m + s of the A operand), so one 16x16x64 product per 64 channels
+//    gives per digit the integer dot product of 16 slots, recombined in fp32;
+//  * values: the softmax weights p * scale_v of a window, relative to the window's exact
+//    maximum (a first pass scores the window into LDS), are scaled by a power of two to at
+//    most 2^27 and cut into four 7-bit digits (columns 4 m + s of the B operand); the value
+//    codes of 64 slots, transposed through 16-bit loads and byte permutes, are the A
+//    operand.  The integer sums are turned into floats when the running maximum or the
+//    weight scale changes, and at the end of the chunk.
+// Lanes: n16 = lane % 16 and g = lane / 16 as in the operand layouts; in the key product
+// lane (n16, g) holds slot n16 of a 16-slot block for head g; in the value product lane
+// (4 m + s, g) holds digit s of head m for channels 32 g + 8 j + b (register j, product b).
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMmaW = 128;   // slots per window
+constexpr int kMmaPad = 16;  // padding of the LDS score rows (banks of the row writes)
+template <int K>
+__device__ __forceinline__ uint32_t code_bytes(uint32_t x) {  // code 4 b + K of byte b, times code_mul(K)
+  if constexpr (K < 3) return x & (0x03030303u << (2 * K));
+  else return (x >> 2) & 0x30303030u;
+}
+__host__ __device__ constexpr int code_mul(int k) { return k == 0 ? 1 : (k == 1 ? 4 : 16); }
+
+template <int QG>
+__global__ void __launch_bounds__(512) attend_partial_mma(const AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) float s_sc[8][4][kMmaW];             // k scale, k zero, v scale, v zero
+  __shared__ __attribute__((aligned(16))) float s_s[8][4][kMmaW + kMmaPad];    // scores (log2 units) per head
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 8 + wave;
+  if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier in this kernel
+  const int64_t h = w % a.heads, rc = w / a.heads, c = rc % a.n_chunks, r = rc / a.n_chunks;
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.n_sink);
+  const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
+  const int n16 = lane & 15, g = lane >> 4;
+  const int qm = n16 >> 2, qs = n16 & 3;  // head and digit of the lane's column in the value product
+  float* const sc = &s_sc[wave][0][0];
+  float* const ss = &s_s[wave][0][0];
+  constexpr int SR = kMmaW + kMmaPad;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  // per-head max |q~| and sum q~ of the rotated queries
+  const float* qb = a.qrot + (r * a.q_heads + h * QG) * 128;
+  float qmx[4], qsum[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float v0 = m < QG ? qb[m * 128 + lane] : 0.0f, v1 = m < QG ? qb[m * 128 + lane + 64] : 0.0f;
+    qmx[m] = fmaxf(fabsf(v0), fabsf(v1));
+    qsum[m] = v0 + v1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      qmx[m] = fmaxf(qmx[m], __shfl_xor(qmx[m], o));
+      qsum[m] += __shfl_xor(qsum[m], o);
+    }
+  }
+  // query scale 2^e with 16 |q~| 2^e < 2^30
+  float qsc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    int ex;
+    (void)__builtin_frexpf(16.0f * qmx[m], &ex);
+    qsc[m] = __builtin_ldexpf(1.0f, 30 - ex);
+  }
+  // A operand of the key product: lane (4 m + s, g), product u, byte e holds digit s of the
+  // scaled query of channel 16 (2 g + u) + 4 (e % 4) + e / 4
+  i32x4_t qa[2];
+  {
+    const float sqm = qm == 0 ? qsc[0] : (qm == 1 ? qsc[1] : (qm == 2 ? qsc[2] : qsc[3]));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float qv[16];
+      const float* src = qb + qm * 128 + 16 * (2 * g + u);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qv[i] = qm < QG ? src[i] : 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int e = 4 * d + bb;  // byte e of the operand: code 4 (e % 4) + e / 4 of the word
+          const int32_t Q = (int32_t)__builtin_rintf(qv[4 * (e & 3) + (e >> 2)] * (float)(16 / code_mul(e >> 2)) * sqm);
+          // balanced base-256 digits: T = Q + 0x808080, digit s = byte s of T - 128 (s < 3), T >> 24 (s = 3)
+          const int32_t T = Q + 0x808080;
+          const uint32_t byte = ((uint32_t)(T >> (8 * qs)) & 0xffu) ^ (qs < 3 ? 0x80u : 0u);
+          word |= byte << (8 * bb);
+        }
+        qa[u][d] = (int32_t)word;
+      }
+    }
+  }
+  // key-product lane role: head g; score = (k_scale * raw * rs + k_zero * zq) in log2 units
+  const float sc2 = a.scale * kLog2e;
+  const float sqg = g == 0 ? qsc[0] : (g == 1 ? qsc[1] : (g == 2 ? qsc[2] : qsc[3]));
+  const float rs = sc2 / (16.0f * sqg);
+  const float zq = g < QG ? sc2 * (g == 0 ? qsum[0] : (g == 1 ? qsum[1] : (g == 2 ? qsum[2] : qsum[3]))) : 0.0f;
+
+  i32x4_t cv[8];
+  float fv[8][4];
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cv[b][j] = 0;
+      fv[b][j] = 0.0f;
+    }
+  float Mrun = -INFINITY;               // running maximum of head qm (log2 units)
+  float Lp = 0.0f, Zp = 0.0f;           // pending sums of p 2^E and p 2^E v_zero
+  float Lf = 0.0f, Zf = 0.0f;
+  int Ecur = 0, since = 0;
+  bool first = true;
+  auto flush = [&](float corr) __attribute__((always_inline)) {
+    const float kb = __builtin_ldexpf(1.0f, 7 * qs - Ecur);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const float k = kb * (1.0f / (float)code_mul(b & 3));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        fv[b][j] = (fv[b][j] + (float)cv[b][j] * k) * corr;
+        cv[b][j] = 0;
+      }
+    }
+    const float le = __builtin_ldexpf(1.0f, -Ecur);
+    Lf = (Lf + Lp * le) * corr;
+    Zf = (Zf + Zp * le) * corr;
+    Lp = 0.0f;
+    Zp = 0.0f;
+  };
+
+  for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += kMmaW) {
+    const int nv = (int)min((int64_t)kMmaW, t_end - wt0);  // valid slots of the window (>= 1)
+    const int nblk = 4 * ((nv + 63) >> 6);                 // 16-slot blocks scored (whole 64-slot groups)
+    // scales and zeros of the window's slots (clamped to the last valid slot)
+    float vsm = 0.0f;
+    for (int i = lane; i < 16 * nblk; i += 64) {
+      const int64_t t = wt0 + min(i, nv - 1);
+      const int64_t vec = (r * a.tokens + t) * a.heads + h;
+      const float vs = f16_value(a.v_scale[vec]);
+      sc[i] = f16_value(a.k_scale[vec]);
+      sc[kMmaW + i] = f16_value(a.k_zero[vec]);
+      sc[2 * kMmaW + i] = vs;
+      sc[3 * kMmaW + i] = f16_value(a.v_zero[vec]);
+      vsm = fmaxf(vsm, fabsf(vs));
+    }
+    wave_lds_sync();
+    // pass 1: scores of the window into LDS, window maximum per head
+    float mw = -INFINITY;
+    for (int bk = 0; bk < nblk; ++bk) {
+      const int i = 16 * bk + n16;
+      const int64_t t = wt0 + min(i, nv - 1);
+      const int64_t vec = (r * a.tokens + t) * a.heads + h;
+      const uint2 kw = *reinterpret_cast<const uint2*>(a.k_codes + vec * 32 + 8 * g);
+      const i32x4_t b0 = {(int32_t)code_bytes<0>(kw.x), (int32_t)code_bytes<1>(kw.x), (int32_t)code_bytes<2>(kw.x),
+                          (int32_t)code_bytes<3>(kw.x)};
+      const i32x4_t b1 = {(int32_t)code_bytes<0>(kw.y), (int32_t)code_bytes<1>(kw.y), (int32_t)code_bytes<2>(kw.y),
+                          (int32_t)code_bytes<3>(kw.y)};
+      i32x4_t acc = {0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], b0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], b1, acc, 0, 0, 0);
+      // lane (n16, g) holds digits 0..3 of head g for slot i
+      const float raw = __builtin_fmaf((float)acc[3], 16777216.0f,
+                                       __builtin_fmaf((float)acc[2], 65536.0f,
+                                                      __builtin_fmaf((float)acc[1], 256.0f, (float)acc[0])));
+      float s = __builtin_fmaf(sc[i] * raw, rs, sc[kMmaW + i] * zq);
+      s = i < nv ? s : -INFINITY;
+      ss[g * SR + i] = s;
+      mw = fmaxf(mw, s);
+    }
+    mw = max_x1(mw);
+    mw = max_x2(mw);
+    mw = fmaxf(mw, __shfl_xor(mw, 4));
+    mw = fmaxf(mw, __shfl_xor(mw, 8));
+    const float mwin = __shfl(mw, 16 * qm);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) vsm = fmaxf(vsm, __shfl_xor(vsm, o));
+    int ex;
+    (void)__builtin_frexpf(vsm, &ex);
+    const int Ew = 27 - ex;  // v_scale 2^Ew < 2^27 for every slot of the window
+    const float Mnew = fmaxf(Mrun, mwin);
+    const bool grow = __builtin_amdgcn_ballot_w64(Mnew > Mrun) != 0;
+    if (grow || first || Ew < Ecur || since >= 1024) {  // wave-uniform
+      flush(__builtin_amdgcn_exp2f(Mrun - Mnew));
+      Mrun = Mnew;
+      Ecur = Ew;
+      since = 0;
+      first = false;
+    }
+    ++since;
+    wave_lds_sync();
+    // pass 2: weights of 64-slot groups against the value codes
+    const float Mk = Mrun - (float)Ecur;  // p 2^E = exp2(s - Mk)
+    for (int q4 = 0; q4 < nblk; q4 += 4) {
+      uint32_t X[4], Y[4], D[4];
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int i0 = 16 * (q4 + bt) + 4 * g;  // window slot of the lane's 4 slots
+        const float4 sv = *reinterpret_cast<const float4*>(&ss[qm * SR + i0]);
+        const float4 vsv = *reinterpret_cast<const float4*>(&sc[2 * kMmaW + i0]);
+        const float4 vzv = *reinterpret_cast<const float4*>(&sc[3 * kMmaW + i0]);
+        const float svs[4] = {sv.x, sv.y, sv.z, sv.w}, vss[4] = {vsv.x, vsv.y, vsv.z, vsv.w},
+                    vzs[4] = {vzv.x, vzv.y, vzv.z, vzv.w};
+        uint32_t dd = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(svs[j] - Mk);
+          Lp += p;
+          Zp = __builtin_fmaf(p, vzs[j], Zp);
+          const uint32_t N = (uint32_t)__builtin_fmaf(p, vss[j], 0.5f);
+          dd |= ((N >> (7 * qs)) & 0x7fu) << (8 * j);
+        }
+        D[bt] = dd;
+        uint32_t u[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t t = wt0 + min(i0 + j, nv - 1);
+          const int64_t vec = (r * a.tokens + t) * a.heads + h;
+          u[j] = *reinterpret_cast<const uint16_t*>(a.v_codes + vec * 32 + 2 * n16);
+        }
+        const uint32_t lo = u[0] | (u[1] << 16), hi = u[2] | (u[3] << 16);
+        X[bt] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);  // byte j: channels 8 n16 .. +3 of slot j
+        Y[bt] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // byte j: channels 8 n16 + 4 .. +7
+      }
+      const i32x4_t bop = {(int32_t)D[0], (int32_t)D[1], (int32_t)D[2], (int32_t)D[3]};
+#define KVQ_VPROD(B, SRC, K)                                                                                      \
+  {                                                                                                               \
+    const i32x4_t ap = {(int32_t)code_bytes<K>(SRC[0]), (int32_t)code_bytes<K>(SRC[1]),                           \
+                        (int32_t)code_bytes<K>(SRC[2]), (int32_t)code_bytes<K>(SRC[3])};                          \
+    cv[B] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap, bop, cv[B], 0, 0, 0);                                       \
+  }
+      KVQ_VPROD(0, X, 0)
+      KVQ_VPROD(1, X, 1)
+      KVQ_VPROD(2, X, 2)
+      KVQ_VPROD(3, X, 3)
+      KVQ_VPROD(4, Y, 0)
+      KVQ_VPROD(5, Y, 1)
+      KVQ_VPROD(6, Y, 2)
+      KVQ_VPROD(7, Y, 3)
+#undef KVQ_VPROD
+    }
+    wave_lds_sync();
+  }
+  if (t_begin < t_end) flush(1.0f);
+  // sum the four digits of each value (lanes 4 m + s), and the weights over the lane groups
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      fv[b][j] = add_x1(fv[b][j]);
+      fv[b][j] = add_x2(fv[b][j]);
+    }
+  Lf += __shfl_xor(Lf, 16);
+  Lf += __shfl_xor(Lf, 32);
+  Zf += __shfl_xor(Zf, 16);
+  Zf += __shfl_xor(Zf, 32);
+  if (qm < QG) {
+    float* pb = a.part + ((r * a.q_heads + h * QG + qm) * a.n_chunks + c) * kAttendPart;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (qs == j) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) pb[32 * g + 8 * j + b] = fv[b][j] + Zf;  // channel 32 g + 8 j + b
+      }
+    if (qs == 0 && g == 0) {
+      pb[128] = (t_begin < t_end) ? Mrun * 0.6931471805599453f : -INFINITY;
+      pb[129] = Lf;
     }
   }
 }
@@ -1952,7 +2230,13 @@ int launch_attend_t(const AttendArgs& a, hipStream_t s) {
   if ((np + 3) / 4 > 0x7fffffff || (nq + 3) / 4 > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(attend_rotate_q, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
   if (hipError_t e = hipGetLastError()) return (int)e;
-  hipLaunchKernelGGL((attend_partial<BITS, QG>), dim3((unsigned)((np + 3) / 4)), dim3(256), 0, s, a);
+#if KVQ_ATT_MMA
+  if (BITS == 2 && a.group_log2 == 7 && ((uintptr_t)a.k_codes & 7) == 0 && ((uintptr_t)a.v_codes & 1) == 0) {
+    if ((np + 7) / 8 > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attend_partial_mma<QG>), dim3((unsigned)((np + 7) / 8)), dim3(512), 0, s, a);
+  } else
+#endif
+    hipLaunchKernelGGL((attend_partial<BITS, QG>), dim3((unsigned)((np + 3) / 4)), dim3(256), 0, s, a);
   if (hipError_t e = hipGetLastError()) return (int)e;
   hipLaunchKernelGGL(attend_combine, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
   return (int)hipGetLastError();

@@ -53,6 +53,8 @@ def _case(r, t, h, bits, g, rope, use_perm, n_sink, name):
     (2, 4, 32, 3, False),
     (4, 4, 64, 0, True),
     (2, 2, 32, 4, True),
+    (1, 2, 128, 0, True),    # matrix-core partial pass with one and two query heads per KV head
+    (2, 2, 128, 2, False),
 ])
 def test_attend_small(qg, bits, g, n_sink, perm_v):
     r, t, h = 5, 203, 3
