@@ -1716,6 +1716,7 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
 // lane (n16, g) holds slot n16 of a 16-slot block for head g; in the value product lane
 // (4 m + s, g) holds digit s of head m for channels 32 g + 8 j + b (register j, product b).
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kMmaW = 128;   // slots per window
 constexpr int kMmaPad = 16;  // padding of the LDS score rows (banks of the row writes)
 template <int K>
@@ -1725,12 +1726,23 @@ __device__ __forceinline__ uint32_t code_bytes(uint32_t x) {  // code 4 b + K of
 }
 __host__ __device__ constexpr int code_mul(int k) { return k == 0 ? 1 : (k == 1 ? 4 : 16); }
 
+// Tasks are (row, chunk, head) with the head fastest; blocks take 4 consecutive tasks, and
+// blocks 16 k + x and 16 k + 8 + x (x < 8) take consecutive task quads, so that both halves
+// of the heads of a (row, chunk) are read on one XCD (blocks go round-robin over the 8 XCDs)
+// and share its L2 for the scale planes.  Per window of 128 slots: the value codes go to LDS
+// (16-byte loads), the key product scores the slots (lane (n16, g): slot n16 of each 16-slot
+// block, head g), the window maximum decides a flush, each lane turns its scores into weight
+// integers in LDS, and the value product reads them as digits.  Code and scale planes are
+// read through descriptors sized to the window's valid slots: reads past them return zeros.
 template <int QG>
-__global__ void __launch_bounds__(512) attend_partial_mma(const AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_sc[8][4][kMmaW];             // k scale, k zero, v scale, v zero
-  __shared__ __attribute__((aligned(16))) float s_s[8][4][kMmaW + kMmaPad];    // scores (log2 units) per head
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 8 + wave;
+__global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) float4 s_sc[4][kMmaW];                // k scale, k zero, v scale, v zero
+  __shared__ __attribute__((aligned(16))) uint32_t s_n[4][4][kMmaW + kMmaPad];  // weight integers per head
+  __shared__ __attribute__((aligned(16))) uint8_t s_vc[4][kMmaW * 40];          // value codes, slot s at 32 s + 32 (s / 4)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t blk = blockIdx.x;
+  const int64_t quad = (blk >> 4) * 16 + ((blk & 7) << 1) + ((blk >> 3) & 1);
+  const int64_t w = quad * 4 + wave;
   if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier in this kernel
   const int64_t h = w % a.heads, rc = w / a.heads, c = rc % a.n_chunks, r = rc / a.n_chunks;
   int64_t len = a.tokens;
@@ -1742,8 +1754,9 @@ __global__ void __launch_bounds__(512) attend_partial_mma(const AttendArgs a) {
   const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
   const int n16 = lane & 15, g = lane >> 4;
   const int qm = n16 >> 2, qs = n16 & 3;  // head and digit of the lane's column in the value product
-  float* const sc = &s_sc[wave][0][0];
-  float* const ss = &s_s[wave][0][0];
+  float4* const sc = &s_sc[wave][0];
+  uint32_t* const sn = &s_n[wave][0][0];
+  uint8_t* const vc = &s_vc[wave][0];
   constexpr int SR = kMmaW + kMmaPad;
   constexpr float kLog2e = 1.4426950408889634f;
 
@@ -1803,29 +1816,35 @@ __global__ void __launch_bounds__(512) attend_partial_mma(const AttendArgs a) {
   const float zq = g < QG ? sc2 * (g == 0 ? qsum[0] : (g == 1 ? qsum[1] : (g == 2 ? qsum[2] : qsum[3]))) : 0.0f;
 
   i32x4_t cv[8];
-  float fv[8][4];
+  float fo[8];  // value product: channels 32 g + 8 qs + b of head qm, summed over the digits
 #pragma unroll
-  for (int b = 0; b < 8; ++b)
+  for (int b = 0; b < 8; ++b) {
+    fo[b] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      cv[b][j] = 0;
-      fv[b][j] = 0.0f;
-    }
-  float Mrun = -INFINITY;               // running maximum of head qm (log2 units)
-  float Lp = 0.0f, Zp = 0.0f;           // pending sums of p 2^E and p 2^E v_zero
+    for (int j = 0; j < 4; ++j) cv[b][j] = 0;
+  }
+  float Mrun = -INFINITY;      // running maximum of head g (log2 units)
+  float Lp = 0.0f, Zp = 0.0f;  // head g, the lane's slots: pending sums of p 2^E and p 2^E v_zero
   float Lf = 0.0f, Zf = 0.0f;
   int Ecur = 0, since = 0;
   bool first = true;
+  // integer sums to floats: weight each digit, sum the 4 digit lanes, keep register j = qs
   auto flush = [&](float corr) __attribute__((always_inline)) {
+    const float corr_m = __shfl(corr, 16 * qm);  // the factor of head qm
     const float kb = __builtin_ldexpf(1.0f, 7 * qs - Ecur);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const float k = kb * (1.0f / (float)code_mul(b & 3));
+      float add = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        fv[b][j] = (fv[b][j] + (float)cv[b][j] * k) * corr;
+        float v = (float)cv[b][j] * k;
+        v = add_x1(v);
+        v = add_x2(v);
+        add = qs == j ? v : add;
         cv[b][j] = 0;
       }
+      fo[b] = (fo[b] + add) * corr_m;
     }
     const float le = __builtin_ldexpf(1.0f, -Ecur);
     Lf = (Lf + Lp * le) * corr;
@@ -1834,56 +1853,116 @@ __global__ void __launch_bounds__(512) attend_partial_mma(const AttendArgs a) {
     Zp = 0.0f;
   };
 
+  const uint32_t sT = (uint32_t)a.heads * 32u;  // bytes between slots in a code plane
+  const uint32_t sH2 = (uint32_t)a.heads * 2u;  // bytes between slots in a scale plane
+  const int64_t rh0 = r * a.tokens * a.heads + h;
+  const uint32_t koff = (uint32_t)n16 * sT + 8u * (uint32_t)g;   // key-code bytes of the lane in a block
+  const uint32_t vrd = 160u * (uint32_t)g + 2u * (uint32_t)n16;  // LDS value codes: slot 4 g, bytes 2 n16
+  // Loads of a window (value codes, scales, key codes) are issued one window ahead: the value
+  // codes and scales of window w + 1 after window w's are staged in LDS, its key codes after
+  // window w's key product.  Descriptors cover the valid slots of the window they serve; a
+  // window at or past the end of the chunk gets empty descriptors (its loads read zeros).
+  auto win_bytes = [&](int64_t w0, uint32_t per_slot, uint32_t tail) -> uint32_t {
+    const int64_t n = min((int64_t)kMmaW, t_end - w0);
+    return n > 0 ? (uint32_t)(n - 1) * per_slot + tail : 0u;
+  };
+  u32x4_t vq[4];
+  u32x2_t kq[8];
+  uint32_t sq[2][4];
+  auto load_vs = [&](int64_t w0) __attribute__((always_inline)) {  // value codes and scales
+    const int64_t vw = rh0 + w0 * a.heads;
+    const uint32_t cb = win_bytes(w0, sT, 32u), sb = win_bytes(w0, sH2, 2u);
+    const buf_t bvc = make_buf(a.v_codes + vw * 32, cb);
+    const buf_t bks = make_buf(a.k_scale + vw, sb), bkz = make_buf(a.k_zero + vw, sb);
+    const buf_t bvs = make_buf(a.v_scale + vw, sb), bvz = make_buf(a.v_zero + vw, sb);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t cc = (uint32_t)(lane + 64 * k);
+      vq[k] = __builtin_amdgcn_raw_buffer_load_b128(bvc, (cc >> 1) * sT + 16u * (cc & 1u), 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t o = (uint32_t)(lane + 64 * k) * sH2;
+      sq[k][0] = __builtin_amdgcn_raw_buffer_load_b16(bks, o, 0, 0);
+      sq[k][1] = __builtin_amdgcn_raw_buffer_load_b16(bkz, o, 0, 0);
+      sq[k][2] = __builtin_amdgcn_raw_buffer_load_b16(bvs, o, 0, 0);
+      sq[k][3] = __builtin_amdgcn_raw_buffer_load_b16(bvz, o, 0, 0);
+    }
+  };
+  auto load_k = [&](int64_t w0) __attribute__((always_inline)) {  // key codes, lane (n16, g)
+    const int64_t vw = rh0 + w0 * a.heads;
+    const buf_t bkc = make_buf(a.k_codes + vw * 32, win_bytes(w0, sT, 32u));
+#pragma unroll
+    for (int bk = 0; bk < 8; ++bk)
+      kq[bk] = __builtin_amdgcn_raw_buffer_load_b64(bkc, koff + (uint32_t)(16 * bk) * sT, 0, 0);
+  };
+  if (t_begin < t_end) {
+    load_vs(t_begin);
+    load_k(t_begin);
+  }
   for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += kMmaW) {
-    const int nv = (int)min((int64_t)kMmaW, t_end - wt0);  // valid slots of the window (>= 1)
-    const int nblk = 4 * ((nv + 63) >> 6);                 // 16-slot blocks scored (whole 64-slot groups)
-    // scales and zeros of the window's slots (clamped to the last valid slot)
+    const int nv = (int)min((int64_t)kMmaW, t_end - wt0);  // valid slots of the window (>= 1); the
+    // rest of a window reads zeros through the descriptors and is masked by its slot index
     float vsm = 0.0f;
-    for (int i = lane; i < 16 * nblk; i += 64) {
-      const int64_t t = wt0 + min(i, nv - 1);
-      const int64_t vec = (r * a.tokens + t) * a.heads + h;
-      const float vs = f16_value(a.v_scale[vec]);
-      sc[i] = f16_value(a.k_scale[vec]);
-      sc[kMmaW + i] = f16_value(a.k_zero[vec]);
-      sc[2 * kMmaW + i] = vs;
-      sc[3 * kMmaW + i] = f16_value(a.v_zero[vec]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = lane + 64 * k;
+      const float vs = f16_value(sq[k][2]);
+      sc[i] = make_float4(f16_value(sq[k][0]), f16_value(sq[k][1]), vs, f16_value(sq[k][3]));
       vsm = fmaxf(vsm, fabsf(vs));
     }
-    wave_lds_sync();
-    // pass 1: scores of the window into LDS, window maximum per head
-    float mw = -INFINITY;
-    for (int bk = 0; bk < nblk; ++bk) {
-      const int i = 16 * bk + n16;
-      const int64_t t = wt0 + min(i, nv - 1);
-      const int64_t vec = (r * a.tokens + t) * a.heads + h;
-      const uint2 kw = *reinterpret_cast<const uint2*>(a.k_codes + vec * 32 + 8 * g);
-      const i32x4_t b0 = {(int32_t)code_bytes<0>(kw.x), (int32_t)code_bytes<1>(kw.x), (int32_t)code_bytes<2>(kw.x),
-                          (int32_t)code_bytes<3>(kw.x)};
-      const i32x4_t b1 = {(int32_t)code_bytes<0>(kw.y), (int32_t)code_bytes<1>(kw.y), (int32_t)code_bytes<2>(kw.y),
-                          (int32_t)code_bytes<3>(kw.y)};
-      i32x4_t acc = {0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], b0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], b1, acc, 0, 0, 0);
-      // lane (n16, g) holds digits 0..3 of head g for slot i
-      const float raw = __builtin_fmaf((float)acc[3], 16777216.0f,
-                                       __builtin_fmaf((float)acc[2], 65536.0f,
-                                                      __builtin_fmaf((float)acc[1], 256.0f, (float)acc[0])));
-      float s = __builtin_fmaf(sc[i] * raw, rs, sc[kMmaW + i] * zq);
-      s = i < nv ? s : -INFINITY;
-      ss[g * SR + i] = s;
-      mw = fmaxf(mw, s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t cc = (uint32_t)(lane + 64 * k), sl = cc >> 1;
+      *reinterpret_cast<u32x4_t*>(vc + 32u * sl + 32u * (sl >> 2) + 16u * (cc & 1u)) = vq[k];
     }
+    load_vs(wt0 + kMmaW);
+    wave_lds_sync();
+    // pass 1: scores of the lane's slots (head g), window maximum per head; the products of
+    // 4 blocks are issued before any is read
+    float scv[8];
+    float mw = -INFINITY;
+#pragma unroll
+    for (int q4 = 0; q4 < 8; q4 += 4) {
+      i32x4_t acc[4];
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const u32x2_t kv = kq[q4 + bt];
+        const i32x4_t b0 = {(int32_t)code_bytes<0>(kv.x), (int32_t)code_bytes<1>(kv.x), (int32_t)code_bytes<2>(kv.x),
+                            (int32_t)code_bytes<3>(kv.x)};
+        acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], b0, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const u32x2_t kv = kq[q4 + bt];
+        const i32x4_t b1 = {(int32_t)code_bytes<0>(kv.y), (int32_t)code_bytes<1>(kv.y), (int32_t)code_bytes<2>(kv.y),
+                            (int32_t)code_bytes<3>(kv.y)};
+        acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], b1, acc[bt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int i = 16 * (q4 + bt) + n16;
+        // lane (n16, g) holds digits 0..3 of head g for slot i
+        const float raw = __builtin_fmaf((float)acc[bt][3], 16777216.0f,
+                                         __builtin_fmaf((float)acc[bt][2], 65536.0f,
+                                                        __builtin_fmaf((float)acc[bt][1], 256.0f, (float)acc[bt][0])));
+        const float4 s4 = sc[i];
+        const float sco = __builtin_fmaf(s4.x * raw, rs, s4.y * zq);
+        scv[q4 + bt] = i < nv ? sco : -INFINITY;
+        mw = fmaxf(mw, scv[q4 + bt]);
+      }
+    }
+    load_k(wt0 + kMmaW);
     mw = max_x1(mw);
     mw = max_x2(mw);
     mw = fmaxf(mw, __shfl_xor(mw, 4));
-    mw = fmaxf(mw, __shfl_xor(mw, 8));
-    const float mwin = __shfl(mw, 16 * qm);
+    mw = fmaxf(mw, __shfl_xor(mw, 8));  // every lane of row g: the window maximum of head g
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) vsm = fmaxf(vsm, __shfl_xor(vsm, o));
     int ex;
     (void)__builtin_frexpf(vsm, &ex);
     const int Ew = 27 - ex;  // v_scale 2^Ew < 2^27 for every slot of the window
-    const float Mnew = fmaxf(Mrun, mwin);
+    const float Mnew = fmaxf(Mrun, mw);
     const bool grow = __builtin_amdgcn_ballot_w64(Mnew > Mrun) != 0;
     if (grow || first || Ew < Ecur || since >= 1024) {  // wave-uniform
       flush(__builtin_amdgcn_exp2f(Mrun - Mnew));
@@ -1893,83 +1972,78 @@ __global__ void __launch_bounds__(512) attend_partial_mma(const AttendArgs a) {
       first = false;
     }
     ++since;
-    wave_lds_sync();
-    // pass 2: weights of 64-slot groups against the value codes
+    // pass 1.5: weight integers p v_scale 2^E of the lane's slots, sums of p and p v_zero
     const float Mk = Mrun - (float)Ecur;  // p 2^E = exp2(s - Mk)
-    for (int q4 = 0; q4 < nblk; q4 += 4) {
-      uint32_t X[4], Y[4], D[4];
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        const int i0 = 16 * (q4 + bt) + 4 * g;  // window slot of the lane's 4 slots
-        const float4 sv = *reinterpret_cast<const float4*>(&ss[qm * SR + i0]);
-        const float4 vsv = *reinterpret_cast<const float4*>(&sc[2 * kMmaW + i0]);
-        const float4 vzv = *reinterpret_cast<const float4*>(&sc[3 * kMmaW + i0]);
-        const float svs[4] = {sv.x, sv.y, sv.z, sv.w}, vss[4] = {vsv.x, vsv.y, vsv.z, vsv.w},
-                    vzs[4] = {vzv.x, vzv.y, vzv.z, vzv.w};
-        uint32_t dd = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(svs[j] - Mk);
-          Lp += p;
-          Zp = __builtin_fmaf(p, vzs[j], Zp);
-          const uint32_t N = (uint32_t)__builtin_fmaf(p, vss[j], 0.5f);
-          dd |= ((N >> (7 * qs)) & 0x7fu) << (8 * j);
-        }
-        D[bt] = dd;
-        uint32_t u[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t t = wt0 + min(i0 + j, nv - 1);
-          const int64_t vec = (r * a.tokens + t) * a.heads + h;
-          u[j] = *reinterpret_cast<const uint16_t*>(a.v_codes + vec * 32 + 2 * n16);
-        }
-        const uint32_t lo = u[0] | (u[1] << 16), hi = u[2] | (u[3] << 16);
-        X[bt] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);  // byte j: channels 8 n16 .. +3 of slot j
-        Y[bt] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // byte j: channels 8 n16 + 4 .. +7
+    for (int bk = 0; bk < 8; ++bk) {
+        const int i = 16 * bk + n16;
+        const float pe = __builtin_amdgcn_exp2f(scv[bk] - Mk);
+        const float4 s4 = sc[i];
+        Lp += pe;
+        Zp = __builtin_fmaf(pe, s4.w, Zp);
+        sn[g * SR + i] = (uint32_t)__builtin_fmaf(pe, s4.z, 0.5f);
       }
-      const i32x4_t bop = {(int32_t)D[0], (int32_t)D[1], (int32_t)D[2], (int32_t)D[3]};
+    wave_lds_sync();
+    // pass 2: value product per 64-slot group
+#pragma unroll
+    for (int q4 = 0; q4 < 8; q4 += 4) {
+      {
+        uint32_t D[4], X[4], Y[4];
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+          const int i0 = 16 * (q4 + bt) + 4 * g;  // window slot of the lane's 4 slots
+          const u32x4_t nw = *reinterpret_cast<const u32x4_t*>(&sn[qm * SR + i0]);
+          const uint32_t sh = 7u * (uint32_t)qs;
+          D[bt] = ((nw.x >> sh) & 0x7fu) | (((nw.y >> sh) & 0x7fu) << 8) | (((nw.z >> sh) & 0x7fu) << 16) |
+                  (((nw.w >> sh) & 0x7fu) << 24);
+          const uint8_t* p0 = vc + vrd + 640u * (uint32_t)(q4 + bt);
+          u16x2_t lo, hi;
+          lo[0] = *reinterpret_cast<const uint16_t*>(p0);
+          lo[1] = *reinterpret_cast<const uint16_t*>(p0 + 32);
+          hi[0] = *reinterpret_cast<const uint16_t*>(p0 + 64);
+          hi[1] = *reinterpret_cast<const uint16_t*>(p0 + 96);
+          const uint32_t lw = __builtin_bit_cast(uint32_t, lo), hw = __builtin_bit_cast(uint32_t, hi);
+          X[bt] = __builtin_amdgcn_perm(hw, lw, 0x06040200u);  // byte j: channels 8 n16 .. +3 of slot j
+          Y[bt] = __builtin_amdgcn_perm(hw, lw, 0x07050301u);  // byte j: channels 8 n16 + 4 .. +7
+        }
+        const i32x4_t bop = {(int32_t)D[0], (int32_t)D[1], (int32_t)D[2], (int32_t)D[3]};
 #define KVQ_VPROD(B, SRC, K)                                                                                      \
   {                                                                                                               \
     const i32x4_t ap = {(int32_t)code_bytes<K>(SRC[0]), (int32_t)code_bytes<K>(SRC[1]),                           \
                         (int32_t)code_bytes<K>(SRC[2]), (int32_t)code_bytes<K>(SRC[3])};                          \
     cv[B] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap, bop, cv[B], 0, 0, 0);                                       \
   }
-      KVQ_VPROD(0, X, 0)
-      KVQ_VPROD(1, X, 1)
-      KVQ_VPROD(2, X, 2)
-      KVQ_VPROD(3, X, 3)
-      KVQ_VPROD(4, Y, 0)
-      KVQ_VPROD(5, Y, 1)
-      KVQ_VPROD(6, Y, 2)
-      KVQ_VPROD(7, Y, 3)
+        KVQ_VPROD(0, X, 0)
+        KVQ_VPROD(1, X, 1)
+        KVQ_VPROD(2, X, 2)
+        KVQ_VPROD(3, X, 3)
+        KVQ_VPROD(4, Y, 0)
+        KVQ_VPROD(5, Y, 1)
+        KVQ_VPROD(6, Y, 2)
+        KVQ_VPROD(7, Y, 3)
 #undef KVQ_VPROD
+      }
     }
     wave_lds_sync();
   }
   if (t_begin < t_end) flush(1.0f);
-  // sum the four digits of each value (lanes 4 m + s), and the weights over the lane groups
-#pragma unroll
-  for (int b = 0; b < 8; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      fv[b][j] = add_x1(fv[b][j]);
-      fv[b][j] = add_x2(fv[b][j]);
-    }
-  Lf += __shfl_xor(Lf, 16);
-  Lf += __shfl_xor(Lf, 32);
-  Zf += __shfl_xor(Zf, 16);
-  Zf += __shfl_xor(Zf, 32);
+  // sums of head g over the 16 slot lanes of row g, then head qm's for the output lanes
+  Lf = add_x1(Lf);
+  Lf = add_x2(Lf);
+  Lf += __shfl_xor(Lf, 4);
+  Lf += __shfl_xor(Lf, 8);
+  Zf = add_x1(Zf);
+  Zf = add_x2(Zf);
+  Zf += __shfl_xor(Zf, 4);
+  Zf += __shfl_xor(Zf, 8);
+  const float Lm = __shfl(Lf, 16 * qm), Zm = __shfl(Zf, 16 * qm), Mm = __shfl(Mrun, 16 * qm);
   if (qm < QG) {
     float* pb = a.part + ((r * a.q_heads + h * QG + qm) * a.n_chunks + c) * kAttendPart;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (qs == j) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) pb[32 * g + 8 * j + b] = fv[b][j] + Zf;  // channel 32 g + 8 j + b
-      }
+    for (int b = 0; b < 8; ++b) pb[32 * g + 8 * qs + b] = fo[b] + Zm;  // channel 32 g + 8 qs + b
     if (qs == 0 && g == 0) {
-      pb[128] = (t_begin < t_end) ? Mrun * 0.6931471805599453f : -INFINITY;
-      pb[129] = Lf;
+      pb[128] = (t_begin < t_end) ? Mm * 0.6931471805599453f : -INFINITY;
+      pb[129] = Lm;
     }
   }
 }
@@ -2232,8 +2306,10 @@ int launch_attend_t(const AttendArgs& a, hipStream_t s) {
   if (hipError_t e = hipGetLastError()) return (int)e;
 #if KVQ_ATT_MMA
   if (BITS == 2 && a.group_log2 == 7 && ((uintptr_t)a.k_codes & 7) == 0 && ((uintptr_t)a.v_codes & 1) == 0) {
-    if ((np + 7) / 8 > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attend_partial_mma<QG>), dim3((unsigned)((np + 7) / 8)), dim3(512), 0, s, a);
+    // whole groups of 16 blocks, so the XCD-aware order maps the blocks onto every task
+    const int64_t nb = ((np + 3) / 4 + 15) / 16 * 16;
+    if (nb > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attend_partial_mma<QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
   } else
 #endif
     hipLaunchKernelGGL((attend_partial<BITS, QG>), dim3((unsigned)((np + 3) / 4)), dim3(256), 0, s, a);
