@@ -1734,6 +1734,33 @@ __host__ __device__ constexpr int code_mul(int k) { return k == 0 ? 1 : (k == 1 
 // block, head g), the window maximum decides a flush, each lane turns its scores into weight
 // integers in LDS, and the value product reads them as digits.  Code and scale planes are
 // read through descriptors sized to the window's valid slots: reads past them return zeros.
+// Reductions over the 16 lanes of each row (every lane gets its row's result) with DPP:
+// quad permutes for lanes xor 1 and xor 2, row rotations by 4 and 8.
+__device__ __forceinline__ float dpp_f(float v, int ctrl) {
+  switch (ctrl) {  // the control must be a constant of the builtin
+    case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    case 0x124: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  }
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f(v, 0xB1));
+  v = fmaxf(v, dpp_f(v, 0x4E));
+  v = fmaxf(v, dpp_f(v, 0x124));
+  return fmaxf(v, dpp_f(v, 0x128));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f(v, 0xB1);
+  v += dpp_f(v, 0x4E);
+  v += dpp_f(v, 0x124);
+  return v + dpp_f(v, 0x128);
+}
+// the value of row m (lanes 16 m .. 16 m + 15 hold it), wave-uniform
+__device__ __forceinline__ float row_value(float v, int m) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * m));
+}
+
 template <int QG>
 __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
   __shared__ __attribute__((aligned(16))) float4 s_sc[4][kMmaW];                // k scale, k zero, v scale, v zero
@@ -1766,13 +1793,9 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const float v0 = m < QG ? qb[m * 128 + lane] : 0.0f, v1 = m < QG ? qb[m * 128 + lane + 64] : 0.0f;
-    qmx[m] = fmaxf(fabsf(v0), fabsf(v1));
-    qsum[m] = v0 + v1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      qmx[m] = fmaxf(qmx[m], __shfl_xor(qmx[m], o));
-      qsum[m] += __shfl_xor(qsum[m], o);
-    }
+    const float x = row_max16(fmaxf(fabsf(v0), fabsf(v1))), y = row_sum16(v0 + v1);
+    qmx[m] = fmaxf(fmaxf(row_value(x, 0), row_value(x, 1)), fmaxf(row_value(x, 2), row_value(x, 3)));
+    qsum[m] = (row_value(y, 0) + row_value(y, 1)) + (row_value(y, 2) + row_value(y, 3));
   }
   // query scale 2^e with 16 |q~| 2^e < 2^30
   float qsc[4];
@@ -1953,12 +1976,9 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
       }
     }
     load_k(wt0 + kMmaW);
-    mw = max_x1(mw);
-    mw = max_x2(mw);
-    mw = fmaxf(mw, __shfl_xor(mw, 4));
-    mw = fmaxf(mw, __shfl_xor(mw, 8));  // every lane of row g: the window maximum of head g
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) vsm = fmaxf(vsm, __shfl_xor(vsm, o));
+    mw = row_max16(mw);  // every lane of row g: the window maximum of head g
+    vsm = row_max16(vsm);
+    vsm = fmaxf(fmaxf(row_value(vsm, 0), row_value(vsm, 1)), fmaxf(row_value(vsm, 2), row_value(vsm, 3)));
     int ex;
     (void)__builtin_frexpf(vsm, &ex);
     const int Ew = 27 - ex;  // v_scale 2^Ew < 2^27 for every slot of the window
@@ -2028,14 +2048,8 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
   }
   if (t_begin < t_end) flush(1.0f);
   // sums of head g over the 16 slot lanes of row g, then head qm's for the output lanes
-  Lf = add_x1(Lf);
-  Lf = add_x2(Lf);
-  Lf += __shfl_xor(Lf, 4);
-  Lf += __shfl_xor(Lf, 8);
-  Zf = add_x1(Zf);
-  Zf = add_x2(Zf);
-  Zf += __shfl_xor(Zf, 4);
-  Zf += __shfl_xor(Zf, 8);
+  Lf = row_sum16(Lf);
+  Zf = row_sum16(Zf);
   const float Lm = __shfl(Lf, 16 * qm), Zm = __shfl(Zf, 16 * qm), Mm = __shfl(Mrun, 16 * qm);
   if (qm < QG) {
     float* pb = a.part + ((r * a.q_heads + h * QG + qm) * a.n_chunks + c) * kAttendPart;
