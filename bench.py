@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "KV vectors encoded+decoded/sec and achieved HBM GB/s (% peak), d=128 2-bit"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+MFMA_INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix-core peak, AMD published (no sparsity)
 # 32-bit VALU peak in lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one add, mul,
 # fma, min, max or convert per lane per cycle; packed two-wide FP32 is not used by these
 # kernels, so the published 157.3 TFLOP/s -- FMA = 2 flops, two lanes per packed op -- is
@@ -285,7 +286,9 @@ def main():
     attend_ms = a.elapsed_time(b) / n_rep
     attend_bytes = pl_bytes["K"] + pl_bytes["V"]  # the encoded cache, read once
     bf16_bytes = in_bytes["K"] + in_bytes["V"]  # what the same attention reads from a bf16 cache
-    attend_fma = r0 * t0_ * h0 * (q_heads // h0) * d0 * 2  # score and value multiply-adds
+    # int8 matrix-core operations as issued (2 per multiply-add), per (slot, KV head): for the
+    # keys two 16x16x64 products per 16 slots, for the values eight per 64 slots
+    attend_mfma_ops = r0 * t0_ * h0 * 2 * (2 * 16 * 16 * 64 // 16 + 8 * 16 * 16 * 64 // 64)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -324,10 +327,12 @@ def main():
                    "GBps": round(attend_bytes / (attend_ms * 1e-3) / 1e9, 1),
                    "bf16_cache_bytes": bf16_bytes,
                    "bf16_cache_read_at_hbm_peak_ms": round(bf16_bytes / (HBM_PEAK_GBPS * 1e9) * 1e3, 4),
-                   "valu_fma": attend_fma,
-                   "valu_frac": round(attend_fma / (attend_ms * 1e-3) / (VALU_PEAK_TOPS * 1e12), 4),
+                   "hbm_frac": round(attend_bytes / (attend_ms * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4),
+                   "mfma_int8_ops": attend_mfma_ops,
+                   "mfma_int8_frac": round(attend_mfma_ops / (attend_ms * 1e-3) / (MFMA_INT8_PEAK_TOPS * 1e12), 4),
                    "what": "decode-step attention over the encoded K/V cache in the rotated domain "
-                           "(kvq_attend), VALU-bound"},
+                           "(kvq_attend): exact int8 matrix-core products of the codes with 8-bit digits of "
+                           "the rotated queries and of the softmax weights"},
         "append": {"us_per_step": round(append_us, 2), "vectors_per_step": append_vec,
                    "what": "decode-step cache update: K and V of every row appended at per-row positions "
                            "(kvq_append, K with RoPE + perm), launch-latency bound"},
