@@ -1717,7 +1717,10 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
 // (4 m + s, g) holds digit s of head m for channels 32 g + 8 j + b (register j, product b).
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
-constexpr int kMmaW = 128;   // slots per window
+#ifndef KVQ_MMA_W
+#define KVQ_MMA_W 128
+#endif
+constexpr int kMmaW = KVQ_MMA_W;  // slots per window (a multiple of 64)
 constexpr int kMmaPad = 16;  // padding of the LDS score rows (banks of the row writes)
 template <int K>
 __device__ __forceinline__ uint32_t code_bytes(uint32_t x) {  // code 4 b + K of byte b, times code_mul(K)
@@ -1761,32 +1764,37 @@ __device__ __forceinline__ float row_value(float v, int m) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * m));
 }
 
-template <int QG>
-__global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) float4 s_sc[4][kMmaW];                // k scale, k zero, v scale, v zero
-  __shared__ __attribute__((aligned(16))) uint32_t s_n[4][4][kMmaW + kMmaPad];  // weight integers per head
-  __shared__ __attribute__((aligned(16))) uint8_t s_vc[4][kMmaW * 40];          // value codes, slot s at 32 s + 32 (s / 4)
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t blk = blockIdx.x;
-  const int64_t quad = (blk >> 4) * 16 + ((blk & 7) << 1) + ((blk >> 3) & 1);
-  const int64_t w = quad * 4 + wave;
-  if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier in this kernel
-  const int64_t h = w % a.heads, rc = w / a.heads, c = rc % a.n_chunks, r = rc / a.n_chunks;
-  int64_t len = a.tokens;
-  if (a.lengths) {
-    const int64_t n = a.lengths[r];
-    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+// The eight value products of a 64-slot group: A = the codes of channel 8 n16 + b spread by
+// code_bytes (X: channels 8 n16 .. +3, Y: 8 n16 + 4 .. +7; byte j of word bt = slot j of
+// block bt), B = the weight digits bop.
+__device__ __forceinline__ void value_product(const uint32_t (&X)[4], const uint32_t (&Y)[4], const i32x4_t& bop,
+                                              i32x4_t (&cv)[8]) {
+#define KVQ_VPROD(B, SRC, K)                                                                        \
+  {                                                                                                 \
+    const i32x4_t ap = {(int32_t)code_bytes<K>(SRC[0]), (int32_t)code_bytes<K>(SRC[1]),             \
+                        (int32_t)code_bytes<K>(SRC[2]), (int32_t)code_bytes<K>(SRC[3])};            \
+    cv[B] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap, bop, cv[B], 0, 0, 0);                         \
   }
-  const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.n_sink);
-  const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
-  const int n16 = lane & 15, g = lane >> 4;
-  const int qm = n16 >> 2, qs = n16 & 3;  // head and digit of the lane's column in the value product
-  float4* const sc = &s_sc[wave][0];
-  uint32_t* const sn = &s_n[wave][0][0];
-  uint8_t* const vc = &s_vc[wave][0];
-  constexpr int SR = kMmaW + kMmaPad;
-  constexpr float kLog2e = 1.4426950408889634f;
+  KVQ_VPROD(0, X, 0)
+  KVQ_VPROD(1, X, 1)
+  KVQ_VPROD(2, X, 2)
+  KVQ_VPROD(3, X, 3)
+  KVQ_VPROD(4, Y, 0)
+  KVQ_VPROD(5, Y, 1)
+  KVQ_VPROD(6, Y, 2)
+  KVQ_VPROD(7, Y, 3)
+#undef KVQ_VPROD
+}
 
+// Query side of the key product for (row r, KV head h): A operands qa (lane (4 m + s, g),
+// product u, byte e: digit s of head m's scaled query, channel 16 (2 g + u) + 4 (e % 4) + e / 4),
+// and for the lane's key-product head g the factors of score = k_scale raw rs + k_zero zq
+// (log2 units).
+template <int QG>
+__device__ __forceinline__ void mma_query(const AttendArgs& a, int64_t r, int64_t h, int lane, i32x4_t (&qa)[2],
+                                          float& rs, float& zq) {
+  const int n16 = lane & 15, g = lane >> 4, qm = n16 >> 2, qs = n16 & 3;
+  constexpr float kLog2e = 1.4426950408889634f;
   // per-head max |q~| and sum q~ of the rotated queries
   const float* qb = a.qrot + (r * a.q_heads + h * QG) * 128;
   float qmx[4], qsum[4];
@@ -1807,7 +1815,6 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
   }
   // A operand of the key product: lane (4 m + s, g), product u, byte e holds digit s of the
   // scaled query of channel 16 (2 g + u) + 4 (e % 4) + e / 4
-  i32x4_t qa[2];
   {
     const float sqm = qm == 0 ? qsc[0] : (qm == 1 ? qsc[1] : (qm == 2 ? qsc[2] : qsc[3]));
 #pragma unroll
@@ -1835,8 +1842,38 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
   // key-product lane role: head g; score = (k_scale * raw * rs + k_zero * zq) in log2 units
   const float sc2 = a.scale * kLog2e;
   const float sqg = g == 0 ? qsc[0] : (g == 1 ? qsc[1] : (g == 2 ? qsc[2] : qsc[3]));
-  const float rs = sc2 / (16.0f * sqg);
-  const float zq = g < QG ? sc2 * (g == 0 ? qsum[0] : (g == 1 ? qsum[1] : (g == 2 ? qsum[2] : qsum[3]))) : 0.0f;
+  rs = sc2 / (16.0f * sqg);
+  zq = g < QG ? sc2 * (g == 0 ? qsum[0] : (g == 1 ? qsum[1] : (g == 2 ? qsum[2] : qsum[3]))) : 0.0f;
+}
+
+template <int QG>
+__global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) float4 s_sc[4][kMmaW];                // k scale, k zero, v scale, v zero
+  __shared__ __attribute__((aligned(16))) uint32_t s_n[4][4][kMmaW + kMmaPad];  // weight integers per head
+  __shared__ __attribute__((aligned(16))) uint8_t s_vc[4][kMmaW * 40];          // value codes, slot s at 32 s + 32 (s / 4)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t blk = blockIdx.x;
+  const int64_t quad = (blk >> 4) * 16 + ((blk & 7) << 1) + ((blk >> 3) & 1);
+  const int64_t w = quad * 4 + wave;
+  if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier in this kernel
+  const int64_t h = w % a.heads, rc = w / a.heads, c = rc % a.n_chunks, r = rc / a.n_chunks;
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.n_sink);
+  const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
+  const int n16 = lane & 15, g = lane >> 4;
+  const int qm = n16 >> 2, qs = n16 & 3;  // head and digit of the lane's column in the value product
+  float4* const sc = &s_sc[wave][0];
+  uint32_t* const sn = &s_n[wave][0][0];
+  uint8_t* const vc = &s_vc[wave][0];
+  constexpr int SR = kMmaW + kMmaPad;
+  
+  i32x4_t qa[2];
+  float rs, zq;
+  mma_query<QG>(a, r, h, lane, qa, rs, zq);
 
   i32x4_t cv[8];
   float fo[8];  // value product: channels 32 g + 8 qs + b of head qm, summed over the digits
@@ -1889,9 +1926,9 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
     const int64_t n = min((int64_t)kMmaW, t_end - w0);
     return n > 0 ? (uint32_t)(n - 1) * per_slot + tail : 0u;
   };
-  u32x4_t vq[4];
-  u32x2_t kq[8];
-  uint32_t sq[2][4];
+  u32x4_t vq[kMmaW / 32];
+  u32x2_t kq[kMmaW / 16];
+  uint32_t sq[kMmaW / 64][4];
   auto load_vs = [&](int64_t w0) __attribute__((always_inline)) {  // value codes and scales
     const int64_t vw = rh0 + w0 * a.heads;
     const uint32_t cb = win_bytes(w0, sT, 32u), sb = win_bytes(w0, sH2, 2u);
@@ -1899,12 +1936,12 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
     const buf_t bks = make_buf(a.k_scale + vw, sb), bkz = make_buf(a.k_zero + vw, sb);
     const buf_t bvs = make_buf(a.v_scale + vw, sb), bvz = make_buf(a.v_zero + vw, sb);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kMmaW / 32; ++k) {
       const uint32_t cc = (uint32_t)(lane + 64 * k);
       vq[k] = __builtin_amdgcn_raw_buffer_load_b128(bvc, (cc >> 1) * sT + 16u * (cc & 1u), 0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kMmaW / 64; ++k) {
       const uint32_t o = (uint32_t)(lane + 64 * k) * sH2;
       sq[k][0] = __builtin_amdgcn_raw_buffer_load_b16(bks, o, 0, 0);
       sq[k][1] = __builtin_amdgcn_raw_buffer_load_b16(bkz, o, 0, 0);
@@ -1916,7 +1953,7 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
     const int64_t vw = rh0 + w0 * a.heads;
     const buf_t bkc = make_buf(a.k_codes + vw * 32, win_bytes(w0, sT, 32u));
 #pragma unroll
-    for (int bk = 0; bk < 8; ++bk)
+    for (int bk = 0; bk < kMmaW / 16; ++bk)
       kq[bk] = __builtin_amdgcn_raw_buffer_load_b64(bkc, koff + (uint32_t)(16 * bk) * sT, 0, 0);
   };
   if (t_begin < t_end) {
@@ -1928,14 +1965,14 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
     // rest of a window reads zeros through the descriptors and is masked by its slot index
     float vsm = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kMmaW / 64; ++k) {
       const int i = lane + 64 * k;
       const float vs = f16_value(sq[k][2]);
       sc[i] = make_float4(f16_value(sq[k][0]), f16_value(sq[k][1]), vs, f16_value(sq[k][3]));
       vsm = fmaxf(vsm, fabsf(vs));
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kMmaW / 32; ++k) {
       const uint32_t cc = (uint32_t)(lane + 64 * k), sl = cc >> 1;
       *reinterpret_cast<u32x4_t*>(vc + 32u * sl + 32u * (sl >> 2) + 16u * (cc & 1u)) = vq[k];
     }
@@ -1943,10 +1980,10 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
     wave_lds_sync();
     // pass 1: scores of the lane's slots (head g), window maximum per head; the products of
     // 4 blocks are issued before any is read
-    float scv[8];
+    float scv[kMmaW / 16];
     float mw = -INFINITY;
 #pragma unroll
-    for (int q4 = 0; q4 < 8; q4 += 4) {
+    for (int q4 = 0; q4 < kMmaW / 16; q4 += 4) {
       i32x4_t acc[4];
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
@@ -1995,7 +2032,7 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
     // pass 1.5: weight integers p v_scale 2^E of the lane's slots, sums of p and p v_zero
     const float Mk = Mrun - (float)Ecur;  // p 2^E = exp2(s - Mk)
 #pragma unroll
-    for (int bk = 0; bk < 8; ++bk) {
+    for (int bk = 0; bk < kMmaW / 16; ++bk) {
         const int i = 16 * bk + n16;
         const float pe = __builtin_amdgcn_exp2f(scv[bk] - Mk);
         const float4 s4 = sc[i];
@@ -2006,7 +2043,7 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
     wave_lds_sync();
     // pass 2: value product per 64-slot group
 #pragma unroll
-    for (int q4 = 0; q4 < 8; q4 += 4) {
+    for (int q4 = 0; q4 < kMmaW / 16; q4 += 4) {
       {
         uint32_t D[4], X[4], Y[4];
 #pragma unroll
@@ -2027,21 +2064,7 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
           Y[bt] = __builtin_amdgcn_perm(hw, lw, 0x07050301u);  // byte j: channels 8 n16 + 4 .. +7
         }
         const i32x4_t bop = {(int32_t)D[0], (int32_t)D[1], (int32_t)D[2], (int32_t)D[3]};
-#define KVQ_VPROD(B, SRC, K)                                                                                      \
-  {                                                                                                               \
-    const i32x4_t ap = {(int32_t)code_bytes<K>(SRC[0]), (int32_t)code_bytes<K>(SRC[1]),                           \
-                        (int32_t)code_bytes<K>(SRC[2]), (int32_t)code_bytes<K>(SRC[3])};                          \
-    cv[B] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap, bop, cv[B], 0, 0, 0);                                       \
-  }
-        KVQ_VPROD(0, X, 0)
-        KVQ_VPROD(1, X, 1)
-        KVQ_VPROD(2, X, 2)
-        KVQ_VPROD(3, X, 3)
-        KVQ_VPROD(4, Y, 0)
-        KVQ_VPROD(5, Y, 1)
-        KVQ_VPROD(6, Y, 2)
-        KVQ_VPROD(7, Y, 3)
-#undef KVQ_VPROD
+        value_product(X, Y, bop, cv);
       }
     }
     wave_lds_sync();
@@ -2055,6 +2078,218 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
     float* pb = a.part + ((r * a.q_heads + h * QG + qm) * a.n_chunks + c) * kAttendPart;
 #pragma unroll
     for (int b = 0; b < 8; ++b) pb[32 * g + 8 * qs + b] = fo[b] + Zm;  // channel 32 g + 8 qs + b
+    if (qs == 0 && g == 0) {
+      pb[128] = (t_begin < t_end) ? Mm * 0.6931471805599453f : -INFINITY;
+      pb[129] = Lm;
+    }
+  }
+}
+
+// The same pass with the 4 waves of a block on 4 consecutive KV heads of one (row, chunk), for
+// caches whose head count is a multiple of 4: the block loads each window's code rows of its
+// 4 heads (128 contiguous bytes per slot and plane, whole 128-byte lines) and their scales
+// into LDS once, one window ahead, and each wave computes its head from there.  Rows of a code
+// window are padded to 136 bytes: the key reads (8 bytes, slot n16 of a block) and the value
+// reads (32-bit words, slots 4 g + j) then fall into distinct banks.
+constexpr int kRowB = 136;
+template <int QG>
+__global__ void __launch_bounds__(256) attend_partial_mma_blk(const AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_kc[kMmaW * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vc[kMmaW * kRowB];
+  __shared__ __attribute__((aligned(16))) uint16_t s_sr[4][kMmaW][4];          // (k scale, k zero, v scale, v zero), slot, head
+  __shared__ __attribute__((aligned(16))) uint32_t s_n[4][4][kMmaW + kMmaPad];  // per wave: weight integers per head
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int64_t blk = blockIdx.x;
+  const int64_t quad = (blk >> 4) * 16 + ((blk & 7) << 1) + ((blk >> 3) & 1);
+  if (quad * 4 >= a.rows * a.heads * a.n_chunks) return;  // block-uniform: the task count is a multiple of 4
+  const int64_t w = quad * 4 + wave;
+  const int64_t h = w % a.heads, rc = w / a.heads, c = rc % a.n_chunks, r = rc / a.n_chunks;
+  const int64_t h0 = h - wave;  // the block's first head (heads are a multiple of 4)
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.n_sink);
+  const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
+  const int n16 = lane & 15, g = lane >> 4;
+  const int qm = n16 >> 2, qs = n16 & 3;
+  uint32_t* const sn = &s_n[wave][0][0];
+  constexpr int SR = kMmaW + kMmaPad;
+
+  i32x4_t qa[2];
+  float rs, zq;
+  mma_query<QG>(a, r, h, lane, qa, rs, zq);
+
+  i32x4_t cv[8];
+  float fo[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    fo[b] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cv[b][j] = 0;
+  }
+  float Mrun = -INFINITY, Lp = 0.0f, Zp = 0.0f, Lf = 0.0f, Zf = 0.0f;
+  int Ecur = 0, since = 0;
+  bool first = true;
+  auto flush = [&](float corr) __attribute__((always_inline)) {
+    const float corr_m = __shfl(corr, 16 * qm);
+    const float kb = __builtin_ldexpf(1.0f, 7 * qs - Ecur);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const float k = kb * (1.0f / (float)code_mul(b & 3));
+      float add = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = (float)cv[b][j] * k;
+        v = add_x1(v);
+        v = add_x2(v);
+        add = qs == j ? v : add;
+        cv[b][j] = 0;
+      }
+      fo[b] = (fo[b] + add) * corr_m;
+    }
+    const float le = __builtin_ldexpf(1.0f, -Ecur);
+    Lf = (Lf + Lp * le) * corr;
+    Zf = (Zf + Zp * le) * corr;
+    Lp = 0.0f;
+    Zp = 0.0f;
+  };
+
+  const uint32_t sT = (uint32_t)a.heads * 32u, sH2 = (uint32_t)a.heads * 2u;
+  const int64_t rb0 = r * a.tokens * a.heads + h0;  // vector index of (row, slot 0, head h0)
+  constexpr int NU = kMmaW / 32;                    // 16-byte units per thread and plane
+  constexpr int NS = kMmaW / 64;                    // scale slots per thread
+  const int sp = tid >> 6;                          // the thread's scale plane
+  const uint16_t* const splane = sp == 0 ? a.k_scale : (sp == 1 ? a.k_zero : (sp == 2 ? a.v_scale : a.v_zero));
+  u32x4_t kq[NU], vq[NU];
+  u32x2_t sq[NS];
+  auto load_win = [&](int64_t w0) __attribute__((always_inline)) {
+    const int64_t vb = rb0 + w0 * a.heads;
+    const int64_t n = min((int64_t)kMmaW, t_end - w0);
+    const uint32_t cb = n > 0 ? (uint32_t)(n - 1) * sT + 128u : 0u, sb = n > 0 ? (uint32_t)(n - 1) * sH2 + 8u : 0u;
+    const buf_t bkc = make_buf(a.k_codes + vb * 32, cb), bvc = make_buf(a.v_codes + vb * 32, cb);
+    const buf_t bs = make_buf(splane + vb, sb);
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const uint32_t u = (uint32_t)(tid + 256 * k);  // slot u / 8, bytes 16 (u % 8) of the 4 heads' 128
+      const uint32_t off = (u >> 3) * sT + 16u * (u & 7u);
+      kq[k] = __builtin_amdgcn_raw_buffer_load_b128(bkc, off, 0, 0);
+      vq[k] = __builtin_amdgcn_raw_buffer_load_b128(bvc, off, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < NS; ++e) sq[e] = __builtin_amdgcn_raw_buffer_load_b64(bs, (uint32_t)(NS * (tid & 63) + e) * sH2, 0, 0);
+  };
+  const uint32_t vsel = (n16 & 1) ? 0x07060302u : 0x05040100u;  // the lane's 16-bit half of two words
+  if (t_begin < t_end) load_win(t_begin);
+  for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += kMmaW) {
+    const int nv = (int)min((int64_t)kMmaW, t_end - wt0);
+    __syncthreads();  // every wave is done with the previous window's LDS
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const uint32_t u = (uint32_t)(tid + 256 * k), o = (u >> 3) * kRowB + 16u * (u & 7u);
+      *reinterpret_cast<u32x2_t*>(s_kc + o) = u32x2_t{kq[k].x, kq[k].y};
+      *reinterpret_cast<u32x2_t*>(s_kc + o + 8) = u32x2_t{kq[k].z, kq[k].w};
+      *reinterpret_cast<u32x2_t*>(s_vc + o) = u32x2_t{vq[k].x, vq[k].y};
+      *reinterpret_cast<u32x2_t*>(s_vc + o + 8) = u32x2_t{vq[k].z, vq[k].w};
+    }
+#pragma unroll
+    for (int e = 0; e < NS; ++e) *reinterpret_cast<u32x2_t*>(&s_sr[sp][NS * (tid & 63) + e][0]) = sq[e];
+    __syncthreads();
+    load_win(wt0 + kMmaW);
+    float vsm = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) vsm = fmaxf(vsm, fabsf(f16_value(s_sr[2][lane + 64 * k][wave])));
+    // pass 1: key product from LDS
+    float scv[kMmaW / 16];
+    float mw = -INFINITY;
+#pragma unroll
+    for (int q4 = 0; q4 < kMmaW / 16; q4 += 4) {
+      u32x2_t kv[4];
+      i32x4_t acc[4];
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        kv[bt] = *reinterpret_cast<const u32x2_t*>(s_kc + (16 * (q4 + bt) + n16) * kRowB + 32 * wave + 8 * g);
+        const i32x4_t b0 = {(int32_t)code_bytes<0>(kv[bt].x), (int32_t)code_bytes<1>(kv[bt].x),
+                            (int32_t)code_bytes<2>(kv[bt].x), (int32_t)code_bytes<3>(kv[bt].x)};
+        acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], b0, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const i32x4_t b1 = {(int32_t)code_bytes<0>(kv[bt].y), (int32_t)code_bytes<1>(kv[bt].y),
+                            (int32_t)code_bytes<2>(kv[bt].y), (int32_t)code_bytes<3>(kv[bt].y)};
+        acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], b1, acc[bt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int i = 16 * (q4 + bt) + n16;
+        const float raw = __builtin_fmaf((float)acc[bt][3], 16777216.0f,
+                                         __builtin_fmaf((float)acc[bt][2], 65536.0f,
+                                                        __builtin_fmaf((float)acc[bt][1], 256.0f, (float)acc[bt][0])));
+        const float sco = __builtin_fmaf(f16_value(s_sr[0][i][wave]) * raw, rs, f16_value(s_sr[1][i][wave]) * zq);
+        scv[q4 + bt] = i < nv ? sco : -INFINITY;
+        mw = fmaxf(mw, scv[q4 + bt]);
+      }
+    }
+    mw = row_max16(mw);
+    vsm = row_max16(vsm);
+    vsm = fmaxf(fmaxf(row_value(vsm, 0), row_value(vsm, 1)), fmaxf(row_value(vsm, 2), row_value(vsm, 3)));
+    int ex;
+    (void)__builtin_frexpf(vsm, &ex);
+    const int Ew = 27 - ex;
+    const float Mnew = fmaxf(Mrun, mw);
+    const bool grow = __builtin_amdgcn_ballot_w64(Mnew > Mrun) != 0;
+    if (grow || first || Ew < Ecur || since >= 1024) {  // wave-uniform
+      flush(__builtin_amdgcn_exp2f(Mrun - Mnew));
+      Mrun = Mnew;
+      Ecur = Ew;
+      since = 0;
+      first = false;
+    }
+    ++since;
+    // pass 1.5: weight integers of the lane's slots
+    const float Mk = Mrun - (float)Ecur;
+#pragma unroll
+    for (int bk = 0; bk < kMmaW / 16; ++bk) {
+      const int i = 16 * bk + n16;
+      const float pe = __builtin_amdgcn_exp2f(scv[bk] - Mk);
+      Lp += pe;
+      Zp = __builtin_fmaf(pe, f16_value(s_sr[3][i][wave]), Zp);
+      sn[g * SR + i] = (uint32_t)__builtin_fmaf(pe, f16_value(s_sr[2][i][wave]), 0.5f);
+    }
+    wave_lds_sync();
+    // pass 2: value product per 64-slot group
+#pragma unroll
+    for (int q4 = 0; q4 < kMmaW / 16; q4 += 4) {
+      uint32_t D[4], X[4], Y[4];
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int i0 = 16 * (q4 + bt) + 4 * g;
+        const u32x4_t nw = *reinterpret_cast<const u32x4_t*>(&sn[qm * SR + i0]);
+        const uint32_t sh = 7u * (uint32_t)qs;
+        D[bt] = ((nw.x >> sh) & 0x7fu) | (((nw.y >> sh) & 0x7fu) << 8) | (((nw.z >> sh) & 0x7fu) << 16) |
+                (((nw.w >> sh) & 0x7fu) << 24);
+        const uint8_t* p0 = s_vc + i0 * kRowB + 32 * wave + 4 * (n16 >> 1);
+        const uint32_t d0 = *reinterpret_cast<const uint32_t*>(p0), d1 = *reinterpret_cast<const uint32_t*>(p0 + kRowB);
+        const uint32_t d2 = *reinterpret_cast<const uint32_t*>(p0 + 2 * kRowB),
+                       d3 = *reinterpret_cast<const uint32_t*>(p0 + 3 * kRowB);
+        const uint32_t lw = __builtin_amdgcn_perm(d1, d0, vsel), hw = __builtin_amdgcn_perm(d3, d2, vsel);
+        X[bt] = __builtin_amdgcn_perm(hw, lw, 0x06040200u);
+        Y[bt] = __builtin_amdgcn_perm(hw, lw, 0x07050301u);
+      }
+      const i32x4_t bop = {(int32_t)D[0], (int32_t)D[1], (int32_t)D[2], (int32_t)D[3]};
+      value_product(X, Y, bop, cv);
+    }
+  }
+  if (t_begin < t_end) flush(1.0f);
+  Lf = row_sum16(Lf);
+  Zf = row_sum16(Zf);
+  const float Lm = __shfl(Lf, 16 * qm), Zm = __shfl(Zf, 16 * qm), Mm = __shfl(Mrun, 16 * qm);
+  if (qm < QG) {
+    float* pb = a.part + ((r * a.q_heads + h * QG + qm) * a.n_chunks + c) * kAttendPart;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) pb[32 * g + 8 * qs + b] = fo[b] + Zm;
     if (qs == 0 && g == 0) {
       pb[128] = (t_begin < t_end) ? Mm * 0.6931471805599453f : -INFINITY;
       pb[129] = Lm;
@@ -2323,7 +2558,12 @@ int launch_attend_t(const AttendArgs& a, hipStream_t s) {
     // whole groups of 16 blocks, so the XCD-aware order maps the blocks onto every task
     const int64_t nb = ((np + 3) / 4 + 15) / 16 * 16;
     if (nb > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attend_partial_mma<QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    const uintptr_t al = (uintptr_t)a.k_codes | (uintptr_t)a.v_codes | (uintptr_t)a.k_scale | (uintptr_t)a.k_zero |
+                         (uintptr_t)a.v_scale | (uintptr_t)a.v_zero;
+    if (a.heads % 4 == 0 && (al & 7) == 0)
+      hipLaunchKernelGGL((attend_partial_mma_blk<QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attend_partial_mma<QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
   } else
 #endif
     hipLaunchKernelGGL((attend_partial<BITS, QG>), dim3((unsigned)((np + 3) / 4)), dim3(256), 0, s, a);

@@ -47,18 +47,21 @@ def _case(r, t, h, bits, g, rope, use_perm, n_sink, name):
                                 quant="minmax", rot="fwht", rope=rope, n_sink=n_sink, use_perm=use_perm)
 
 
-@pytest.mark.parametrize("qg,bits,g,n_sink,perm_v", [
-    (4, 2, 128, 4, False),   # Llama-3 shape of K and V, reduced
-    (1, 2, 64, 0, True),
-    (2, 4, 32, 3, False),
-    (4, 4, 64, 0, True),
-    (2, 2, 32, 4, True),
-    (1, 2, 128, 0, True),    # matrix-core partial pass with one and two query heads per KV head
-    (2, 2, 128, 2, False),
+@pytest.mark.parametrize("qg,bits,g,n_sink,perm_v,h", [
+    (4, 2, 128, 4, False, 3),   # Llama-3 shape of K and V, reduced
+    (1, 2, 64, 0, True, 3),
+    (2, 4, 32, 3, False, 3),
+    (4, 4, 64, 0, True, 3),
+    (2, 2, 32, 4, True, 3),
+    (1, 2, 128, 0, True, 3),    # matrix-core partial pass with one and two query heads per KV head
+    (2, 2, 128, 2, False, 3),
+    (4, 2, 128, 4, False, 8),   # block-cooperative matrix-core pass (KV heads a multiple of 4)
+    (1, 2, 128, 0, True, 4),
+    (2, 2, 128, 2, False, 4),
 ])
-def test_attend_small(qg, bits, g, n_sink, perm_v):
-    r, t, h = 5, 203, 3
-    seed = 500 + 10 * qg + bits + g + n_sink + (7 if perm_v else 0)
+def test_attend_small(qg, bits, g, n_sink, perm_v, h):
+    r, t = 5, 203
+    seed = 500 + 10 * qg + bits + g + n_sink + (7 if perm_v else 0) + 1000 * (h - 3)
     ck = _case(r, t, h, bits, g, True, True, n_sink, "K")
     cv = _case(r, t, h, bits, g, False, perm_v, n_sink, "V")
     dk = workloads.synth_case(ck, seed)
@@ -121,6 +124,42 @@ def test_attend_llama3_cache_full_size():
         e = _compare(out[row:row + 1], ref, vmax, f"llama3 row {row} len {int(ln[0])}")
         say(f"  row {row} len {int(ln[0])}: max |err| {e:.3g}")
 
+
+
+@pytest.mark.parametrize("h", [6, 8])
+def test_attend_several_windows_per_chunk(h):
+    """A cache with enough rows that each chunk spans two windows of the matrix-core pass (the
+    second one partial), for the per-wave pass (6 KV heads) and the block-cooperative one (8):
+    inputs drawn on the GPU, sampled rows checked against the oracle."""
+    r, t = 96, 4096
+    seed = 7100 + h
+    ck = _case(r, t, h, 2, 128, True, True, 4, "K")
+    cv = _case(r, t, h, 2, 128, False, False, 4, "V")
+    perm = np.random.default_rng(seed).permutation(128).astype(np.int64)
+    cfg_k, cfg_v = gu.make_config(ck, perm), gu.make_config(cv, None)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    xk = torch.randn((r, t, h, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    xv = torch.randn((r, t, h, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    pk_t, pv_t = kvq.encode(xk, cfg_k), kvq.encode(xv, cfg_v)
+    del xk, xv
+    rng = np.random.default_rng(seed + 1)
+    q = rng.standard_normal((r, 4 * h, 128)).astype(np.float32)
+    lengths = rng.integers(1, t + 1, size=r).astype(np.int32)
+    lengths[:2] = [t, 1000]
+    say(f"[case] attend two windows per chunk: {r} x {t} x {h} heads")
+    out = kvq.attend(torch.from_numpy(q).cuda(), pk_t, cfg_k, pv_t, cfg_v, lengths=torch.from_numpy(lengths).cuda())
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    pk, pv = parity.params_for(ck, perm), parity.params_for(cv, None)
+    for row in (0, 1, 50):
+        one = lambda pl: {k: gu.planes_numpy({k: v[row:row + 1]})[k] for k, v in pl.items()}
+        kdec = oracle.decode(one(pk_t), pk, (1, t, h, 128))
+        vdec = oracle.decode(one(pv_t), pv, (1, t, h, 128))
+        ln = lengths[row:row + 1]
+        ref = oracle.attend_decoded(q[row:row + 1].astype(np.float64), kdec, vdec, ln, 128 ** -0.5)
+        vmax = np.array([np.abs(vdec[0, :int(ln[0])]).max()])
+        e = _compare(out[row:row + 1], ref, vmax, f"two windows row {row} len {int(ln[0])}")
+        say(f"  row {row} len {int(ln[0])}: max |err| {e:.3g}")
 
 @pytest.mark.parametrize("t,h,qg,n_sink,lengths", [
     (5, 1, 1, 0, [7, -3, 5, 2]),      # fewer slots than one step; lengths past the cache and negative
