@@ -161,7 +161,10 @@ kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* posit
  * the keys' permutation P, q . k_t = (M P q) . y_t for the stored y_t = zero + code * scale,
  * and the values are summed in the rotated domain and rotated back once per output (the
  * rotation of the RotateKV page, whose decode-stage speed-up this serves).  Sink slots are
- * read from the fp16 sink planes.
+ * read from the fp16 sink planes.  Scores and sums are fp32; for 2-bit codes with one group
+ * of 128 channels the products run exactly on the int8 matrix cores, with the rotated query
+ * rounded to 2^-31 of 16 times its largest element and each softmax weight to 2^-27 of the
+ * largest weight x value scale of its 128-slot window.
  *   cfg_k, cfg_v  the K and V caches: same rows R, slots T, heads H, head_dim 128, bits
  *                 (2 or 4), group (32, 64 or 128), n_sink (at most 64), Walsh-Hadamard and
  *                 min-max, pos_offset 0 (slot t holds position t); each its own permutation
