@@ -272,12 +272,12 @@ def main():
     oa = torch.empty_like(qa)
     wsa = torch.empty(kvq.attend_workspace_size(cfgs["K"], q_heads), dtype=torch.uint8, device=dev)
     with torch.cuda.stream(stream):
-        for _ in range(2):
+        for _ in range(3):
             kvq.attend(qa, planes["K"], cfgs["K"], planes["V"], cfgs["V"], out=oa, workspace=wsa, stream=stream)
         stream.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        n_rep = 10
+        n_rep = 30
         a.record(stream)
         for _ in range(n_rep):
             kvq.attend(qa, planes["K"], cfgs["K"], planes["V"], cfgs["V"], out=oa, workspace=wsa, stream=stream)

@@ -165,6 +165,9 @@ def test_attend_several_windows_per_chunk(h):
     (5, 1, 1, 0, [7, -3, 5, 2]),      # fewer slots than one step; lengths past the cache and negative
     (5, 2, 2, 6, [5, 3, 0, 9]),       # every slot a sink
     (9, 1, 4, 1, [9, 8, 1, 2]),       # one step plus one slot
+    (5, 4, 1, 0, [7, -3, 5, 2]),      # the same on the block-cooperative matrix-core pass (4 KV heads)
+    (9, 4, 4, 1, [9, 8, 1, 2]),
+    (5, 8, 2, 6, [5, 3, 0, 9]),
 ])
 def test_attend_edge_shapes(t, h, qg, n_sink, lengths):
     r = len(lengths)
