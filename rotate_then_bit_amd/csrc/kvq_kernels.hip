@@ -1706,12 +1706,14 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
 //    a power of two, divided by mul and rounded to a 31-bit integer, cut into four signed
 //    8-bit digits (rows 4 m + s of the A operand), so one 16x16x64 product per 64 channels
 //    gives per digit the integer dot product of 16 slots, recombined in fp32;
-//  * values: the softmax weights p * scale_v of a window, relative to the window's exact
-//    maximum (a first pass scores the window into LDS), are scaled by a power of two to at
-//    most 2^27 and cut into four 7-bit digits (columns 4 m + s of the B operand); the value
-//    codes of 64 slots, transposed through 16-bit loads and byte permutes, are the A
-//    operand.  The integer sums are turned into floats when the running maximum or the
-//    weight scale changes, and at the end of the chunk.
+//  * values: per window of slots, the key pass scores every slot first (the scores stay in
+//    registers) and updates the running maximum; then each lane turns its own slots' weights
+//    p * scale_v, relative to that maximum and scaled by a power of two to at most 2^27, into
+//    integers in LDS, which the value product reads as four signed 8-bit digits (columns 4 m + s
+//    of the B operand); the value codes of 64 slots, staged in LDS and read back transposed
+//    (16-bit halves regrouped by byte permutes), are the A operand.  The integer sums are
+//    turned into floats when the running maximum or the weight scale changes, every 1024
+//    windows (int32 headroom), and at the end of the chunk.
 // Lanes: n16 = lane % 16 and g = lane / 16 as in the operand layouts; in the key product
 // lane (n16, g) holds slot n16 of a 16-slot block for head g; in the value product lane
 // (4 m + s, g) holds digit s of head m for channels 32 g + 8 j + b (register j, product b).
@@ -1721,7 +1723,7 @@ typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 #define KVQ_MMA_W 128
 #endif
 constexpr int kMmaW = KVQ_MMA_W;  // slots per window (a multiple of 64)
-constexpr int kMmaPad = 16;  // padding of the LDS score rows (banks of the row writes)
+constexpr int kMmaPad = 16;  // padding of the LDS weight-integer rows (banks of the row writes)
 template <int K>
 __device__ __forceinline__ uint32_t code_bytes(uint32_t x) {  // code 4 b + K of byte b, times code_mul(K)
   if constexpr (K < 3) return x & (0x03030303u << (2 * K));
@@ -1763,6 +1765,11 @@ __device__ __forceinline__ float row_sum16(float v) {
 __device__ __forceinline__ float row_value(float v, int m) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * m));
 }
+
+// A weight integer N < 2^27 as four balanced signed 8-bit digits, one per byte:
+// N = sum_s d_s 256^s with d_0..d_2 in [-128, 127] (bytes of N + 0x808080, minus 128) and
+// d_3 = (N + 0x808080) >> 24 in [0, 8].
+__device__ __forceinline__ uint32_t weight_digits(uint32_t n) { return (n + 0x808080u) ^ 0x808080u; }
 
 // The eight value products of a 64-slot group: A = the codes of channel 8 n16 + b spread by
 // code_bytes (X: channels 8 n16 .. +3, Y: 8 n16 + 4 .. +7; byte j of word bt = slot j of
@@ -1891,7 +1898,7 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
   // integer sums to floats: weight each digit, sum the 4 digit lanes, keep register j = qs
   auto flush = [&](float corr) __attribute__((always_inline)) {
     const float corr_m = __shfl(corr, 16 * qm);  // the factor of head qm
-    const float kb = __builtin_ldexpf(1.0f, 7 * qs - Ecur);
+    const float kb = __builtin_ldexpf(1.0f, 8 * qs - Ecur);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const float k = kb * (1.0f / (float)code_mul(b & 3));
@@ -1918,6 +1925,7 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
   const int64_t rh0 = r * a.tokens * a.heads + h;
   const uint32_t koff = (uint32_t)n16 * sT + 8u * (uint32_t)g;   // key-code bytes of the lane in a block
   const uint32_t vrd = 160u * (uint32_t)g + 2u * (uint32_t)n16;  // LDS value codes: slot 4 g, bytes 2 n16
+  const uint32_t dsel = (uint32_t)qs | ((uint32_t)qs + 4u) << 8;  // byte qs of two words -> bytes 0, 1
   // Loads of a window (value codes, scales, key codes) are issued one window ahead: the value
   // codes and scales of window w + 1 after window w's are staged in LDS, its key codes after
   // window w's key product.  Descriptors cover the valid slots of the window they serve; a
@@ -2038,7 +2046,7 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
         const float4 s4 = sc[i];
         Lp += pe;
         Zp = __builtin_fmaf(pe, s4.w, Zp);
-        sn[g * SR + i] = (uint32_t)__builtin_fmaf(pe, s4.z, 0.5f);
+        sn[g * SR + i] = weight_digits((uint32_t)__builtin_fmaf(pe, s4.z, 0.5f));
       }
     wave_lds_sync();
     // pass 2: value product per 64-slot group
@@ -2050,9 +2058,8 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
         for (int bt = 0; bt < 4; ++bt) {
           const int i0 = 16 * (q4 + bt) + 4 * g;  // window slot of the lane's 4 slots
           const u32x4_t nw = *reinterpret_cast<const u32x4_t*>(&sn[qm * SR + i0]);
-          const uint32_t sh = 7u * (uint32_t)qs;
-          D[bt] = ((nw.x >> sh) & 0x7fu) | (((nw.y >> sh) & 0x7fu) << 8) | (((nw.z >> sh) & 0x7fu) << 16) |
-                  (((nw.w >> sh) & 0x7fu) << 24);
+          D[bt] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(nw.w, nw.z, dsel), __builtin_amdgcn_perm(nw.y, nw.x, dsel),
+                                        0x05040100u);  // byte j: digit qs of slot i0 + j
           const uint8_t* p0 = vc + vrd + 640u * (uint32_t)(q4 + bt);
           u16x2_t lo, hi;
           lo[0] = *reinterpret_cast<const uint16_t*>(p0);
@@ -2137,7 +2144,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
   bool first = true;
   auto flush = [&](float corr) __attribute__((always_inline)) {
     const float corr_m = __shfl(corr, 16 * qm);
-    const float kb = __builtin_ldexpf(1.0f, 7 * qs - Ecur);
+    const float kb = __builtin_ldexpf(1.0f, 8 * qs - Ecur);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const float k = kb * (1.0f / (float)code_mul(b & 3));
@@ -2184,6 +2191,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     for (int e = 0; e < NS; ++e) sq[e] = __builtin_amdgcn_raw_buffer_load_b64(bs, (uint32_t)(NS * (tid & 63) + e) * sH2, 0, 0);
   };
   const uint32_t vsel = (n16 & 1) ? 0x07060302u : 0x05040100u;  // the lane's 16-bit half of two words
+  const uint32_t dsel = (uint32_t)qs | ((uint32_t)qs + 4u) << 8;  // byte qs of two words -> bytes 0, 1
   if (t_begin < t_end) load_win(t_begin);
   for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += kMmaW) {
     const int nv = (int)min((int64_t)kMmaW, t_end - wt0);
@@ -2258,7 +2266,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
       const float pe = __builtin_amdgcn_exp2f(scv[bk] - Mk);
       Lp += pe;
       Zp = __builtin_fmaf(pe, f16_value(s_sr[3][i][wave]), Zp);
-      sn[g * SR + i] = (uint32_t)__builtin_fmaf(pe, f16_value(s_sr[2][i][wave]), 0.5f);
+      sn[g * SR + i] = weight_digits((uint32_t)__builtin_fmaf(pe, f16_value(s_sr[2][i][wave]), 0.5f));
     }
     wave_lds_sync();
     // pass 2: value product per 64-slot group
@@ -2269,9 +2277,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
       for (int bt = 0; bt < 4; ++bt) {
         const int i0 = 16 * (q4 + bt) + 4 * g;
         const u32x4_t nw = *reinterpret_cast<const u32x4_t*>(&sn[qm * SR + i0]);
-        const uint32_t sh = 7u * (uint32_t)qs;
-        D[bt] = ((nw.x >> sh) & 0x7fu) | (((nw.y >> sh) & 0x7fu) << 8) | (((nw.z >> sh) & 0x7fu) << 16) |
-                (((nw.w >> sh) & 0x7fu) << 24);
+        D[bt] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(nw.w, nw.z, dsel), __builtin_amdgcn_perm(nw.y, nw.x, dsel),
+                                      0x05040100u);  // byte j: digit qs of slot i0 + j
         const uint8_t* p0 = s_vc + i0 * kRowB + 32 * wave + 4 * (n16 >> 1);
         const uint32_t d0 = *reinterpret_cast<const uint32_t*>(p0), d1 = *reinterpret_cast<const uint32_t*>(p0 + kRowB);
         const uint32_t d2 = *reinterpret_cast<const uint32_t*>(p0 + 2 * kRowB),
