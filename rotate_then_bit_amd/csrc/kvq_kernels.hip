@@ -1797,7 +1797,7 @@ __device__ __forceinline__ void value_product(const uint32_t (&X)[4], const uint
 // product u, byte e: digit s of head m's scaled query, channel 16 (2 g + u) + 4 (e % 4) + e / 4),
 // and for the lane's key-product head g the factors of score = k_scale raw rs + k_zero zq
 // (log2 units).
-template <int QG>
+template <int QG, int BITS = 2>
 __device__ __forceinline__ void mma_query(const AttendArgs& a, int64_t r, int64_t h, int lane, i32x4_t (&qa)[2],
                                           float& rs, float& zq) {
   const int n16 = lane & 15, g = lane >> 4, qm = n16 >> 2, qs = n16 & 3;
@@ -1827,6 +1827,8 @@ __device__ __forceinline__ void mma_query(const AttendArgs& a, int64_t r, int64_
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float qv[16];
+      // the 16 channels of product u in lane group g: 2-bit, 16 (2 g + u) + 4 (e % 4) + e / 4;
+      // 4-bit, 32 g + 16 u + 8 (e / 8) + 2 (e % 4) + (e / 4) % 2
       const float* src = qb + qm * 128 + 16 * (2 * g + u);
 #pragma unroll
       for (int i = 0; i < 16; ++i) qv[i] = qm < QG ? src[i] : 0.0f;
@@ -1835,8 +1837,10 @@ __device__ __forceinline__ void mma_query(const AttendArgs& a, int64_t r, int64_
         uint32_t word = 0;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const int e = 4 * d + bb;  // byte e of the operand: code 4 (e % 4) + e / 4 of the word
-          const int32_t Q = (int32_t)__builtin_rintf(qv[4 * (e & 3) + (e >> 2)] * (float)(16 / code_mul(e >> 2)) * sqm);
+          const int e = 4 * d + bb;
+          const int ci = BITS == 2 ? 4 * (e & 3) + (e >> 2) : 8 * (e >> 3) + 2 * (e & 3) + ((e >> 2) & 1);
+          const float mul = BITS == 2 ? (float)(16 / code_mul(e >> 2)) : 16.0f;
+          const int32_t Q = (int32_t)__builtin_rintf(qv[ci] * mul * sqm);
           // balanced base-256 digits: T = Q + 0x808080, digit s = byte s of T - 128 (s < 3), T >> 24 (s = 3)
           const int32_t T = Q + 0x808080;
           const uint32_t byte = ((uint32_t)(T >> (8 * qs)) & 0xffu) ^ (qs < 3 ? 0x80u : 0u);
@@ -2098,15 +2102,21 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
 // into LDS once, one window ahead, and each wave computes its head from there.  Rows of a code
 // window are padded to 136 bytes: the key reads (8 bytes, slot n16 of a block) and the value
 // reads (32-bit words, slots 4 g + j) then fall into distinct banks.
-constexpr int kRowB = 136;
+// Per code width: code bytes per head and slot, slots per window, LDS bytes per slot row.
+template <int BITS> struct BlkGeo {
+  static constexpr int CB = 16 * BITS;
+  static constexpr int W = BITS == 2 ? kMmaW : 64;
+  static constexpr int ROWB = BITS == 2 ? 136 : 272;
+};
 // (at most 168 VGPRs: 3 waves per SIMD measured 9 % faster than 2 at 232; its two spills are
 // outside the window loop)
-template <int QG>
+template <int BITS, int QG>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) attend_partial_mma_blk(const AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_kc[kMmaW * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vc[kMmaW * kRowB];
-  __shared__ __attribute__((aligned(16))) uint16_t s_sr[4][kMmaW][4];          // (k scale, k zero, v scale, v zero), slot, head
-  __shared__ __attribute__((aligned(16))) uint32_t s_n[4][4][kMmaW + kMmaPad];  // per wave: weight integers per head
+  constexpr int CB = BlkGeo<BITS>::CB, WN = BlkGeo<BITS>::W, kRowB = BlkGeo<BITS>::ROWB;
+  __shared__ __attribute__((aligned(16))) uint8_t s_kc[WN * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vc[WN * kRowB];
+  __shared__ __attribute__((aligned(16))) uint16_t s_sr[4][WN][4];          // (k scale, k zero, v scale, v zero), slot, head
+  __shared__ __attribute__((aligned(16))) uint32_t s_n[4][4][WN + kMmaPad];  // per wave: weight integers per head
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t blk = blockIdx.x;
@@ -2125,11 +2135,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
   const int n16 = lane & 15, g = lane >> 4;
   const int qm = n16 >> 2, qs = n16 & 3;
   uint32_t* const sn = &s_n[wave][0][0];
-  constexpr int SR = kMmaW + kMmaPad;
+  constexpr int SR = WN + kMmaPad;
 
   i32x4_t qa[2];
   float rs, zq;
-  mma_query<QG>(a, r, h, lane, qa, rs, zq);
+  mma_query<QG, BITS>(a, r, h, lane, qa, rs, zq);
 
   i32x4_t cv[8];
   float fo[8];
@@ -2147,7 +2157,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     const float kb = __builtin_ldexpf(1.0f, 8 * qs - Ecur);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const float k = kb * (1.0f / (float)code_mul(b & 3));
+      const float k = BITS == 2 ? kb * (1.0f / (float)code_mul(b & 3)) : kb;
       float add = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -2166,24 +2176,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     Zp = 0.0f;
   };
 
-  const uint32_t sT = (uint32_t)a.heads * 32u, sH2 = (uint32_t)a.heads * 2u;
+  const uint32_t sT = (uint32_t)a.heads * (uint32_t)CB, sH2 = (uint32_t)a.heads * 2u;
   const int64_t rb0 = r * a.tokens * a.heads + h0;  // vector index of (row, slot 0, head h0)
-  constexpr int NU = kMmaW / 32;                    // 16-byte units per thread and plane
-  constexpr int NS = kMmaW / 64;                    // scale slots per thread
+  constexpr int UPS = CB / 4;                       // 16-byte units per slot (4 heads)
+  constexpr int NU = WN * UPS / 256;                // 16-byte units per thread and plane
+  constexpr int NS = WN / 64;                       // scale slots per thread
   const int sp = tid >> 6;                          // the thread's scale plane
   const uint16_t* const splane = sp == 0 ? a.k_scale : (sp == 1 ? a.k_zero : (sp == 2 ? a.v_scale : a.v_zero));
   u32x4_t kq[NU], vq[NU];
   u32x2_t sq[NS];
   auto load_win = [&](int64_t w0) __attribute__((always_inline)) {
     const int64_t vb = rb0 + w0 * a.heads;
-    const int64_t n = min((int64_t)kMmaW, t_end - w0);
-    const uint32_t cb = n > 0 ? (uint32_t)(n - 1) * sT + 128u : 0u, sb = n > 0 ? (uint32_t)(n - 1) * sH2 + 8u : 0u;
-    const buf_t bkc = make_buf(a.k_codes + vb * 32, cb), bvc = make_buf(a.v_codes + vb * 32, cb);
+    const int64_t n = min((int64_t)WN, t_end - w0);
+    const uint32_t cb = n > 0 ? (uint32_t)(n - 1) * sT + 4u * CB : 0u, sb = n > 0 ? (uint32_t)(n - 1) * sH2 + 8u : 0u;
+    const buf_t bkc = make_buf(a.k_codes + vb * CB, cb), bvc = make_buf(a.v_codes + vb * CB, cb);
     const buf_t bs = make_buf(splane + vb, sb);
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-      const uint32_t u = (uint32_t)(tid + 256 * k);  // slot u / 8, bytes 16 (u % 8) of the 4 heads' 128
-      const uint32_t off = (u >> 3) * sT + 16u * (u & 7u);
+      const uint32_t u = (uint32_t)(tid + 256 * k);  // slot u / UPS, bytes 16 (u % UPS) of the 4 heads' row
+      const uint32_t off = (u / UPS) * sT + 16u * (u % UPS);
       kq[k] = __builtin_amdgcn_raw_buffer_load_b128(bkc, off, 0, 0);
       vq[k] = __builtin_amdgcn_raw_buffer_load_b128(bvc, off, 0, 0);
     }
@@ -2193,12 +2204,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
   const uint32_t vsel = (n16 & 1) ? 0x07060302u : 0x05040100u;  // the lane's 16-bit half of two words
   const uint32_t dsel = (uint32_t)qs | ((uint32_t)qs + 4u) << 8;  // byte qs of two words -> bytes 0, 1
   if (t_begin < t_end) load_win(t_begin);
-  for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += kMmaW) {
-    const int nv = (int)min((int64_t)kMmaW, t_end - wt0);
+  for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += WN) {
+    const int nv = (int)min((int64_t)WN, t_end - wt0);
     __syncthreads();  // every wave is done with the previous window's LDS
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-      const uint32_t u = (uint32_t)(tid + 256 * k), o = (u >> 3) * kRowB + 16u * (u & 7u);
+      const uint32_t u = (uint32_t)(tid + 256 * k), o = (u / UPS) * kRowB + 16u * (u % UPS);
       *reinterpret_cast<u32x2_t*>(s_kc + o) = u32x2_t{kq[k].x, kq[k].y};
       *reinterpret_cast<u32x2_t*>(s_kc + o + 8) = u32x2_t{kq[k].z, kq[k].w};
       *reinterpret_cast<u32x2_t*>(s_vc + o) = u32x2_t{vq[k].x, vq[k].y};
@@ -2207,29 +2218,46 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
 #pragma unroll
     for (int e = 0; e < NS; ++e) *reinterpret_cast<u32x2_t*>(&s_sr[sp][NS * (tid & 63) + e][0]) = sq[e];
     __syncthreads();
-    load_win(wt0 + kMmaW);
+    load_win(wt0 + WN);
     float vsm = 0.0f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) vsm = fmaxf(vsm, fabsf(f16_value(s_sr[2][lane + 64 * k][wave])));
     // pass 1: key product from LDS
-    float scv[kMmaW / 16];
+    float scv[WN / 16];
     float mw = -INFINITY;
 #pragma unroll
-    for (int q4 = 0; q4 < kMmaW / 16; q4 += 4) {
-      u32x2_t kv[4];
+    for (int q4 = 0; q4 < WN / 16; q4 += 4) {
       i32x4_t acc[4];
+      if constexpr (BITS == 2) {
+        u32x2_t kv[4];
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        kv[bt] = *reinterpret_cast<const u32x2_t*>(s_kc + (16 * (q4 + bt) + n16) * kRowB + 32 * wave + 8 * g);
-        const i32x4_t b0 = {(int32_t)code_bytes<0>(kv[bt].x), (int32_t)code_bytes<1>(kv[bt].x),
-                            (int32_t)code_bytes<2>(kv[bt].x), (int32_t)code_bytes<3>(kv[bt].x)};
-        acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], b0, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
-      }
+        for (int bt = 0; bt < 4; ++bt) {
+          kv[bt] = *reinterpret_cast<const u32x2_t*>(s_kc + (16 * (q4 + bt) + n16) * kRowB + CB * wave + 8 * g);
+          const i32x4_t b0 = {(int32_t)code_bytes<0>(kv[bt].x), (int32_t)code_bytes<1>(kv[bt].x),
+                              (int32_t)code_bytes<2>(kv[bt].x), (int32_t)code_bytes<3>(kv[bt].x)};
+          acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], b0, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+        }
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        const i32x4_t b1 = {(int32_t)code_bytes<0>(kv[bt].y), (int32_t)code_bytes<1>(kv[bt].y),
-                            (int32_t)code_bytes<2>(kv[bt].y), (int32_t)code_bytes<3>(kv[bt].y)};
-        acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], b1, acc[bt], 0, 0, 0);
+        for (int bt = 0; bt < 4; ++bt) {
+          const i32x4_t b1 = {(int32_t)code_bytes<0>(kv[bt].y), (int32_t)code_bytes<1>(kv[bt].y),
+                              (int32_t)code_bytes<2>(kv[bt].y), (int32_t)code_bytes<3>(kv[bt].y)};
+          acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], b1, acc[bt], 0, 0, 0);
+        }
+      } else {  // 4-bit: a word's codes 2 b (low nibbles) and 2 b + 1 (high nibbles)
+        u32x4_t kv[4];
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+          kv[bt] = *reinterpret_cast<const u32x4_t*>(s_kc + (16 * (q4 + bt) + n16) * kRowB + CB * wave + 16 * g);
+          const i32x4_t b0 = {(int32_t)(kv[bt].x & 0x0F0F0F0Fu), (int32_t)((kv[bt].x >> 4) & 0x0F0F0F0Fu),
+                              (int32_t)(kv[bt].y & 0x0F0F0F0Fu), (int32_t)((kv[bt].y >> 4) & 0x0F0F0F0Fu)};
+          acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], b0, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+          const i32x4_t b1 = {(int32_t)(kv[bt].z & 0x0F0F0F0Fu), (int32_t)((kv[bt].z >> 4) & 0x0F0F0F0Fu),
+                              (int32_t)(kv[bt].w & 0x0F0F0F0Fu), (int32_t)((kv[bt].w >> 4) & 0x0F0F0F0Fu)};
+          acc[bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], b1, acc[bt], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
@@ -2261,7 +2289,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     // pass 1.5: weight integers of the lane's slots
     const float Mk = Mrun - (float)Ecur;
 #pragma unroll
-    for (int bk = 0; bk < kMmaW / 16; ++bk) {
+    for (int bk = 0; bk < WN / 16; ++bk) {
       const int i = 16 * bk + n16;
       const float pe = __builtin_amdgcn_exp2f(scv[bk] - Mk);
       Lp += pe;
@@ -2271,24 +2299,49 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     wave_lds_sync();
     // pass 2: value product per 64-slot group
 #pragma unroll
-    for (int q4 = 0; q4 < kMmaW / 16; q4 += 4) {
-      uint32_t D[4], X[4], Y[4];
+    for (int q4 = 0; q4 < WN / 16; q4 += 4) {
+      uint32_t D[4], X[4][4];  // X[b][bt]: byte j = code byte b of the lane's channels in slot j of block bt
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
         const int i0 = 16 * (q4 + bt) + 4 * g;
         const u32x4_t nw = *reinterpret_cast<const u32x4_t*>(&sn[qm * SR + i0]);
         D[bt] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(nw.w, nw.z, dsel), __builtin_amdgcn_perm(nw.y, nw.x, dsel),
                                       0x05040100u);  // byte j: digit qs of slot i0 + j
-        const uint8_t* p0 = s_vc + i0 * kRowB + 32 * wave + 4 * (n16 >> 1);
-        const uint32_t d0 = *reinterpret_cast<const uint32_t*>(p0), d1 = *reinterpret_cast<const uint32_t*>(p0 + kRowB);
-        const uint32_t d2 = *reinterpret_cast<const uint32_t*>(p0 + 2 * kRowB),
-                       d3 = *reinterpret_cast<const uint32_t*>(p0 + 3 * kRowB);
-        const uint32_t lw = __builtin_amdgcn_perm(d1, d0, vsel), hw = __builtin_amdgcn_perm(d3, d2, vsel);
-        X[bt] = __builtin_amdgcn_perm(hw, lw, 0x06040200u);
-        Y[bt] = __builtin_amdgcn_perm(hw, lw, 0x07050301u);
+        if constexpr (BITS == 2) {
+          const uint8_t* p0 = s_vc + i0 * kRowB + CB * wave + 4 * (n16 >> 1);
+          const uint32_t d0 = *reinterpret_cast<const uint32_t*>(p0), d1 = *reinterpret_cast<const uint32_t*>(p0 + kRowB);
+          const uint32_t d2 = *reinterpret_cast<const uint32_t*>(p0 + 2 * kRowB),
+                         d3 = *reinterpret_cast<const uint32_t*>(p0 + 3 * kRowB);
+          const uint32_t lw = __builtin_amdgcn_perm(d1, d0, vsel), hw = __builtin_amdgcn_perm(d3, d2, vsel);
+          X[0][bt] = __builtin_amdgcn_perm(hw, lw, 0x06040200u);
+          X[1][bt] = __builtin_amdgcn_perm(hw, lw, 0x07050301u);
+        } else {  // 4-bit: the lane's 4 code bytes (channels 8 n16 .. +7) of 4 slots, transposed
+          const uint8_t* p0 = s_vc + i0 * kRowB + CB * wave + 4 * n16;
+          const uint32_t d0 = *reinterpret_cast<const uint32_t*>(p0), d1 = *reinterpret_cast<const uint32_t*>(p0 + kRowB);
+          const uint32_t d2 = *reinterpret_cast<const uint32_t*>(p0 + 2 * kRowB),
+                         d3 = *reinterpret_cast<const uint32_t*>(p0 + 3 * kRowB);
+          const uint32_t t01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u), t23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+          const uint32_t u01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u), u23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+          X[0][bt] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+          X[1][bt] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+          X[2][bt] = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
+          X[3][bt] = __builtin_amdgcn_perm(u23, u01, 0x07060302u);
+        }
       }
       const i32x4_t bop = {(int32_t)D[0], (int32_t)D[1], (int32_t)D[2], (int32_t)D[3]};
-      value_product(X, Y, bop, cv);
+      if constexpr (BITS == 2) {
+        value_product(X[0], X[1], bop, cv);
+      } else {  // product 2 b + c: channel 8 n16 + 2 b + c, c = low / high nibble of code byte b
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const i32x4_t lo = {(int32_t)(X[bb][0] & 0x0F0F0F0Fu), (int32_t)(X[bb][1] & 0x0F0F0F0Fu),
+                              (int32_t)(X[bb][2] & 0x0F0F0F0Fu), (int32_t)(X[bb][3] & 0x0F0F0F0Fu)};
+          const i32x4_t hi = {(int32_t)((X[bb][0] >> 4) & 0x0F0F0F0Fu), (int32_t)((X[bb][1] >> 4) & 0x0F0F0F0Fu),
+                              (int32_t)((X[bb][2] >> 4) & 0x0F0F0F0Fu), (int32_t)((X[bb][3] >> 4) & 0x0F0F0F0Fu)};
+          cv[2 * bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(lo, bop, cv[2 * bb], 0, 0, 0);
+          cv[2 * bb + 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(hi, bop, cv[2 * bb + 1], 0, 0, 0);
+        }
+      }
     }
   }
   if (t_begin < t_end) flush(1.0f);
@@ -2563,14 +2616,20 @@ int launch_attend_t(const AttendArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attend_rotate_q, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
   if (hipError_t e = hipGetLastError()) return (int)e;
 #if KVQ_ATT_MMA
-  if (BITS == 2 && a.group_log2 == 7 && ((uintptr_t)a.k_codes & 7) == 0 && ((uintptr_t)a.v_codes & 1) == 0) {
+  const uintptr_t al4 = (uintptr_t)a.k_codes | (uintptr_t)a.v_codes | (uintptr_t)a.k_scale | (uintptr_t)a.k_zero |
+                        (uintptr_t)a.v_scale | (uintptr_t)a.v_zero;
+  if (BITS == 4 && a.group_log2 == 7 && a.heads % 4 == 0 && (al4 & 7) == 0) {
+    const int64_t nb = ((np + 3) / 4 + 15) / 16 * 16;  // whole groups of 16 blocks (XCD-aware order)
+    if (nb > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attend_partial_mma_blk<4, QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
+  } else if (BITS == 2 && a.group_log2 == 7 && ((uintptr_t)a.k_codes & 7) == 0 && ((uintptr_t)a.v_codes & 1) == 0) {
     // whole groups of 16 blocks, so the XCD-aware order maps the blocks onto every task
     const int64_t nb = ((np + 3) / 4 + 15) / 16 * 16;
     if (nb > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
     const uintptr_t al = (uintptr_t)a.k_codes | (uintptr_t)a.v_codes | (uintptr_t)a.k_scale | (uintptr_t)a.k_zero |
                          (uintptr_t)a.v_scale | (uintptr_t)a.v_zero;
     if (a.heads % 4 == 0 && (al & 7) == 0)
-      hipLaunchKernelGGL((attend_partial_mma_blk<QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attend_partial_mma_blk<2, QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((attend_partial_mma<QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
   } else

@@ -58,6 +58,8 @@ def _case(r, t, h, bits, g, rope, use_perm, n_sink, name):
     (4, 2, 128, 4, False, 8),   # block-cooperative matrix-core pass (KV heads a multiple of 4)
     (1, 2, 128, 0, True, 4),
     (2, 2, 128, 2, False, 4),
+    (4, 4, 128, 4, False, 4),   # 4-bit codes on the block-cooperative pass
+    (2, 4, 128, 0, True, 8),
 ])
 def test_attend_small(qg, bits, g, n_sink, perm_v, h):
     r, t = 5, 203
@@ -126,15 +128,16 @@ def test_attend_llama3_cache_full_size():
 
 
 
-@pytest.mark.parametrize("h", [6, 8])
-def test_attend_several_windows_per_chunk(h):
+@pytest.mark.parametrize("h,bits", [(6, 2), (8, 2), (8, 4)])
+def test_attend_several_windows_per_chunk(h, bits):
     """A cache with enough rows that each chunk spans two windows of the matrix-core pass (the
-    second one partial), for the per-wave pass (6 KV heads) and the block-cooperative one (8):
+    second one partial), for the per-wave pass (6 KV heads) and the block-cooperative one (8; 2-
+    and 4-bit codes):
     inputs drawn on the GPU, sampled rows checked against the oracle."""
     r, t = 96, 4096
-    seed = 7100 + h
-    ck = _case(r, t, h, 2, 128, True, True, 4, "K")
-    cv = _case(r, t, h, 2, 128, False, False, 4, "V")
+    seed = 7100 + h + 10 * bits
+    ck = _case(r, t, h, bits, 128, True, True, 4, "K")
+    cv = _case(r, t, h, bits, 128, False, False, 4, "V")
     perm = np.random.default_rng(seed).permutation(128).astype(np.int64)
     cfg_k, cfg_v = gu.make_config(ck, perm), gu.make_config(cv, None)
     gen = torch.Generator(device="cuda").manual_seed(seed)
@@ -146,7 +149,7 @@ def test_attend_several_windows_per_chunk(h):
     q = rng.standard_normal((r, 4 * h, 128)).astype(np.float32)
     lengths = rng.integers(1, t + 1, size=r).astype(np.int32)
     lengths[:2] = [t, 1000]
-    say(f"[case] attend two windows per chunk: {r} x {t} x {h} heads")
+    say(f"[case] attend several windows per chunk: {r} x {t} x {h} heads, {bits}-bit")
     out = kvq.attend(torch.from_numpy(q).cuda(), pk_t, cfg_k, pv_t, cfg_v, lengths=torch.from_numpy(lengths).cuda())
     torch.cuda.synchronize()
     out = out.cpu().numpy()
