@@ -393,7 +393,8 @@ kvq_status check_attend(const kvq_config* cfg_k, const kvq_config* cfg_v, int64_
   if (qg != 1 && qg != 2 && qg != 4)
     return fail(KVQ_ERR_UNSUPPORTED, "attention supports 1, 2 or 4 query heads per KV head");
   int32_t nc = 1, ct = 8;
-  kvq::attend_chunks(cfg_k->rows, cfg_k->heads, cfg_k->tokens, &nc, &ct);
+  const bool mma_blk = cfg_k->group_size == 128 && cfg_k->heads % 4 == 0;  // bits are 2 or 4 here
+  kvq::attend_chunks(cfg_k->rows, cfg_k->heads, cfg_k->tokens, mma_blk, &nc, &ct);
   int64_t nq = 0, tmp = 0;
   if (!mul_ok(cfg_k->rows, q_heads, &nq) || !mul_ok(nq, (int64_t)nc * kvq::kAttendPart + 128, &tmp) ||
       tmp > (int64_t(1) << 40))
