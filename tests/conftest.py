@@ -12,6 +12,23 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+def pytest_sessionfinish(session, exitstatus):
+    """The 1e-5 bound on code mismatches at rounding ties, over every code compared in the
+    session (each comparison also holds it, rounded up to one tie).  Runs whatever subset
+    of the tests was collected, so it cannot be skipped by selection or ordering."""
+    par = sys.modules.get("tests.parity")
+    if par is None or par.SESSION["codes"] == 0:
+        return
+    s = par.SESSION
+    msg = f"[parity] {s['tie_mismatches']} code mismatches at rounding ties in {s['codes']} codes compared"
+    ok = s["tie_mismatches"] <= par.CODE_MISMATCH_MAX * s["codes"]
+    rep = session.config.pluginmanager.get_plugin("terminalreporter")
+    if rep is not None:
+        rep.write_line(msg + ("" if ok else f": above the bound {par.CODE_MISMATCH_MAX}"), red=not ok)
+    if not ok:
+        session.exitstatus = pytest.ExitCode.TESTS_FAILED
+
+
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 

@@ -22,6 +22,46 @@ def _rng(k=0):
 
 
 # --------------------------------------------------------------------------- #
+# widening of the stored input
+# --------------------------------------------------------------------------- #
+# bf16 bit patterns and their values from the format's definition (1 sign bit, 8 exponent
+# bits with bias 127, 7 fraction bits; exponent field 0 is subnormal: 2^-126 * f / 2^7)
+BF16_PATTERNS = [
+    (0x3F80, 1.0),
+    (0xC049, -3.140625),                         # -(1 + 73/128) * 2^1
+    (0x0001, 2.0 ** -133),                       # smallest subnormal
+    (0x007F, 127 * 2.0 ** -133),                 # largest subnormal
+    (0x0080, 2.0 ** -126),                       # smallest normal
+    (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127),    # largest finite
+    (0x4780, 65536.0),
+    (0x3E80, 0.25),
+    (0xBF81, -(1.0 + 2.0 ** -7)),
+]
+# fp16: 1 sign, 5 exponent bits with bias 15, 10 fraction bits
+F16_PATTERNS = [(0x3C00, 1.0), (0x0001, 2.0 ** -24), (0x7BFF, 65504.0), (0xC200, -3.0), (0x3555, 1365 / 4096)]
+
+
+def check_widen_exact():
+    """bf16 and fp16 bit patterns widen to the values the formats define; -0 keeps its sign;
+    random finite bf16 patterns agree with torch's own bfloat16 conversion (library)."""
+    import torch
+    bits = np.array([b for b, _ in BF16_PATTERNS], dtype=np.uint16)
+    got = codec.widen(bits, "bf16")
+    assert got.dtype == np.float64
+    assert np.array_equal(got, np.array([v for _, v in BF16_PATTERNS])), got
+    neg0 = codec.widen(np.array([0x8000], dtype=np.uint16), "bf16")
+    assert neg0[0] == 0.0 and np.signbit(neg0[0])
+    h = np.array([b for b, _ in F16_PATTERNS], dtype=np.uint16).view(np.float16)
+    assert np.array_equal(codec.widen(h, "f16"), np.array([v for _, v in F16_PATTERNS]))
+    f = np.array([1.5, -2.0 ** -140, 3.4e38], dtype=np.float32)
+    assert np.array_equal(codec.widen(f, "f32"), f.astype(np.float64))
+    raw = _rng(40).integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    raw = raw[(raw & 0x7F80) != 0x7F80]  # finite patterns only
+    ref = torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(codec.widen(raw, "bf16"), ref)
+
+
+# --------------------------------------------------------------------------- #
 # RoPE
 # --------------------------------------------------------------------------- #
 def check_rope_theta_special_values():

@@ -207,9 +207,7 @@ def test_every_output_byte_written_and_deterministic():
         kvq.encode(xt, cfg, planes=planes)
         torch.cuda.synchronize()
         outs.append(gu.planes_numpy(planes))
-    for k in outs[0]:
-        if k == "sink":
-            continue  # slots of positions beyond T are not this call's to write
+    for k in outs[0]:  # the sink plane too: T > n_sink, so all 4 sink slots are this call's
         assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
         assert np.array_equal(outs[0][k].view(np.uint8), outs[2][k].view(np.uint8)), k
     # decode output fully written too
@@ -283,10 +281,3 @@ def test_widehead_full_size_sampled():
     rows = sorted(set([0, 31] + rng.integers(0, 32, 3).tolist()))
     tokens = list(range(0, 24)) + list(range(8190, 8200)) + list(range(16380, 16384))
     _sample_check("widehead", rows, tokens)
-
-
-def test_zz_session_tie_fraction():
-    """Across every comparison above, code mismatches (all at rounding ties) stay <= 1e-5."""
-    s = parity.SESSION
-    say(f"[session] {s['tie_mismatches']} tie mismatches in {s['codes']} codes")
-    assert s["tie_mismatches"] <= parity.CODE_MISMATCH_MAX * max(s["codes"], 1)

@@ -114,6 +114,23 @@ def _pack_msb_first(q, bits):
     return np.packbits(stream, axis=-1, bitorder="big").reshape(q.shape[:-1] + (d * bits // 8,))
 
 
+_orig_widen = codec.widen
+
+
+def _widen_shift_15(raw, dtype):
+    # bf16 bits shifted one place short of the float32 position
+    if dtype == "bf16":
+        return (np.asarray(raw, dtype=np.uint16).astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+    return _orig_widen(raw, dtype)
+
+
+def _widen_bf16_as_f16(raw, dtype):
+    # bf16 bits read as an IEEE half
+    if dtype == "bf16":
+        return np.asarray(raw, dtype=np.uint16).view(np.float16).astype(np.float64)
+    return _orig_widen(raw, dtype)
+
+
 _orig_decode = codec.decode
 
 
@@ -173,6 +190,8 @@ MUTATIONS = {
     "decode_perm_gather": (codec, "decode", _decode_gather_not_scatter),
     "decode_rho_plus_eps": (codec, "decode", _decode_rho_plus_eps),
     "append_slot_is_position": (codec, "append", _append_slot_is_position),
+    "widen_bf16_shift_15": (codec, "widen", _widen_shift_15),
+    "widen_bf16_as_f16": (codec, "widen", _widen_bf16_as_f16),
     "attention_heads_interleaved": (_attention, "attend_decoded", _attend_heads_interleaved),
 }
 
