@@ -9,8 +9,10 @@ Argument marshalling only -- every step of the codec runs in the HIP kernels of
     planes = kvq.encode(x, cfg)                 # dict of torch tensors
     y = kvq.decode(planes, cfg, out_dtype="bf16")
 
-The library is required: importing this package without a built ``libkvq.so``
-raises, and there is no CPU fallback.
+The library is required: it is loaded on the first call that needs it, and that
+call raises ImportError when ``libkvq.so`` has not been built.  There is no CPU
+fallback.  (Importing the package itself needs no library, so the build script
+can run from a clean checkout.)
 """
 from __future__ import annotations
 
@@ -112,17 +114,26 @@ def _load():
     return lib
 
 
-_lib = _load()
+_lib_handle = None
+
+
+def _L():
+    """The loaded library (loaded on first use; raises ImportError if it was never built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        _lib_handle = _load()
+    return _lib_handle
 
 
 def abi_version() -> int:
-    return int(_lib.kvq_abi_version())
+    return int(_L().kvq_abi_version())
 
 
 def _check(status: int):
     if status != 0:
-        raise KvqError(status, (_lib.kvq_last_error_message() or b"").decode() or
-                       _lib.kvq_status_string(status).decode())
+        lib = _L()
+        raise KvqError(status, (lib.kvq_last_error_message() or b"").decode() or
+                       lib.kvq_status_string(status).decode())
 
 
 @dataclass
@@ -175,13 +186,13 @@ class Config:
 
 def validate(cfg: Config) -> None:
     c = cfg.c_struct()
-    _check(_lib.kvq_validate(ctypes.byref(c)))
+    _check(_L().kvq_validate(ctypes.byref(c)))
 
 
 def packed_sizes(cfg: Config) -> Dict[str, int]:
     c = cfg.c_struct()
     out = [ctypes.c_size_t() for _ in range(5)]
-    _check(_lib.kvq_packed_sizes(ctypes.byref(c), *[ctypes.byref(o) for o in out]))
+    _check(_L().kvq_packed_sizes(ctypes.byref(c), *[ctypes.byref(o) for o in out]))
     return dict(zip(("codes", "scale", "zero", "norm", "sink"), (int(o.value) for o in out)))
 
 
@@ -226,7 +237,7 @@ def encode(x, cfg: Config, planes=None, stream=None):
         planes = empty_planes(cfg, device=x.device)
     c = cfg.c_struct()
     p = _planes_struct(planes)
-    _check(_lib.kvq_encode(ctypes.byref(c), _ptr(x), ctypes.byref(p), _stream_handle(stream)))
+    _check(_L().kvq_encode(ctypes.byref(c), _ptr(x), ctypes.byref(p), _stream_handle(stream)))
     return planes
 
 
@@ -242,7 +253,7 @@ def append(x, positions, cache, cfg: Config, stream=None):
         raise ValueError("positions must be a contiguous int64 tensor with one entry per row")
     c = cfg.c_struct()
     p = _planes_struct(cache)
-    _check(_lib.kvq_append(ctypes.byref(c), _ptr(x), _ptr(positions), ctypes.byref(p), _stream_handle(stream)))
+    _check(_L().kvq_append(ctypes.byref(c), _ptr(x), _ptr(positions), ctypes.byref(p), _stream_handle(stream)))
     return cache
 
 
@@ -250,7 +261,7 @@ def attend_workspace_size(k_cfg: Config, q_heads: int) -> int:
     """Bytes of device workspace ``attend`` needs for this cache shape and query-head count."""
     c = k_cfg.c_struct()
     n = ctypes.c_size_t()
-    _check(_lib.kvq_attend_workspace_size(ctypes.byref(c), int(q_heads), ctypes.byref(n)))
+    _check(_L().kvq_attend_workspace_size(ctypes.byref(c), int(q_heads), ctypes.byref(n)))
     return int(n.value)
 
 
@@ -274,7 +285,7 @@ def attend(q, k_planes, k_cfg: Config, v_planes, v_cfg: Config, lengths=None, sc
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ck, cv = k_cfg.c_struct(), v_cfg.c_struct()
     pk, pv = _planes_struct(k_planes), _planes_struct(v_planes)
-    _check(_lib.kvq_attend(ctypes.byref(ck), ctypes.byref(pk), ctypes.byref(cv), ctypes.byref(pv), _ptr(q), q_heads,
+    _check(_L().kvq_attend(ctypes.byref(ck), ctypes.byref(pk), ctypes.byref(cv), ctypes.byref(pv), _ptr(q), q_heads,
                            _ptr(lengths), float(scale), _ptr(out), int(workspace.data_ptr()),
                            int(workspace.numel() * workspace.element_size()), _stream_handle(stream)))
     return out
@@ -291,12 +302,12 @@ def decode(planes, cfg: Config, out_dtype: str = "f32", out=None, stream=None):
                           device=planes["codes"].device)
     c = cfg.c_struct()
     p = _planes_struct(planes)
-    _check(_lib.kvq_decode(ctypes.byref(c), ctypes.byref(p), _ptr(out), DTYPES[out_dtype], _stream_handle(stream)))
+    _check(_L().kvq_decode(ctypes.byref(c), ctypes.byref(p), _ptr(out), DTYPES[out_dtype], _stream_handle(stream)))
     return out
 
 
 def lloyd_max_gaussian(bits: int, sigma: float) -> np.ndarray:
     """Host-side Lloyd-Max codebook for N(0, sigma^2) (float32, ascending)."""
     out = np.zeros(2 ** bits, dtype=np.float32)
-    _check(_lib.kvq_lloyd_max_gaussian(int(bits), float(sigma), out.ctypes.data))
+    _check(_L().kvq_lloyd_max_gaussian(int(bits), float(sigma), out.ctypes.data))
     return out
