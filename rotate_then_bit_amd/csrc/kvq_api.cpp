@@ -84,7 +84,8 @@ kvq_status check_config(const kvq_config* cfg, Derived* dv) {
   if (cfg->rope != 0 && cfg->rope != 1) return fail(KVQ_ERR_PARAM, "rope must be 0 or 1");
   if (cfg->rope && !(isfinite(cfg->rope_base) && cfg->rope_base > 1.0))
     return fail(KVQ_ERR_PARAM, "rope_base must be finite and > 1");
-  if (cfg->pos_offset < 0 || cfg->pos_offset + cfg->tokens > (int64_t(1) << 31))
+  // (tokens >= 0 here, so the right-hand side cannot overflow; pos_offset + tokens could)
+  if (cfg->pos_offset < 0 || cfg->pos_offset > (int64_t(1) << 31) - cfg->tokens)
     return fail(KVQ_ERR_PARAM, "positions must lie in [0, 2^31]");
   if (cfg->n_sink < 0) return fail(KVQ_ERR_PARAM, "n_sink must be >= 0");
 
@@ -438,7 +439,7 @@ kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_co
   kvq::AttendArgs a;
   kvq_status st = check_attend(cfg_k, cfg_v, q_heads, &need, &a);
   if (st != KVQ_OK) return st;
-  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(KVQ_ERR_PARAM, "scale must be finite");
+  if (!isfinite(scale)) return fail(KVQ_ERR_PARAM, "scale must be finite");
   Derived dk, dv;
   (void)check_config(cfg_k, &dk);  // both already accepted above; this fills the derived sizes
   (void)check_config(cfg_v, &dv);

@@ -56,6 +56,8 @@ BAD = [
     ("codebook_nan", dict(quant="lloyd", codebook=np.array([0, 1, np.nan, 2], dtype=np.float32)), 6),
     ("rope_base", dict(rope=True, rope_base=1.0), 6),
     ("positions", dict(pos_offset=2 ** 31), 6),
+    ("positions_end", dict(pos_offset=2 ** 31 - 7), 6),      # 8 tokens end one past 2^31
+    ("positions_wrap", dict(pos_offset=2 ** 63 - 4), 6),     # pos_offset + tokens would wrap negative
     ("n_sink", dict(n_sink=-1), 6),
     ("stride_align", dict(strides=(1024, 32, 3)), 7),
     ("stride_neg", dict(strides=(-8, 8, 8)), 2),
@@ -235,5 +237,13 @@ def test_attend_workspace_size_and_refusals_on_the_host():
     assert lib.kvq_attend(*args(q=4100)) == 7
     assert lib.kvq_attend(*args(wsz=16)) == 2        # workspace too small
     assert lib.kvq_attend(*args(sc=float("nan"))) == 6
+    assert lib.kvq_attend(*args(sc=float("inf"))) == 6
+    # a finite scale near FLT_MAX passes the scale check (the NULL q is what is refused)
+    assert lib.kvq_attend(*args(q=None, sc=3.3e38)) == 1
     assert lib.kvq_attend(ctypes.byref(ck), ctypes.byref(pk), None, ctypes.byref(pv), 4096, 8, None, 0.1, 4096,
                           4096, ws, None) == 1        # cfg_v NULL
+
+
+def test_positions_up_to_the_limit_are_accepted():
+    kvq.validate(_cfg(pos_offset=2 ** 31 - 8))  # 8 tokens: the last position is 2^31 - 1
+    kvq.validate(_cfg(shape=(1, 0, 4, 128), pos_offset=2 ** 31))
