@@ -327,28 +327,10 @@ __device__ __forceinline__ void widen_chunk(const RawRow<DT>& raw, int c, float*
   }
 }
 
-// v_dot2 of a 16-bit pair with (+-1, +-1) and a float addend: x0 * s0 + x1 * s1 + acc
-// (products exact, one float sum).  Through the compiler builtin, so that the compiler
-// sees a dot instruction and schedules its result hazards.
-template <int DT, int S0, int S1>
-__device__ __forceinline__ float dot2pm(uint32_t pair, float acc) {
-  if constexpr (DT == DT_BF16) {
-    const bf16x2_t c = {(__bf16)(float)S0, (__bf16)(float)S1};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), c, acc, false);
-  } else {
-    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-    const h2_t c = {(_Float16)(float)S0, (_Float16)(float)S1};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, pair), c, acc, false);
-  }
-}
-
 // Widen a 16-bit row and apply the first two Walsh-Hadamard stages (slot bits 0 and 1)
 // at once: each group of 4 channels (two dwords p, r) gives
 //   x0+x1+x2+x3, x0-x1+x2-x3, x0+x1-x2-x3, x0-x1-x2+x3
 // from two v_dot2 of p (x0+x1, x0-x1) and four v_dot2 of r with those as addends.
-#ifndef KVQ_DOT_ASM
-#define KVQ_DOT_ASM 1
-#endif
 // Eight outputs (two groups of 4 channels, dwords X Y and Z W) with the three-address
 // dot instruction OP: the builtins select the accumulating two-address form, which costs
 // a copy of every partial sum used twice and a zeroed register for every zero addend.
@@ -370,36 +352,16 @@ __device__ __forceinline__ float dot2pm(uint32_t pair, float acc) {
 template <int DT>
 __device__ __forceinline__ void widen_row_h4(const RawRow<DT>& raw, float* v) {
   static_assert(DT != DT_F32, "16-bit inputs only");
-#if KVQ_DOT_ASM
-  {
-    // packed (+-1, +-1) pairs: low half multiplies the even channel
-    constexpr uint32_t P1 = (DT == DT_BF16) ? 0x3F80u : 0x3C00u, M1 = P1 | 0x8000u;
-    const uint32_t c11 = P1 | P1 << 16, c1m = P1 | M1 << 16, cmm = M1 | M1 << 16, cm1 = M1 | P1 << 16;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float* o = v + 8 * k;
-      if constexpr (DT == DT_BF16) {
-        KVQ_H4_BLOCK("v_dot2_f32_bf16", o, raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w)
-      } else {
-        KVQ_H4_BLOCK("v_dot2_f32_f16", o, raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w)
-      }
-    }
-    return;
-  }
-#endif
+  // packed (+-1, +-1) pairs: low half multiplies the even channel
+  constexpr uint32_t P1 = (DT == DT_BF16) ? 0x3F80u : 0x3C00u, M1 = P1 | 0x8000u;
+  const uint32_t c11 = P1 | P1 << 16, c1m = P1 | M1 << 16, cmm = M1 | M1 << 16, cm1 = M1 | P1 << 16;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t ws[4] = {raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w};
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const uint32_t p = ws[2 * g], r = ws[2 * g + 1];
-      const float s = dot2pm<DT, 1, 1>(p, 0.0f);
-      const float d = dot2pm<DT, 1, -1>(p, 0.0f);
-      float* o = v + 8 * k + 4 * g;
-      o[0] = dot2pm<DT, 1, 1>(r, s);
-      o[1] = dot2pm<DT, 1, -1>(r, d);
-      o[2] = dot2pm<DT, -1, -1>(r, s);
-      o[3] = dot2pm<DT, -1, 1>(r, d);
+    float* o = v + 8 * k;
+    if constexpr (DT == DT_BF16) {
+      KVQ_H4_BLOCK("v_dot2_f32_bf16", o, raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w)
+    } else {
+      KVQ_H4_BLOCK("v_dot2_f32_f16", o, raw.w[k].x, raw.w[k].y, raw.w[k].z, raw.w[k].w)
     }
   }
 }
@@ -614,10 +576,7 @@ __device__ __forceinline__ uint32_t enc_perm_bytes(bool perm) {
 // RoPE table: a token's D/2 (cos, sin) pairs, the 16 pairs lane l reads at byte l * kTrigLane
 // (128 bytes of pairs + 16 of padding: 16-byte LDS reads are served 16 lanes at a time on
 // 64 banks of 4 bytes, and with the padding the lanes of a vector read different banks).
-#ifndef KVQ_TRIG_PAD
-#define KVQ_TRIG_PAD 1
-#endif
-constexpr int kTrigLane = KVQ_TRIG_PAD ? 144 : 128;
+constexpr int kTrigLane = 144;
 template <int D>
 constexpr int trig_row() {
   return Geo<D>::LV * kTrigLane;
@@ -1501,16 +1460,10 @@ struct AttSlot {
 // (lane / 8, lane % 8) holds channels 16 l .. 16 l + 15 of the token slot tk of each step of
 // 8 slots; the 8 lanes of a slot reduce its scores, and each slot keeps its own running
 // maximum, denominator and rotated-domain sums until the wave merges them at the end.
-#ifndef KVQ_ATT_MMA
-#define KVQ_ATT_MMA 1
-#endif
-#ifndef KVQ_ATT_LDSQ
-#define KVQ_ATT_LDSQ 1
-#endif
 template <int BITS, int QG>
 __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
   // the rotated query slices live in LDS (read every step) instead of 16 * QG registers
-  __shared__ __attribute__((aligned(16))) float s_qv[KVQ_ATT_LDSQ ? 4 : 1][KVQ_ATT_LDSQ ? QG * 128 : 1];
+  __shared__ __attribute__((aligned(16))) float s_qv[4][QG * 128];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
@@ -1529,7 +1482,6 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
   constexpr int LB = 2 * BITS;             // code bytes per lane (16 codes)
 
   float sl[QG];
-#if KVQ_ATT_LDSQ
   {
     const float* src = a.qrot + (r * a.q_heads + h * QG) * 128;
     for (int i = lane; i < QG * 128; i += 64) s_qv[wave][i] = src[i];
@@ -1545,19 +1497,6 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
       sl[m] += (__uint_as_float(v.x) + __uint_as_float(v.y)) + (__uint_as_float(v.z) + __uint_as_float(v.w));
     }
   }
-#else
-  float qv[QG][16];
-#pragma unroll
-  for (int m = 0; m < QG; ++m) {
-    const float* src = a.qrot + ((r * a.q_heads + h * QG + m) * 128 + 16 * l);
-    sl[m] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      qv[m][i] = src[i];
-      sl[m] += qv[m][i];
-    }
-  }
-#endif
   float mx[QG], ls[QG], zs[QG], acc[QG][16];
 #pragma unroll
   for (int m = 0; m < QG; ++m) {
@@ -1612,14 +1551,11 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
       unpack(cur.kw, code);
       const float ks = f16_value(cur.ks), kz = f16_value(cur.kz);
       float s[QG];
-#if KVQ_ATT_LDSQ
       uint32_t qa = qaddr;
       asm volatile("" : "+v"(qa));  // read the slices here, each step (not hoisted into registers)
-#endif
 #pragma unroll
       for (int m = 0; m < QG; ++m) {
         float d = 0.0f;
-#if KVQ_ATT_LDSQ
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const u32x4_t v = lds_ld4(qa + 512u * m + 16u * k);
@@ -1628,10 +1564,6 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
           d = __builtin_fmaf(__uint_as_float(v.z), code[4 * k + 2], d);
           d = __builtin_fmaf(__uint_as_float(v.w), code[4 * k + 3], d);
         }
-#else
-#pragma unroll
-        for (int i = 0; i < 16; ++i) d = __builtin_fmaf(qv[m][i], code[i], d);
-#endif
         float part = __builtin_fmaf(ks, d, kz * sl[m]);  // q~ . (zero + code * scale) over 16 channels
         part = add_x1(part);
         part = add_x2(part);
@@ -1719,10 +1651,7 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
 // (4 m + s, g) holds digit s of head m for channels 32 g + 8 j + b (register j, product b).
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
-#ifndef KVQ_MMA_W
-#define KVQ_MMA_W 128
-#endif
-constexpr int kMmaW = KVQ_MMA_W;  // slots per window (a multiple of 64)
+constexpr int kMmaW = 128;  // slots per window (a multiple of 64)
 constexpr int kMmaPad = 16;  // padding of the LDS weight-integer rows (banks of the row writes)
 template <int K>
 __device__ __forceinline__ uint32_t code_bytes(uint32_t x) {  // code 4 b + K of byte b, times code_mul(K)
@@ -2615,7 +2544,6 @@ int launch_attend_t(const AttendArgs& a, hipStream_t s) {
   if ((np + 3) / 4 > 0x7fffffff || (nq + 3) / 4 > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(attend_rotate_q, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
   if (hipError_t e = hipGetLastError()) return (int)e;
-#if KVQ_ATT_MMA
   const uintptr_t al4 = (uintptr_t)a.k_codes | (uintptr_t)a.v_codes | (uintptr_t)a.k_scale | (uintptr_t)a.k_zero |
                         (uintptr_t)a.v_scale | (uintptr_t)a.v_zero;
   if (BITS == 4 && a.group_log2 == 7 && a.heads % 4 == 0 && (al4 & 7) == 0) {
@@ -2633,7 +2561,6 @@ int launch_attend_t(const AttendArgs& a, hipStream_t s) {
     else
       hipLaunchKernelGGL((attend_partial_mma<QG>), dim3((unsigned)nb), dim3(256), 0, s, a);
   } else
-#endif
     hipLaunchKernelGGL((attend_partial<BITS, QG>), dim3((unsigned)((np + 3) / 4)), dim3(256), 0, s, a);
   if (hipError_t e = hipGetLastError()) return (int)e;
   hipLaunchKernelGGL(attend_combine, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
