@@ -31,8 +31,8 @@
  * post-RoPE key a cache holds.
  *
  * Threading and memory: the library allocates nothing and keeps no state
- * between calls except a thread-local error message.  The caller owns every
- * buffer.  Calls only enqueue work on the given HIP stream and never
+ * between calls except a thread-local error message and the static device
+ * workspace of kvq_attend_noalloc.  The caller owns every other buffer.  Calls only enqueue work on the given HIP stream and never
  * synchronise; buffers must stay alive until that work completes.  All
  * argument checking happens on the host before anything is enqueued, so a
  * call that returns an error has done nothing.
@@ -182,6 +182,23 @@ kvq_status kvq_attend_workspace_size(const kvq_config* cfg_k, int64_t q_heads, s
 kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v, const kvq_planes* v,
                       const float* q, int64_t q_heads, const int32_t* lengths, float scale, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free variant of kvq_attend, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, results and errors are those of kvq_attend without the workspace: the
+ * workspace is instead a static device array inside the library, of
+ * kvq_attend_noalloc_max_workspace() bytes (32 MiB; one copy on each GPU the library runs
+ * on, held until the process ends; its device address is looked up on the first call on
+ * each device).  A cache and query-head count whose kvq_attend_workspace_size exceeds that
+ * returns KVQ_ERR_SHAPE before anything is enqueued.  The call allocates nothing.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (on
+ * different streams, or from different threads) race and give wrong results; serialise
+ * them.  The array keeps the last call's contents; no call relies on them (every byte a
+ * call reads was written by that call). */
+kvq_status kvq_attend_noalloc(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v,
+                              const kvq_planes* v, const float* q, int64_t q_heads, const int32_t* lengths, float scale,
+                              float* out, void* stream);
+size_t kvq_attend_noalloc_max_workspace(void);
 
 /* Decode in's planes into y (DEVICE, contiguous [R,T,H,D] of y_dtype).  Asynchronous.
  * y must not alias any plane. */

@@ -23,7 +23,8 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
-__all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_workspace_size", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
+__all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_noalloc", "attend_noalloc_max_workspace",
+           "attend_workspace_size", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
            "library_path", "abi_version", "DTYPES", "ROTATIONS", "QUANTIZERS", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +35,8 @@ DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 ROTATIONS = {"none": 0, "fwht": 1, "so4": 2}
 QUANTIZERS = {"minmax": 0, "lloyd": 1}
 EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append",
-                    "kvq_attend_workspace_size", "kvq_attend", "kvq_decode", "kvq_lloyd_max_gaussian",
+                    "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_attend_noalloc_max_workspace",
+                    "kvq_decode", "kvq_lloyd_max_gaussian",
                     "kvq_status_string", "kvq_last_error_message")
 
 
@@ -102,12 +104,17 @@ def _load():
     lib.kvq_attend.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Planes), ctypes.POINTER(_Config),
                                ctypes.POINTER(_Planes), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.kvq_attend_noalloc.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Planes), ctypes.POINTER(_Config),
+                                       ctypes.POINTER(_Planes), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvq_attend_noalloc_max_workspace.restype = ctypes.c_size_t
+    lib.kvq_attend_noalloc_max_workspace.argtypes = []
     lib.kvq_lloyd_max_gaussian.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_last_error_message.restype = ctypes.c_char_p
     for fn in ("kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append", "kvq_decode", "kvq_lloyd_max_gaussian",
-               "kvq_attend_workspace_size", "kvq_attend"):
+               "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -289,6 +296,32 @@ def attend(q, k_planes, k_cfg: Config, v_planes, v_cfg: Config, lengths=None, sc
                            _ptr(lengths), float(scale), _ptr(out), int(workspace.data_ptr()),
                            int(workspace.numel() * workspace.element_size()), _stream_handle(stream)))
     return out
+
+
+def attend_noalloc(q, k_planes, k_cfg: Config, v_planes, v_cfg: Config, lengths=None, scale=None, out=None,
+                   stream=None):
+    """``attend`` through the allocation-free entry point: the workspace is the library's
+    static device array (``attend_noalloc_max_workspace()`` bytes per GPU); calls on one GPU
+    must not overlap.  ``out`` must be given by callers that cannot allocate."""
+    import torch
+    r, q_heads = int(q.shape[0]), int(q.shape[1])
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float32 tensor [rows, q_heads, 128]")
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() != r or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous int32 tensor with one entry per row")
+    if scale is None:
+        scale = float(k_cfg.shape[-1]) ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    ck, cv = k_cfg.c_struct(), v_cfg.c_struct()
+    pk, pv = _planes_struct(k_planes), _planes_struct(v_planes)
+    _check(_L().kvq_attend_noalloc(ctypes.byref(ck), ctypes.byref(pk), ctypes.byref(cv), ctypes.byref(pv), _ptr(q),
+                                   q_heads, _ptr(lengths), float(scale), _ptr(out), _stream_handle(stream)))
+    return out
+
+
+def attend_noalloc_max_workspace() -> int:
+    return int(_L().kvq_attend_noalloc_max_workspace())
 
 
 _TORCH_DT = {"f16": "float16", "bf16": "bfloat16", "f32": "float32"}

@@ -431,9 +431,13 @@ kvq_status kvq_attend_workspace_size(const kvq_config* cfg_k, int64_t q_heads, s
   return st == KVQ_OK ? ok() : st;
 }
 
-kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v, const kvq_planes* v,
-                      const float* q, int64_t q_heads, const int32_t* lengths, float scale, float* out,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// kvq_attend and kvq_attend_noalloc: every check, then the launches.  With workspace NULL and
+// use_scratch set, the workspace is the library's static device array (looked up only after
+// every check has passed, so an error return has made no HIP call).
+kvq_status attend_impl(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v, const kvq_planes* v,
+                       const float* q, int64_t q_heads, const int32_t* lengths, float scale, float* out,
+                       void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
   if (!cfg_v) return fail(KVQ_ERR_NULL, "cfg_v is NULL");
   size_t need = 0;
   kvq::AttendArgs a;
@@ -449,12 +453,21 @@ kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_co
   if ((st = check_planes(cfg_k, dk, k)) != KVQ_OK) return st;
   if ((st = check_planes(cfg_v, dv, v)) != KVQ_OK) return st;
   if (cfg_k->n_sink > 0 && (!k->sink || !v->sink)) return fail(KVQ_ERR_NULL, "sink plane is NULL");
-  if (!q || !out || !workspace) return fail(KVQ_ERR_NULL, "q, out or workspace is NULL");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
+  if (!q || !out) return fail(KVQ_ERR_NULL, "q or out is NULL");
+  if (!use_scratch && !workspace) return fail(KVQ_ERR_NULL, "workspace is NULL");
+  if (!aligned16(q) || !aligned16(out) || (!use_scratch && !aligned16(workspace)))
     return fail(KVQ_ERR_ALIGN, "q, out and workspace must be 16-byte aligned");
   if (lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) return fail(KVQ_ERR_ALIGN, "lengths not 4-byte aligned");
-  if (workspace_bytes < need)
+  if (use_scratch) {
+    if (need > kvq::kAttendScratchBytes)
+      return fail(KVQ_ERR_SHAPE, "kvq_attend_noalloc: this cache and query-head count need %zu bytes of workspace, "
+                                 "above its fixed %zu (use kvq_attend with a workspace)",
+                  need, kvq::kAttendScratchBytes);
+    if (const int e = kvq::attend_scratch(&workspace))
+      return fail(KVQ_ERR_DEVICE, "kvq_attend_noalloc: device workspace lookup failed: %s", kvq::device_error_string(e));
+  } else if (workspace_bytes < need) {
     return fail(KVQ_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  }
   a.k_codes = static_cast<const uint8_t*>(k->codes);
   a.k_scale = static_cast<const uint16_t*>(k->scale);
   a.k_zero = static_cast<const uint16_t*>(k->zero);
@@ -473,6 +486,21 @@ kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_co
   if (err != 0) return fail(KVQ_ERR_DEVICE, "attention launch failed: %s", kvq::device_error_string(err));
   return ok();
 }
+}  // namespace
+
+kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v, const kvq_planes* v,
+                      const float* q, int64_t q_heads, const int32_t* lengths, float scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return attend_impl(cfg_k, k, cfg_v, v, q, q_heads, lengths, scale, out, workspace, workspace_bytes, false, stream);
+}
+
+kvq_status kvq_attend_noalloc(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v,
+                              const kvq_planes* v, const float* q, int64_t q_heads, const int32_t* lengths, float scale,
+                              float* out, void* stream) {
+  return attend_impl(cfg_k, k, cfg_v, v, q, q_heads, lengths, scale, out, nullptr, 0, true, stream);
+}
+
+size_t kvq_attend_noalloc_max_workspace(void) { return kvq::kAttendScratchBytes; }
 
 kvq_status kvq_lloyd_max_gaussian(int32_t bits, double sigma, float* codebook_out) {
   if (!codebook_out) return fail(KVQ_ERR_NULL, "codebook_out is NULL");

@@ -2,6 +2,7 @@
 // kernels (kvq_kernels.hip).  Not installed; callers use include/kvq.h.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace kvq {
@@ -113,6 +114,12 @@ inline void attend_chunks(int64_t rows, int64_t heads, int64_t tokens, bool mma_
   *chunk = (int32_t)ct;
 }
 int launch_attend(int bits, int qg, const AttendArgs& a, void* stream);
+// The allocation-free attention entry point keeps its workspace in a static device array of
+// this many bytes (one copy per GPU, held until the process ends).
+constexpr size_t kAttendScratchBytes = size_t(32) << 20;
+// Device address of that array on the current device (looked up once per device with
+// hipGetSymbolAddress); returns a hipError_t as int.
+int attend_scratch(void** ptr);
 
 // Launch helpers, one per (direction, dtype, head_dim), defined in kvq_kernels.hip.
 // Each returns a hipError_t as int (0 = success).

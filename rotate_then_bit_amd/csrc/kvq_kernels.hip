@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -2567,6 +2568,30 @@ int launch_attend_t(const AttendArgs& a, hipStream_t s) {
   return (int)hipGetLastError();
 }
 }  // namespace
+// Workspace of kvq_attend_noalloc: callers that cannot allocate get the rotated queries and the
+// partials here instead of in a buffer of their own.  Host code never passes the array's name to
+// a kernel (on the host it names a stand-in, not device memory): it passes the device address
+// looked up below, one per device.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kAttendScratchBytes];
+
+int attend_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
+}
+
 int launch_attend(int bits, int qg, const AttendArgs& a, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (bits == 2) {
