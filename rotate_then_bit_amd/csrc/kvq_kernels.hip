@@ -124,10 +124,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 #define KVQ_QP2 " quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
 
 // v <- partner(v) * m + v for 8 values, partner = lane xor 1.  The leading s_nop gives
-// the 5 wait states a DPP read needs after an EXEC write (2 after a VALU write of its
-// operands), since the compiler does not look inside the asm.
+// the 2 wait states a DPP read needs after a VALU write of its operand, since the compiler
+// does not look inside the asm (no VALU instruction in these kernels writes EXEC, which
+// would need 5).
 __device__ __forceinline__ void fmac_x1(float* v, float m) {
-  asm("s_nop 4\n\t"
+  asm("s_nop 1\n\t"
       "v_fmac_f32_dpp %0, %0, %8" KVQ_QP1 "\n\t"
       "v_fmac_f32_dpp %1, %1, %8" KVQ_QP1 "\n\t"
       "v_fmac_f32_dpp %2, %2, %8" KVQ_QP1 "\n\t"
@@ -142,7 +143,7 @@ __device__ __forceinline__ void fmac_x1(float* v, float m) {
 }
 
 __device__ __forceinline__ void fmac_x2(float* v, float m) {
-  asm("s_nop 4\n\t"
+  asm("s_nop 1\n\t"
       "v_fmac_f32_dpp %0, %0, %8" KVQ_QP2 "\n\t"
       "v_fmac_f32_dpp %1, %1, %8" KVQ_QP2 "\n\t"
       "v_fmac_f32_dpp %2, %2, %8" KVQ_QP2 "\n\t"
@@ -162,27 +163,27 @@ __device__ __forceinline__ float swz_x4(float v) {
 }
 
 __device__ __forceinline__ float min_x1(float v) {
-  asm("s_nop 4\n\tv_min_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
+  asm("s_nop 1\n\tv_min_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float min_x2(float v) {
-  asm("s_nop 4\n\tv_min_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
+  asm("s_nop 1\n\tv_min_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float max_x1(float v) {
-  asm("s_nop 4\n\tv_max_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float max_x2(float v) {
-  asm("s_nop 4\n\tv_max_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float add_x1(float v) {
-  asm("s_nop 4\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP1 : "+v"(v));
   return v;
 }
 __device__ __forceinline__ float add_x2(float v) {
-  asm("s_nop 4\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
   return v;
 }
 
@@ -250,18 +251,19 @@ __device__ __forceinline__ float f16_value(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
-// fp16 with directed rounding, from the IEEE bit pattern of the nearest value.
+// fp16 with directed rounding, from the conversion that rounds toward zero: for x < 0 an
+// inexact result moves one step away from zero (down), for x >= 0 it is already rounded
+// down.  x must not be -0 (the callers add +0 first).
 __device__ __forceinline__ uint32_t f16_round_down(float x) {
-  _Float16 h = (_Float16)x;
-  uint32_t b = __builtin_bit_cast(uint16_t, h);
-  if ((float)h > x) b = (b & 0x8000u) ? b + 1u : (b == 0u ? 0x8001u : b - 1u);
-  return b;
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, 0.0f));  // high half 0
+  const float back = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  return h + ((back != x && x < 0.0f) ? 1u : 0u);
 }
-__device__ __forceinline__ uint32_t f16_round_up(float x) {
-  _Float16 h = (_Float16)x;
-  uint32_t b = __builtin_bit_cast(uint16_t, h);
-  if ((float)h < x) b = (b & 0x8000u) ? (b == 0x8000u ? 0x0001u : b - 1u) : b + 1u;
-  return b;
+// The same rounded up, for x >= 0 (a scale): an inexact result moves one step up.
+__device__ __forceinline__ uint32_t f16_round_up_nonneg(float x) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, 0.0f));
+  const float back = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  return h + (back != x ? 1u : 0u);
 }
 
 // One lane's 32 channels of one vector as stored: 4 x 16 bytes for 16-bit types,
@@ -879,7 +881,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       const uint32_t zb = f16_round_down(mn + 0.0f);
       const float z = f16_value(zb);
       constexpr float kInvLevels = 1.0f / (float)((1 << BITS) - 1);
-      const uint32_t sb = f16_round_up((mx - z) * kInvLevels + 0.0f);
+      const uint32_t sb = f16_round_up_nonneg((mx - z) * kInvLevels + 0.0f);
       const float sc = f16_value(sb);
       {
         // every lane of a group holds the same values and stores them
@@ -1426,27 +1428,32 @@ inline unsigned sink_blocks(const CodecArgs& a, int lv) {
 // summed unrotated.  Three passes: rotate the queries; per (row, KV head, chunk of slots)
 // a partial softmax-weighted sum; per (row, query head) the merge of the chunks, the
 // rotation back, the sinks and the normalisation.
-__device__ __forceinline__ float hsign(uint32_t a, uint32_t b) {
-  return (__builtin_popcount(a & b) & 1) ? -1.0f : 1.0f;
-}
 constexpr float kInvSqrt128 = 0.08838834764831845f;
 
-// rotated queries M P q: one wave per (row, query head), lane i computes channels i, i + 64
+// Unnormalised Walsh-Hadamard transform (Sylvester order) of 128 values held by a wave as
+// v0 = x[lane], v1 = x[lane + 64]: index bit 6 in the lane, bits 0..5 across lanes (7 stages
+// of the butterfly network, 14 additions per lane).
+__device__ __forceinline__ void fwht128_wave(float& v0, float& v1, int lane) {
+  const float a = v0, b = v1;
+  v0 = a + b;
+  v1 = a - b;
+#pragma unroll
+  for (int bit = 1; bit < 64; bit <<= 1) {
+    const float p0 = __shfl_xor(v0, bit), p1 = __shfl_xor(v1, bit);
+    v0 = (lane & bit) ? p0 - v0 : v0 + p0;
+    v1 = (lane & bit) ? p1 - v1 : v1 + p1;
+  }
+}
+
+// rotated queries M P q: one wave per (row, query head); lane i holds channels i and i + 64
 __global__ void __launch_bounds__(256) attend_rotate_q(const AttendArgs a) {
-  __shared__ float s_q[4][128];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.q_heads) return;  // wave-uniform; no block barrier in this kernel
   const float* q = a.q + w * 128;
-  float* sq = s_q[wave];
-  for (int k = lane; k < 128; k += 64) sq[k] = q[a.use_perm_k ? a.perm_k[k] : k];  // (P q)[k] = q[perm[k]]
-  wave_lds_sync();
-  float z0 = 0.0f, z1 = 0.0f;
-  for (int k = 0; k < 128; ++k) {
-    const float v = sq[k];
-    z0 = __builtin_fmaf(hsign((uint32_t)lane, (uint32_t)k), v, z0);
-    z1 = __builtin_fmaf(hsign((uint32_t)lane + 64u, (uint32_t)k), v, z1);
-  }
+  // (P q)[k] = q[perm[k]]
+  float z0 = q[a.use_perm_k ? a.perm_k[lane] : lane], z1 = q[a.use_perm_k ? a.perm_k[lane + 64] : lane + 64];
+  fwht128_wave(z0, z1, lane);
   a.qrot[w * 128 + lane] = z0 * kInvSqrt128;
   a.qrot[w * 128 + lane + 64] = z1 * kInvSqrt128;
 }
@@ -2291,7 +2298,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
 
 // Merge the chunks of each (row, query head), rotate back, add the sink slots, normalise.
 __global__ void __launch_bounds__(256) attend_combine(const AttendArgs a) {
-  __shared__ float s_acc[4][128];
   __shared__ float s_out[4][128];
   __shared__ float s_sc[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -2316,17 +2322,9 @@ __global__ void __launch_bounds__(256) attend_combine(const AttendArgs a) {
     a1 = __builtin_fmaf(f, pb[c * kAttendPart + lane + 64], a1);
   }
   // back from the rotated domain: z = M acc, then out[perm[j]] = z[j]
-  float* sa = s_acc[wave];
   float* so = s_out[wave];
-  sa[lane] = a0;
-  sa[lane + 64] = a1;
-  wave_lds_sync();
-  float z0 = 0.0f, z1 = 0.0f;
-  for (int k = 0; k < 128; ++k) {
-    const float v = sa[k];
-    z0 = __builtin_fmaf(hsign((uint32_t)lane, (uint32_t)k), v, z0);
-    z1 = __builtin_fmaf(hsign((uint32_t)lane + 64u, (uint32_t)k), v, z1);
-  }
+  float z0 = a0, z1 = a1;
+  fwht128_wave(z0, z1, lane);
   so[a.use_perm_v ? a.perm_v[lane] : lane] = z0 * kInvSqrt128;
   so[a.use_perm_v ? a.perm_v[lane + 64] : lane + 64] = z1 * kInvSqrt128;
   wave_lds_sync();
