@@ -653,4 +653,108 @@ def check_attention_rotated_domain():
     assert np.allclose(got, ref, atol=1e-11)
 
 
+
+
+# --------------------------------------------------------------------------- #
+# calibration of the RotateKV variants (channel statistics, reordering, sinks)
+# --------------------------------------------------------------------------- #
+def check_channel_stats():
+    """Brute-force loops (sinks left out); RoPE'd statistic of a one-channel input equals the
+    mean |cos| / |sin| of its angles (library trig); position 0 alone gives mean |x|."""
+    from oracle import calibration as cal
+    rng = _rng(30)
+    x = rng.standard_normal((2, 7, 3, 8)) * np.arange(1, 9)
+    got = cal.channel_stats(x, n_sink=2)
+    want = np.zeros(8)
+    n = 0
+    for r in range(2):
+        for t in range(2, 7):
+            for h in range(3):
+                n += 1
+                for c in range(8):
+                    want[c] += abs(x[r, t, h, c])
+    assert np.allclose(got, want / n, rtol=1e-14)
+    d, t = 128, 300
+    x1 = np.zeros((1, t, 1, d))
+    i = 5
+    x1[..., 2 * i] = 1.0
+    th = 10000.0 ** (-2.0 * i / d)
+    pos = 17 + np.arange(t)
+    s = cal.channel_stats(x1, rope=True, pos_offset=17)
+    assert np.isclose(s[2 * i], np.mean(np.abs(np.cos(pos * th))), rtol=1e-13)
+    assert np.isclose(s[2 * i + 1], np.mean(np.abs(np.sin(pos * th))), rtol=1e-13)
+    assert np.all(np.delete(s, [2 * i, 2 * i + 1]) == 0.0)
+    x0 = rng.standard_normal((3, 1, 2, 128))
+    assert np.allclose(cal.channel_stats(x0, rope=True), np.abs(x0).reshape(-1, 128).mean(0), rtol=1e-14)
+
+
+def check_outlier_perm():
+    """Worked placement; a bijection; equal statistics in channel order; and the property
+    the reading rests on: a huge channel placed at a multiple of G leaves every group's
+    range of the rotated vector unchanged, placed elsewhere it widens it."""
+    from oracle import calibration as cal
+    st = np.ones(128)
+    st[[5, 77, 3, 100, 9]] = [10.0, 9.0, 8.0, 7.0, 6.0]
+    p = cal.outlier_perm(st, 32)
+    assert sorted(p.tolist()) == list(range(128))
+    assert [int(p[j]) for j in (0, 32, 64, 96)] == [5, 77, 3, 100]
+    rest = [int(p[j]) for j in range(128) if j % 32]
+    assert rest == sorted(set(range(128)) - {5, 77, 3, 100})
+    assert list(cal.outlier_perm(np.ones(128), 128)) == list(range(128))  # equal statistics: channel order
+    p2 = cal.outlier_perm(np.ones(64), 32)
+    assert [int(p2[0]), int(p2[32])] == [0, 1] and list(p2[1:32]) == list(range(2, 33)) and list(p2[33:]) == list(range(33, 64))
+    rng = _rng(31)
+    for g in (32, 64, 128):
+        x = rng.standard_normal((5, 128))
+        c = 41
+        x[:, c] += 200.0
+        st = cal.channel_stats(x[None, :, None, :])
+        perm = cal.outlier_perm(st, g).astype(np.int64)
+        assert perm[0] == c
+        x0 = x.copy()
+        x0[:, c] = 0.0
+
+        def ranges(v, pm):
+            z = rotations.fwht(v[:, pm]).reshape(5, 128 // g, g)
+            return z.max(-1) - z.min(-1)
+        assert np.allclose(ranges(x, perm), ranges(x0, perm), atol=1e-9)
+        bad = perm.copy()
+        bad[[0, 1]] = bad[[1, 0]]  # the outlier at position 1: signs alternate inside each group
+        assert np.all(ranges(x, bad) > ranges(x0, bad) + 10.0)
+
+
+def check_sink_detection():
+    """Token norms: numpy's norm, unchanged by RoPE; the lower median's rank property
+    (brute force); a worked row (x50 and x20 tokens among unit ones); loops on random data."""
+    from oracle import calibration as cal
+    rng = _rng(32)
+    x = rng.standard_normal((3, 11, 2, 128))
+    nrm = cal.token_norms(x)
+    assert np.allclose(nrm, np.linalg.norm(x.reshape(3, 11, -1), axis=-1), rtol=1e-14)
+    assert np.allclose(nrm, cal.token_norms(rope.rope(x, np.arange(11) + 1000)), rtol=1e-12)
+    for n in (1, 2, 5, 8, 33):
+        v = rng.standard_normal(n)
+        m = cal.lower_median(v)
+        k = (n - 1) // 2
+        assert np.sum(v < m) <= k and np.sum(v <= m) >= k + 1 and m in v
+        if n % 2:
+            assert m == np.median(v)
+    xs = np.ones((1, 10, 1, 4))
+    xs[0, 0] *= 50.0
+    xs[0, 3] *= 20.0
+    xs[0, 6] *= 7.9
+    f, c, pfx = cal.detect_sinks(xs, 8.0)
+    assert f[0].tolist() == [True, False, False, True] + [False] * 6 and c[0] == 2 and pfx[0] == 4
+    f, c, pfx = cal.detect_sinks(np.ones((2, 5, 1, 4)), 1.0)
+    assert not f.any() and list(pfx) == [0, 0]
+    y = rng.standard_normal((2, 9, 3, 16)) * rng.uniform(0.2, 3.0, (2, 9, 1, 1))
+    f, c, pfx = cal.detect_sinks(y, 1.5)
+    for r in range(2):
+        nn = [np.sqrt(np.sum(y[r, t] ** 2)) for t in range(9)]
+        med = sorted(nn)[4]
+        want = [v > 1.5 * med for v in nn]
+        assert f[r].tolist() == want and c[r] == sum(want)
+        assert pfx[r] == (max(i for i, w in enumerate(want) if w) + 1 if any(want) else 0)
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

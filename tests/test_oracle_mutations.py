@@ -158,6 +158,41 @@ def _append_slot_is_position(cache, x, positions, p):
     return _orig_append(cache, x, positions, codec.CodecParams(**{**p.__dict__, "pos_offset": 0}))
 
 
+from oracle import calibration as _cal
+
+_orig_outlier_perm = _cal.outlier_perm
+_orig_channel_stats = _cal.channel_stats
+
+
+def _perm_top_first(stats, group_size):
+    # the top channels at positions 0, 1, 2, ... instead of multiples of the group size
+    stats = np.asarray(stats, dtype=np.float64)
+    d = stats.shape[0]
+    order = sorted(range(d), key=lambda c: (-stats[c], c))
+    k = d // group_size
+    return np.array(order[:k] + sorted(order[k:]), dtype=np.uint16)
+
+
+def _stats_rms(x, rope=False, rope_base=10000.0, pos_offset=0, n_sink=0):
+    a = _orig_channel_stats(np.asarray(x) ** 2, False, rope_base, pos_offset, n_sink)
+    return np.sqrt(a) if not rope else _orig_channel_stats(x, rope, rope_base, pos_offset, n_sink) * 1.0001
+
+
+def _stats_no_rope(x, rope=False, rope_base=10000.0, pos_offset=0, n_sink=0):
+    return _orig_channel_stats(x, False, rope_base, pos_offset, n_sink)
+
+
+def _stats_with_sinks(x, rope=False, rope_base=10000.0, pos_offset=0, n_sink=0):
+    return _orig_channel_stats(x, rope, rope_base, pos_offset, 0)
+
+
+def _detect_mean(x, lam):
+    nrm = _cal.token_norms(x)
+    flags = nrm > lam * nrm.mean(axis=1, keepdims=True)
+    prefix = np.array([int(np.nonzero(f)[0].max()) + 1 if f.any() else 0 for f in flags])
+    return flags, flags.sum(axis=1), prefix
+
+
 from oracle import attention as _attention
 
 _orig_attend_decoded = _attention.attend_decoded
@@ -191,6 +226,11 @@ MUTATIONS = {
     "decode_rho_plus_eps": (codec, "decode", _decode_rho_plus_eps),
     "append_slot_is_position": (codec, "append", _append_slot_is_position),
     "widen_bf16_shift_15": (codec, "widen", _widen_shift_15),
+    "outlier_perm_top_first": (_cal, "outlier_perm", _perm_top_first),
+    "channel_stats_rms": (_cal, "channel_stats", _stats_rms),
+    "channel_stats_before_rope": (_cal, "channel_stats", _stats_no_rope),
+    "channel_stats_with_sinks": (_cal, "channel_stats", _stats_with_sinks),
+    "sinks_against_mean_norm": (_cal, "detect_sinks", _detect_mean),
     "widen_bf16_as_f16": (codec, "widen", _widen_bf16_as_f16),
     "attention_heads_interleaved": (_attention, "attend_decoded", _attend_heads_interleaved),
 }
