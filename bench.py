@@ -460,6 +460,38 @@ def main():
     # keys two 16x16x64 products per 16 slots, for the values eight per 64 slots
     attend_mfma_ops = r0 * t0_ * h0 * 2 * (2 * 16 * 16 * 64 // 16 + 8 * 16 * 16 * 64 // 64)
 
+    # context, outside the timed region: the RotateKV calibration passes over a slice of the
+    # cache (8 rows of K: 2^23 vectors): per-channel statistics of the post-RoPE keys for the
+    # outlier-aware permutation, and activation-based sink detection (token norms, median)
+    cal_rows = 8
+    ksl = data["inputs"]["K"][:cal_rows]
+    cal_cfg = kvq.Config(shape=tuple(ksl.shape), dtype="bf16", bits=2, group_size=128, rope=True, n_sink=4)
+    ws_cal = torch.empty(max(8, kvq.channel_stats_workspace_size(cal_cfg)), dtype=torch.uint8, device=dev)
+    cal_t = {}
+    with torch.cuda.stream(stream):
+        for name, fn in (("channel_stats", lambda: kvq.channel_stats(ksl, cal_cfg, workspace=ws_cal, stream=stream)),
+                         ("detect_sinks", lambda: kvq.detect_sinks(ksl, cal_cfg, 8.0, stream=stream))):
+            for _ in range(2):
+                fn()
+            stream.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(10):
+                fn()
+            b.record(stream)
+            stream.synchronize()
+            cal_t[name] = a.elapsed_time(b) / 10
+    cal_bytes = int(ksl.numel() * 2)
+    calib = {"slice": f"K rows 0-{cal_rows - 1} of the cache ({int(ksl.shape[0] * ksl.shape[1] * ksl.shape[2])} vectors, "
+                      f"{cal_bytes} bytes read)",
+             **{k: {"ms": round(v, 4), "GBps": round(cal_bytes / (v * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(cal_bytes / (v * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)} for k, v in cal_t.items()},
+             "what": "RotateKV calibration: per-channel mean |post-RoPE key| for the outlier-aware permutation "
+                     "(kvq_channel_stats) and sink detection by token norm against lambda x the row median "
+                     "(kvq_detect_sinks); run once per calibration, not per step"}
+    del ksl, ws_cal
+
     cpu = None
     if pool is not None:
         cpu = cpu_baseline(pool, n_workers, data["inputs"], wl.cases, perm, args.cpu_seconds)
@@ -509,6 +541,7 @@ def main():
                    "what": "decode-step attention over the encoded K/V cache in the rotated domain "
                            "(kvq_attend): exact int8 matrix-core products of the codes with 8-bit digits of "
                            "the rotated queries and of the softmax weights"},
+        "calibration": calib,
         "append": {"us_per_step": round(append_us, 2), "vectors_per_step": append_vec,
                    "what": "decode-step cache update: K and V of every row appended at per-row positions "
                            "(kvq_append, K with RoPE + perm), launch-latency bound"},

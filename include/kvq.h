@@ -205,6 +205,42 @@ size_t kvq_attend_noalloc_max_workspace(void);
 kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int32_t y_dtype,
                       void* stream);
 
+/* Calibration of the outlier-aware channel reordering (RotateKV page, method summary and key
+ * design: channel reordering adapts the Walsh-Hadamard rotation to the channel-wise outlier
+ * distribution).  Reads a calibration slice x exactly as kvq_encode would (cfg's shape, dtype,
+ * strides, RoPE, positions; sink positions p < n_sink are left out) and writes
+ *   stats    DEVICE double [head_dim]: mean |y_c| over every non-sink vector, y the post-RoPE
+ *            vector (the input itself without RoPE); 0 for an empty slice.
+ *   workspace DEVICE, 8-byte aligned, at least kvq_channel_stats_workspace_size(cfg) bytes
+ *            (per-wave float64 sums; scratch between calls).
+ * Sums are float64, in a fixed order (deterministic).  Asynchronous. */
+kvq_status kvq_channel_stats_workspace_size(const kvq_config* cfg, size_t* bytes);
+kvq_status kvq_channel_stats(const kvq_config* cfg, const void* x, double* stats, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Host-only: the outlier-aware gather map perm (HOST uint16 [head_dim], for kvq_config.perm)
+ * from per-channel statistics (HOST double [head_dim], e.g. kvq_channel_stats copied back).
+ * The head_dim / group_size channels with the largest statistic go to positions 0, G, 2G, ...
+ * (largest first; equal statistics in increasing channel order); the other channels fill the
+ * remaining positions in increasing order.  After the Sylvester-ordered Walsh-Hadamard
+ * transform a channel at a multiple of G enters every coefficient of a min-max group with the
+ * same sign, so it shifts the group (absorbed by its zero) without widening its range. */
+kvq_status kvq_outlier_perm(const double* stats, int64_t head_dim, int32_t group_size, uint16_t* perm);
+
+/* Activation-based attention-sink detection (RotateKV page: attention-sink-aware
+ * quantization identifies the sinks from their massive activations).  For every row r and
+ * token t of x (read as kvq_encode reads it; RoPE does not change a norm):
+ *   norms[r, t]  DEVICE double [R, T]: L2 norm of the token over all heads and channels
+ *                (squares summed in float64, exact for 16-bit inputs);
+ *   medians[r]   DEVICE double [R]: the row's lower median norm (rank floor((T-1)/2));
+ *   flags[r, t]  DEVICE uint8 [R, T]: 1 where norms[r, t] > lambda * medians[r];
+ *   counts[r]    DEVICE int32 [R]: flagged tokens; prefix[r] DEVICE int32 [R]: one past the
+ *                last flagged token (0 if none) -- the n_sink that keeps every detected sink
+ *                of the row in the codec's fp16 sink slots.
+ * lambda: finite, >= 0.  Asynchronous. */
+kvq_status kvq_detect_sinks(const kvq_config* cfg, const void* x, double lambda, double* norms, uint8_t* flags,
+                            int32_t* counts, int32_t* prefix, double* medians, void* stream);
+
 /* Host-only: Lloyd-Max codebook (2^bits ascending levels) for N(0, sigma^2), written
  * to codebook_out as float32; the classical fixed point of midpoint thresholds and
  * conditional-mean levels, iterated in double precision (IsoQuant page, section 3.1

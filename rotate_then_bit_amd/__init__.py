@@ -24,6 +24,7 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 
 __all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_noalloc", "attend_noalloc_max_workspace",
+           "channel_stats", "channel_stats_workspace_size", "outlier_perm", "detect_sinks",
            "attend_workspace_size", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
            "library_path", "abi_version", "DTYPES", "ROTATIONS", "QUANTIZERS", "EXPORTED_SYMBOLS"]
 
@@ -36,7 +37,8 @@ ROTATIONS = {"none": 0, "fwht": 1, "so4": 2}
 QUANTIZERS = {"minmax": 0, "lloyd": 1}
 EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append",
                     "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_attend_noalloc_max_workspace",
-                    "kvq_decode", "kvq_lloyd_max_gaussian",
+                    "kvq_decode", "kvq_lloyd_max_gaussian", "kvq_channel_stats_workspace_size", "kvq_channel_stats",
+                    "kvq_outlier_perm", "kvq_detect_sinks",
                     "kvq_status_string", "kvq_last_error_message")
 
 
@@ -109,12 +111,18 @@ def _load():
                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     lib.kvq_attend_noalloc_max_workspace.restype = ctypes.c_size_t
     lib.kvq_attend_noalloc_max_workspace.argtypes = []
+    lib.kvq_channel_stats_workspace_size.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_channel_stats.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]
+    lib.kvq_outlier_perm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    lib.kvq_detect_sinks.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.c_double] + [ctypes.c_void_p] * 6
     lib.kvq_lloyd_max_gaussian.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_last_error_message.restype = ctypes.c_char_p
     for fn in ("kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append", "kvq_decode", "kvq_lloyd_max_gaussian",
-               "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc"):
+               "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_channel_stats_workspace_size",
+               "kvq_channel_stats", "kvq_outlier_perm", "kvq_detect_sinks"):
         getattr(lib, fn).restype = ctypes.c_int
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -337,6 +345,52 @@ def decode(planes, cfg: Config, out_dtype: str = "f32", out=None, stream=None):
     p = _planes_struct(planes)
     _check(_L().kvq_decode(ctypes.byref(c), ctypes.byref(p), _ptr(out), DTYPES[out_dtype], _stream_handle(stream)))
     return out
+
+
+def channel_stats_workspace_size(cfg: Config) -> int:
+    """Bytes of device workspace ``channel_stats`` needs for this slice shape."""
+    c = cfg.c_struct()
+    n = ctypes.c_size_t()
+    _check(_L().kvq_channel_stats_workspace_size(ctypes.byref(c), ctypes.byref(n)))
+    return int(n.value)
+
+
+def channel_stats(x, cfg: Config, workspace=None, stream=None):
+    """Per-channel mean |y_c| (float64 device tensor [D]) of the calibration slice ``x``, read
+    as ``encode`` reads it (post-RoPE for keys, sink positions left out)."""
+    import torch
+    c = cfg.c_struct()
+    if workspace is None:
+        workspace = torch.empty(max(channel_stats_workspace_size(cfg), 8), dtype=torch.uint8, device=x.device)
+    stats = torch.empty(int(cfg.shape[-1]), dtype=torch.float64, device=x.device)
+    _check(_L().kvq_channel_stats(ctypes.byref(c), _ptr(x), int(stats.data_ptr()), int(workspace.data_ptr()),
+                                  int(workspace.numel() * workspace.element_size()), _stream_handle(stream)))
+    return stats
+
+
+def outlier_perm(stats, group_size: int) -> np.ndarray:
+    """Host-side outlier-aware gather map (uint16 [D]) from per-channel statistics."""
+    st = np.ascontiguousarray(np.asarray(stats, dtype=np.float64))
+    perm = np.zeros(st.shape[0], dtype=np.uint16)
+    _check(_L().kvq_outlier_perm(st.ctypes.data, int(st.shape[0]), int(group_size), perm.ctypes.data))
+    return perm
+
+
+def detect_sinks(x, cfg: Config, lam: float, stream=None):
+    """Activation-based sink detection of the slice ``x``: returns device tensors
+    (norms f64 [R,T], flags u8 [R,T], counts i32 [R], prefix i32 [R], medians f64 [R])."""
+    import torch
+    r, t = int(cfg.shape[0]), int(cfg.shape[1])
+    dev = x.device
+    norms = torch.empty((r, t), dtype=torch.float64, device=dev)
+    flags = torch.empty((r, t), dtype=torch.uint8, device=dev)
+    counts = torch.empty(r, dtype=torch.int32, device=dev)
+    prefix = torch.empty(r, dtype=torch.int32, device=dev)
+    medians = torch.empty(r, dtype=torch.float64, device=dev)
+    c = cfg.c_struct()
+    _check(_L().kvq_detect_sinks(ctypes.byref(c), _ptr(x), float(lam), _ptr(norms), _ptr(flags), _ptr(counts),
+                                 _ptr(prefix), _ptr(medians), _stream_handle(stream)))
+    return norms, flags, counts, prefix, medians
 
 
 def lloyd_max_gaussian(bits: int, sigma: float) -> np.ndarray:

@@ -502,6 +502,125 @@ kvq_status kvq_attend_noalloc(const kvq_config* cfg_k, const kvq_planes* k, cons
 
 size_t kvq_attend_noalloc_max_workspace(void) { return kvq::kAttendScratchBytes; }
 
+namespace {
+// the calibration calls read x exactly as kvq_encode does (shape, dtype, strides, RoPE,
+// positions and sinks from cfg)
+void fill_calib(const kvq_config* cfg, const Derived& dv, const void* x, kvq::CalibArgs* a) {
+  memset(a, 0, sizeof *a);
+  a->x = x;
+  a->rows = cfg->rows;
+  a->tokens = cfg->tokens;
+  a->heads = cfg->heads;
+  a->head_dim = cfg->head_dim;
+  a->sr = dv.sr;
+  a->st = dv.st;
+  a->sh = dv.sh;
+  a->pos_offset = cfg->pos_offset;
+  a->rope = cfg->rope;
+  a->rope_log2_base = cfg->rope ? log2(cfg->rope_base) : 0.0;
+  a->n_sink = cfg->n_sink;
+  a->dtype = cfg->dtype;
+  a->tpw = kvq::calib_tokens_per_wave(cfg->rows, cfg->tokens);
+  a->n_waves = cfg->rows * ((cfg->tokens + a->tpw - 1) / a->tpw);
+}
+}  // namespace
+
+kvq_status kvq_channel_stats_workspace_size(const kvq_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+  Derived dv;
+  kvq_status st = check_config(cfg, &dv);
+  if (st != KVQ_OK) return st;
+  kvq::CalibArgs a;
+  fill_calib(cfg, dv, nullptr, &a);
+  *bytes = (size_t)a.n_waves * (size_t)cfg->head_dim * sizeof(double);
+  return ok();
+}
+
+kvq_status kvq_channel_stats(const kvq_config* cfg, const void* x, double* stats, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Derived dv;
+  kvq_status st = check_config(cfg, &dv);
+  if (st != KVQ_OK) return st;
+  if (!stats) return fail(KVQ_ERR_NULL, "stats is NULL");
+  if (reinterpret_cast<uintptr_t>(stats) & 7u) return fail(KVQ_ERR_ALIGN, "stats not 8-byte aligned");
+  kvq::CalibArgs a;
+  fill_calib(cfg, dv, x, &a);
+  const size_t need = (size_t)a.n_waves * (size_t)cfg->head_dim * sizeof(double);
+  if (need > 0) {
+    if (!x) return fail(KVQ_ERR_NULL, "x is NULL");
+    if (!aligned16(x)) return fail(KVQ_ERR_ALIGN, "x not 16-byte aligned");
+    if (!workspace) return fail(KVQ_ERR_NULL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 7u) return fail(KVQ_ERR_ALIGN, "workspace not 8-byte aligned");
+    if (workspace_bytes < need) return fail(KVQ_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  a.part = static_cast<double*>(workspace);
+  a.stats = stats;
+  if (a.n_waves > (int64_t(1) << 33)) return fail(KVQ_ERR_SHAPE, "calibration slice too large");
+  const int err = kvq::launch_channel_stats(a, stream);
+  if (err != 0) return fail(KVQ_ERR_DEVICE, "channel statistics launch failed: %s", kvq::device_error_string(err));
+  return ok();
+}
+
+kvq_status kvq_outlier_perm(const double* stats, int64_t head_dim, int32_t group_size, uint16_t* perm) {
+  if (!stats || !perm) return fail(KVQ_ERR_NULL, "stats or perm is NULL");
+  if (head_dim != 128 && head_dim != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim %lld (supported: 128, 256)", (long long)head_dim);
+  if (!(group_size == 32 || group_size == 64 || group_size == 128 || group_size == 256) || group_size > head_dim)
+    return fail(KVQ_ERR_GROUP, "group_size %d (32, 64, 128 or 256, at most head_dim)", group_size);
+  const int d = (int)head_dim;
+  for (int c = 0; c < d; ++c)
+    if (!isfinite(stats[c])) return fail(KVQ_ERR_PARAM, "stats[%d] is not finite", c);
+  // channels by decreasing statistic, equal statistics in increasing channel order
+  int order[kvq::kMaxHeadDim];
+  for (int c = 0; c < d; ++c) order[c] = c;
+  std::stable_sort(order, order + d, [&](int i, int j) { return stats[i] > stats[j]; });
+  const int k = d / group_size;
+  bool top[kvq::kMaxHeadDim] = {false};
+  for (int a = 0; a < k; ++a) {
+    perm[a * group_size] = (uint16_t)order[a];
+    top[order[a]] = true;
+  }
+  // the other channels, in increasing order, fill the positions that are not multiples of G
+  int j = 0;
+  for (int c = 0; c < d; ++c) {
+    if (top[c]) continue;
+    while (j % group_size == 0) ++j;
+    perm[j++] = (uint16_t)c;
+  }
+  return ok();
+}
+
+kvq_status kvq_detect_sinks(const kvq_config* cfg, const void* x, double lambda, double* norms, uint8_t* flags,
+                            int32_t* counts, int32_t* prefix, double* medians, void* stream) {
+  Derived dv;
+  kvq_status st = check_config(cfg, &dv);
+  if (st != KVQ_OK) return st;
+  if (!(isfinite(lambda) && lambda >= 0.0)) return fail(KVQ_ERR_PARAM, "lambda must be finite and >= 0");
+  if (cfg->rows == 0) return ok();
+  if (!counts || !prefix || !medians) return fail(KVQ_ERR_NULL, "counts, prefix or medians is NULL");
+  if ((reinterpret_cast<uintptr_t>(counts) & 3u) || (reinterpret_cast<uintptr_t>(prefix) & 3u) ||
+      (reinterpret_cast<uintptr_t>(medians) & 7u))
+    return fail(KVQ_ERR_ALIGN, "counts, prefix (4 bytes) or medians (8 bytes) misaligned");
+  if (cfg->tokens > 0) {
+    if (!x || !norms || !flags) return fail(KVQ_ERR_NULL, "x, norms or flags is NULL");
+    if (!aligned16(x)) return fail(KVQ_ERR_ALIGN, "x not 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(norms) & 7u) return fail(KVQ_ERR_ALIGN, "norms not 8-byte aligned");
+  }
+  kvq::CalibArgs a;
+  fill_calib(cfg, dv, x, &a);
+  a.lambda = lambda;
+  a.norms = norms;
+  a.flags = flags;
+  a.counts = counts;
+  a.prefix = prefix;
+  a.medians = medians;
+  if (cfg->rows > 0x7fffffff || cfg->rows * cfg->tokens > (int64_t(1) << 33))
+    return fail(KVQ_ERR_SHAPE, "calibration slice too large");
+  const int err = kvq::launch_detect_sinks(a, stream);
+  if (err != 0) return fail(KVQ_ERR_DEVICE, "sink detection launch failed: %s", kvq::device_error_string(err));
+  return ok();
+}
+
 kvq_status kvq_lloyd_max_gaussian(int32_t bits, double sigma, float* codebook_out) {
   if (!codebook_out) return fail(KVQ_ERR_NULL, "codebook_out is NULL");
   if (bits < 1 || bits > 4) return fail(KVQ_ERR_BITS, "bits %d (1..4)", bits);

@@ -121,6 +121,35 @@ constexpr size_t kAttendScratchBytes = size_t(32) << 20;
 // hipGetSymbolAddress); returns a hipError_t as int.
 int attend_scratch(void** ptr);
 
+// Calibration of the RotateKV variants: per-channel statistics of a calibration slice (for the
+// outlier-aware permutation) and activation-based sink detection.
+struct CalibArgs {
+  const void* x;  // [R, T, H, D] with strides (elements)
+  int64_t rows, tokens, heads, head_dim;
+  int64_t sr, st, sh;
+  int64_t pos_offset;
+  double rope_log2_base;
+  int32_t dtype, rope, n_sink;
+  int32_t tpw;       // tokens per wave of the statistics pass
+  int64_t n_waves;   // waves of the statistics pass: rows * ceil(tokens / tpw)
+  double* part;      // workspace [n_waves, D]: per-wave sums of |y_c|
+  double* stats;     // [D]: mean |y_c| over the non-sink vectors
+  double lambda;     // sink threshold (times the row's lower median token norm)
+  double* norms;     // [R, T] token norms
+  uint8_t* flags;    // [R, T]
+  int32_t* counts;   // [R]
+  int32_t* prefix;   // [R]: one past the last flagged token (0 if none)
+  double* medians;   // [R] lower median token norm
+};
+inline int32_t calib_tokens_per_wave(int64_t rows, int64_t tokens) {
+  // about 8 K waves over the slice, at least 16 tokens each
+  const int64_t want = (rows * tokens + 8191) / 8192;
+  const int64_t t = ((want > 16 ? want : 16) + 15) / 16 * 16;
+  return (int32_t)(t > (1 << 20) ? (1 << 20) : t);
+}
+int launch_channel_stats(const CalibArgs& a, void* stream);
+int launch_detect_sinks(const CalibArgs& a, void* stream);
+
 // Launch helpers, one per (direction, dtype, head_dim), defined in kvq_kernels.hip.
 // Each returns a hipError_t as int (0 = success).
 #define KVQ_DECLARE_LAUNCH(NAME) int NAME(int bits, int rot, int quant, const CodecArgs& a, void* stream);

@@ -2603,4 +2603,253 @@ int launch_attend(int bits, int qg, const AttendArgs& a, void* stream) {
 }
 #endif
 
+#if KVQ_UNIT == 13 || KVQ_UNIT == -1
+// ---------------------------------------------------------------------------
+// CALIBRATION OF THE ROTATEKV VARIANTS
+// ---------------------------------------------------------------------------
+// Channel statistics for the outlier-aware permutation: mean |y_c| of the post-RoPE vectors of
+// a calibration slice, sink positions left out.  Token norms and a per-row median for the
+// activation-based sink detection.  Both read the slice once; neither is on the codec's path.
+namespace {
+// One wave per (row, run of tpw tokens).  Lane i owns the channel pairs (2i, 2i + 1) (and
+// (2i + 128, 2i + 129) at d = 256), so each load instruction of the wave covers one vector's
+// bytes contiguously, and the pair's cos/sin is computed once per token for all heads.  Sums
+// of |y| are float64 per lane; the per-wave sums go to the workspace.
+template <int DT, int D>
+__global__ void __launch_bounds__(256) channel_stats_kernel(const CalibArgs a) {
+  constexpr int NP = D / 128;  // channel pairs per lane
+  constexpr int ES = (DT == DT_F32) ? 4 : 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.n_waves) return;  // wave-uniform; no block barrier in this kernel
+  const int64_t nchunk = (a.tokens + a.tpw - 1) / a.tpw;
+  const int64_t r = w / nchunk, t0 = (w % nchunk) * a.tpw;
+  const int64_t t1 = min(t0 + (int64_t)a.tpw, a.tokens);
+  double theta[NP], s0[NP], s1[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    theta[k] = exp2(-(2.0 * (double)(lane + 64 * k) / (double)D) * a.rope_log2_base);
+    s0[k] = 0.0;
+    s1[k] = 0.0;
+  }
+  const char* base = reinterpret_cast<const char*>(a.x);
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t pos = a.pos_offset + t;
+    if (pos < a.n_sink) continue;  // a sink position (wave-uniform)
+    float c[NP], sn[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      c[k] = 1.0f;
+      sn[k] = 0.0f;
+      if (a.rope) rope_cos_sin(pos, theta[k], &c[k], &sn[k]);
+    }
+    for (int64_t h = 0; h < a.heads; ++h) {
+      const char* v = base + (r * a.sr + t * a.st + h * a.sh) * ES;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const int i = lane + 64 * k;  // pair index
+        float x0, x1;
+        if constexpr (DT == DT_F32) {
+          const f32x2_t xx = *reinterpret_cast<const f32x2_t*>(v + 8 * i);
+          x0 = xx.x;
+          x1 = xx.y;
+        } else {
+          const uint32_t wd = *reinterpret_cast<const uint32_t*>(v + 4 * i);
+          if constexpr (DT == DT_BF16) {
+            x0 = __uint_as_float(wd << 16);
+            x1 = __uint_as_float(wd & 0xffff0000u);
+          } else {
+            x0 = f16_value(wd & 0xffffu);
+            x1 = f16_value(wd >> 16);
+          }
+        }
+        float y0 = x0, y1 = x1;
+        if (a.rope) {
+          y0 = __builtin_fmaf(x0, c[k], -x1 * sn[k]);
+          y1 = __builtin_fmaf(x0, sn[k], x1 * c[k]);
+        }
+        s0[k] += (double)fabsf(y0);
+        s1[k] += (double)fabsf(y1);
+      }
+    }
+  }
+  double* pb = a.part + w * D;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int i = lane + 64 * k;
+    pb[2 * i] = s0[k];
+    pb[2 * i + 1] = s1[k];
+  }
+}
+
+// stats[c] = (sum over waves of the per-wave sums) / (vectors counted); one block per channel,
+// a fixed reduction order (deterministic).
+template <int D>
+__global__ void __launch_bounds__(256) channel_stats_final(const CalibArgs a) {
+  __shared__ double red[256];
+  const int c = blockIdx.x, tid = threadIdx.x;
+  double s = 0.0;
+  for (int64_t w = tid; w < a.n_waves; w += 256) s += a.part[w * D + c];
+  red[tid] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int64_t sink = (int64_t)a.n_sink - a.pos_offset;
+    sink = sink < 0 ? 0 : (sink > a.tokens ? a.tokens : sink);
+    const double n = (double)(a.rows * a.heads * (a.tokens - sink));
+    a.stats[c] = n > 0.0 ? red[0] / n : 0.0;
+  }
+}
+
+// Token norms: one wave per (row, token); the token's heads are read in 16-byte pieces, the
+// squares summed in float64 (exact for 16-bit inputs: each square has at most 22 significant
+// bits, and float32 squares at most 48), then reduced across the wave.
+template <int DT, int D>
+__global__ void __launch_bounds__(256) token_norm_kernel(const CalibArgs a) {
+  constexpr int ES = (DT == DT_F32) ? 4 : 2;
+  constexpr int CPV = D * ES / 16;  // 16-byte pieces per vector
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.tokens) return;  // wave-uniform
+  const int64_t r = w / a.tokens, t = w % a.tokens;
+  const char* base = reinterpret_cast<const char*>(a.x) + (r * a.sr + t * a.st) * ES;
+  double acc = 0.0;
+  for (int64_t k = lane; k < a.heads * CPV; k += 64) {
+    const int64_t h = k / CPV, cc = k % CPV;
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(base + h * a.sh * ES + 16 * cc);
+    const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (DT == DT_F32) {
+        const double x = (double)__uint_as_float(ws[e]);
+        acc = __builtin_fma(x, x, acc);
+      } else {
+        const double x0 = (double)(DT == DT_BF16 ? __uint_as_float(ws[e] << 16) : f16_value(ws[e] & 0xffffu));
+        const double x1 = (double)(DT == DT_BF16 ? __uint_as_float(ws[e] & 0xffff0000u) : f16_value(ws[e] >> 16));
+        acc = __builtin_fma(x0, x0, acc);
+        acc = __builtin_fma(x1, x1, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) a.norms[w] = __builtin_sqrt(acc);
+}
+
+// Per row: the lower median of the T token norms by an exact radix select on their bit
+// patterns (non-negative doubles order as unsigned integers), eight 8-bit digits from the top;
+// then the flags (norm > lambda * median), their count and one past the last flagged token.
+__global__ void __launch_bounds__(256) sink_select_kernel(const CalibArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ int64_t s_k;
+  __shared__ int s_b;
+  __shared__ int s_count, s_last;
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t T = a.tokens;
+  const double* nr = a.norms + r * T;
+  if (T == 0) {
+    if (tid == 0) {
+      a.counts[r] = 0;
+      a.prefix[r] = 0;
+      a.medians[r] = 0.0;
+    }
+    return;  // block-uniform
+  }
+  uint64_t prefix = 0, mask = 0;
+  int64_t k = (T - 1) / 2;  // rank of the lower median among the values that match the prefix
+  for (int d = 7; d >= 0; --d) {
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int64_t t = tid; t < T; t += 256) {
+      const uint64_t v = (uint64_t)__double_as_longlong(nr[t]);
+      if ((v & mask) == prefix) atomicAdd(&hist[(v >> (8 * d)) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int64_t below = 0;
+      int b = 0;
+      for (; b < 255; ++b) {
+        if (below + (int64_t)hist[b] > k) break;
+        below += hist[b];
+      }
+      s_k = k - below;
+      s_b = b;
+    }
+    __syncthreads();
+    k = s_k;
+    prefix |= (uint64_t)s_b << (8 * d);
+    mask |= (uint64_t)255u << (8 * d);
+    __syncthreads();  // every thread has read s_k and s_b before the next digit's histogram
+  }
+  const double med = __longlong_as_double((long long)prefix);
+  if (tid == 0) {
+    s_count = 0;
+    s_last = -1;
+  }
+  __syncthreads();
+  const double thr = a.lambda * med;
+  int cnt = 0, last = -1;
+  for (int64_t t = tid; t < T; t += 256) {
+    const bool f = nr[t] > thr;
+    a.flags[r * T + t] = f ? 1 : 0;
+    cnt += f ? 1 : 0;
+    last = f ? (int)t : last;
+  }
+  atomicAdd(&s_count, cnt);
+  atomicMax(&s_last, last);
+  __syncthreads();
+  if (tid == 0) {
+    a.counts[r] = s_count;
+    a.prefix[r] = s_last + 1;
+    a.medians[r] = med;
+  }
+}
+
+template <int DT, int D>
+int launch_stats_t(const CalibArgs& a, hipStream_t s) {
+  if (a.n_waves > 0) {
+    hipLaunchKernelGGL((channel_stats_kernel<DT, D>), dim3((unsigned)((a.n_waves + 3) / 4)), dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError()) return (int)e;
+  }
+  // (an empty slice still gets its statistics written: all zero)
+  hipLaunchKernelGGL((channel_stats_final<D>), dim3(D), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+template <int DT, int D>
+int launch_sinks_t(const CalibArgs& a, hipStream_t s) {
+  if (a.rows == 0) return 0;
+  const int64_t nw = a.rows * a.tokens;
+  if (nw > 0) {
+    hipLaunchKernelGGL((token_norm_kernel<DT, D>), dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError()) return (int)e;
+  }
+  hipLaunchKernelGGL(sink_select_kernel, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+}  // namespace
+
+int launch_channel_stats(const CalibArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool d128 = a.head_dim == 128;
+  switch (a.dtype) {
+    case DT_F16: return d128 ? launch_stats_t<DT_F16, 128>(a, s) : launch_stats_t<DT_F16, 256>(a, s);
+    case DT_BF16: return d128 ? launch_stats_t<DT_BF16, 128>(a, s) : launch_stats_t<DT_BF16, 256>(a, s);
+    default: return d128 ? launch_stats_t<DT_F32, 128>(a, s) : launch_stats_t<DT_F32, 256>(a, s);
+  }
+}
+int launch_detect_sinks(const CalibArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool d128 = a.head_dim == 128;
+  switch (a.dtype) {
+    case DT_F16: return d128 ? launch_sinks_t<DT_F16, 128>(a, s) : launch_sinks_t<DT_F16, 256>(a, s);
+    case DT_BF16: return d128 ? launch_sinks_t<DT_BF16, 128>(a, s) : launch_sinks_t<DT_BF16, 256>(a, s);
+    default: return d128 ? launch_sinks_t<DT_F32, 128>(a, s) : launch_sinks_t<DT_F32, 256>(a, s);
+  }
+}
+#endif
+
 }  // namespace kvq

@@ -247,3 +247,40 @@ def test_attend_workspace_size_and_refusals_on_the_host():
 def test_positions_up_to_the_limit_are_accepted():
     kvq.validate(_cfg(pos_offset=2 ** 31 - 8))  # 8 tokens: the last position is 2^31 - 1
     kvq.validate(_cfg(shape=(1, 0, 4, 128), pos_offset=2 ** 31))
+
+
+# --------------------------------------------------------------------------- #
+# calibration (host-side parts; no kernel is launched)
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("d,g", [(128, 32), (128, 64), (128, 128), (256, 32), (256, 256)])
+def test_outlier_perm_host_matches_oracle(d, g):
+    """The library's host permutation equals the oracle's for random statistics, for
+    statistics with ties, and for a few large outlier channels."""
+    from oracle import calibration as cal
+    rng = np.random.default_rng(d + g)
+    cases = [rng.random(d), np.round(rng.random(d) * 4) / 4, np.ones(d)]
+    big = rng.random(d)
+    big[rng.choice(d, 7, replace=False)] += 50.0
+    cases.append(big)
+    for st in cases:
+        assert np.array_equal(kvq.outlier_perm(st, g), cal.outlier_perm(st, g))
+
+
+def test_calibration_refusals_on_the_host():
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.outlier_perm(np.ones(128), 48)
+    assert e.value.status == 4
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.outlier_perm(np.array([np.nan] + [1.0] * 127), 32)
+    assert e.value.status == 6
+    lib = ctypes.CDLL(kvq.library_path())
+    lib.kvq_channel_stats.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]
+    lib.kvq_detect_sinks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double] + [ctypes.c_void_p] * 6
+    c = _cfg().c_struct()
+    assert lib.kvq_channel_stats(ctypes.byref(c), 4096, None, 4096, 1 << 20, None) == 1        # stats NULL
+    assert lib.kvq_channel_stats(ctypes.byref(c), 4096, 4096, 4096, 8, None) == 2              # workspace too small
+    assert lib.kvq_channel_stats(ctypes.byref(c), 4100, 4096, 4096, 1 << 20, None) == 7        # x misaligned
+    assert lib.kvq_detect_sinks(ctypes.byref(c), 4096, -1.0, 4096, 4096, 4096, 4096, 4096, None) == 6
+    assert lib.kvq_detect_sinks(ctypes.byref(c), 4096, float("inf"), 4096, 4096, 4096, 4096, 4096, None) == 6
+    assert lib.kvq_detect_sinks(ctypes.byref(c), None, 8.0, 4096, 4096, 4096, 4096, 4096, None) == 1
+    assert lib.kvq_detect_sinks(ctypes.byref(c), 4096, 8.0, 4096, 4096, None, 4096, 4096, None) == 1
