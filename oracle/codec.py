@@ -30,6 +30,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
+from . import dynamic as _dyn
 from . import pack as _pack
 from . import quant as _quant
 from . import rotations as _rot
@@ -50,6 +51,11 @@ class CodecParams:
     quat: Optional[np.ndarray] = None  # [D/4][2][4] (qL, qR), (w, x, y, z)
     codebook: Optional[np.ndarray] = None  # [2^bits] ascending (Lloyd-Max)
     eps: float = 1e-6
+    # dynamic codebook (Lloyd-Max only; see ``dynamic``): per rotated channel scale, the wide
+    # channels and the 2^(bits+1)-level codebook they use; ``codebook`` is then the N(0,1) one
+    chan_scale: Optional[np.ndarray] = None
+    chan_wide: Optional[np.ndarray] = None
+    codebook_wide: Optional[np.ndarray] = None
 
 
 def widen(raw: np.ndarray, dtype: str) -> np.ndarray:
@@ -115,19 +121,20 @@ def encode(x: np.ndarray, p: CodecParams) -> Dict[str, np.ndarray]:
         out["sink_written"][pos[ti]] = True
 
     keep = ~is_sink
-    u = y[:, keep]
+    z, rho = _front(y[:, keep], p)
     if p.quant == "lloyd":
-        rho = np.sqrt(np.sum(u * u, axis=-1))
-        u = u / (rho + p.eps)[..., None]
         out["norm"][:, keep] = rho.astype(np.float32)
-    if p.perm is not None:
-        u = u[..., np.asarray(p.perm, dtype=np.int64)]
-    z = _rotate(u, p)
     if p.quant == "minmax":
         scale, zero = _quant.minmax_params(z, b, g)
         q, tt = _quant.minmax_codes(z, scale, zero, b, g)
         out["scale"][:, keep] = scale
         out["zero"][:, keep] = zero
+    elif p.chan_scale is not None:
+        q, top, tt = _dyn.dyn_codes(z, p.chan_scale, p.chan_wide, p.codebook, p.codebook_wide, b)
+        out["extra"] = np.zeros((r, t, h, d // 128), dtype=np.uint8)
+        out["extra"][:, keep] = _dyn.pack_extra(top, p.chan_wide)
+        out["top"] = np.zeros((r, t, h, d), dtype=np.uint8)
+        out["top"][:, keep] = top
     else:
         q = _quant.lloyd_codes(z, p.codebook)
         tt = z
@@ -138,6 +145,32 @@ def encode(x: np.ndarray, p: CodecParams) -> Dict[str, np.ndarray]:
     return out
 
 
+def _front(y: np.ndarray, p: CodecParams):
+    """Norm separation (Lloyd-Max), permutation and rotation of post-RoPE vectors y:
+    returns (z, rho) with rho None for min-max."""
+    u = y
+    rho = None
+    if p.quant == "lloyd":
+        rho = np.sqrt(np.sum(u * u, axis=-1))
+        u = u / (rho + p.eps)[..., None]
+    if p.perm is not None:
+        u = u[..., np.asarray(p.perm, dtype=np.int64)]
+    return _rotate(u, p), rho
+
+
+def rotated_moments(x: np.ndarray, p: CodecParams) -> np.ndarray:
+    """Per rotated channel mean z_j^2 over the non-sink vectors of a calibration slice x: the
+    online statistics of the dynamic codebook (IsoQuant page, section 4.2, step 1)."""
+    x = np.asarray(x, dtype=np.float64)
+    r, t, h, d = x.shape
+    pos = p.pos_offset + np.arange(t, dtype=np.int64)
+    y = _rope(x, pos, p.rope_base) if p.rope else x
+    keep = pos >= p.n_sink
+    z, _ = _front(y[:, keep], p)
+    n = z.shape[0] * z.shape[1] * z.shape[2]
+    return (z * z).reshape(-1, d).sum(axis=0) / n if n else np.zeros(d)
+
+
 def decode(planes: Dict[str, np.ndarray], p: CodecParams, shape) -> np.ndarray:
     """Decode stored planes back to [R, T, H, D] float64 (post-RoPE, original channel order)."""
     r, t, h, d = shape
@@ -145,6 +178,9 @@ def decode(planes: Dict[str, np.ndarray], p: CodecParams, shape) -> np.ndarray:
     q = _pack.unpack(planes["codes"], b, d)
     if p.quant == "minmax":
         yhat = _quant.minmax_dequant(q, planes["scale"], planes["zero"], g)
+    elif p.chan_scale is not None:
+        top = _dyn.unpack_extra(planes["extra"], p.chan_wide)
+        yhat = _dyn.dyn_dequant(q, top, p.chan_scale, p.chan_wide, p.codebook, p.codebook_wide, b)
     else:
         yhat = _quant.lloyd_dequant(q, p.codebook)
     w = _unrotate(yhat, p)
@@ -161,7 +197,7 @@ def decode(planes: Dict[str, np.ndarray], p: CodecParams, shape) -> np.ndarray:
     return v
 
 
-PLANE_NAMES = ("codes", "scale", "zero", "norm", "sink")
+PLANE_NAMES = ("codes", "scale", "zero", "norm", "sink", "extra")
 
 
 def append(cache: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, p: CodecParams) -> Dict[str, np.ndarray]:
@@ -185,7 +221,7 @@ def append(cache: Dict[str, np.ndarray], x: np.ndarray, positions: np.ndarray, p
         if not 0 <= slot < slots:
             continue
         one = encode(x[r][None, None], replace(p, pos_offset=pos))
-        for name in ("codes", "scale", "zero", "norm"):
+        for name in ("codes", "scale", "zero", "norm", "extra"):
             if name in out and name in one:
                 out[name][r, slot] = one[name][0, 0]
         if pos < p.n_sink:

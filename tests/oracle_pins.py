@@ -757,4 +757,91 @@ def check_sink_detection():
         assert pfx[r] == (max(i for i, w in enumerate(want) if w) + 1 if any(want) else 0)
 
 
+# --------------------------------------------------------------------------- #
+# IsoQuant dynamic codebook
+# --------------------------------------------------------------------------- #
+def check_dynamic_kl_scale():
+    """The KL-closest zero-mean Gaussian to a heavy-tailed sample (Student-t, library log
+    density) has s^2 = mean z^2: the cross-entropy over a fine grid of s is smallest there."""
+    from scipy.stats import norm as _norm
+    from oracle import dynamic as dyn
+    rng = _rng(40)
+    z = rng.standard_t(3, size=20000) * 0.07
+    m = np.mean(z * z)
+    grid = np.sqrt(m) * np.linspace(0.8, 1.2, 401)
+    ce = [-np.mean(_norm.logpdf(z, scale=sg)) for sg in grid]
+    assert abs(grid[int(np.argmin(ce))] - np.sqrt(m)) <= (grid[1] - grid[0])
+    mm = rng.uniform(0.1, 4.0, 128)
+    mm[[7, 99, 3, 50, 51, 52, 53, 60]] = 9.0 + np.arange(8)
+    sc, wide, cb, cbw = dyn.dynamic_codebook(mm, 3)
+    assert np.allclose(sc, np.sqrt(mm), rtol=1e-15) and wide.sum() == 8
+    assert set(np.nonzero(wide)[0].tolist()) == {7, 99, 3, 50, 51, 52, 53, 60}
+    assert np.allclose(cb, lloyd.fit_gaussian(3, 1.0)) and np.allclose(cbw, lloyd.fit_gaussian(4, 1.0))
+
+
+def check_dynamic_codes():
+    """Codes = the nearest level of the channel's own scaled codebook (brute force), wide
+    channels over 2^(b+1) levels; the extra plane's worked example and round trip."""
+    from oracle import dynamic as dyn
+    rng = _rng(41)
+    d, b = 128, 3
+    mm = rng.uniform(0.5, 2.0, d) / d
+    sc, wide, cb, cbw = dyn.dynamic_codebook(mm, b)
+    z = rng.standard_normal((50, d)) * sc * rng.uniform(0.5, 2.5, (50, 1))
+    q, top, _ = dyn.dyn_codes(z, sc, wide, cb, cbw, b)
+    full = q.astype(np.int64) + (top.astype(np.int64) << b)
+    for j in range(d):
+        lev = (cbw if wide[j] else cb) * sc[j]
+        nearest = np.argmin(np.abs(z[:, j][:, None] - lev[None, :]), axis=1)
+        assert np.array_equal(full[:, j], nearest), j
+        assert np.all(top[:, j] == 0) or wide[j]
+    y = dyn.dyn_dequant(q, top, sc, wide, cb, cbw, b)
+    assert np.array_equal(y, np.where(wide, cbw[full], cb[np.minimum(full, 7)]) * sc)
+    w = np.zeros(128, dtype=bool)
+    w[[3, 10, 20, 30, 40, 50, 60, 127]] = True
+    tp = np.zeros((1, 128), dtype=np.uint8)
+    tp[0, [3, 20, 30, 127]] = 1
+    ex = dyn.pack_extra(tp, w)
+    assert ex.shape == (1, 1) and ex[0, 0] == 0b10001101
+    assert np.array_equal(dyn.unpack_extra(ex, w), tp)
+
+
+def check_dynamic_pipeline():
+    """Moments: brute force, and Parseval (sum over channels = mean (rho/(rho+eps))^2); a round
+    trip is within half a level gap of each scaled codebook; on channels of unequal spread the
+    dynamic codebook's error is below the static N(0, 1/D) codebook's."""
+    from oracle import dynamic as dyn
+    rng = _rng(42)
+    d = 128
+    x = rng.standard_normal((2, 9, 2, d)) * np.concatenate([np.full(64, 0.3), np.full(64, 2.0)])
+    perm = rng.permutation(d)
+    p = codec.CodecParams(bits=3, group_size=d, quant="lloyd", rot="fwht", perm=perm, n_sink=2)
+    m = codec.rotated_moments(x, p)
+    want = np.zeros(d)
+    n = 0
+    for r in range(2):
+        for t in range(2, 9):
+            for h in range(2):
+                u = x[r, t, h] / (np.linalg.norm(x[r, t, h]) + 1e-6)
+                zz = rotations.hadamard(d) @ u[perm] / np.sqrt(d)
+                want += zz * zz
+                n += 1
+    assert np.allclose(m, want / n, rtol=1e-12)
+    rho = np.linalg.norm(x[:, 2:], axis=-1)
+    assert np.isclose(m.sum(), np.mean((rho / (rho + 1e-6)) ** 2), rtol=1e-12)
+    xr = rng.standard_normal((1, 400, 1, d)) * np.exp(rng.uniform(-1.5, 1.5, d))
+    pr = codec.CodecParams(bits=3, group_size=d, quant="lloyd", rot="none")
+    sc, wide, cb, cbw = dyn.dynamic_codebook(codec.rotated_moments(xr, pr), 3)
+    pd = codec.CodecParams(bits=3, group_size=d, quant="lloyd", rot="none", codebook=cb, chan_scale=sc,
+                           chan_wide=wide, codebook_wide=cbw)
+    out = codec.encode(xr, pd)
+    yd = codec.decode(out, pd, xr.shape)
+    assert np.array_equal(out["extra"], dyn.pack_extra(out["top"], wide))
+    lev = dyn.dyn_dequant(out["q"], out["top"], sc, wide, cb, cbw, 3)
+    assert np.allclose(yd, lev * out["norm"].astype(np.float64)[..., None], rtol=1e-15, atol=0)
+    ps = codec.CodecParams(bits=3, group_size=d, quant="lloyd", rot="none", codebook=lloyd.fit_gaussian(3, 1 / np.sqrt(d)))
+    ys = codec.decode(codec.encode(xr, ps), ps, xr.shape)
+    assert np.sum((yd - xr) ** 2) < 0.5 * np.sum((ys - xr) ** 2)
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

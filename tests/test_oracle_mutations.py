@@ -193,6 +193,35 @@ def _detect_mean(x, lam):
     return flags, flags.sum(axis=1), prefix
 
 
+from oracle import dynamic as _dyn
+
+_orig_dynamic_codebook = _dyn.dynamic_codebook
+_orig_dyn_codes = _dyn.dyn_codes
+_orig_pack_extra = _dyn.pack_extra
+
+
+def _dyncb_variance(moments, bits):
+    sc, wide, cb, cbw = _orig_dynamic_codebook(moments, bits)
+    return sc * sc, wide, cb, cbw  # the variance taken as the scale
+
+
+def _dyncb_smallest_wide(moments, bits):
+    sc, wide, cb, cbw = _orig_dynamic_codebook(moments, bits)
+    order = np.argsort(sc, kind="stable")
+    w = np.zeros_like(wide)
+    w[order[:wide.sum()]] = True
+    return sc, w, cb, cbw
+
+
+def _dyn_codes_no_wide(z, scale, wide, cb, cb_wide, bits):
+    return _orig_dyn_codes(z, scale, np.zeros_like(np.asarray(wide, dtype=bool)), cb, cb_wide, bits)
+
+
+def _pack_extra_msb(top, wide):
+    idx = np.nonzero(np.asarray(wide, dtype=bool))[0]
+    return np.packbits(np.asarray(top, dtype=np.uint8)[..., idx], axis=-1, bitorder="big")
+
+
 from oracle import attention as _attention
 
 _orig_attend_decoded = _attention.attend_decoded
@@ -227,6 +256,10 @@ MUTATIONS = {
     "append_slot_is_position": (codec, "append", _append_slot_is_position),
     "widen_bf16_shift_15": (codec, "widen", _widen_shift_15),
     "outlier_perm_top_first": (_cal, "outlier_perm", _perm_top_first),
+    "dynamic_scale_is_variance": (_dyn, "dynamic_codebook", _dyncb_variance),
+    "dynamic_wide_smallest": (_dyn, "dynamic_codebook", _dyncb_smallest_wide),
+    "dynamic_codes_no_wide": (_dyn, "dyn_codes", _dyn_codes_no_wide),
+    "dynamic_extra_msb_first": (_dyn, "pack_extra", _pack_extra_msb),
     "channel_stats_rms": (_cal, "channel_stats", _stats_rms),
     "channel_stats_before_rope": (_cal, "channel_stats", _stats_no_rope),
     "channel_stats_with_sinks": (_cal, "channel_stats", _stats_with_sinks),
