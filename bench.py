@@ -279,6 +279,59 @@ def time_other_configs(kvq, workloads, dev, stream):
     return res
 
 
+def dynamic_codebook_report(kvq, workloads, dev, stream):
+    """IsoQuant's dynamic codebook against the static one, SO(4) + 3-bit Lloyd-Max: the SNR of
+    the round trip (dB over the non-sink vectors) and the encode/decode times, on the IsoQuant
+    workload (N(0,1), every channel alike) and on the Llama-2 layer's K (4 outlier channels x20,
+    token 0 x50), calibrated on the same tensor."""
+    import numpy as np
+    import torch
+
+    res = {}
+    for key, name in (("isoquant", "X"), ("llama2", "K")):
+        wl = workloads.WORKLOADS[key]
+        c = wl.case(name)
+        h = workloads.host_workload(key)
+        a = h["inputs"][name]
+        x = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        d = c.shape[-1]
+        quat = h["quat"] if h["quat"] is not None else workloads.unit_quaternions(d // 4, np.random.default_rng(1))
+        base = dict(shape=c.shape, dtype=c.dtype, bits=3, quant="lloyd", rot="so4", quat=quat, n_sink=c.n_sink)
+        static = kvq.Config(**base, codebook=kvq.lloyd_max_gaussian(3, 1.0 / np.sqrt(d)))
+        m = kvq.rotated_moments(x, kvq.Config(**base, codebook=kvq.lloyd_max_gaussian(3, 1.0)), stream=stream)
+        torch.cuda.synchronize()
+        sc, wide, cb, cbw = kvq.dynamic_codebook(m.cpu().numpy(), 3)
+        dyn = kvq.Config(**base, codebook=cb, chan_scale=sc, chan_wide=wide, codebook_wide=cbw)
+        xf = x.float()
+        keep = slice(c.n_sink, None)
+        entry = {"workload": wl.title, "rotation": "so4", "bits": 3}
+        for label, cfg in (("static", static), ("dynamic", dyn)):
+            pl = kvq.encode(x, cfg, stream=stream)
+            y = kvq.decode(pl, cfg, out_dtype="f32", stream=stream)
+            torch.cuda.synchronize()
+            err = (y[:, keep] - xf[:, keep]).double().pow(2).sum().item()
+            sig = xf[:, keep].double().pow(2).sum().item()
+            t = {}
+            for kind in ("encode", "decode"):
+                with torch.cuda.stream(stream):
+                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    ev[0].record(stream)
+                    for _ in range(20):
+                        if kind == "encode":
+                            kvq.encode(x, cfg, planes=pl, stream=stream)
+                        else:
+                            kvq.decode(pl, cfg, out_dtype="f32", out=y, stream=stream)
+                    ev[1].record(stream)
+                    stream.synchronize()
+                t[kind] = round(ev[0].elapsed_time(ev[1]) / 20 * 1e3, 2)
+            entry[label] = {"snr_db": round(10 * np.log10(sig / err), 3), "encode_us": t["encode"], "decode_us": t["decode"]}
+        entry["snr_gain_db"] = round(entry["dynamic"]["snr_db"] - entry["static"]["snr_db"], 3)
+        res[key] = entry
+        print(f"[bench] dynamic codebook {key}: {entry['static']['snr_db']} -> {entry['dynamic']['snr_db']} dB",
+              file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -505,6 +558,7 @@ def main():
         del data, planes, outs, qa, oa, wsa, x_new, src
         torch.cuda.empty_cache()
         others = time_other_configs(kvq, workloads, dev, stream)
+        others["dynamic_codebook"] = dynamic_codebook_report(kvq, workloads, dev, stream)
 
     out = {
         "metric": METRIC,

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 typedef enum kvq_status {
   KVQ_OK = 0,
@@ -60,7 +60,7 @@ typedef enum kvq_status {
                               not finite and strictly ascending, bad rope base or
                               position range                                          */
   KVQ_ERR_ALIGN = 7,       /* a device pointer or stride is not 16-byte aligned        */
-  KVQ_ERR_UNSUPPORTED = 8, /* head_dim not in {128, 256}                               */
+  KVQ_ERR_UNSUPPORTED = 8, /* head_dim not in {128, 256}, or a combination not built   */
   KVQ_ERR_ABI = 9,         /* cfg->abi_version != KVQ_ABI_VERSION                      */
   KVQ_ERR_DEVICE = 10,     /* the HIP runtime refused the launch (message has detail)  */
   KVQ_ERR_INTERNAL = 11
@@ -68,7 +68,7 @@ typedef enum kvq_status {
 
 /* Element types (enum values are stored as int32_t in the structs below). */
 typedef enum kvq_dtype { KVQ_F16 = 0, KVQ_BF16 = 1, KVQ_F32 = 2 } kvq_dtype;
-typedef enum kvq_rot { KVQ_ROT_NONE = 0, KVQ_ROT_FWHT = 1, KVQ_ROT_SO4 = 2 } kvq_rot;
+typedef enum kvq_rot { KVQ_ROT_NONE = 0, KVQ_ROT_FWHT = 1, KVQ_ROT_SO4 = 2, KVQ_ROT_DENSE = 3 } kvq_rot;
 typedef enum kvq_quant { KVQ_Q_MINMAX = 0, KVQ_Q_LLOYD = 1 } kvq_quant;
 
 typedef struct kvq_config {
@@ -95,6 +95,18 @@ typedef struct kvq_config {
                                unit norm within 1e-4; required for KVQ_ROT_SO4         */
   const float* codebook;    /* HOST [2^bits] strictly ascending, finite; required for
                                KVQ_Q_LLOYD                                             */
+  /* Dynamic codebook (IsoQuant page, section 4.2), Lloyd-Max only; all NULL = off.  Rotated
+   * channel j is quantized against codebook scaled by chan_scale[j]; the head_dim/16 channels
+   * with chan_wide[j] = 1 use codebook_wide (twice the levels) scaled the same way, the top bit
+   * of their bits+1-bit code going to the extra plane.  kvq_dynamic_codebook derives all three
+   * from kvq_rotated_moments. */
+  const float* chan_scale;    /* HOST [D], finite and > 0                                 */
+  const uint8_t* chan_wide;   /* HOST [D], 0 or 1, exactly D/16 ones                       */
+  const float* codebook_wide; /* HOST [2^(bits+1)] strictly ascending, finite              */
+  /* KVQ_ROT_DENSE: DEVICE [D][D] float32 row-major, z_i = sum_j M[i][j] u_j; orthogonal (a
+   * precondition the host cannot check: decode applies the transpose).  The A/B baseline of
+   * a dense random rotation (IsoQuant page, section 1). */
+  const float* rot_matrix;
 } kvq_config;
 
 /* Packed planes, all DEVICE pointers, 16-byte aligned, contiguous, row-major:
@@ -103,14 +115,17 @@ typedef struct kvq_config {
  *   zero  [R,T,H,D/G]      fp16   -- min-max only
  *   norm  [R,T,H]          fp32   -- Lloyd-Max only (rho)
  *   sink  [R,n_sink,H,D]   fp16   -- when n_sink > 0; slot p holds position p.
+ *   extra [R,T,H,D/128]    u8     -- dynamic codebook only: bit k (LSB first) is the top
+ *                                    code bit of the k-th wide channel (increasing order)
  * Planes a configuration does not use may be NULL.  Sink vectors have all-zero
- * codes, scale, zero and norm slots. */
+ * codes, scale, zero, norm and extra slots. */
 typedef struct kvq_planes {
   void* codes;
   void* scale;
   void* zero;
   void* norm;
   void* sink;
+  void* extra;
 } kvq_planes;
 
 /* KVQ_ABI_VERSION of the loaded library. */
@@ -119,9 +134,9 @@ int32_t kvq_abi_version(void);
 /* Host-only: check a configuration (no device access). */
 kvq_status kvq_validate(const kvq_config* cfg);
 
-/* Host-only: byte sizes of the five planes for cfg (0 for planes it does not use). */
+/* Host-only: byte sizes of the six planes for cfg (0 for planes it does not use). */
 kvq_status kvq_packed_sizes(const kvq_config* cfg, size_t* codes_bytes, size_t* scale_bytes,
-                            size_t* zero_bytes, size_t* norm_bytes, size_t* sink_bytes);
+                            size_t* zero_bytes, size_t* norm_bytes, size_t* sink_bytes, size_t* extra_bytes);
 
 /* Encode x (DEVICE, dtype cfg->dtype, [R,T,H,D] with cfg's strides) into out's planes.
  * stream: a hipStream_t (NULL = the default stream).  Asynchronous.  x must not
@@ -241,7 +256,27 @@ kvq_status kvq_outlier_perm(const double* stats, int64_t head_dim, int32_t group
 kvq_status kvq_detect_sinks(const kvq_config* cfg, const void* x, double lambda, double* norms, uint8_t* flags,
                             int32_t* counts, int32_t* prefix, double* medians, void* stream);
 
-/* Host-only: Lloyd-Max codebook (2^bits ascending levels) for N(0, sigma^2), written
+/* Dynamic codebook calibration (IsoQuant page, section 4.2: per-channel statistics gathered
+ * online, KL-optimised boundaries, a codebook twice the size for outlier channels).
+ * kvq_rotated_moments runs the codec's front end (RoPE, norm separation u = y/(rho + 1e-6),
+ * permutation, rotation; cfg->quant must be KVQ_Q_LLOYD) on every non-sink vector of the
+ * calibration slice x and writes
+ *   moments    DEVICE double [D]: mean z_j^2 per rotated channel j;
+ *   workspace  DEVICE, 8-byte aligned, at least kvq_channel_stats_workspace_size(cfg) bytes.
+ * Asynchronous; float64 sums in a fixed order. */
+kvq_status kvq_rotated_moments(const kvq_config* cfg, const void* x, double* moments, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Host-only: the dynamic codebook from the moments (HOST double [D], each > 0):
+ * chan_scale[j] = sqrt(moments[j]) -- the zero-mean Gaussian closest to channel j in KL
+ * divergence has its second moment; chan_wide: 1 on the D/16 channels with the largest
+ * moments (equal moments in increasing channel order); codebook and codebook_wide: the
+ * Lloyd-Max codebooks of N(0, 1) with 2^bits and 2^(bits+1) levels.  All outputs HOST
+ * arrays of D, D, 2^bits and 2^(bits+1) entries, ready for kvq_config. */
+kvq_status kvq_dynamic_codebook(const double* moments, int64_t head_dim, int32_t bits, float* chan_scale,
+                                uint8_t* chan_wide, float* codebook, float* codebook_wide);
+
+/* Host-only: Lloyd-Max codebook (2^bits ascending levels, bits 1..5) for N(0, sigma^2), written
  * to codebook_out as float32; the classical fixed point of midpoint thresholds and
  * conditional-mean levels, iterated in double precision (IsoQuant page, section 3.1
  * names the Lloyd-Max quantizer; the fitting procedure is the textbook one). */

@@ -24,21 +24,22 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 
 __all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_noalloc", "attend_noalloc_max_workspace",
-           "channel_stats", "channel_stats_workspace_size", "outlier_perm", "detect_sinks",
+           "channel_stats", "channel_stats_workspace_size", "outlier_perm", "detect_sinks", "rotated_moments",
+           "dynamic_codebook",
            "attend_workspace_size", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
            "library_path", "abi_version", "DTYPES", "ROTATIONS", "QUANTIZERS", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
-ROTATIONS = {"none": 0, "fwht": 1, "so4": 2}
+ROTATIONS = {"none": 0, "fwht": 1, "so4": 2, "dense": 3}
 QUANTIZERS = {"minmax": 0, "lloyd": 1}
 EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append",
                     "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_attend_noalloc_max_workspace",
                     "kvq_decode", "kvq_lloyd_max_gaussian", "kvq_channel_stats_workspace_size", "kvq_channel_stats",
-                    "kvq_outlier_perm", "kvq_detect_sinks",
+                    "kvq_outlier_perm", "kvq_detect_sinks", "kvq_rotated_moments", "kvq_dynamic_codebook",
                     "kvq_status_string", "kvq_last_error_message")
 
 
@@ -64,11 +65,15 @@ class _Config(ctypes.Structure):
         ("perm", ctypes.c_void_p),
         ("quat", ctypes.c_void_p),
         ("codebook", ctypes.c_void_p),
+        ("chan_scale", ctypes.c_void_p),
+        ("chan_wide", ctypes.c_void_p),
+        ("codebook_wide", ctypes.c_void_p),
+        ("rot_matrix", ctypes.c_void_p),
     ]
 
 
 class _Planes(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("codes", "scale", "zero", "norm", "sink")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("codes", "scale", "zero", "norm", "sink", "extra")]
 
 
 class KvqError(RuntimeError):
@@ -96,7 +101,7 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     lib.kvq_abi_version.restype = ctypes.c_int32
     lib.kvq_validate.argtypes = [ctypes.POINTER(_Config)]
-    lib.kvq_packed_sizes.argtypes = [ctypes.POINTER(_Config)] + [ctypes.POINTER(ctypes.c_size_t)] * 5
+    lib.kvq_packed_sizes.argtypes = [ctypes.POINTER(_Config)] + [ctypes.POINTER(ctypes.c_size_t)] * 6
     lib.kvq_encode.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.POINTER(_Planes), ctypes.c_void_p]
     lib.kvq_append.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Planes),
                                ctypes.c_void_p]
@@ -116,13 +121,17 @@ def _load():
                                       ctypes.c_size_t, ctypes.c_void_p]
     lib.kvq_outlier_perm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
     lib.kvq_detect_sinks.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.c_double] + [ctypes.c_void_p] * 6
+    lib.kvq_rotated_moments.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+    lib.kvq_dynamic_codebook.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 4
     lib.kvq_lloyd_max_gaussian.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_last_error_message.restype = ctypes.c_char_p
     for fn in ("kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append", "kvq_decode", "kvq_lloyd_max_gaussian",
                "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_channel_stats_workspace_size",
-               "kvq_channel_stats", "kvq_outlier_perm", "kvq_detect_sinks"):
+               "kvq_channel_stats", "kvq_outlier_perm", "kvq_detect_sinks", "kvq_rotated_moments",
+               "kvq_dynamic_codebook"):
         getattr(lib, fn).restype = ctypes.c_int
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -168,6 +177,10 @@ class Config:
     perm: Optional[np.ndarray] = None
     quat: Optional[np.ndarray] = None
     codebook: Optional[np.ndarray] = None
+    chan_scale: Optional[np.ndarray] = None     # dynamic codebook: per rotated channel scale
+    chan_wide: Optional[np.ndarray] = None      # dynamic codebook: 0/1, D/16 ones
+    codebook_wide: Optional[np.ndarray] = None  # dynamic codebook: 2^(bits+1) levels
+    rot_matrix: Optional[object] = None         # dense rotation: float32 device tensor [D, D]
     strides: Optional[Sequence[int]] = None  # (stride_r, stride_t, stride_h) in elements
     _keep: list = field(default_factory=list, repr=False)
 
@@ -189,13 +202,15 @@ class Config:
         c.pos_offset = int(self.pos_offset)
         self._keep = []
         for name, arr, dt in (("perm", self.perm, np.uint16), ("quat", self.quat, np.float32),
-                              ("codebook", self.codebook, np.float32)):
+                              ("codebook", self.codebook, np.float32), ("chan_scale", self.chan_scale, np.float32),
+                              ("chan_wide", self.chan_wide, np.uint8), ("codebook_wide", self.codebook_wide, np.float32)):
             if arr is None:
                 setattr(c, name, None)
             else:
                 a = np.ascontiguousarray(np.asarray(arr, dtype=dt))
                 self._keep.append(a)
                 setattr(c, name, a.ctypes.data)
+        c.rot_matrix = None if self.rot_matrix is None else int(self.rot_matrix.data_ptr())
         return c
 
 
@@ -206,9 +221,9 @@ def validate(cfg: Config) -> None:
 
 def packed_sizes(cfg: Config) -> Dict[str, int]:
     c = cfg.c_struct()
-    out = [ctypes.c_size_t() for _ in range(5)]
+    out = [ctypes.c_size_t() for _ in range(6)]
     _check(_L().kvq_packed_sizes(ctypes.byref(c), *[ctypes.byref(o) for o in out]))
-    return dict(zip(("codes", "scale", "zero", "norm", "sink"), (int(o.value) for o in out)))
+    return dict(zip(("codes", "scale", "zero", "norm", "sink", "extra"), (int(o.value) for o in out)))
 
 
 def _stream_handle(stream) -> int:
@@ -235,13 +250,15 @@ def empty_planes(cfg: Config, device="cuda") -> Dict[str, "object"]:
         out["norm"] = torch.empty((r, t, h), dtype=torch.float32, device=device)
     if cfg.n_sink > 0:
         out["sink"] = torch.empty((r, cfg.n_sink, h, d), dtype=torch.float16, device=device)
+    if sz["extra"]:
+        out["extra"] = torch.empty((r, t, h, d // 128), dtype=torch.uint8, device=device)
     assert out["codes"].numel() == sz["codes"]
     return out
 
 
 def _planes_struct(planes) -> _Planes:
     p = _Planes()
-    for n in ("codes", "scale", "zero", "norm", "sink"):
+    for n in ("codes", "scale", "zero", "norm", "sink", "extra"):
         setattr(p, n, _ptr(planes.get(n)))
     return p
 
@@ -391,6 +408,33 @@ def detect_sinks(x, cfg: Config, lam: float, stream=None):
     _check(_L().kvq_detect_sinks(ctypes.byref(c), _ptr(x), float(lam), _ptr(norms), _ptr(flags), _ptr(counts),
                                  _ptr(prefix), _ptr(medians), _stream_handle(stream)))
     return norms, flags, counts, prefix, medians
+
+
+def rotated_moments(x, cfg: Config, workspace=None, stream=None):
+    """Per rotated channel mean z_j^2 (float64 device tensor [D]) of the calibration slice
+    ``x`` through the codec's front end (cfg.quant must be "lloyd")."""
+    import torch
+    c = cfg.c_struct()
+    if workspace is None:
+        workspace = torch.empty(max(channel_stats_workspace_size(cfg), 8), dtype=torch.uint8, device=x.device)
+    m = torch.empty(int(cfg.shape[-1]), dtype=torch.float64, device=x.device)
+    _check(_L().kvq_rotated_moments(ctypes.byref(c), _ptr(x), int(m.data_ptr()), int(workspace.data_ptr()),
+                                    int(workspace.numel() * workspace.element_size()), _stream_handle(stream)))
+    return m
+
+
+def dynamic_codebook(moments, bits: int):
+    """Host-side dynamic codebook from per-channel moments: (chan_scale f32 [D], chan_wide u8 [D],
+    codebook f32 [2^bits], codebook_wide f32 [2^(bits+1)])."""
+    m = np.ascontiguousarray(np.asarray(moments, dtype=np.float64))
+    d = m.shape[0]
+    sc = np.zeros(d, dtype=np.float32)
+    wide = np.zeros(d, dtype=np.uint8)
+    cb = np.zeros(2 ** bits, dtype=np.float32)
+    cbw = np.zeros(2 ** (bits + 1), dtype=np.float32)
+    _check(_L().kvq_dynamic_codebook(m.ctypes.data, d, int(bits), sc.ctypes.data, wide.ctypes.data, cb.ctypes.data,
+                                     cbw.ctypes.data))
+    return sc, wide, cb, cbw
 
 
 def lloyd_max_gaussian(bits: int, sigma: float) -> np.ndarray:

@@ -55,6 +55,7 @@ struct Derived {
   int64_t sr = 0, st = 0, sh = 0;
   int64_t code_bytes = 0;   // per vector
   int64_t ngroups = 0;      // per vector (min-max)
+  int64_t extra_bytes = 0;  // per vector (dynamic codebook)
 };
 
 kvq_status check_config(const kvq_config* cfg, Derived* dv) {
@@ -62,7 +63,7 @@ kvq_status check_config(const kvq_config* cfg, Derived* dv) {
   if (cfg->abi_version != KVQ_ABI_VERSION)
     return fail(KVQ_ERR_ABI, "abi_version %d, library is %d", cfg->abi_version, KVQ_ABI_VERSION);
   if (cfg->dtype < KVQ_F16 || cfg->dtype > KVQ_F32) return fail(KVQ_ERR_ROT, "unknown dtype %d", cfg->dtype);
-  if (cfg->rot < KVQ_ROT_NONE || cfg->rot > KVQ_ROT_SO4) return fail(KVQ_ERR_ROT, "unknown rotation %d", cfg->rot);
+  if (cfg->rot < KVQ_ROT_NONE || cfg->rot > KVQ_ROT_DENSE) return fail(KVQ_ERR_ROT, "unknown rotation %d", cfg->rot);
   if (cfg->quant < KVQ_Q_MINMAX || cfg->quant > KVQ_Q_LLOYD)
     return fail(KVQ_ERR_ROT, "unknown quantizer %d", cfg->quant);
   if (cfg->rows < 0 || cfg->tokens < 0 || cfg->heads < 0 || cfg->head_dim < 0)
@@ -149,14 +150,42 @@ kvq_status check_config(const kvq_config* cfg, Derived* dv) {
         return fail(KVQ_ERR_PARAM, "codebook not strictly ascending at %d", i);
     }
   }
+  // dynamic codebook
+  const bool any_dyn = cfg->chan_scale || cfg->chan_wide || cfg->codebook_wide;
+  if (any_dyn) {
+    if (!cfg->chan_scale || !cfg->chan_wide || !cfg->codebook_wide)
+      return fail(KVQ_ERR_NULL, "the dynamic codebook needs chan_scale, chan_wide and codebook_wide");
+    if (cfg->quant != KVQ_Q_LLOYD) return fail(KVQ_ERR_PARAM, "the dynamic codebook is a Lloyd-Max codebook");
+    int n_wide = 0;
+    for (int64_t j = 0; j < d; ++j) {
+      if (!(isfinite(cfg->chan_scale[j]) && cfg->chan_scale[j] > 0.0f))
+        return fail(KVQ_ERR_PARAM, "chan_scale[%lld] must be finite and > 0", (long long)j);
+      if (cfg->chan_wide[j] > 1) return fail(KVQ_ERR_PARAM, "chan_wide[%lld] must be 0 or 1", (long long)j);
+      n_wide += cfg->chan_wide[j];
+    }
+    if (n_wide != d / 16) return fail(KVQ_ERR_PARAM, "chan_wide has %d ones, head_dim/16 = %lld needed", n_wide,
+                                      (long long)(d / 16));
+    const int n_levels = 2 << cfg->bits;
+    for (int i = 0; i < n_levels; ++i) {
+      if (!isfinite(cfg->codebook_wide[i])) return fail(KVQ_ERR_PARAM, "codebook_wide entry %d not finite", i);
+      if (i > 0 && !(cfg->codebook_wide[i] > cfg->codebook_wide[i - 1]))
+        return fail(KVQ_ERR_PARAM, "codebook_wide not strictly ascending at %d", i);
+    }
+  }
+  if (cfg->rot == KVQ_ROT_DENSE) {
+    if (!cfg->rot_matrix) return fail(KVQ_ERR_NULL, "rot_matrix is required for the dense rotation");
+    if (!aligned16(cfg->rot_matrix)) return fail(KVQ_ERR_ALIGN, "rot_matrix not 16-byte aligned");
+  }
   dv->n_vec = rth;
   dv->code_bytes = d * cfg->bits / 8;
   dv->ngroups = cfg->quant == KVQ_Q_MINMAX ? d / cfg->group_size : 0;
+  dv->extra_bytes = any_dyn ? d / 128 : 0;
   return KVQ_OK;
 }
 
 void plane_sizes(const kvq_config* cfg, const Derived& dv, size_t* codes, size_t* scale, size_t* zero,
-                 size_t* norm, size_t* sink) {
+                 size_t* norm, size_t* sink, size_t* extra) {
+  *extra = (size_t)(dv.n_vec * dv.extra_bytes);
   *codes = (size_t)(dv.n_vec * dv.code_bytes);
   *scale = (size_t)(dv.n_vec * dv.ngroups * 2);
   *zero = *scale;
@@ -179,6 +208,10 @@ kvq_status check_planes(const kvq_config* cfg, const Derived& dv, const kvq_plan
   } else {
     if (!pl->norm) return fail(KVQ_ERR_NULL, "norm plane is NULL");
     if (!aligned16(pl->norm)) return fail(KVQ_ERR_ALIGN, "norm plane not 16-byte aligned");
+  }
+  if (dv.extra_bytes) {
+    if (!pl->extra) return fail(KVQ_ERR_NULL, "extra plane is NULL (dynamic codebook)");
+    if (!aligned16(pl->extra)) return fail(KVQ_ERR_ALIGN, "extra plane not 16-byte aligned");
   }
   if (sinks_in_range(cfg)) {
     if (!pl->sink) return fail(KVQ_ERR_NULL, "sink plane is NULL");
@@ -216,6 +249,14 @@ void fill_args(const kvq_config* cfg, const Derived& dv, kvq::CodecArgs* a) {
     for (int64_t i = 0; i < cfg->head_dim; ++i) a->perm[i] = (uint8_t)cfg->perm[i];
   if (cfg->rot == KVQ_ROT_SO4) memcpy(a->quat, cfg->quat, sizeof(float) * cfg->head_dim / 4 * 8);
   if (cfg->quant == KVQ_Q_LLOYD) memcpy(a->codebook, cfg->codebook, sizeof(float) * (1 << cfg->bits));
+  if (dv.extra_bytes) {
+    a->dyn = 1;
+    memcpy(a->chan_scale, cfg->chan_scale, sizeof(float) * cfg->head_dim);
+    memcpy(a->codebook_wide, cfg->codebook_wide, sizeof(float) * (2 << cfg->bits));
+    int k = 0;
+    for (int64_t j = 0; j < cfg->head_dim; ++j) a->wide_rank[j] = cfg->chan_wide[j] ? (uint8_t)k++ : 0xff;
+  }
+  a->rot_matrix = cfg->rot == KVQ_ROT_DENSE ? cfg->rot_matrix : nullptr;
 }
 
 // ---- Lloyd-Max (host, double precision) ----
@@ -236,12 +277,12 @@ kvq_status kvq_validate(const kvq_config* cfg) {
 }
 
 kvq_status kvq_packed_sizes(const kvq_config* cfg, size_t* codes, size_t* scale, size_t* zero, size_t* norm,
-                            size_t* sink) {
+                            size_t* sink, size_t* extra) {
   Derived dv;
   kvq_status st = check_config(cfg, &dv);
   if (st != KVQ_OK) return st;
-  if (!codes || !scale || !zero || !norm || !sink) return fail(KVQ_ERR_NULL, "size output pointer is NULL");
-  plane_sizes(cfg, dv, codes, scale, zero, norm, sink);
+  if (!codes || !scale || !zero || !norm || !sink || !extra) return fail(KVQ_ERR_NULL, "size output pointer is NULL");
+  plane_sizes(cfg, dv, codes, scale, zero, norm, sink, extra);
   return ok();
 }
 
@@ -249,6 +290,7 @@ kvq_status kvq_encode(const kvq_config* cfg, const void* x, const kvq_planes* ou
   Derived dv;
   kvq_status st = check_config(cfg, &dv);
   if (st != KVQ_OK) return st;
+  if (cfg->rot == KVQ_ROT_DENSE) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: not in the codec");
   if ((st = check_planes(cfg, dv, out)) != KVQ_OK) return st;
   if (dv.n_vec == 0) return ok();
   if (!x) return fail(KVQ_ERR_NULL, "x is NULL");
@@ -261,6 +303,7 @@ kvq_status kvq_encode(const kvq_config* cfg, const void* x, const kvq_planes* ou
   a.zero = static_cast<uint16_t*>(out->zero);
   a.norm = static_cast<float*>(out->norm);
   a.sink = static_cast<uint16_t*>(out->sink);
+  a.extra = static_cast<uint8_t*>(out->extra);
   plan_work(cfg, &a);
   const bool d128 = cfg->head_dim == 128;
   int err;
@@ -284,6 +327,7 @@ kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* posit
   Derived dv;
   kvq_status st = check_config(cfg, &dv);  // cfg describes the cache: tokens = slots per row
   if (st != KVQ_OK) return st;
+  if (cfg->rot == KVQ_ROT_DENSE) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: not in the codec");
   if (!cache) return fail(KVQ_ERR_NULL, "cache planes is NULL");
   if (dv.n_vec == 0) return ok();
   if ((st = check_planes(cfg, dv, cache)) != KVQ_OK) return st;
@@ -310,6 +354,7 @@ kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* posit
   a.zero = static_cast<uint16_t*>(cache->zero);
   a.norm = static_cast<float*>(cache->norm);
   a.sink = static_cast<uint16_t*>(cache->sink);
+  a.extra = static_cast<uint8_t*>(cache->extra);
   const int vpw = cfg->head_dim == 128 ? 16 : 8;
   a.n_tiles = (cfg->heads + vpw - 1) / vpw;
   a.n_items = cfg->rows * a.n_tiles;
@@ -335,6 +380,7 @@ kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int3
   Derived dv;
   kvq_status st = check_config(cfg, &dv);
   if (st != KVQ_OK) return st;
+  if (cfg->rot == KVQ_ROT_DENSE) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: not in the codec");
   if (y_dtype < KVQ_F16 || y_dtype > KVQ_F32) return fail(KVQ_ERR_ROT, "unknown output dtype %d", y_dtype);
   if ((st = check_planes(cfg, dv, in)) != KVQ_OK) return st;
   if (dv.n_vec == 0) return ok();
@@ -348,6 +394,7 @@ kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int3
   a.zero = static_cast<uint16_t*>(in->zero);
   a.norm = static_cast<float*>(in->norm);
   a.sink = static_cast<uint16_t*>(in->sink);
+  a.extra = static_cast<uint8_t*>(in->extra);
   plan_work(cfg, &a);
   const bool d128 = cfg->head_dim == 128;
   int err;
@@ -561,6 +608,62 @@ kvq_status kvq_channel_stats(const kvq_config* cfg, const void* x, double* stats
   return ok();
 }
 
+kvq_status kvq_rotated_moments(const kvq_config* cfg, const void* x, double* moments, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  Derived dv;
+  kvq_status st = check_config(cfg, &dv);
+  if (st != KVQ_OK) return st;
+  if (cfg->quant != KVQ_Q_LLOYD) return fail(KVQ_ERR_PARAM, "rotated moments belong to the Lloyd-Max path (quant)");
+  if (!moments) return fail(KVQ_ERR_NULL, "moments is NULL");
+  if (reinterpret_cast<uintptr_t>(moments) & 7u) return fail(KVQ_ERR_ALIGN, "moments not 8-byte aligned");
+  kvq::CalibArgs a;
+  fill_calib(cfg, dv, x, &a);
+  const size_t need = (size_t)a.n_waves * (size_t)cfg->head_dim * sizeof(double);
+  if (need > 0) {
+    if (!x) return fail(KVQ_ERR_NULL, "x is NULL");
+    if (!aligned16(x)) return fail(KVQ_ERR_ALIGN, "x not 16-byte aligned");
+    if (!workspace) return fail(KVQ_ERR_NULL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 7u) return fail(KVQ_ERR_ALIGN, "workspace not 8-byte aligned");
+    if (workspace_bytes < need) return fail(KVQ_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  if (a.n_waves > (int64_t(1) << 33)) return fail(KVQ_ERR_SHAPE, "calibration slice too large");
+  a.part = static_cast<double*>(workspace);
+  a.stats = moments;
+  a.rot = cfg->rot;
+  a.rot_matrix = cfg->rot == KVQ_ROT_DENSE ? cfg->rot_matrix : nullptr;
+  a.use_perm = cfg->perm ? 1 : 0;
+  if (cfg->perm)
+    for (int64_t i = 0; i < cfg->head_dim; ++i) a.perm[i] = (uint8_t)cfg->perm[i];
+  if (cfg->rot == KVQ_ROT_SO4) memcpy(a.quat, cfg->quat, sizeof(float) * cfg->head_dim / 4 * 8);
+  const int err = kvq::launch_rotated_moments(a, stream);
+  if (err != 0) return fail(KVQ_ERR_DEVICE, "rotated moments launch failed: %s", kvq::device_error_string(err));
+  return ok();
+}
+
+kvq_status kvq_dynamic_codebook(const double* moments, int64_t head_dim, int32_t bits, float* chan_scale,
+                                uint8_t* chan_wide, float* codebook, float* codebook_wide) {
+  if (!moments || !chan_scale || !chan_wide || !codebook || !codebook_wide)
+    return fail(KVQ_ERR_NULL, "an argument of kvq_dynamic_codebook is NULL");
+  if (head_dim != 128 && head_dim != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim %lld (supported: 128, 256)", (long long)head_dim);
+  if (bits < 2 || bits > 4) return fail(KVQ_ERR_BITS, "bits %d (supported: 2, 3, 4)", bits);
+  const int d = (int)head_dim;
+  for (int j = 0; j < d; ++j)
+    if (!(isfinite(moments[j]) && moments[j] > 0.0))
+      return fail(KVQ_ERR_PARAM, "moments[%d] must be finite and > 0", j);
+  // the KL-closest zero-mean Gaussian to a channel is the one with its second moment
+  for (int j = 0; j < d; ++j) chan_scale[j] = (float)sqrt(moments[j]);
+  // wide channels: the d/16 largest scales (equal scales in increasing channel order)
+  int order[kvq::kMaxHeadDim];
+  for (int j = 0; j < d; ++j) order[j] = j;
+  std::stable_sort(order, order + d, [&](int i, int j) { return moments[i] > moments[j]; });
+  for (int j = 0; j < d; ++j) chan_wide[j] = 0;
+  for (int k = 0; k < d / 16; ++k) chan_wide[order[k]] = 1;
+  kvq_status st = kvq_lloyd_max_gaussian(bits, 1.0, codebook);
+  if (st != KVQ_OK) return st;
+  return kvq_lloyd_max_gaussian(bits + 1, 1.0, codebook_wide);
+}
+
 kvq_status kvq_outlier_perm(const double* stats, int64_t head_dim, int32_t group_size, uint16_t* perm) {
   if (!stats || !perm) return fail(KVQ_ERR_NULL, "stats or perm is NULL");
   if (head_dim != 128 && head_dim != 256)
@@ -623,10 +726,10 @@ kvq_status kvq_detect_sinks(const kvq_config* cfg, const void* x, double lambda,
 
 kvq_status kvq_lloyd_max_gaussian(int32_t bits, double sigma, float* codebook_out) {
   if (!codebook_out) return fail(KVQ_ERR_NULL, "codebook_out is NULL");
-  if (bits < 1 || bits > 4) return fail(KVQ_ERR_BITS, "bits %d (1..4)", bits);
+  if (bits < 1 || bits > 5) return fail(KVQ_ERR_BITS, "bits %d (1..5)", bits);
   if (!(isfinite(sigma) && sigma > 0.0)) return fail(KVQ_ERR_PARAM, "sigma must be finite and > 0");
   const int n = 1 << bits;
-  double c[16], lo[16], hi[16];
+  double c[32], lo[32], hi[32];
   // symmetric start, evenly spread over +-2 standard deviations
   for (int k = 0; k < n; ++k) c[k] = -2.0 + 4.0 * (k + 0.5) / n;
   for (int it = 0; it < 1000000; ++it) {

@@ -64,11 +64,21 @@ struct CodecArgs {
   // cap token slots per row; NULL for a plain encode
   const int64_t* row_pos;
   int64_t cap;
+  // dynamic codebook (Lloyd-Max): dyn = 1 when on; wide_rank[j] = k for the k-th wide channel,
+  // 0xff for the others; the extra plane holds the wide channels' top code bits
+  int32_t dyn;
+  uint8_t* extra;
+  // dense rotation (DEVICE [D][D], row-major)
+  const float* rot_matrix;
   // parameters
   uint8_t perm[kMaxHeadDim];
   float quat[kMaxHeadDim / 4 * 8];
   float codebook[kMaxCodebook];
+  float codebook_wide[2 * kMaxCodebook];
+  float chan_scale[kMaxHeadDim];
+  uint8_t wide_rank[kMaxHeadDim];
 };
+static_assert(sizeof(CodecArgs) <= 4096, "kernel arguments above 4 KiB");
 
 // Decode-step attention over an encoded cache (d = 128, Walsh-Hadamard + min-max).  The
 // workspace holds the rotated queries [rows, q_heads, 128] and, per (row, query head,
@@ -140,6 +150,11 @@ struct CalibArgs {
   int32_t* counts;   // [R]
   int32_t* prefix;   // [R]: one past the last flagged token (0 if none)
   double* medians;   // [R] lower median token norm
+  // rotated moments (dynamic codebook): the codec's front end on each vector
+  int32_t rot, use_perm;
+  const float* rot_matrix;       // DEVICE [D][D] (dense rotation)
+  uint8_t perm[kMaxHeadDim];
+  float quat[kMaxHeadDim / 4 * 8];
 };
 inline int32_t calib_tokens_per_wave(int64_t rows, int64_t tokens) {
   // about 8 K waves over the slice, at least 16 tokens each
@@ -149,6 +164,7 @@ inline int32_t calib_tokens_per_wave(int64_t rows, int64_t tokens) {
 }
 int launch_channel_stats(const CalibArgs& a, void* stream);
 int launch_detect_sinks(const CalibArgs& a, void* stream);
+int launch_rotated_moments(const CalibArgs& a, void* stream);
 
 // Launch helpers, one per (direction, dtype, head_dim), defined in kvq_kernels.hip.
 // Each returns a hipError_t as int (0 = success).

@@ -39,7 +39,7 @@ namespace kvq {
 namespace {
 
 enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
-enum { ROT_NONE = 0, ROT_FWHT = 1, ROT_SO4 = 2 };
+enum { ROT_NONE = 0, ROT_FWHT = 1, ROT_SO4 = 2, ROT_DENSE = 3 };
 enum { Q_MINMAX = 0, Q_LLOYD = 1 };
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -200,6 +200,15 @@ __device__ __forceinline__ float vec_max(float v) {
   v = max_x1(v);
   v = max_x2(v);
   if constexpr (LV == 8) v = fmaxf(v, swz_x4(v));
+  return v;
+}
+
+// Bitwise OR over the LV lanes of a vector (every lane gets the result).
+template <int LV>
+__device__ __forceinline__ uint32_t vec_or(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // lane xor 1
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // lane xor 2
+  if constexpr (LV == 8) v |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
   return v;
 }
 
@@ -608,8 +617,18 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   __shared__ double s_theta[ROPE_ANY ? D / 2 : 1];
   __shared__ float s_mat[ROT == ROT_SO4 ? (D / 4) * 16 : 1];
   __shared__ __attribute__((aligned(16))) uint16_t s_goff[PERM_ANY ? D : 8];
+  // dynamic codebook: 1 / scale and the wide-channel rank of each rotated channel
+  __shared__ float s_cinv[QUANT == Q_LLOYD ? D : 1];
+  __shared__ uint8_t s_rank[QUANT == Q_LLOYD ? D : 1];
 
   const int tid = threadIdx.x;
+  if constexpr (QUANT == Q_LLOYD) {
+    if (a.dyn)
+      for (int j = tid; j < D; j += blockDim.x) {
+        s_cinv[j] = 1.0f / a.chan_scale[j];
+        s_rank[j] = a.wide_rank[j];
+      }
+  }
   if constexpr (PERM_ANY) {
     // byte offset of channel perm[j] in a staging row, for the gather
     if (PERM)
@@ -765,6 +784,12 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
         } else {
           __builtin_amdgcn_raw_buffer_store_b32(0u, make_buf_item(a.norm + vec0, (uint32_t)(4 * nvalid)),
                                                 4u * (uint32_t)q, 0, 0);
+          if (a.dyn && l == 0) {
+            constexpr int EB = D / 128;
+            const buf_t eb = make_buf_item(a.extra + vec0 * EB, (uint32_t)(EB * nvalid));
+            if constexpr (EB == 1) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, eb, (uint32_t)q, 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, eb, 2u * (uint32_t)q, 0, 0);
+          }
         }
         return;
       }
@@ -948,15 +973,51 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       for (int i = 0; i < NT; ++i) tau[i] = 0.5f * (a.codebook[i] + a.codebook[i + 1]);
 #pragma unroll
       for (int w = 0; w < BITS; ++w) cw.w[w] = 0u;
+      if (!a.dyn) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float z = v[i] * A;
-        uint32_t c = 0;
+        for (int i = 0; i < 32; ++i) {
+          const float z = v[i] * A;
+          uint32_t c = 0;
 #pragma unroll
-        for (int k = 0; k < NT; ++k) c += (z > tau[k]) ? 1u : 0u;
-        const int bit = BITS * i, w = bit >> 5, sh = bit & 31;
-        cw.w[w] |= c << sh;
-        if (BITS == 3 && sh > 29) cw.w[w + 1] |= c >> (32 - sh);
+          for (int k = 0; k < NT; ++k) c += (z > tau[k]) ? 1u : 0u;
+          const int bit = BITS * i, w = bit >> 5, sh = bit & 31;
+          cw.w[w] |= c << sh;
+          if (BITS == 3 && sh > 29) cw.w[w + 1] |= c >> (32 - sh);
+        }
+      } else {
+        // dynamic codebook: channel j compares z_j / scale_j against the N(0,1) midpoints; a wide
+        // channel against the 2^(b+1)-level codebook's, its top code bit going to the extra plane
+        constexpr int NTW = (2 << BITS) - 1;
+        float tw[NTW];
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) tw[i] = 0.5f * (a.codebook_wide[i] + a.codebook_wide[i + 1]);
+        uint32_t ex = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int j = 32 * l + i;
+          const float t = (v[i] * A) * s_cinv[j];
+          const uint32_t rk = s_rank[j];
+          uint32_t c = 0;
+          if (rk != 0xffu) {
+#pragma unroll
+            for (int k = 0; k < NTW; ++k) c += (t > tw[k]) ? 1u : 0u;
+            ex |= (c >> BITS) << rk;
+            c &= (1u << BITS) - 1u;
+          } else {
+#pragma unroll
+            for (int k = 0; k < NT; ++k) c += (t > tau[k]) ? 1u : 0u;
+          }
+          const int bit = BITS * i, w = bit >> 5, sh = bit & 31;
+          cw.w[w] |= c << sh;
+          if (BITS == 3 && sh > 29) cw.w[w + 1] |= c >> (32 - sh);
+        }
+        ex = vec_or<LV>(ex);
+        constexpr int EB = D / 128;  // extra bytes per vector
+        const buf_t eb = make_buf_item(a.extra + vec0 * EB, (uint32_t)(EB * nvalid));
+        if (l == 0) {
+          if constexpr (EB == 1) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)ex, eb, (uint32_t)q, 0, 0);
+          else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ex, eb, 2u * (uint32_t)q, 0, 0);
+        }
       }
     }
     store_lane_codes<BITS>(make_buf_item(a.codes + vec0 * CB, (uint32_t)(CB * nvalid)),
@@ -1020,6 +1081,10 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   extern __shared__ float s_stage[];
   __shared__ float s_mat[ROT == ROT_SO4 ? (D / 4) * 16 : 1];
   __shared__ float s_cb[kMaxCodebook];
+  // dynamic codebook: the wide codebook, each rotated channel's scale and wide-channel rank
+  __shared__ float s_cbw[QUANT == Q_LLOYD ? 2 * kMaxCodebook : 1];
+  __shared__ float s_csc[QUANT == Q_LLOYD ? D : 1];
+  __shared__ uint8_t s_rank[QUANT == Q_LLOYD ? D : 1];
 
   const int tid = threadIdx.x;
   if constexpr (ROT == ROT_SO4) {
@@ -1027,6 +1092,13 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   }
   if constexpr (QUANT == Q_LLOYD) {
     if (tid < (1 << BITS)) s_cb[tid] = a.codebook[tid];
+    if (a.dyn) {
+      if (tid < (2 << BITS)) s_cbw[tid] = a.codebook_wide[tid];
+      for (int j = tid; j < D; j += blockDim.x) {
+        s_csc[j] = a.chan_scale[j];
+        s_rank[j] = a.wide_rank[j];
+      }
+    }
   }
   // block-shared parameters ready; the barrier also starts the block's four waves (adjacent
   // tiles) together, which measured about 2 % faster even where there are no parameters
@@ -1065,6 +1137,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     uint32_t sc, zr;  // fp16 bits of scale and zero (min-max), combined only where used,
                       // so that nothing waits for the prefetch before the current item
     float rho;    // Lloyd-Max
+    uint32_t ex;  // dynamic codebook: the vector's extra bits
   };
   // the packed planes of item (tile, row); with on == false (wave-uniform) nothing is read
   auto fetch = [&](Packed& pk, const LaneTile& lt, int64_t row, bool on) __attribute__((always_inline)) {
@@ -1083,6 +1156,13 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     } else {
       pk.rho = __uint_as_float(
           __builtin_amdgcn_raw_buffer_load_b32(make_buf(a.norm + vec0, 4 * nvalid), 4u * (uint32_t)q, 0, kNT));
+      pk.ex = 0u;
+      if (a.dyn) {
+        constexpr int EB = D / 128;
+        const buf_t eb = make_buf(a.extra + vec0 * EB, EB * nvalid);
+        if constexpr (EB == 1) pk.ex = __builtin_amdgcn_raw_buffer_load_b8(eb, (uint32_t)q, 0, 0);
+        else pk.ex = __builtin_amdgcn_raw_buffer_load_b16(eb, 2u * (uint32_t)q, 0, 0);
+      }
     }
   };
 
@@ -1160,9 +1240,18 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
         const float sc = f16_value(pk.sc), z = f16_value(pk.zr);
 #pragma unroll
         for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf((float)code_at<BITS>(pk.c, i), sc, z);
-      } else {
+      } else if (!a.dyn) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) v[i] = s_cb[code_at<BITS>(pk.c, i)];
+      } else {
+        // dynamic codebook: scale_j times the level of the channel's own codebook
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int j = 32 * l + i;
+          const uint32_t c = code_at<BITS>(pk.c, i), rk = s_rank[j];
+          const float lev = (rk != 0xffu) ? s_cbw[c | (((pk.ex >> (rk & 31u)) & 1u) << BITS)] : s_cb[c];
+          v[i] = lev * s_csc[j];
+        }
       }
       float outscale = 1.0f;
       if constexpr (ROT == ROT_FWHT) {
@@ -1354,6 +1443,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_sink_kernel(const 
     }
   } else {
     if (l == 0) a.norm[vec] = 0.0f;
+    if (a.dyn && l == 0)
+      for (int e = 0; e < D / 128; ++e) a.extra[vec * (D / 128) + e] = 0;
   }
 }
 
@@ -2809,6 +2900,151 @@ __global__ void __launch_bounds__(256) sink_select_kernel(const CalibArgs a) {
   }
 }
 
+// Rotated moments for the dynamic codebook: the codec's front end (RoPE, norm separation,
+// permutation, rotation) on each vector, then per rotated channel the sum of z^2.  One wave per
+// (row, run of tokens), one vector at a time: lane i holds channels i + 64 k (k < D/64), so the
+// channel bits 0..5 are lane bits (shuffles) and the rest register bits.
+template <int DT, int D>
+__global__ void __launch_bounds__(256) rotated_moments_kernel(const CalibArgs a) {
+  constexpr int K = D / 64;
+  constexpr int ES = (DT == DT_F32) ? 4 : 2;
+  __shared__ float s_mat[(D / 4) * 16];
+  __shared__ float s_u[4][D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (a.rot == ROT_SO4)
+    for (int b = threadIdx.x; b < D / 4; b += blockDim.x) build_so4(&a.quat[8 * b], &s_mat[16 * b]);
+  __syncthreads();
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.n_waves) return;  // wave-uniform; no barrier follows
+  const int64_t nchunk = (a.tokens + a.tpw - 1) / a.tpw;
+  const int64_t r = w / nchunk, t0 = (w % nchunk) * a.tpw;
+  const int64_t t1 = min(t0 + (int64_t)a.tpw, a.tokens);
+  double theta[K], acc[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    theta[k] = exp2(-(2.0 * (double)((lane + 64 * k) >> 1) / (double)D) * a.rope_log2_base);
+    acc[k] = 0.0;
+  }
+  const float norm_c = (float)(1.0 / __builtin_sqrt((double)D));
+  const char* base = reinterpret_cast<const char*>(a.x);
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t pos = a.pos_offset + t;
+    if (pos < a.n_sink) continue;  // wave-uniform
+    float c[K], sn[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      c[k] = 1.0f;
+      sn[k] = 0.0f;
+      if (a.rope) rope_cos_sin(pos, theta[k], &c[k], &sn[k]);
+    }
+    for (int64_t h = 0; h < a.heads; ++h) {
+      const char* vp = base + (r * a.sr + t * a.st + h * a.sh) * ES;
+      float u[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int ch = lane + 64 * k;
+        if constexpr (DT == DT_F32) u[k] = reinterpret_cast<const float*>(vp)[ch];
+        else if constexpr (DT == DT_BF16) u[k] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vp)[ch] << 16);
+        else u[k] = f16_value(reinterpret_cast<const uint16_t*>(vp)[ch]);
+      }
+      if (a.rope) {  // pair (2i, 2i + 1) = lanes (2m, 2m + 1) of the same register
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float p = __shfl_xor(u[k], 1);
+          u[k] = (lane & 1) ? __builtin_fmaf(p, sn[k], u[k] * c[k]) : __builtin_fmaf(u[k], c[k], -p * sn[k]);
+        }
+      }
+      // norm separation: u / (rho + 1e-6)
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) ss = __builtin_fmaf(u[k], u[k], ss);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      const float inv = 1.0f / (__builtin_sqrtf(ss) + 1e-6f);
+#pragma unroll
+      for (int k = 0; k < K; ++k) u[k] *= inv;
+      if (a.use_perm) {  // u'[c] = u[perm[c]]
+        float v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int src = a.perm[lane + 64 * k];
+          float val = 0.0f;
+#pragma unroll
+          for (int kk = 0; kk < K; ++kk) {
+            const float x = __shfl(u[kk], src & 63);
+            val = (src >> 6) == kk ? x : val;
+          }
+          v[k] = val;
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) u[k] = v[k];
+      }
+      float z[K];
+      if (a.rot == ROT_FWHT) {
+        // bits 6.. in the lane (registers), bits 0..5 across lanes; then 1/sqrt(D)
+#pragma unroll
+        for (int hb = 1; hb < K; hb <<= 1)
+#pragma unroll
+          for (int k = 0; k < K; ++k)
+            if (!(k & hb)) {
+              const float x = u[k], y = u[k + hb];
+              u[k] = x + y;
+              u[k + hb] = x - y;
+            }
+#pragma unroll
+        for (int bit = 1; bit < 64; bit <<= 1)
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            const float p = __shfl_xor(u[k], bit);
+            u[k] = (lane & bit) ? p - u[k] : u[k] + p;
+          }
+#pragma unroll
+        for (int k = 0; k < K; ++k) z[k] = u[k] * norm_c;
+      } else if (a.rot == ROT_SO4) {  // block b = channels 4b .. 4b + 3 = lanes 4m .. 4m + 3
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int ch = lane + 64 * k, b = ch >> 2, row = ch & 3;
+          float acc4 = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc4 = __builtin_fmaf(s_mat[16 * b + 4 * row + i], __shfl(u[k], (lane & ~3) + i), acc4);
+          z[k] = acc4;
+        }
+      } else if (a.rot == ROT_DENSE) {  // z_i = sum_j M[i][j] u_j, u staged in LDS
+        float* su = s_u[wave];
+#pragma unroll
+        for (int k = 0; k < K; ++k) su[lane + 64 * k] = u[k];
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float* row = a.rot_matrix + (int64_t)(lane + 64 * k) * D;
+          float acc1 = 0.0f;
+          for (int j = 0; j < D; ++j) acc1 = __builtin_fmaf(row[j], su[j], acc1);
+          z[k] = acc1;
+        }
+        wave_lds_sync();
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) z[k] = u[k];
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc[k] += (double)z[k] * (double)z[k];
+    }
+  }
+  double* pb = a.part + w * D;
+#pragma unroll
+  for (int k = 0; k < K; ++k) pb[lane + 64 * k] = acc[k];
+}
+
+template <int DT, int D>
+int launch_moments_t(const CalibArgs& a, hipStream_t s) {
+  if (a.n_waves > 0) {
+    hipLaunchKernelGGL((rotated_moments_kernel<DT, D>), dim3((unsigned)((a.n_waves + 3) / 4)), dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError()) return (int)e;
+  }
+  hipLaunchKernelGGL((channel_stats_final<D>), dim3(D), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+
 template <int DT, int D>
 int launch_stats_t(const CalibArgs& a, hipStream_t s) {
   if (a.n_waves > 0) {
@@ -2839,6 +3075,15 @@ int launch_channel_stats(const CalibArgs& a, void* stream) {
     case DT_F16: return d128 ? launch_stats_t<DT_F16, 128>(a, s) : launch_stats_t<DT_F16, 256>(a, s);
     case DT_BF16: return d128 ? launch_stats_t<DT_BF16, 128>(a, s) : launch_stats_t<DT_BF16, 256>(a, s);
     default: return d128 ? launch_stats_t<DT_F32, 128>(a, s) : launch_stats_t<DT_F32, 256>(a, s);
+  }
+}
+int launch_rotated_moments(const CalibArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool d128 = a.head_dim == 128;
+  switch (a.dtype) {
+    case DT_F16: return d128 ? launch_moments_t<DT_F16, 128>(a, s) : launch_moments_t<DT_F16, 256>(a, s);
+    case DT_BF16: return d128 ? launch_moments_t<DT_BF16, 128>(a, s) : launch_moments_t<DT_BF16, 256>(a, s);
+    default: return d128 ? launch_moments_t<DT_F32, 128>(a, s) : launch_moments_t<DT_F32, 256>(a, s);
   }
 }
 int launch_detect_sinks(const CalibArgs& a, void* stream) {

@@ -98,6 +98,8 @@ def compare_encode(gpu: dict, ora: dict, p: codec.CodecParams, shape, label: str
             assert np.all(gpu["zero"][:, sk].view(np.uint16) == 0), f"{label}: sink zero slots not zero"
         else:
             assert np.all(gpu["norm"][:, sk] == 0), f"{label}: sink norm slots not zero"
+            if p.chan_scale is not None:
+                assert np.all(gpu["extra"][:, sk] == 0), f"{label}: sink extra slots not zero"
         written = ora["sink_written"]
         gs = gpu["sink"][:, written]
         os_ = ora["sink"][:, written]
@@ -161,6 +163,24 @@ def compare_encode(gpu: dict, ora: dict, p: codec.CodecParams, shape, label: str
         mism = qg != q_ref
         frac = np.abs(tg - np.floor(tg) - 0.5)
         tie = frac < CODE_TIE
+    elif p.chan_scale is not None:
+        # dynamic codebook: compare the full code (b bits + the wide channels' top bit) against
+        # the thresholds of each channel's own codebook, in units of its level gaps
+        from oracle import dynamic as odyn
+        wide = np.asarray(p.chan_wide, dtype=bool)
+        top_g = odyn.unpack_extra(gpu["extra"], wide)[:, keep]
+        qg = qg.astype(np.int64) + (top_g.astype(np.int64) << b)
+        q_ref = qo.astype(np.int64) + (ora["top"][:, keep].astype(np.int64) << b)
+        mism = qg != q_ref
+        tie = np.zeros(mism.shape, dtype=bool)
+        for book, sel in ((np.asarray(p.codebook, np.float64), ~wide), (np.asarray(p.codebook_wide, np.float64), wide)):
+            tau = 0.5 * (book[:-1] + book[1:])
+            dist = np.abs(tt[..., sel, None] - tau) / np.diff(book)
+            tie[..., sel] = (dist < CODE_TIE).any(-1)
+        ng = gpu["norm"][:, keep].astype(np.float64)
+        no = ora["norm"][:, keep].astype(np.float64)
+        rel = np.abs(ng - no) / np.maximum(np.abs(no), 1e-30)
+        assert np.all((rel <= NORM_REL) | (np.abs(ng - no) < 1e-30)), f"{label}: norm differs, max rel {rel.max():.3g}"
     else:
         q_ref = qo
         mism = qg != q_ref

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(kvq.library_path())
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert kvq.abi_version() == 1
+    assert kvq.abi_version() == 2
 
 
 def _cfg(**kw):
@@ -74,7 +74,7 @@ def test_validation_errors(name, kw, status):
 
 def test_abi_version_mismatch():
     c = _cfg().c_struct()
-    c.abi_version = 2
+    c.abi_version = 1
     lib = ctypes.CDLL(kvq.library_path())
     lib.kvq_validate.argtypes = [ctypes.c_void_p]
     assert lib.kvq_validate(ctypes.byref(c)) == 9
@@ -148,7 +148,7 @@ def test_llama3_cache_bytes():
     assert (sz["codes"] + sz["scale"] + sz["zero"]) == 36 * n
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("sigma", [1.0, 1.0 / np.sqrt(128.0), 1.0 / 16.0])
 def test_host_lloyd_max_matches_oracle(bits, sigma):
     got = kvq.lloyd_max_gaussian(bits, sigma)
@@ -158,7 +158,7 @@ def test_host_lloyd_max_matches_oracle(bits, sigma):
 
 def test_host_lloyd_max_rejects_bad_arguments():
     with pytest.raises(kvq.KvqError):
-        kvq.lloyd_max_gaussian(5, 1.0)
+        kvq.lloyd_max_gaussian(6, 1.0)
     with pytest.raises(kvq.KvqError):
         kvq.lloyd_max_gaussian(2, -1.0)
 
@@ -284,3 +284,41 @@ def test_calibration_refusals_on_the_host():
     assert lib.kvq_detect_sinks(ctypes.byref(c), 4096, float("inf"), 4096, 4096, 4096, 4096, 4096, None) == 6
     assert lib.kvq_detect_sinks(ctypes.byref(c), None, 8.0, 4096, 4096, 4096, 4096, 4096, None) == 1
     assert lib.kvq_detect_sinks(ctypes.byref(c), 4096, 8.0, 4096, 4096, None, 4096, 4096, None) == 1
+
+
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3), (256, 4)])
+def test_dynamic_codebook_host_matches_oracle(d, bits):
+    """The library's host dynamic codebook equals the oracle's: scales (float32 of the square
+    root), the D/16 wide channels, and both Lloyd-Max codebooks."""
+    from oracle import dynamic as dyn
+    rng = np.random.default_rng(d + bits)
+    m = rng.uniform(0.2, 3.0, d) / d
+    m[rng.choice(d, 5, replace=False)] *= 30.0
+    m[:4] = m[4]  # ties
+    sc, wide, cb, cbw = kvq.dynamic_codebook(m, bits)
+    osc, owide, ocb, ocbw = dyn.dynamic_codebook(m, bits)
+    assert np.array_equal(sc, osc.astype(np.float32))
+    assert np.array_equal(wide.astype(bool), owide)
+    assert np.allclose(cb, ocb, rtol=2e-7, atol=0) and np.allclose(cbw, ocbw, rtol=2e-7, atol=0)
+    with pytest.raises(kvq.KvqError):
+        kvq.dynamic_codebook(np.zeros(d), bits)
+
+
+def test_dynamic_codebook_config_refusals():
+    d = 128
+    sc = np.ones(d, np.float32)
+    wide = np.zeros(d, np.uint8)
+    wide[:8] = 1
+    cb = np.linspace(-1, 1, 8).astype(np.float32)
+    cbw = np.linspace(-1, 1, 16).astype(np.float32)
+    base = dict(shape=(1, 4, 2, d), bits=3, quant="lloyd", codebook=cb, chan_scale=sc, chan_wide=wide, codebook_wide=cbw)
+    kvq.validate(_cfg(**base))
+    for kw, status in ((dict(chan_wide=None), 1), (dict(quant="minmax"), 6),
+                       (dict(chan_scale=np.where(np.arange(d) == 3, 0.0, 1.0).astype(np.float32)), 6),
+                       (dict(chan_wide=np.ones(d, np.uint8)), 6), (dict(codebook_wide=cbw[::-1].copy()), 6),
+                       (dict(rot="dense"), 1)):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.validate(_cfg(**{**base, **kw}))
+        assert e.value.status == status, kw
+    sz = kvq.packed_sizes(_cfg(**base))
+    assert sz["extra"] == 1 * 4 * 2 * 1 and sz["norm"] == 1 * 4 * 2 * 4
