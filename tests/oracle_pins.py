@@ -844,4 +844,59 @@ def check_dynamic_pipeline():
     assert np.sum((yd - xr) ** 2) < 0.5 * np.sum((ys - xr) ** 2)
 
 
+# --------------------------------------------------------------------------- #
+# IsoQuant dynamic bit width by attention entropy
+# --------------------------------------------------------------------------- #
+def check_attention_entropy():
+    """Closed forms: n equal keys give ln n; one dominant key gives ~0; two slots give the
+    binary entropy of their logistic weight; scipy's entropy of scipy's softmax (library)."""
+    from scipy.special import softmax
+    from scipy.stats import entropy as sp_entropy
+    from oracle import bitwidth as bw
+    rng = _rng(50)
+    d = 16
+    k = np.zeros((1, 7, 1, d))
+    q = rng.standard_normal((1, 2, d))
+    e = bw.attention_entropy(q, k, np.array([5]), 0.3)
+    assert np.allclose(e, np.log(5.0), rtol=1e-14)
+    k2 = rng.standard_normal((1, 2, 1, d))
+    e2 = bw.attention_entropy(q[:, :1], k2, None, 0.5)
+    s = 0.5 * (k2[0, :, 0] @ q[0, 0])
+    w = 1.0 / (1.0 + np.exp(-(s[0] - s[1])))
+    assert np.isclose(e2[0, 0], -(w * np.log(w) + (1 - w) * np.log(1 - w)), rtol=1e-12)
+    kb = rng.standard_normal((2, 30, 2, d))
+    qb = rng.standard_normal((2, 4, d))
+    eb = bw.attention_entropy(qb, kb, np.array([30, 11]), 0.25)
+    for r, n in ((0, 30), (1, 11)):
+        for m in range(4):
+            p = softmax(0.25 * kb[r, :n, m // 2] @ qb[r, m])
+            assert np.isclose(eb[r, m], sp_entropy(p), rtol=1e-12)
+    assert bw.attention_entropy(qb, kb, np.array([0, 3]), 0.25)[0].tolist() == [0.0] * 4
+    assert np.allclose(bw.head_entropy(eb, 2), [eb[:, :2].mean(), eb[:, 2:].mean()])
+
+
+def check_bit_allocation():
+    """Worked allocations; the sum and range always hold; equal entropies give equal widths;
+    more entropy never gets fewer bits (random cases against brute force over all widths:
+    the allocation minimises sum (b_h - x_h)^2 among valid ones up to ties)."""
+    from itertools import product
+    from oracle import bitwidth as bw
+    assert bw.allocate_bits(np.array([1.0, 1.0, 2.0, 4.0]), 12).tolist() == [2, 2, 4, 4]
+    assert bw.allocate_bits(np.ones(8), 24).tolist() == [3] * 8
+    assert bw.allocate_bits(np.zeros(4), 10).tolist() == [3, 3, 2, 2]
+    assert bw.allocate_bits(np.array([3.0, 1.0, 1.0, 1.0]), 12).tolist() == [4, 3, 3, 2]
+    rng = _rng(51)
+    for _ in range(40):
+        h = int(rng.integers(2, 7))
+        e = rng.uniform(0.0, 5.0, h)
+        tot = int(rng.integers(2 * h, 4 * h + 1))
+        b = bw.allocate_bits(e, tot)
+        assert b.sum() == tot and b.min() >= 2 and b.max() <= 4
+        x = tot * e / e.sum()
+        best = min(sum((c - xi) ** 2 for c, xi in zip(cb, x)) for cb in product(range(2, 5), repeat=h) if sum(cb) == tot)
+        assert np.isclose(np.sum((b - x) ** 2), best, rtol=1e-12, atol=1e-12)
+        order = np.argsort(e)
+        assert np.all(np.diff(b[order]) >= 0)
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

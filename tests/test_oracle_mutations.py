@@ -222,6 +222,27 @@ def _pack_extra_msb(top, wide):
     return np.packbits(np.asarray(top, dtype=np.uint8)[..., idx], axis=-1, bitorder="big")
 
 
+from oracle import bitwidth as _bw
+
+_orig_attention_entropy = _bw.attention_entropy
+_orig_allocate_bits = _bw.allocate_bits
+
+
+def _entropy_bits(q, k, lengths, scale):
+    return _orig_attention_entropy(q, k, lengths, scale) / np.log(2.0)  # in bits, not nats
+
+
+def _allocate_inverse(e, total, lo=2, hi=4):
+    e = np.asarray(e, dtype=np.float64)
+    return _orig_allocate_bits(e.max() + e.min() - e, total, lo, hi)  # more bits to less entropy
+
+
+def _allocate_round(e, total, lo=2, hi=4):
+    e = np.asarray(e, dtype=np.float64)
+    x = total * e / e.sum() if e.sum() > 0 else np.full(len(e), total / len(e))
+    return np.clip(np.rint(x), lo, hi).astype(np.int64)  # rounded, the total not kept
+
+
 from oracle import attention as _attention
 
 _orig_attend_decoded = _attention.attend_decoded
@@ -256,6 +277,9 @@ MUTATIONS = {
     "append_slot_is_position": (codec, "append", _append_slot_is_position),
     "widen_bf16_shift_15": (codec, "widen", _widen_shift_15),
     "outlier_perm_top_first": (_cal, "outlier_perm", _perm_top_first),
+    "entropy_in_bits": (_bw, "attention_entropy", _entropy_bits),
+    "bits_inverse_to_entropy": (_bw, "allocate_bits", _allocate_inverse),
+    "bits_rounded_total_lost": (_bw, "allocate_bits", _allocate_round),
     "dynamic_scale_is_variance": (_dyn, "dynamic_codebook", _dyncb_variance),
     "dynamic_wide_smallest": (_dyn, "dynamic_codebook", _dyncb_smallest_wide),
     "dynamic_codes_no_wide": (_dyn, "dyn_codes", _dyn_codes_no_wide),
