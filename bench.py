@@ -535,14 +535,41 @@ def main():
             b.record(stream)
             stream.synchronize()
             cal_t[name] = a.elapsed_time(b) / 10
+    # the dynamic bit width's entropy pass over the same 8 rows of the encoded K cache (32 query
+    # heads): per-query-head attention entropy, averaged per KV head, and the widths for an
+    # average of 3 bits
+    kpl = {n: v[:cal_rows] for n, v in planes["K"].items() if n != "sink"}
+    kpl["sink"] = planes["K"]["sink"][:cal_rows]
+    kcfg8 = kvq.Config(**{**cfgs["K"].__dict__, "shape": (cal_rows,) + tuple(cases["K"].shape[1:]), "_keep": []})
+    q8 = torch.randn((cal_rows, 32, 128), generator=gen, device=dev, dtype=torch.float32)
+    with torch.cuda.stream(stream):
+        ent = kvq.attention_entropy(q8, kpl, kcfg8, stream=stream)
+        stream.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            kvq.attention_entropy(q8, kpl, kcfg8, out=ent, stream=stream)
+        b.record(stream)
+        stream.synchronize()
+    cal_t["attention_entropy"] = a.elapsed_time(b) / 5
+    e_head = ent.double().view(cal_rows, 8, 4).mean(dim=(0, 2)).cpu().numpy()
+    widths = kvq.allocate_bits(e_head, 3 * 8)
     cal_bytes = int(ksl.numel() * 2)
     calib = {"slice": f"K rows 0-{cal_rows - 1} of the cache ({int(ksl.shape[0] * ksl.shape[1] * ksl.shape[2])} vectors, "
                       f"{cal_bytes} bytes read)",
              **{k: {"ms": round(v, 4), "GBps": round(cal_bytes / (v * 1e-3) / 1e9, 1),
-                    "hbm_frac": round(cal_bytes / (v * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)} for k, v in cal_t.items()},
-             "what": "RotateKV calibration: per-channel mean |post-RoPE key| for the outlier-aware permutation "
-                     "(kvq_channel_stats) and sink detection by token norm against lambda x the row median "
-                     "(kvq_detect_sinks); run once per calibration, not per step"}
+                    "hbm_frac": round(cal_bytes / (v * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)}
+                for k, v in cal_t.items() if k != "attention_entropy"},
+             "attention_entropy": {"ms": round(cal_t["attention_entropy"], 4),
+                                   "what": "entropy of 32 query heads' softmax over the 8 rows' encoded K "
+                                           "(36 bytes per vector) in the rotated domain",
+                                   "head_entropy_nats": [round(float(v), 4) for v in e_head],
+                                   "widths_for_3_bits_average": widths.tolist()},
+             "what": "calibration passes, run once, not per step: RotateKV per-channel mean |post-RoPE key| for "
+                     "the outlier-aware permutation (kvq_channel_stats), sink detection by token norm against "
+                     "lambda x the row median (kvq_detect_sinks); IsoQuant attention entropy for per-head "
+                     "bit widths (kvq_attention_entropy, kvq_allocate_bits)"}
     del ksl, ws_cal
 
     cpu = None

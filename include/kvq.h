@@ -276,6 +276,30 @@ kvq_status kvq_rotated_moments(const kvq_config* cfg, const void* x, double* mom
 kvq_status kvq_dynamic_codebook(const double* moments, int64_t head_dim, int32_t bits, float* chan_scale,
                                 uint8_t* chan_wide, float* codebook, float* codebook_wide);
 
+/* Dynamic bit width (IsoQuant page, section 6.2: each head's attention entropy, widths in
+ * proportion, the quantization kernel of each width).  kvq_attention_entropy writes
+ *   entropy  DEVICE float [R, q_heads]: the entropy (nats) of the softmax attention of q[r, m]
+ *            over the first lengths[r] slots of the K cache (as kvq_attend scores them:
+ *            scale * q . k, keys in the rotated domain, sinks from the fp16 planes); 0 for a
+ *            row with no slot.
+ * cfg_k: Walsh-Hadamard + min-max, head_dim 128 or 256, 2/3/4 bits, any group, pos_offset 0;
+ * q DEVICE float [R, q_heads, D] contiguous, q_heads = heads * g, g in {1, 2, 4, 8}; lengths
+ * DEVICE int32 [R] or NULL; workspace DEVICE, 16-byte aligned, at least
+ * kvq_attention_entropy_workspace_size bytes.  Asynchronous. */
+kvq_status kvq_attention_entropy_workspace_size(const kvq_config* cfg_k, int64_t q_heads, size_t* bytes);
+kvq_status kvq_attention_entropy(const kvq_config* cfg_k, const kvq_planes* k, const float* q, int64_t q_heads,
+                                 const int32_t* lengths, float scale, float* entropy, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Host-only: per-head widths bits[h] in [lo, hi] (2 <= lo <= hi <= 4) summing to total, in
+ * proportion to entropy[h] (HOST double [heads], each finite >= 0; e.g. the mean of
+ * kvq_attention_entropy over rows and the query heads of KV head h): the share
+ * total * e_h / sum(e) floored into [lo, hi], then one bit at a time to the largest remainder
+ * (lowest head first) while short, off the smallest remainder (highest head first) while over.
+ * Each head is then encoded at its width (a head shard through the stride arguments). */
+kvq_status kvq_allocate_bits(const double* entropy, int64_t heads, int32_t total, int32_t lo, int32_t hi,
+                             int32_t* bits);
+
 /* Host-only: Lloyd-Max codebook (2^bits ascending levels, bits 1..5) for N(0, sigma^2), written
  * to codebook_out as float32; the classical fixed point of midpoint thresholds and
  * conditional-mean levels, iterated in double precision (IsoQuant page, section 3.1

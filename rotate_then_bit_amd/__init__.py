@@ -25,7 +25,7 @@ import numpy as np
 
 __all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_noalloc", "attend_noalloc_max_workspace",
            "channel_stats", "channel_stats_workspace_size", "outlier_perm", "detect_sinks", "rotated_moments",
-           "dynamic_codebook",
+           "dynamic_codebook", "attention_entropy", "allocate_bits", "encode_heads",
            "attend_workspace_size", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
            "library_path", "abi_version", "DTYPES", "ROTATIONS", "QUANTIZERS", "EXPORTED_SYMBOLS"]
 
@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_
                     "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_attend_noalloc_max_workspace",
                     "kvq_decode", "kvq_lloyd_max_gaussian", "kvq_channel_stats_workspace_size", "kvq_channel_stats",
                     "kvq_outlier_perm", "kvq_detect_sinks", "kvq_rotated_moments", "kvq_dynamic_codebook",
+                    "kvq_attention_entropy_workspace_size", "kvq_attention_entropy", "kvq_allocate_bits",
                     "kvq_status_string", "kvq_last_error_message")
 
 
@@ -124,6 +125,13 @@ def _load():
     lib.kvq_rotated_moments.argtypes = [ctypes.POINTER(_Config), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]
     lib.kvq_dynamic_codebook.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 4
+    lib.kvq_attention_entropy_workspace_size.argtypes = [ctypes.POINTER(_Config), ctypes.c_int64,
+                                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_attention_entropy.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Planes), ctypes.c_void_p,
+                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.kvq_allocate_bits.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p]
     lib.kvq_lloyd_max_gaussian.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_status_string.argtypes = [ctypes.c_int]
@@ -131,7 +139,8 @@ def _load():
     for fn in ("kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append", "kvq_decode", "kvq_lloyd_max_gaussian",
                "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_channel_stats_workspace_size",
                "kvq_channel_stats", "kvq_outlier_perm", "kvq_detect_sinks", "kvq_rotated_moments",
-               "kvq_dynamic_codebook"):
+               "kvq_dynamic_codebook", "kvq_attention_entropy_workspace_size", "kvq_attention_entropy",
+               "kvq_allocate_bits"):
         getattr(lib, fn).restype = ctypes.c_int
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -435,6 +444,51 @@ def dynamic_codebook(moments, bits: int):
     _check(_L().kvq_dynamic_codebook(m.ctypes.data, d, int(bits), sc.ctypes.data, wide.ctypes.data, cb.ctypes.data,
                                      cbw.ctypes.data))
     return sc, wide, cb, cbw
+
+
+def attention_entropy(q, k_planes, k_cfg: Config, lengths=None, scale=None, out=None, workspace=None, stream=None):
+    """Entropy (nats, float32 device tensor [R, q_heads]) of each query head's softmax attention
+    over the encoded K cache."""
+    import torch
+    r, q_heads = int(q.shape[0]), int(q.shape[1])
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float32 tensor [rows, q_heads, head_dim]")
+    if scale is None:
+        scale = float(k_cfg.shape[-1]) ** -0.5
+    c = k_cfg.c_struct()
+    n = ctypes.c_size_t()
+    _check(_L().kvq_attention_entropy_workspace_size(ctypes.byref(c), q_heads, ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((r, q_heads), dtype=torch.float32, device=q.device)
+    pk = _planes_struct(k_planes)
+    _check(_L().kvq_attention_entropy(ctypes.byref(c), ctypes.byref(pk), _ptr(q), q_heads, _ptr(lengths), float(scale),
+                                      _ptr(out), int(workspace.data_ptr()),
+                                      int(workspace.numel() * workspace.element_size()), _stream_handle(stream)))
+    return out
+
+
+def allocate_bits(entropy, total: int, lo: int = 2, hi: int = 4) -> np.ndarray:
+    """Host-side per-head widths (int32 [heads]) in proportion to the heads' entropies."""
+    e = np.ascontiguousarray(np.asarray(entropy, dtype=np.float64))
+    b = np.zeros(e.shape[0], dtype=np.int32)
+    _check(_L().kvq_allocate_bits(e.ctypes.data, e.shape[0], int(total), int(lo), int(hi), b.ctypes.data))
+    return b
+
+
+def encode_heads(x, cfg: Config, bits_per_head, stream=None):
+    """Encode each KV head of ``x`` ([R,T,H,D], contiguous or strided as cfg.strides) at its own
+    width: head h is a head shard (the stride arguments select it) encoded with
+    bits_per_head[h].  Returns a list of (Config, planes), one per head."""
+    r, t, h, d = (int(v) for v in cfg.shape)
+    sr, st, sh = cfg.strides if cfg.strides is not None else tuple(int(v) for v in x.stride()[:3])
+    out = []
+    for i in range(h):
+        ci = Config(**{**cfg.__dict__, "shape": (r, t, 1, d), "bits": int(bits_per_head[i]), "strides": (sr, st, sh),
+                       "_keep": []})
+        out.append((ci, encode(x[:, :, i:i + 1], ci, stream=stream)))
+    return out
 
 
 def lloyd_max_gaussian(bits: int, sigma: float) -> np.ndarray:

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
@@ -721,6 +722,128 @@ kvq_status kvq_detect_sinks(const kvq_config* cfg, const void* x, double lambda,
     return fail(KVQ_ERR_SHAPE, "calibration slice too large");
   const int err = kvq::launch_detect_sinks(a, stream);
   if (err != 0) return fail(KVQ_ERR_DEVICE, "sink detection launch failed: %s", kvq::device_error_string(err));
+  return ok();
+}
+
+namespace {
+kvq_status check_entropy(const kvq_config* cfg, int64_t q_heads, size_t* ws_bytes, kvq::EntropyArgs* a) {
+  Derived dv;
+  kvq_status st = check_config(cfg, &dv);
+  if (st != KVQ_OK) return st;
+  if (cfg->rot != KVQ_ROT_FWHT || cfg->quant != KVQ_Q_MINMAX)
+    return fail(KVQ_ERR_UNSUPPORTED, "attention entropy reads Walsh-Hadamard + min-max caches");
+  if (cfg->pos_offset != 0) return fail(KVQ_ERR_UNSUPPORTED, "attention entropy needs pos_offset 0 (slot = position)");
+  if (cfg->heads <= 0 || q_heads <= 0 || q_heads % cfg->heads != 0)
+    return fail(KVQ_ERR_SHAPE, "q_heads must be a positive multiple of heads");
+  const int64_t qg = q_heads / cfg->heads;
+  if (qg != 1 && qg != 2 && qg != 4 && qg != 8)
+    return fail(KVQ_ERR_UNSUPPORTED, "attention entropy supports 1, 2, 4 or 8 query heads per KV head");
+  int32_t nc = 1, ct = 8;
+  kvq::attend_chunks(cfg->rows, cfg->heads, cfg->tokens, false, &nc, &ct);
+  int64_t nq = 0, tmp = 0;
+  if (!mul_ok(cfg->rows, q_heads, &nq) || !mul_ok(nq, (int64_t)nc * 4 + cfg->head_dim, &tmp) || tmp > (int64_t(1) << 40))
+    return fail(KVQ_ERR_SHAPE, "entropy workspace too large");
+  const size_t q_bytes = (size_t)(nq * cfg->head_dim * 4 + 255) / 256 * 256;
+  *ws_bytes = q_bytes + (size_t)nq * (size_t)nc * 16;
+  if (a) {
+    memset(a, 0, sizeof *a);
+    a->rows = cfg->rows;
+    a->tokens = cfg->tokens;
+    a->heads = cfg->heads;
+    a->q_heads = q_heads;
+    a->head_dim = cfg->head_dim;
+    a->bits = cfg->bits;
+    a->group_log2 = ilog2(cfg->group_size);
+    a->n_sink = cfg->n_sink;
+    a->n_chunks = nc;
+    a->chunk = ct;
+    a->use_perm = cfg->perm ? 1 : 0;
+    if (cfg->perm)
+      for (int64_t i = 0; i < cfg->head_dim; ++i) a->perm[i] = (uint8_t)cfg->perm[i];
+  }
+  return KVQ_OK;
+}
+}  // namespace
+
+kvq_status kvq_attention_entropy_workspace_size(const kvq_config* cfg_k, int64_t q_heads, size_t* bytes) {
+  if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+  kvq_status st = check_entropy(cfg_k, q_heads, bytes, nullptr);
+  return st == KVQ_OK ? ok() : st;
+}
+
+kvq_status kvq_attention_entropy(const kvq_config* cfg_k, const kvq_planes* k, const float* q, int64_t q_heads,
+                                 const int32_t* lengths, float scale, float* entropy, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  kvq::EntropyArgs a;
+  kvq_status st = check_entropy(cfg_k, q_heads, &need, &a);
+  if (st != KVQ_OK) return st;
+  if (!isfinite(scale)) return fail(KVQ_ERR_PARAM, "scale must be finite");
+  if (!k) return fail(KVQ_ERR_NULL, "planes is NULL");
+  if (cfg_k->rows == 0) return ok();
+  Derived dk;
+  (void)check_config(cfg_k, &dk);
+  if ((st = check_planes(cfg_k, dk, k)) != KVQ_OK) return st;
+  if (cfg_k->n_sink > 0 && !k->sink) return fail(KVQ_ERR_NULL, "sink plane is NULL");
+  if (!q || !entropy || !workspace) return fail(KVQ_ERR_NULL, "q, entropy or workspace is NULL");
+  if (!aligned16(q) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(entropy) & 3u))
+    return fail(KVQ_ERR_ALIGN, "q and workspace must be 16-byte aligned, entropy 4-byte");
+  if (lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) return fail(KVQ_ERR_ALIGN, "lengths not 4-byte aligned");
+  if (workspace_bytes < need) return fail(KVQ_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  a.k_codes = static_cast<const uint8_t*>(k->codes);
+  a.k_scale = static_cast<const uint16_t*>(k->scale);
+  a.k_zero = static_cast<const uint16_t*>(k->zero);
+  a.k_sink = static_cast<const uint16_t*>(k->sink);
+  a.q = q;
+  a.entropy = entropy;
+  a.qrot = static_cast<float*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    (size_t)(a.rows * q_heads * cfg_k->head_dim * 4 + 255) / 256 * 256);
+  a.lengths = lengths;
+  a.scale = scale;
+  if ((a.rows * a.heads * a.n_chunks + 3) / 4 > 0x7fffffff || (a.rows * q_heads + 3) / 4 > 0x7fffffff)
+    return fail(KVQ_ERR_SHAPE, "cache too large for one entropy launch");
+  const int err = kvq::launch_entropy(a, stream);
+  if (err != 0) return fail(KVQ_ERR_DEVICE, "attention entropy launch failed: %s", kvq::device_error_string(err));
+  return ok();
+}
+
+kvq_status kvq_allocate_bits(const double* entropy, int64_t heads, int32_t total, int32_t lo, int32_t hi,
+                             int32_t* bits) {
+  if (!entropy || !bits) return fail(KVQ_ERR_NULL, "entropy or bits is NULL");
+  if (heads <= 0 || heads > 32768) return fail(KVQ_ERR_SHAPE, "heads %lld (1 .. 32768)", (long long)heads);
+  if (lo < 2 || hi > 4 || lo > hi) return fail(KVQ_ERR_BITS, "widths [%d, %d] (within 2 .. 4)", lo, hi);
+  if ((int64_t)lo * heads > total || (int64_t)hi * heads < total)
+    return fail(KVQ_ERR_PARAM, "total %d bits outside [%lld, %lld]", total, (long long)(lo * heads),
+                (long long)(hi * heads));
+  double sum = 0.0;
+  for (int64_t i = 0; i < heads; ++i) {
+    if (!(isfinite(entropy[i]) && entropy[i] >= 0.0)) return fail(KVQ_ERR_PARAM, "entropy[%lld] must be finite, >= 0", (long long)i);
+    sum += entropy[i];
+  }
+  // the ideal share, floored into [lo, hi]; single bits by largest (smallest) remainder
+  std::vector<double> x((size_t)heads);
+  int64_t have = 0;
+  for (int64_t i = 0; i < heads; ++i) {
+    x[i] = sum > 0.0 ? (double)total * entropy[i] / sum : (double)total / (double)heads;
+    const double f = floor(x[i]);
+    bits[i] = (int32_t)(f < lo ? lo : (f > hi ? hi : f));
+    have += bits[i];
+  }
+  while (have < total) {
+    int64_t best = -1;
+    for (int64_t i = 0; i < heads; ++i)
+      if (bits[i] < hi && (best < 0 || x[i] - bits[i] > x[best] - bits[best])) best = i;
+    ++bits[best];
+    ++have;
+  }
+  while (have > total) {
+    int64_t best = -1;
+    for (int64_t i = 0; i < heads; ++i)
+      if (bits[i] > lo && (best < 0 || x[i] - bits[i] <= x[best] - bits[best])) best = i;
+    --bits[best];
+    --have;
+  }
   return ok();
 }
 

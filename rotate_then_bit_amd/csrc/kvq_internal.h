@@ -106,6 +106,28 @@ struct AttendArgs {
   uint8_t perm_k[128];
   uint8_t perm_v[128];
 };
+// Attention entropy per (row, query head) over an encoded K cache (Walsh-Hadamard + min-max,
+// head_dim 128 or 256, 2/3/4 bits): the workspace holds the rotated queries [rows, q_heads, D]
+// and per (row, query head, chunk) the partial (max, sum of e^(s - max), sum of
+// e^(s - max) (s - max)).
+struct EntropyArgs {
+  const uint8_t* k_codes;
+  const uint16_t* k_scale;
+  const uint16_t* k_zero;
+  const uint16_t* k_sink;
+  const float* q;
+  float* entropy;   // [rows, q_heads]
+  float* qrot;
+  float* part;      // [rows, q_heads, n_chunks, 4]
+  const int32_t* lengths;
+  int64_t rows, tokens, heads, q_heads, head_dim;
+  int32_t bits, group_log2, n_sink, n_chunks, chunk;
+  float scale;
+  int32_t use_perm;
+  uint8_t perm[kMaxHeadDim];
+};
+int launch_entropy(const EntropyArgs& a, void* stream);
+
 // the chunking of the slot axis for a cache shape (same rule on both sides of the ABI).  Waves
 // in flight for the partial pass: 8 K where the block-cooperative matrix-core pass runs (one
 // group of 128 channels, heads a multiple of 4: measured 4.5 % faster than 16 K at the Llama-3

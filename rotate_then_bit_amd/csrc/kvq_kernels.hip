@@ -3035,6 +3035,225 @@ __global__ void __launch_bounds__(256) rotated_moments_kernel(const CalibArgs a)
   for (int k = 0; k < K; ++k) pb[lane + 64 * k] = acc[k];
 }
 
+// ---------------------------------------------------------------------------
+// Attention entropy (dynamic bit width): per (row, query head) the entropy of the softmax over
+// the row's slots, scored in the rotated domain as the attention does (q . k = (M P q) . y).
+// ---------------------------------------------------------------------------
+// rotated queries: one wave per (row, query head); lane i holds channels i + 64 k
+template <int D>
+__global__ void __launch_bounds__(256) entropy_rotate_q(const EntropyArgs a) {
+  constexpr int K = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.q_heads) return;  // wave-uniform; no barrier in this kernel
+  const float* q = a.q + w * D;
+  float u[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int c = lane + 64 * k;
+    u[k] = q[a.use_perm ? a.perm[c] : c];  // (P q)[c] = q[perm[c]]
+  }
+#pragma unroll
+  for (int hb = 1; hb < K; hb <<= 1)
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (!(k & hb)) {
+        const float x = u[k], y = u[k + hb];
+        u[k] = x + y;
+        u[k + hb] = x - y;
+      }
+#pragma unroll
+  for (int bit = 1; bit < 64; bit <<= 1)
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float p = __shfl_xor(u[k], bit);
+      u[k] = (lane & bit) ? p - u[k] : u[k] + p;
+    }
+  const float nc = (float)(1.0 / __builtin_sqrt((double)D));
+#pragma unroll
+  for (int k = 0; k < K; ++k) a.qrot[w * D + lane + 64 * k] = u[k] * nc;
+}
+
+// online (max, L = sum e^(s - max), S = sum e^(s - max) (s - max)) with one more score
+__device__ __forceinline__ void ent_push(float& M, float& L, float& S, float s) {
+  if (s > M) {
+    if (M == -INFINITY) {  // the first score: nothing to rescale (and -inf * 0 would be NaN)
+      L = 0.0f;
+      S = 0.0f;
+    } else {
+      const float f = __expf(M - s);
+      S = f * (S + (M - s) * L);
+      L = f * L;
+    }
+    M = s;
+  }
+  const float p = __expf(s - M);
+  L += p;
+  S = __builtin_fmaf(p, s - M, S);
+}
+// (M, L, S) merged with another triple
+__device__ __forceinline__ void ent_merge(float& M, float& L, float& S, float M2, float L2, float S2) {
+  if (M2 == -INFINITY) return;
+  if (M == -INFINITY) {
+    M = M2;
+    L = L2;
+    S = S2;
+    return;
+  }
+  const float Mn = fmaxf(M, M2);
+  const float f1 = __expf(M - Mn), f2 = __expf(M2 - Mn);
+  S = f1 * (S + (M - Mn) * L) + f2 * (S2 + (M2 - Mn) * L2);
+  L = f1 * L + f2 * L2;
+  M = Mn;
+}
+
+// Partial pass: one wave per (row, KV head, chunk of slots); each lane scores its own slots
+// (t = t_begin + lane + 64 i) against the QG rotated queries held in LDS.
+template <int D, int BITS, int QG>
+__global__ void __launch_bounds__(256) entropy_partial(const EntropyArgs a) {
+  constexpr int CB = D * BITS / 8;  // code bytes per vector
+  __shared__ float s_q[4][QG * D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
+  const int64_t c = w % a.n_chunks, rh = w / a.n_chunks, h = rh % a.heads, r = rh / a.heads;
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.n_sink);
+  const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
+  float* sq = s_q[wave];
+  const float* src = a.qrot + (r * a.q_heads + h * QG) * D;
+  for (int i = lane; i < QG * D; i += 64) sq[i] = src[i];
+  wave_lds_sync();
+  const int G = 1 << a.group_log2, ng = D >> a.group_log2;
+  float M[QG], L[QG], S[QG];
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    M[m] = -INFINITY;
+    L[m] = 0.0f;
+    S[m] = 0.0f;
+  }
+  for (int64_t t = t_begin + lane; t < t_end; t += 64) {
+    const int64_t vec = (r * a.tokens + t) * a.heads + h;
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(a.k_codes + vec * CB);
+    float dot[QG], qs[QG], sc[QG];
+#pragma unroll
+    for (int m = 0; m < QG; ++m) {
+      sc[m] = 0.0f;
+      dot[m] = 0.0f;
+      qs[m] = 0.0f;
+    }
+    // blocks of 32 channels (BITS code words each; groups are whole blocks)
+#pragma unroll 1
+    for (int blk = 0; blk < D / 32; ++blk) {
+      uint32_t wd[BITS];
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) wd[k] = cw[BITS * blk + k];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int bit = BITS * i, wi = bit >> 5, sh = bit & 31;
+        uint32_t code = wd[wi] >> sh;
+        if (BITS == 3 && sh > 29) code |= wd[wi + 1] << (32 - sh);
+        const float cf = (float)(code & ((1u << BITS) - 1u));
+#pragma unroll
+        for (int m = 0; m < QG; ++m) {
+          const float qv = sq[m * D + 32 * blk + i];
+          dot[m] = __builtin_fmaf(qv, cf, dot[m]);
+          qs[m] += qv;
+        }
+      }
+      if ((((blk + 1) << 5) & (G - 1)) == 0) {  // the end of a group: q . (zero + code * scale)
+        const int g = (32 * blk) >> a.group_log2;
+        const float gs = f16_value(a.k_scale[vec * ng + g]), gz = f16_value(a.k_zero[vec * ng + g]);
+#pragma unroll
+        for (int m = 0; m < QG; ++m) {
+          sc[m] = __builtin_fmaf(gs, dot[m], __builtin_fmaf(gz, qs[m], sc[m]));
+          dot[m] = 0.0f;
+          qs[m] = 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < QG; ++m) ent_push(M[m], L[m], S[m], sc[m] * a.scale);
+  }
+  // merge the wave's lanes, write the chunk's partial for each query head
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    float Mm = M[m], Lm = L[m], Sm = S[m];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float M2 = __shfl_xor(Mm, o), L2 = __shfl_xor(Lm, o), S2 = __shfl_xor(Sm, o);
+      ent_merge(Mm, Lm, Sm, M2, L2, S2);
+    }
+    if (lane == 0) {
+      float* pb = a.part + ((r * a.q_heads + h * QG + m) * a.n_chunks + c) * 4;
+      pb[0] = Mm;
+      pb[1] = Lm;
+      pb[2] = Sm;
+    }
+  }
+}
+
+// Merge the chunks and the fp16 sink slots (raw query against unrotated keys); H = ln L - S / L.
+template <int D>
+__global__ void __launch_bounds__(256) entropy_combine(const EntropyArgs a) {
+  constexpr int K = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.q_heads) return;  // wave-uniform; no barrier in this kernel
+  const int64_t r = w / a.q_heads, m = w % a.q_heads;
+  const int64_t h = m / (a.q_heads / a.heads);
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  float M = -INFINITY, L = 0.0f, S = 0.0f;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const float* pb = a.part + (w * a.n_chunks + c) * 4;
+    ent_merge(M, L, S, pb[0], pb[1], pb[2]);
+  }
+  const int nsk = (int)min((int64_t)a.n_sink, len);
+  const float* qr = a.q + w * D;
+  float qv[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) qv[k] = qr[lane + 64 * k];
+  for (int t = 0; t < nsk; ++t) {
+    const uint16_t* kk = a.k_sink + ((r * a.n_sink + t) * a.heads + h) * D;
+    float d = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) d = __builtin_fmaf(qv[k], f16_value(kk[lane + 64 * k]), d);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) d += __shfl_xor(d, o);
+    ent_push(M, L, S, d * a.scale);
+  }
+  if (lane == 0) a.entropy[w] = L > 0.0f ? __logf(L) - S / L : 0.0f;
+}
+
+template <int D, int BITS, int QG>
+int launch_entropy_t(const EntropyArgs& a, hipStream_t s) {
+  const int64_t nq = a.rows * a.q_heads, np = a.rows * a.heads * a.n_chunks;
+  if (nq == 0) return 0;
+  hipLaunchKernelGGL((entropy_rotate_q<D>), dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  hipLaunchKernelGGL((entropy_partial<D, BITS, QG>), dim3((unsigned)((np + 3) / 4)), dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  hipLaunchKernelGGL((entropy_combine<D>), dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+template <int D, int BITS>
+int pick_entropy_qg(const EntropyArgs& a, hipStream_t s) {
+  switch (a.q_heads / a.heads) {
+    case 1: return launch_entropy_t<D, BITS, 1>(a, s);
+    case 2: return launch_entropy_t<D, BITS, 2>(a, s);
+    case 4: return launch_entropy_t<D, BITS, 4>(a, s);
+    default: return launch_entropy_t<D, BITS, 8>(a, s);
+  }
+}
+
 template <int DT, int D>
 int launch_moments_t(const CalibArgs& a, hipStream_t s) {
   if (a.n_waves > 0) {
@@ -3076,6 +3295,17 @@ int launch_channel_stats(const CalibArgs& a, void* stream) {
     case DT_BF16: return d128 ? launch_stats_t<DT_BF16, 128>(a, s) : launch_stats_t<DT_BF16, 256>(a, s);
     default: return d128 ? launch_stats_t<DT_F32, 128>(a, s) : launch_stats_t<DT_F32, 256>(a, s);
   }
+}
+int launch_entropy(const EntropyArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (a.head_dim == 128) {
+    if (a.bits == 2) return pick_entropy_qg<128, 2>(a, s);
+    if (a.bits == 3) return pick_entropy_qg<128, 3>(a, s);
+    return pick_entropy_qg<128, 4>(a, s);
+  }
+  if (a.bits == 2) return pick_entropy_qg<256, 2>(a, s);
+  if (a.bits == 3) return pick_entropy_qg<256, 3>(a, s);
+  return pick_entropy_qg<256, 4>(a, s);
 }
 int launch_rotated_moments(const CalibArgs& a, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -8,6 +8,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+# A host-only build of the C ABI (sanitized, no GPU) can stand in for libkvq.so: see
+# tests/test_sanitized_host.py, which sets this variable for its child test run.
+if os.environ.get("KVQ_TEST_LIBRARY"):
+    import rotate_then_bit_amd as _kvq
+
+    _kvq._LIB_PATH = os.environ["KVQ_TEST_LIBRARY"]
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 

@@ -322,3 +322,21 @@ def test_dynamic_codebook_config_refusals():
         assert e.value.status == status, kw
     sz = kvq.packed_sizes(_cfg(**base))
     assert sz["extra"] == 1 * 4 * 2 * 1 and sz["norm"] == 1 * 4 * 2 * 4
+
+
+def test_allocate_bits_host_matches_oracle():
+    from oracle import bitwidth as bw
+    rng = np.random.default_rng(77)
+    for _ in range(60):
+        h = int(rng.integers(1, 12))
+        e = rng.uniform(0.0, 9.0, h)
+        if rng.random() < 0.2:
+            e = np.round(e)  # ties
+        if rng.random() < 0.1:
+            e = np.zeros(h)
+        tot = int(rng.integers(2 * h, 4 * h + 1))
+        assert np.array_equal(kvq.allocate_bits(e, tot), bw.allocate_bits(e, tot)), (e, tot)
+    with pytest.raises(kvq.KvqError):
+        kvq.allocate_bits(np.ones(4), 17)
+    with pytest.raises(kvq.KvqError):
+        kvq.allocate_bits(np.array([1.0, -1.0]), 6)
