@@ -218,6 +218,7 @@ def time_other_configs(kvq, workloads, dev, stream):
 
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     res = {}
+    kept = {}
     for key in OTHER_CONFIGS:
         wl = workloads.WORKLOADS[key]
         if wl.device_generated:
@@ -270,13 +271,50 @@ def time_other_configs(kvq, workloads, dev, stream):
                     "vectors_per_s": round(c.n_vectors / (ms * 1e-3), 1), "bytes": nbytes,
                     "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                     "frac_peak": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4)}
-            del planes, y
+            kept[c.name] = (cfg, planes)
+            del y
+        if key == "widehead":
+            entry["attend"] = time_attend_general(kvq, kept, dev, stream)
+            print(f"[bench] widehead attend: {entry['attend']['ms_per_step']:.4g} ms, "
+                  f"{entry['attend']['hbm_frac']:.3f} of HBM", file=sys.stderr, flush=True)
+        kept.clear()
         res[key] = entry
         del inputs, data
         torch.cuda.empty_cache()
         print(f"[bench] {key}: " + ", ".join(f"{k} {v['avg_ms']:.4g} ms" for k, v in entry["launches"].items()),
               file=sys.stderr, flush=True)
     return res
+
+
+def time_attend_general(kvq, kept, dev, stream, qg=2, reps=20):
+    """Decode-step attention over the wide-head cache just encoded (K 2-bit and V 4-bit in groups
+    of 32, head_dim 256; 2 query heads per KV head): the general vector-ALU pass, every slot of
+    every row.  Bytes: the encoded K and V planes, read once."""
+    import torch
+    (cfg_k, pk), (cfg_v, pv) = kept["K"], kept["V"]
+    r, t, h, d = cfg_k.shape
+    gen = torch.Generator(device=dev).manual_seed(5)
+    q = torch.randn((r, qg * h, d), generator=gen, device=dev, dtype=torch.float32)
+    out = torch.empty_like(q)
+    ws = torch.empty(kvq.attend_workspace_size(cfg_k, qg * h, cfg_v), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            kvq.attend(q, pk, cfg_k, pv, cfg_v, out=out, workspace=ws, stream=stream)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            kvq.attend(q, pk, cfg_k, pv, cfg_v, out=out, workspace=ws, stream=stream)
+        b.record(stream)
+        stream.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = plane_bytes(pk) + plane_bytes(pv)
+    return {"ms_per_step": round(ms, 4), "rows": r, "slots": t, "kv_heads": h, "q_heads": qg * h,
+            "encoded_cache_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9), 4),
+            "what": "kvq_attend general pass (vector ALUs): scores and value sums in the rotated domain over "
+                    "K 2-bit and V 4-bit codes, groups of 32, head_dim 256"}
 
 
 def dynamic_codebook_report(kvq, workloads, dev, stream):

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 
 typedef enum kvq_status {
   KVQ_OK = 0,
@@ -172,28 +172,35 @@ kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* posit
  * where k_t, v_t are the cache's decoded vectors (what kvq_decode returns) of KV head
  * m / (q_heads / heads) -- the attention of the EliteKV page, section 7.1 (query scaled,
  * scored against the cached post-RoPE keys, softmax over positions, weighted sum of the
- * cached values).  The keys are never decoded: with the orthonormal Hadamard rotation M and
- * the keys' permutation P, q . k_t = (M P q) . y_t for the stored y_t = zero + code * scale,
- * and the values are summed in the rotated domain and rotated back once per output (the
- * rotation of the RotateKV page, whose decode-stage speed-up this serves).  Sink slots are
- * read from the fp16 sink planes.  Scores and sums are fp32; for 2-bit codes with one group
- * of 128 channels the products run exactly on the int8 matrix cores, with the rotated query
- * rounded to 2^-31 of 16 times its largest element and each softmax weight to 2^-27 of the
- * largest weight x value scale of its 128-slot window.
- *   cfg_k, cfg_v  the K and V caches: same rows R, slots T, heads H, head_dim 128, bits
- *                 (2 or 4), group (32, 64 or 128), n_sink (at most 64), Walsh-Hadamard and
- *                 min-max, pos_offset 0 (slot t holds position t); each its own permutation
- *                 and RoPE flag (keys hold post-RoPE values; q must be rotated by RoPE at its
+ * cached values).  The keys are never decoded: with the orthonormal rotation M (Hadamard /
+ * sqrt(head_dim), or the identity for an unrotated cache) and the keys' permutation P,
+ * q . k_t = (M P q) . y_t for the stored y_t = zero + code * scale, and the values are summed
+ * in the rotated domain and rotated back once per output (the rotation of the RotateKV page,
+ * whose decode-stage speed-up this serves).  Slots whose position (pos_offset + slot) is
+ * below n_sink are read from the fp16 sink planes.  Scores and sums are fp32.  For head_dim
+ * 128, Walsh-Hadamard, K and V of equal bits (2 or 4) and group, pos_offset 0 and at most 4
+ * query heads per KV head, the products run on the int8 matrix cores, exactly for 2-bit
+ * codes with one group of 128 channels (the rotated query rounded to 2^-31 of 16 times its
+ * largest element and each softmax weight to 2^-27 of the largest weight x value scale of
+ * its 128-slot window); every other supported cache takes a vector-ALU pass.
+ *   cfg_k, cfg_v  the K and V caches: same rows R, slots T, heads H, head_dim (128 or 256),
+ *                 n_sink (at most 64), pos_offset, rotation (Walsh-Hadamard or none) and
+ *                 min-max quantizer; each its own bits (2, 3 or 4), group, permutation and
+ *                 RoPE flag (keys hold post-RoPE values; q must be rotated by RoPE at its
  *                 own position by the caller).  Otherwise KVQ_ERR_UNSUPPORTED / KVQ_ERR_SHAPE.
  *   k, v          DEVICE planes of the two caches (as written by kvq_encode / kvq_append).
- *   q, out        DEVICE float32 [R, q_heads, 128], contiguous; q_heads = H * g, g in {1, 2, 4}.
+ *   q, out        DEVICE float32 [R, q_heads, head_dim], contiguous; q_heads = H * g,
+ *                 g in {1, 2, 4, 8}.
  *   lengths       DEVICE int32 [R]: slots each row attends over (clamped to [0, T]); NULL = T.
  *                 A row with no slot gets zeros.
  *   scale         score multiplier (head_dim^-1/2 in the page's code); finite.
- *   workspace     DEVICE, 16-byte aligned, at least kvq_attend_workspace_size(cfg_k, q_heads)
- *                 bytes, owned by the caller; its contents are scratch between calls.
- * Asynchronous; calls that share a workspace must not overlap. */
-kvq_status kvq_attend_workspace_size(const kvq_config* cfg_k, int64_t q_heads, size_t* bytes);
+ *   workspace     DEVICE, 16-byte aligned, at least kvq_attend_workspace_size(cfg_k, cfg_v,
+ *                 q_heads) bytes, owned by the caller; its contents are scratch between calls.
+ * Asynchronous; calls that share a workspace must not overlap.
+ * kvq_attend_workspace_size: the workspace a call with these caches needs (cfg_v NULL: a V
+ * cache configured like cfg_k); the same checks as kvq_attend on the configurations. */
+kvq_status kvq_attend_workspace_size(const kvq_config* cfg_k, const kvq_config* cfg_v, int64_t q_heads,
+                                     size_t* bytes);
 kvq_status kvq_attend(const kvq_config* cfg_k, const kvq_planes* k, const kvq_config* cfg_v, const kvq_planes* v,
                       const float* q, int64_t q_heads, const int32_t* lengths, float scale, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);

@@ -32,7 +32,7 @@ __all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_noalloc",
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 ROTATIONS = {"none": 0, "fwht": 1, "so4": 2, "dense": 3}
 QUANTIZERS = {"minmax": 0, "lloyd": 1}
@@ -108,7 +108,8 @@ def _load():
                                ctypes.c_void_p]
     lib.kvq_decode.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Planes), ctypes.c_void_p, ctypes.c_int32,
                                ctypes.c_void_p]
-    lib.kvq_attend_workspace_size.argtypes = [ctypes.POINTER(_Config), ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_attend_workspace_size.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Config), ctypes.c_int64,
+                                              ctypes.POINTER(ctypes.c_size_t)]
     lib.kvq_attend.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Planes), ctypes.POINTER(_Config),
                                ctypes.POINTER(_Planes), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -298,30 +299,33 @@ def append(x, positions, cache, cfg: Config, stream=None):
     return cache
 
 
-def attend_workspace_size(k_cfg: Config, q_heads: int) -> int:
-    """Bytes of device workspace ``attend`` needs for this cache shape and query-head count."""
+def attend_workspace_size(k_cfg: Config, q_heads: int, v_cfg: Config = None) -> int:
+    """Bytes of device workspace ``attend`` needs for these caches and query-head count
+    (``v_cfg`` None: a V cache configured like K)."""
     c = k_cfg.c_struct()
+    cv = v_cfg.c_struct() if v_cfg is not None else None
     n = ctypes.c_size_t()
-    _check(_L().kvq_attend_workspace_size(ctypes.byref(c), int(q_heads), ctypes.byref(n)))
+    _check(_L().kvq_attend_workspace_size(ctypes.byref(c), ctypes.byref(cv) if cv is not None else None,
+                                          int(q_heads), ctypes.byref(n)))
     return int(n.value)
 
 
 def attend(q, k_planes, k_cfg: Config, v_planes, v_cfg: Config, lengths=None, scale=None, out=None,
            workspace=None, stream=None):
-    """Decode-step attention of ``q`` (float32 device tensor [R, q_heads, 128]) over the encoded
-    K/V cache; ``lengths`` (int32 device tensor [R]) limits each row to its first slots.
-    Returns ``out`` (float32 [R, q_heads, 128])."""
+    """Decode-step attention of ``q`` (float32 device tensor [R, q_heads, head_dim]) over the
+    encoded K/V cache; ``lengths`` (int32 device tensor [R]) limits each row to its first slots.
+    Returns ``out`` (float32 [R, q_heads, head_dim])."""
     import torch
     r, q_heads = int(q.shape[0]), int(q.shape[1])
     if q.dtype != torch.float32 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous float32 tensor [rows, q_heads, 128]")
+        raise ValueError("q must be a contiguous float32 tensor [rows, q_heads, head_dim]")
     if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() != r or not lengths.is_contiguous()):
         raise ValueError("lengths must be a contiguous int32 tensor with one entry per row")
     if scale is None:
         scale = float(k_cfg.shape[-1]) ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    need = attend_workspace_size(k_cfg, q_heads)
+    need = attend_workspace_size(k_cfg, q_heads, v_cfg)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ck, cv = k_cfg.c_struct(), v_cfg.c_struct()
@@ -340,7 +344,7 @@ def attend_noalloc(q, k_planes, k_cfg: Config, v_planes, v_cfg: Config, lengths=
     import torch
     r, q_heads = int(q.shape[0]), int(q.shape[1])
     if q.dtype != torch.float32 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous float32 tensor [rows, q_heads, 128]")
+        raise ValueError("q must be a contiguous float32 tensor [rows, q_heads, head_dim]")
     if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() != r or not lengths.is_contiguous()):
         raise ValueError("lengths must be a contiguous int32 tensor with one entry per row")
     if scale is None:

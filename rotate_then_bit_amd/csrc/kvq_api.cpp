@@ -415,41 +415,47 @@ kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int3
 }
 
 namespace {
-// the configurations decode-step attention supports, and the workspace it needs
+// The configurations decode-step attention supports, the pass that serves them, and the
+// workspace it needs.  cfg_v NULL stands for a V cache configured like K.  The matrix-core
+// passes (fast) take head_dim 128, Walsh-Hadamard, K and V of equal bits (2 or 4) and group,
+// slot t = position t and up to 4 query heads per KV head; the general pass takes the rest.
 kvq_status check_attend(const kvq_config* cfg_k, const kvq_config* cfg_v, int64_t q_heads, size_t* ws_bytes,
-                        kvq::AttendArgs* a) {
+                        kvq::AttendArgs* a, bool* fast_out) {
   Derived dk, dv;
   kvq_status st = check_config(cfg_k, &dk);
   if (st != KVQ_OK) return st;
   if (cfg_v) {
     if ((st = check_config(cfg_v, &dv)) != KVQ_OK) return st;
     if (cfg_v->rows != cfg_k->rows || cfg_v->tokens != cfg_k->tokens || cfg_v->heads != cfg_k->heads ||
-        cfg_v->head_dim != cfg_k->head_dim || cfg_v->bits != cfg_k->bits || cfg_v->group_size != cfg_k->group_size ||
-        cfg_v->n_sink != cfg_k->n_sink || cfg_v->pos_offset != cfg_k->pos_offset || cfg_v->rot != cfg_k->rot ||
-        cfg_v->quant != cfg_k->quant)
-      return fail(KVQ_ERR_SHAPE, "the K and V caches must share rows, slots, heads, head_dim, bits, group, "
-                                 "sinks, pos_offset, rotation and quantizer");
+        cfg_v->head_dim != cfg_k->head_dim || cfg_v->n_sink != cfg_k->n_sink ||
+        cfg_v->pos_offset != cfg_k->pos_offset || cfg_v->rot != cfg_k->rot || cfg_v->quant != cfg_k->quant)
+      return fail(KVQ_ERR_SHAPE, "the K and V caches must share rows, slots, heads, head_dim, sinks, pos_offset, "
+                                 "rotation and quantizer");
   }
-  if (cfg_k->head_dim != 128 || cfg_k->rot != KVQ_ROT_FWHT || cfg_k->quant != KVQ_Q_MINMAX ||
-      (cfg_k->bits != 2 && cfg_k->bits != 4) || cfg_k->group_size < 32 || cfg_k->group_size > 128)
-    return fail(KVQ_ERR_UNSUPPORTED, "attention supports head_dim 128, Walsh-Hadamard, min-max, 2 or 4 bits, "
-                                     "groups of 32, 64 or 128");
-  if (cfg_k->pos_offset != 0) return fail(KVQ_ERR_UNSUPPORTED, "attention needs pos_offset 0 (slot = position)");
-  if (cfg_k->n_sink > 64) return fail(KVQ_ERR_UNSUPPORTED, "attention supports at most 64 sink slots");
+  const kvq_config* cv = cfg_v ? cfg_v : cfg_k;
+  const int64_t d = cfg_k->head_dim;
+  if ((d != 128 && d != 256) || (cfg_k->rot != KVQ_ROT_FWHT && cfg_k->rot != KVQ_ROT_NONE) ||
+      cfg_k->quant != KVQ_Q_MINMAX)
+    return fail(KVQ_ERR_UNSUPPORTED, "attention supports head_dim 128 or 256, Walsh-Hadamard or no rotation, "
+                                     "min-max codes");
+  if (cfg_k->n_sink > 64) return fail(KVQ_ERR_UNSUPPORTED, "attention supports at most 64 sink positions");
   if (cfg_k->heads <= 0 || q_heads <= 0 || q_heads % cfg_k->heads != 0)
     return fail(KVQ_ERR_SHAPE, "q_heads must be a positive multiple of heads");
   const int64_t qg = q_heads / cfg_k->heads;
-  if (qg != 1 && qg != 2 && qg != 4)
-    return fail(KVQ_ERR_UNSUPPORTED, "attention supports 1, 2 or 4 query heads per KV head");
+  if (qg != 1 && qg != 2 && qg != 4 && qg != 8)
+    return fail(KVQ_ERR_UNSUPPORTED, "attention supports 1, 2, 4 or 8 query heads per KV head");
+  const bool fast = d == 128 && cfg_k->rot == KVQ_ROT_FWHT && cv->bits == cfg_k->bits &&
+                    (cfg_k->bits == 2 || cfg_k->bits == 4) && cv->group_size == cfg_k->group_size &&
+                    cfg_k->group_size <= 128 && cfg_k->pos_offset == 0 && qg <= 4;
   int32_t nc = 1, ct = 8;
-  const bool mma_blk = cfg_k->group_size == 128 && cfg_k->heads % 4 == 0;  // bits are 2 or 4 here
+  const bool mma_blk = fast && cfg_k->group_size == 128 && cfg_k->heads % 4 == 0;
   kvq::attend_chunks(cfg_k->rows, cfg_k->heads, cfg_k->tokens, mma_blk, &nc, &ct);
   int64_t nq = 0, tmp = 0;
-  if (!mul_ok(cfg_k->rows, q_heads, &nq) || !mul_ok(nq, (int64_t)nc * kvq::kAttendPart + 128, &tmp) ||
-      tmp > (int64_t(1) << 40))
+  if (!mul_ok(cfg_k->rows, q_heads, &nq) || !mul_ok(nq, (int64_t)nc * (d + 2) + d, &tmp) || tmp > (int64_t(1) << 40))
     return fail(KVQ_ERR_SHAPE, "attention workspace too large");
-  const size_t q_bytes = (size_t)(nq * 128 * 4 + 255) / 256 * 256;
-  *ws_bytes = q_bytes + (size_t)nq * (size_t)nc * kvq::kAttendPart * 4;
+  const size_t q_bytes = (size_t)(nq * d * 4 + 255) / 256 * 256;
+  *ws_bytes = q_bytes + (size_t)nq * (size_t)nc * (size_t)(d + 2) * 4;
+  if (fast_out) *fast_out = fast;
   if (a) {
     memset(a, 0, sizeof *a);
     a->rows = cfg_k->rows;
@@ -457,25 +463,30 @@ kvq_status check_attend(const kvq_config* cfg_k, const kvq_config* cfg_v, int64_
     a->heads = cfg_k->heads;
     a->q_heads = q_heads;
     a->group_log2 = ilog2(cfg_k->group_size);
+    a->v_group_log2 = ilog2(cv->group_size);
     a->n_sink = cfg_k->n_sink;
     a->n_chunks = nc;
     a->chunk = ct;
+    a->rot = cfg_k->rot == KVQ_ROT_FWHT ? 1 : 0;
+    // slots 0 .. sink_slots - 1 hold positions pos_offset .. below n_sink
+    const int64_t ss = (int64_t)cfg_k->n_sink - cfg_k->pos_offset;
+    a->sink_slots = (int32_t)(ss <= 0 ? 0 : (ss < cfg_k->tokens ? ss : cfg_k->tokens));
+    a->sink_base = a->sink_slots > 0 ? (int32_t)cfg_k->pos_offset : 0;
     a->use_perm_k = cfg_k->perm ? 1 : 0;
     if (cfg_k->perm)
-      for (int i = 0; i < 128; ++i) a->perm_k[i] = (uint8_t)cfg_k->perm[i];
-    if (cfg_v) {
-      a->use_perm_v = cfg_v->perm ? 1 : 0;
-      if (cfg_v->perm)
-        for (int i = 0; i < 128; ++i) a->perm_v[i] = (uint8_t)cfg_v->perm[i];
-    }
+      for (int64_t i = 0; i < d; ++i) a->perm_k[i] = (uint8_t)cfg_k->perm[i];
+    a->use_perm_v = cv->perm ? 1 : 0;
+    if (cv->perm)
+      for (int64_t i = 0; i < d; ++i) a->perm_v[i] = (uint8_t)cv->perm[i];
   }
   return KVQ_OK;
 }
 }  // namespace
 
-kvq_status kvq_attend_workspace_size(const kvq_config* cfg_k, int64_t q_heads, size_t* bytes) {
+kvq_status kvq_attend_workspace_size(const kvq_config* cfg_k, const kvq_config* cfg_v, int64_t q_heads,
+                                     size_t* bytes) {
   if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
-  kvq_status st = check_attend(cfg_k, nullptr, q_heads, bytes, nullptr);
+  kvq_status st = check_attend(cfg_k, cfg_v, q_heads, bytes, nullptr, nullptr);
   return st == KVQ_OK ? ok() : st;
 }
 
@@ -488,8 +499,9 @@ kvq_status attend_impl(const kvq_config* cfg_k, const kvq_planes* k, const kvq_c
                        void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
   if (!cfg_v) return fail(KVQ_ERR_NULL, "cfg_v is NULL");
   size_t need = 0;
+  bool fast = false;
   kvq::AttendArgs a;
-  kvq_status st = check_attend(cfg_k, cfg_v, q_heads, &need, &a);
+  kvq_status st = check_attend(cfg_k, cfg_v, q_heads, &need, &a, &fast);
   if (st != KVQ_OK) return st;
   if (!isfinite(scale)) return fail(KVQ_ERR_PARAM, "scale must be finite");
   Derived dk, dv;
@@ -500,7 +512,7 @@ kvq_status attend_impl(const kvq_config* cfg_k, const kvq_planes* k, const kvq_c
   // (a cache with no slot still runs: every output row is then zero)
   if ((st = check_planes(cfg_k, dk, k)) != KVQ_OK) return st;
   if ((st = check_planes(cfg_v, dv, v)) != KVQ_OK) return st;
-  if (cfg_k->n_sink > 0 && (!k->sink || !v->sink)) return fail(KVQ_ERR_NULL, "sink plane is NULL");
+  if (a.sink_slots > 0 && (!k->sink || !v->sink)) return fail(KVQ_ERR_NULL, "sink plane is NULL");
   if (!q || !out) return fail(KVQ_ERR_NULL, "q or out is NULL");
   if (!use_scratch && !workspace) return fail(KVQ_ERR_NULL, "workspace is NULL");
   if (!aligned16(q) || !aligned16(out) || (!use_scratch && !aligned16(workspace)))
@@ -526,11 +538,24 @@ kvq_status attend_impl(const kvq_config* cfg_k, const kvq_planes* k, const kvq_c
   a.v_sink = static_cast<const uint16_t*>(v->sink);
   a.q = q;
   a.out = out;
+  const int64_t d = cfg_k->head_dim;
   a.qrot = static_cast<float*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)(a.rows * q_heads * 128 * 4 + 255) / 256 * 256);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)(a.rows * q_heads * d * 4 + 255) / 256 * 256);
   a.lengths = lengths;
   a.scale = scale;
-  const int err = kvq::launch_attend(cfg_k->bits, (int)(q_heads / cfg_k->heads), a, stream);
+  const int qg = (int)(q_heads / cfg_k->heads);
+  int err;
+  if (fast) {
+    err = kvq::launch_attend(cfg_k->bits, qg, a, stream);
+  } else {
+    const int kb = cfg_k->bits, vb = cfg_v->bits;
+    if (d == 128)
+      err = (kb == 2 ? kvq::launch_attend_gen_d128_k2 : kb == 3 ? kvq::launch_attend_gen_d128_k3
+                                                                 : kvq::launch_attend_gen_d128_k4)(vb, qg, a, stream);
+    else
+      err = (kb == 2 ? kvq::launch_attend_gen_d256_k2 : kb == 3 ? kvq::launch_attend_gen_d256_k3
+                                                                 : kvq::launch_attend_gen_d256_k4)(vb, qg, a, stream);
+  }
   if (err != 0) return fail(KVQ_ERR_DEVICE, "attention launch failed: %s", kvq::device_error_string(err));
   return ok();
 }

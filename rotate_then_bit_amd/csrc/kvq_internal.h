@@ -80,11 +80,12 @@ struct CodecArgs {
 };
 static_assert(sizeof(CodecArgs) <= 4096, "kernel arguments above 4 KiB");
 
-// Decode-step attention over an encoded cache (d = 128, Walsh-Hadamard + min-max).  The
-// workspace holds the rotated queries [rows, q_heads, 128] and, per (row, query head,
-// chunk of slots), a partial result: 128 rotated-domain sums, the running maximum and
-// the softmax denominator.
-constexpr int kAttendPart = 128 + 2;  // floats per partial
+// Decode-step attention over an encoded cache (Walsh-Hadamard or no rotation + min-max).  The
+// workspace holds the rotated queries [rows, q_heads, D] and, per (row, query head, chunk of
+// slots), a partial result: D rotated-domain sums, the running maximum and the softmax
+// denominator.  The matrix-core passes serve d = 128 with K and V alike (kAttendPart floats
+// per partial); the general pass takes D + 2.
+constexpr int kAttendPart = 128 + 2;  // floats per partial at d = 128
 struct AttendArgs {
   const uint8_t* k_codes;
   const uint16_t* k_scale;
@@ -94,17 +95,20 @@ struct AttendArgs {
   const uint16_t* v_scale;
   const uint16_t* v_zero;
   const uint16_t* v_sink;
-  const float* q;        // [rows, q_heads, 128]
-  float* out;            // [rows, q_heads, 128]
+  const float* q;        // [rows, q_heads, D]
+  float* out;            // [rows, q_heads, D]
   float* qrot;           // workspace: rotated queries
-  float* part;           // workspace: partials [rows, q_heads, n_chunks, kAttendPart]
+  float* part;           // workspace: partials [rows, q_heads, n_chunks, D + 2]
   const int32_t* lengths;  // DEVICE [rows] or NULL (every slot)
   int64_t rows, tokens, heads, q_heads;
   int32_t group_log2, n_sink, n_chunks, chunk;  // chunk: slots per chunk (multiple of 8)
   float scale;
   int32_t use_perm_k, use_perm_v;
-  uint8_t perm_k[128];
-  uint8_t perm_v[128];
+  // general pass: rotation (1 Walsh-Hadamard, 0 none), V's group, and the sink slots: slots
+  // 0 .. sink_slots - 1 hold the sink-plane entries sink_base .. (sink_base = pos_offset)
+  int32_t rot, v_group_log2, sink_slots, sink_base;
+  uint8_t perm_k[kMaxHeadDim];
+  uint8_t perm_v[kMaxHeadDim];
 };
 // Attention entropy per (row, query head) over an encoded K cache (Walsh-Hadamard + min-max,
 // head_dim 128 or 256, 2/3/4 bits): the workspace holds the rotated queries [rows, q_heads, D]
@@ -146,6 +150,14 @@ inline void attend_chunks(int64_t rows, int64_t heads, int64_t tokens, bool mma_
   *chunk = (int32_t)ct;
 }
 int launch_attend(int bits, int qg, const AttendArgs& a, void* stream);
+// the general pass (any configuration check_attend admits); one translation unit per
+// (head_dim, K bits)
+int launch_attend_gen_d128_k2(int v_bits, int qg, const AttendArgs& a, void* stream);
+int launch_attend_gen_d128_k3(int v_bits, int qg, const AttendArgs& a, void* stream);
+int launch_attend_gen_d128_k4(int v_bits, int qg, const AttendArgs& a, void* stream);
+int launch_attend_gen_d256_k2(int v_bits, int qg, const AttendArgs& a, void* stream);
+int launch_attend_gen_d256_k3(int v_bits, int qg, const AttendArgs& a, void* stream);
+int launch_attend_gen_d256_k4(int v_bits, int qg, const AttendArgs& a, void* stream);
 // The allocation-free attention entry point keeps its workspace in a static device array of
 // this many bytes (one copy per GPU, held until the process ends).
 constexpr size_t kAttendScratchBytes = size_t(32) << 20;

@@ -2450,6 +2450,354 @@ __global__ void __launch_bounds__(256) attend_combine(const AttendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// DECODE-STEP ATTENTION, GENERAL PASS: head_dim 128 or 256, Walsh-Hadamard or no rotation,
+// min-max codes of 2, 3 or 4 bits for K and V each (each its own group size), 1 to 8 query
+// heads per KV head, and a cache whose slot 0 holds position pos_offset (the sink slots are
+// the positions below n_sink).  The same three passes in the rotated domain as above; the
+// scores and value sums run on the vector ALUs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float swz_x8(float v) {
+  // ds_swizzle bit mode: and 0x1f, or 0, xor 8
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));
+}
+
+// Unnormalised Walsh-Hadamard transform (Sylvester order) of D values held by a wave as
+// u[k] = x[lane + 64 k]: index bits 6.. inside the lane, bits 0..5 across lanes.
+template <int D>
+__device__ __forceinline__ void fwht_wave(float (&u)[D / 64], int lane) {
+  constexpr int K = D / 64;
+#pragma unroll
+  for (int hb = 1; hb < K; hb <<= 1)
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (!(k & hb)) {
+        const float x = u[k], y = u[k + hb];
+        u[k] = x + y;
+        u[k + hb] = x - y;
+      }
+#pragma unroll
+  for (int bit = 1; bit < 64; bit <<= 1)
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float p = __shfl_xor(u[k], bit);
+      u[k] = (lane & bit) ? p - u[k] : u[k] + p;
+    }
+}
+
+// rotated queries M P q (M = H / sqrt(D), or the identity without rotation): one wave per
+// (row, query head)
+template <int D>
+__global__ void __launch_bounds__(256) attend_rotate_q_gen(const AttendArgs a) {
+  constexpr int K = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.q_heads) return;  // wave-uniform; no barrier in this kernel
+  const float* q = a.q + w * D;
+  float u[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int c = lane + 64 * k;
+    u[k] = q[a.use_perm_k ? a.perm_k[c] : c];  // (P q)[c] = q[perm[c]]
+  }
+  float nc = 1.0f;
+  if (a.rot) {
+    fwht_wave<D>(u, lane);
+    nc = (float)(1.0 / __builtin_sqrt((double)D));
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) a.qrot[w * D + lane + 64 * k] = u[k] * nc;
+}
+
+// The 16 codes of a lane (channels 16 l .. 16 l + 15 of a vector, 2 BITS bytes at byte
+// 2 BITS l of its record).  3-bit records put a lane's 6 bytes on a 2-byte boundary when l
+// is odd: the two aligned words that cover them (inside the record: 6 l + 6 <= 6 l' + 8 for
+// l' = l rounded down to even, and the record ends at a multiple of 12 bytes from l' = 0)
+// are shifted down by 16 bits.
+template <int BITS>
+struct SlotCodes {
+  uint32_t w[BITS == 2 ? 1 : 2];
+};
+template <int BITS>
+__device__ __forceinline__ void load_slot_codes(const uint8_t* rec, int l, SlotCodes<BITS>& c) {
+  if constexpr (BITS == 2) {
+    c.w[0] = *reinterpret_cast<const uint32_t*>(rec + 4 * l);
+  } else if constexpr (BITS == 4) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(rec + 8 * l);
+    c.w[0] = v.x;
+    c.w[1] = v.y;
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + ((6 * l) & ~3));
+    c.w[0] = p[0];
+    c.w[1] = p[1];
+  }
+}
+// codes to floats (for 3 bits the word pair is first shifted into place, see above)
+template <int BITS>
+__device__ __forceinline__ void slot_code_floats(SlotCodes<BITS> c, int l, float (&code)[16]) {
+  if constexpr (BITS == 3) {
+    const uint32_t sh = (uint32_t)(l & 1) * 16u;
+    const uint32_t lo = __builtin_amdgcn_alignbit(c.w[1], c.w[0], sh), hi = c.w[1] >> sh;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int bit = 3 * i;
+      uint32_t v;
+      if (bit + 3 <= 32) v = lo >> bit;
+      else if (bit >= 32) v = hi >> (bit - 32);
+      else v = (lo >> bit) | (hi << (32 - bit));
+      code[i] = (float)(v & 7u);
+    }
+  } else {
+    // spread each word's codes over bytes, then one byte-to-float conversion per code
+    constexpr int PER = 32 / BITS, SPR = 8 / BITS;
+    constexpr uint32_t BM = (BITS == 2) ? 0x03030303u : 0x0F0F0F0Fu;
+#pragma unroll
+    for (int j = 0; j < BITS / 2; ++j)
+#pragma unroll
+      for (int k = 0; k < SPR; ++k) {
+        uint32_t e = (c.w[j] >> (BITS * k)) & BM;  // byte b holds code SPR * b + k of word j
+        asm volatile("" : "+v"(e));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) code[PER * j + SPR * b + k] = (float)((e >> (8 * b)) & 0xffu);
+      }
+  }
+}
+
+// Partial pass: one wave per (row, KV head, chunk of slots).  Lane (tk, l) = (lane / LPS,
+// lane % LPS), LPS = D / 16 lanes per slot, holds channels 16 l .. 16 l + 15 of slot tk of
+// each step of 64 / LPS slots; the LPS lanes of a slot reduce its scores, and each slot keeps
+// its own running maximum, denominator and rotated-domain sums until the wave merges them.
+template <int D, int KB, int VB, int QG>
+__global__ void __launch_bounds__(256) attend_partial_gen(const AttendArgs a) {
+  constexpr int LPS = D / 16, SPS = 64 / LPS;
+  constexpr int KCB = D * KB / 8, VCB = D * VB / 8;  // code bytes per vector
+  constexpr int PS = D + 2;                          // floats per partial
+  __shared__ __attribute__((aligned(16))) float s_qv[4][QG * D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
+  const int64_t c = w % a.n_chunks, rh = w / a.n_chunks, h = rh % a.heads, r = rh / a.heads;
+  const int tk = lane / LPS, l = lane % LPS;
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.sink_slots);
+  const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
+  const int64_t kng = D >> a.group_log2, vng = D >> a.v_group_log2;
+  const int kg = (16 * l) >> a.group_log2, vg = (16 * l) >> a.v_group_log2;  // groups of >= 32
+
+  float sl[QG];
+  {
+    const float* src = a.qrot + (r * a.q_heads + h * QG) * D;
+    for (int i = lane; i < QG * D; i += 64) s_qv[wave][i] = src[i];
+    wave_lds_sync();
+  }
+  const uint32_t qaddr = lds_addr(&s_qv[wave][16 * l]);
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    sl[m] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4_t v = lds_ld4(qaddr + 4u * D * m + 16u * k);
+      sl[m] += (__uint_as_float(v.x) + __uint_as_float(v.y)) + (__uint_as_float(v.z) + __uint_as_float(v.w));
+    }
+  }
+  float mx[QG], ls[QG], zs[QG], acc[QG][16];
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    mx[m] = -INFINITY;
+    ls[m] = 0.0f;
+    zs[m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
+  }
+  struct Slot {
+    SlotCodes<KB> k;
+    SlotCodes<VB> v;
+    uint32_t ks, kz, vs, vz;  // fp16 bits of the lane's group scale and zero
+  };
+  // the lane's slot of step t0 (clamped into the chunk for the loads; masked afterwards)
+  auto load = [&](int64_t t0, Slot& s) __attribute__((always_inline)) {
+    int64_t t = t0 + tk;
+    if (t >= t_end) t = t_end - 1;
+    const int64_t vec = (r * a.tokens + t) * a.heads + h;
+    load_slot_codes<KB>(a.k_codes + vec * KCB, l, s.k);
+    load_slot_codes<VB>(a.v_codes + vec * VCB, l, s.v);
+    s.ks = a.k_scale[vec * kng + kg];
+    s.kz = a.k_zero[vec * kng + kg];
+    s.vs = a.v_scale[vec * vng + vg];
+    s.vz = a.v_zero[vec * vng + vg];
+  };
+
+  if (t_begin < t_end) {
+    Slot cur, nxt;
+    load(t_begin, cur);
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += SPS) {
+      if (t0 + SPS < t_end) load(t0 + SPS, nxt);  // wave-uniform: the next step's loads in flight
+      const bool valid = t0 + tk < t_end;
+      float code[16];
+      slot_code_floats<KB>(cur.k, l, code);
+      const float ks = f16_value(cur.ks), kz = f16_value(cur.kz);
+      float s[QG];
+      uint32_t qa = qaddr;
+      asm volatile("" : "+v"(qa));  // read the slices here, each step (not hoisted into registers)
+#pragma unroll
+      for (int m = 0; m < QG; ++m) {
+        float d = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4_t v = lds_ld4(qa + 4u * D * m + 16u * k);
+          d = __builtin_fmaf(__uint_as_float(v.x), code[4 * k + 0], d);
+          d = __builtin_fmaf(__uint_as_float(v.y), code[4 * k + 1], d);
+          d = __builtin_fmaf(__uint_as_float(v.z), code[4 * k + 2], d);
+          d = __builtin_fmaf(__uint_as_float(v.w), code[4 * k + 3], d);
+        }
+        float part = __builtin_fmaf(ks, d, kz * sl[m]);  // q~ . (zero + code * scale) over 16 channels
+        part = add_x1(part);
+        part = add_x2(part);
+        part += swz_x4(part);
+        if constexpr (LPS == 16) part += swz_x8(part);
+        s[m] = valid ? part * a.scale : -INFINITY;
+      }
+      bool grow = false;
+      float mn[QG];
+#pragma unroll
+      for (int m = 0; m < QG; ++m) {
+        mn[m] = fmaxf(mx[m], s[m]);
+        grow |= mn[m] > mx[m];
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int m = 0; m < QG; ++m) {
+          const float corr = (mn[m] > mx[m]) ? __expf(mx[m] - mn[m]) : 1.0f;
+          ls[m] *= corr;
+          zs[m] *= corr;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[m][i] *= corr;
+          mx[m] = mn[m];
+        }
+      }
+      slot_code_floats<VB>(cur.v, l, code);
+      const float vs = f16_value(cur.vs), vz = f16_value(cur.vz);
+#pragma unroll
+      for (int m = 0; m < QG; ++m) {
+        const float p = valid ? __expf(s[m] - mx[m]) : 0.0f;
+        ls[m] += p;
+        zs[m] = __builtin_fmaf(p, vz, zs[m]);
+        const float ps = p * vs;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][i] = __builtin_fmaf(ps, code[i], acc[m][i]);
+      }
+      cur = nxt;
+    }
+  }
+  // merge the wave's slots (lanes xor LPS, 2 LPS, ...) and write the chunk's partial
+#pragma unroll
+  for (int m = 0; m < QG; ++m) {
+    float M = mx[m];
+#pragma unroll
+    for (int o = LPS; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float f = (mx[m] == -INFINITY) ? 0.0f : __expf(mx[m] - M);
+    float L = ls[m] * f;
+#pragma unroll
+    for (int o = LPS; o < 64; o <<= 1) L += __shfl_xor(L, o);
+    float* pb = a.part + ((r * a.q_heads + h * QG + m) * a.n_chunks + c) * PS;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = (acc[m][i] + zs[m]) * f;
+#pragma unroll
+      for (int o = LPS; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      if (tk == 0) pb[16 * l + i] = v;
+    }
+    if (lane == 0) {
+      pb[D] = M;
+      pb[D + 1] = L;
+    }
+  }
+}
+
+// Merge of the chunks, rotation back (z = M acc, out[perm[j]] = z[j]), the sink slots (raw
+// query against the fp16 keys of the sink plane, entry pos_offset + slot) and the
+// normalisation: one wave per (row, query head).
+template <int D>
+__global__ void __launch_bounds__(256) attend_combine_gen(const AttendArgs a) {
+  constexpr int K = D / 64, PS = D + 2;
+  __shared__ float s_out[4][D];
+  __shared__ float s_sc[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= a.rows * a.q_heads) return;  // wave-uniform; no block barrier in this kernel
+  const int64_t r = w / a.q_heads, m = w % a.q_heads;
+  const int64_t h = m / (a.q_heads / a.heads);
+  int64_t len = a.tokens;
+  if (a.lengths) {
+    const int64_t n = a.lengths[r];
+    len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
+  }
+  const float* pb = a.part + w * (int64_t)a.n_chunks * PS;
+  float M = -INFINITY;
+  for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, pb[c * PS + D]);
+  float L = 0.0f, acc[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc[k] = 0.0f;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const float mc = pb[c * PS + D];
+    const float f = (mc == -INFINITY) ? 0.0f : __expf(mc - M);
+    L = __builtin_fmaf(f, pb[c * PS + D + 1], L);
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc[k] = __builtin_fmaf(f, pb[c * PS + lane + 64 * k], acc[k]);
+  }
+  float* so = s_out[wave];
+  float nc = 1.0f;
+  if (a.rot) {
+    fwht_wave<D>(acc, lane);
+    nc = (float)(1.0 / __builtin_sqrt((double)D));
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = lane + 64 * k;
+    so[a.use_perm_v ? a.perm_v[j] : j] = acc[k] * nc;
+  }
+  wave_lds_sync();
+  float y[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) y[k] = so[lane + 64 * k];
+  const int nsk = (int)min((int64_t)a.sink_slots, len);
+  const float* qr = a.q + w * D;
+  float qv[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) qv[k] = qr[lane + 64 * k];
+  float Mp = M;
+  for (int t = 0; t < nsk; ++t) {
+    const uint16_t* kk = a.k_sink + ((r * a.n_sink + a.sink_base + t) * a.heads + h) * D;
+    float d = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) d = __builtin_fmaf(qv[k], f16_value(kk[lane + 64 * k]), d);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) d += __shfl_xor(d, o);
+    const float st = d * a.scale;
+    if (lane == 0) s_sc[wave][t] = st;
+    Mp = fmaxf(Mp, st);
+  }
+  wave_lds_sync();
+  const float f = (M == -INFINITY) ? 0.0f : __expf(M - Mp);
+  float n[K], den = f * L;
+#pragma unroll
+  for (int k = 0; k < K; ++k) n[k] = f * y[k];
+  for (int t = 0; t < nsk; ++t) {
+    const float e = __expf(s_sc[wave][t] - Mp);
+    const uint16_t* vv = a.v_sink + ((r * a.n_sink + a.sink_base + t) * a.heads + h) * D;
+#pragma unroll
+    for (int k = 0; k < K; ++k) n[k] = __builtin_fmaf(e, f16_value(vv[lane + 64 * k]), n[k]);
+    den += e;
+  }
+  float* out = a.out + w * D;
+#pragma unroll
+  for (int k = 0; k < K; ++k) out[lane + 64 * k] = den > 0.0f ? n[k] / den : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
 // launch dispatch
 // ---------------------------------------------------------------------------
 // Grid of a launch: one wave per task (len rows of one tile, or len tiles of one row).
@@ -2692,6 +3040,60 @@ int launch_attend(int bits, int qg, const AttendArgs& a, void* stream) {
   if (qg == 2) return launch_attend_t<4, 2>(a, s);
   return launch_attend_t<4, 4>(a, s);
 }
+#endif
+
+#if (KVQ_UNIT >= 14 && KVQ_UNIT <= 19) || KVQ_UNIT == -1
+namespace {
+template <int D, int KB, int VB, int QG>
+int launch_attend_gen_t(const AttendArgs& a, hipStream_t s) {
+  const int64_t nq = a.rows * a.q_heads;
+  const int64_t np = a.rows * a.heads * a.n_chunks;
+  if (nq == 0) return 0;
+  if ((np + 3) / 4 > 0x7fffffff || (nq + 3) / 4 > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attend_rotate_q_gen<D>), dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  hipLaunchKernelGGL((attend_partial_gen<D, KB, VB, QG>), dim3((unsigned)((np + 3) / 4)), dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  hipLaunchKernelGGL((attend_combine_gen<D>), dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+template <int D, int KB, int VB>
+int pick_attend_gen_qg(int qg, const AttendArgs& a, hipStream_t s) {
+  switch (qg) {
+    case 1: return launch_attend_gen_t<D, KB, VB, 1>(a, s);
+    case 2: return launch_attend_gen_t<D, KB, VB, 2>(a, s);
+    case 4: return launch_attend_gen_t<D, KB, VB, 4>(a, s);
+    default: return launch_attend_gen_t<D, KB, VB, 8>(a, s);
+  }
+}
+template <int D, int KB>
+int pick_attend_gen(int v_bits, int qg, const AttendArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (v_bits) {
+    case 2: return pick_attend_gen_qg<D, KB, 2>(qg, a, s);
+    case 3: return pick_attend_gen_qg<D, KB, 3>(qg, a, s);
+    default: return pick_attend_gen_qg<D, KB, 4>(qg, a, s);
+  }
+}
+}  // namespace
+#endif
+#if KVQ_UNIT == 14 || KVQ_UNIT == -1
+int launch_attend_gen_d128_k2(int vb, int qg, const AttendArgs& a, void* s) { return pick_attend_gen<128, 2>(vb, qg, a, s); }
+#endif
+#if KVQ_UNIT == 15 || KVQ_UNIT == -1
+int launch_attend_gen_d128_k3(int vb, int qg, const AttendArgs& a, void* s) { return pick_attend_gen<128, 3>(vb, qg, a, s); }
+#endif
+#if KVQ_UNIT == 16 || KVQ_UNIT == -1
+int launch_attend_gen_d128_k4(int vb, int qg, const AttendArgs& a, void* s) { return pick_attend_gen<128, 4>(vb, qg, a, s); }
+#endif
+#if KVQ_UNIT == 17 || KVQ_UNIT == -1
+int launch_attend_gen_d256_k2(int vb, int qg, const AttendArgs& a, void* s) { return pick_attend_gen<256, 2>(vb, qg, a, s); }
+#endif
+#if KVQ_UNIT == 18 || KVQ_UNIT == -1
+int launch_attend_gen_d256_k3(int vb, int qg, const AttendArgs& a, void* s) { return pick_attend_gen<256, 3>(vb, qg, a, s); }
+#endif
+#if KVQ_UNIT == 19 || KVQ_UNIT == -1
+int launch_attend_gen_d256_k4(int vb, int qg, const AttendArgs& a, void* s) { return pick_attend_gen<256, 4>(vb, qg, a, s); }
 #endif
 
 #if KVQ_UNIT == 13 || KVQ_UNIT == -1

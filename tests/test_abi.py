@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(kvq.library_path())
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert kvq.abi_version() == 2
+    assert kvq.abi_version() == kvq.ABI_VERSION == 3
 
 
 def _cfg(**kw):
@@ -185,7 +185,7 @@ def _lib_new_entry_points():
     lib.kvq_attend.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p]
-    lib.kvq_attend_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.kvq_attend_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     return lib
 
 
@@ -214,20 +214,37 @@ def test_attend_workspace_size_and_refusals_on_the_host():
     lib = _lib_new_entry_points()
     c = _cfg(shape=(2, 100, 4, 128)).c_struct()
     n = ctypes.c_size_t()
-    assert lib.kvq_attend_workspace_size(ctypes.byref(c), 16, ctypes.byref(n)) == 0
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), None, 16, ctypes.byref(n)) == 0
     assert n.value >= 2 * 16 * 128 * 4 + 2 * 16 * 130 * 4
     assert kvq.attend_workspace_size(kvq.Config(shape=(2, 100, 4, 128), dtype="bf16", bits=2, group_size=128), 16) == n.value
-    assert lib.kvq_attend_workspace_size(ctypes.byref(c), 6, ctypes.byref(n)) == 2     # not a multiple of heads
-    assert lib.kvq_attend_workspace_size(ctypes.byref(c), 32, ctypes.byref(n)) == 8    # 8 query heads per KV head
-    for kw, status in ((dict(rot="none"), 8), (dict(bits=3), 8), (dict(group_size=32, shape=(1, 4, 2, 256)), 8),
-                       (dict(quant="lloyd", codebook=np.linspace(-1, 1, 4).astype(np.float32)), 8),
-                       (dict(pos_offset=3), 8), (dict(n_sink=65), 8)):
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), ctypes.byref(c), 16, ctypes.byref(n)) == 0
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), None, 6, ctypes.byref(n)) == 2     # not a multiple of heads
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), None, 32, ctypes.byref(n)) == 0    # 8 query heads per KV head
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), None, 64, ctypes.byref(n)) == 8    # 16 query heads per KV head
+    # the general pass: no rotation, 3-bit codes, head_dim 256 with groups of 32, positions offset
+    for kw in (dict(rot="none"), dict(bits=3), dict(group_size=32, shape=(1, 4, 2, 256)), dict(pos_offset=3),
+               dict(n_sink=4, pos_offset=2)):
         ck = _cfg(**kw).c_struct()
-        assert lib.kvq_attend_workspace_size(ctypes.byref(ck), 8, ctypes.byref(n)) == status, kw
-    ck, cv = _cfg().c_struct(), _cfg(bits=4).c_struct()
+        assert lib.kvq_attend_workspace_size(ctypes.byref(ck), None, 8, ctypes.byref(n)) == 0, kw
+    for kw, status in ((dict(quant="lloyd", codebook=np.linspace(-1, 1, 4).astype(np.float32)), 8),
+                       (dict(rot="so4", quat=np.tile(np.array([1, 0, 0, 0], np.float32), (32, 2, 1))), 8),
+                       (dict(n_sink=65), 8)):
+        ck = _cfg(**kw).c_struct()
+        assert lib.kvq_attend_workspace_size(ctypes.byref(ck), None, 8, ctypes.byref(n)) == status, kw
+    # K 2-bit and V 4-bit, head_dim 256, groups of 32 (the wide-head cache): rotated queries plus
+    # one partial of 256 sums, maximum and denominator per (row, query head, chunk)
+    kw = dict(shape=(2, 64, 4, 256), group_size=32)
+    ck, cv = _cfg(bits=2, **kw).c_struct(), _cfg(bits=4, **kw).c_struct()
+    assert lib.kvq_attend_workspace_size(ctypes.byref(ck), ctypes.byref(cv), 8, ctypes.byref(n)) == 0
+    assert n.value >= 2 * 8 * 256 * 4 + 2 * 8 * 258 * 4
+    assert kvq.attend_workspace_size(kvq.Config(shape=(2, 64, 4, 256), dtype="bf16", bits=2, group_size=32), 8,
+                                     kvq.Config(shape=(2, 64, 4, 256), dtype="bf16", bits=4, group_size=32)) == n.value
+    cv = _cfg(bits=4, shape=(2, 64, 2, 256), group_size=32).c_struct()
+    assert lib.kvq_attend_workspace_size(ctypes.byref(ck), ctypes.byref(cv), 8, ctypes.byref(n)) == 2  # heads differ
+    ck, cv = _cfg().c_struct(), _cfg(n_sink=2).c_struct()
     pk, pv = _planes(), _planes()
     ws = 1 << 20
-    # the K and V caches must agree
+    # the K and V caches must agree on the slots, heads, sinks, positions, rotation and quantizer
     assert lib.kvq_attend(ctypes.byref(ck), ctypes.byref(pk), ctypes.byref(cv), ctypes.byref(pv), 4096, 8, None,
                           0.1, 4096, 4096, ws, None) == 2
     cv = _cfg().c_struct()
