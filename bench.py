@@ -533,7 +533,7 @@ def main():
     oa = torch.empty_like(qa)
     wsa = torch.empty(kvq.attend_workspace_size(cfgs["K"], q_heads), dtype=torch.uint8, device=dev)
     with torch.cuda.stream(stream):
-        for _ in range(3):
+        for _ in range(10):
             kvq.attend(qa, planes["K"], cfgs["K"], planes["V"], cfgs["V"], out=oa, workspace=wsa, stream=stream)
         stream.synchronize()
         a = torch.cuda.Event(enable_timing=True)

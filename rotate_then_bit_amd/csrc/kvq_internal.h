@@ -132,16 +132,34 @@ struct EntropyArgs {
 };
 int launch_entropy(const EntropyArgs& a, void* stream);
 
-// the chunking of the slot axis for a cache shape (same rule on both sides of the ABI).  Waves
-// in flight for the partial pass: 8 K where the block-cooperative matrix-core pass runs (one
-// group of 128 channels, heads a multiple of 4: measured 4.5 % faster than 16 K at the Llama-3
-// cache, fewer partial rounds of resident blocks), 16 K otherwise.
+// The chunking of the slot axis for a cache shape (same rule on both sides of the ABI).
+// Block-cooperative matrix-core pass (one group of 128 channels, heads a multiple of 4): blocks
+// of 4 tasks, 3 resident per CU (168 VGPRs), 256 CUs on MI355X, so 768 blocks fill the chip
+// once; the chunk count (at most 32) makes the block count the closest to whole rounds of 768,
+// the fewest chunks among equals (at the Llama-3 cache, 3 chunks = one round measured 4 % faster
+// than 8 chunks = 2.67 rounds, and 6 % faster than 4).  Other passes: about 16 K waves.
+constexpr int64_t kAttendBlkRound = 768;
 inline void attend_chunks(int64_t rows, int64_t heads, int64_t tokens, bool mma_blk, int32_t* n_chunks,
                           int32_t* chunk) {
-  const int64_t target = mma_blk ? 8192 : 16384;
-  int64_t nc = (target + rows * heads - 1) / (rows * heads > 0 ? rows * heads : 1);
   const int64_t max_nc = (tokens + 63) / 64;
-  if (nc > max_nc) nc = max_nc;
+  int64_t nc = 1;
+  if (mma_blk) {
+    const int64_t quads = rows * heads / 4 > 0 ? rows * heads / 4 : 1;
+    double best = -1.0;
+    for (int64_t k = 1; k <= 32 && k <= max_nc; ++k) {
+      const double rounds = (double)(quads * k) / (double)kAttendBlkRound;
+      const double whole = rounds <= 1.0 ? 1.0 : __builtin_ceil(rounds);
+      const double eff = rounds / whole;
+      if (eff > best + 1e-9) {
+        best = eff;
+        nc = k;
+      }
+    }
+  } else {
+    const int64_t target = 16384;
+    nc = (target + rows * heads - 1) / (rows * heads > 0 ? rows * heads : 1);
+    if (nc > max_nc) nc = max_nc;
+  }
   if (nc < 1) nc = 1;
   int64_t ct = (tokens + nc - 1) / nc;
   ct = (ct + 7) / 8 * 8;

@@ -130,10 +130,10 @@ def test_attend_llama3_cache_full_size():
 
 @pytest.mark.parametrize("h,bits", [(6, 2), (8, 2), (8, 4)])
 def test_attend_several_windows_per_chunk(h, bits):
-    """A cache with enough rows that each chunk spans two windows of the matrix-core pass (the
-    second one partial), for the per-wave pass (6 KV heads) and the block-cooperative one (8; 2-
-    and 4-bit codes):
-    inputs drawn on the GPU, sampled rows checked against the oracle."""
+    """A cache with enough rows that each chunk spans many windows of the matrix-core pass (the
+    last one partial at the ragged lengths), for the per-wave pass (6 KV heads) and the
+    block-cooperative one (8; 2- and 4-bit codes): inputs drawn on the GPU, sampled rows
+    checked against the oracle."""
     r, t = 96, 4096
     seed = 7100 + h + 10 * bits
     ck = _case(r, t, h, bits, 128, True, True, 4, "K")
