@@ -42,7 +42,7 @@ class CodecParams:
     bits: int
     group_size: int
     quant: str = "minmax"  # "minmax" | "lloyd"
-    rot: str = "fwht"  # "fwht" | "so4" | "none"
+    rot: str = "fwht"  # "fwht" | "so4" | "none" | "dense" | "rotor"
     rope: bool = False
     rope_base: float = 10000.0
     pos_offset: int = 0
@@ -56,6 +56,11 @@ class CodecParams:
     chan_scale: Optional[np.ndarray] = None
     chan_wide: Optional[np.ndarray] = None
     codebook_wide: Optional[np.ndarray] = None
+    # baseline rotations (see ``rotations``): "dense" z = M u with M = rot_matrix [D, D];
+    # "rotor" 3-D rotors rotor_quat [D // 3][4] and the tail angle rotor_tail
+    rot_matrix: Optional[np.ndarray] = None
+    rotor_quat: Optional[np.ndarray] = None
+    rotor_tail: float = 0.0
 
 
 def widen(raw: np.ndarray, dtype: str) -> np.ndarray:
@@ -72,6 +77,10 @@ def _rotate(u: np.ndarray, p: CodecParams) -> np.ndarray:
         return _rot.so4_rotate(u, p.quat)
     if p.rot == "none":
         return np.array(u, dtype=np.float64)
+    if p.rot == "dense":
+        return _rot.dense_rotate(u, p.rot_matrix)
+    if p.rot == "rotor":
+        return _rot.rotor_rotate(u, p.rotor_quat, p.rotor_tail)
     raise ValueError(p.rot)
 
 
@@ -82,6 +91,10 @@ def _unrotate(z: np.ndarray, p: CodecParams) -> np.ndarray:
         return _rot.so4_inverse(z, p.quat)
     if p.rot == "none":
         return np.array(z, dtype=np.float64)
+    if p.rot == "dense":
+        return _rot.dense_inverse(z, p.rot_matrix)
+    if p.rot == "rotor":
+        return _rot.rotor_inverse(z, p.rotor_quat, p.rotor_tail)
     raise ValueError(p.rot)
 
 

@@ -10,6 +10,14 @@
   rotation) and section 3.2 (the Hamilton product with the real part first, and
   the order T(v) = qL (v qR)).  Channels 4b..4b+3 of a vector form block b as
   (w, x, y, z).  The inverse uses the conjugates (section 2.1: q* = a - bi - cj - dk).
+* Baselines the IsoQuant page sets SO(4) against (section 1, the two approaches it compares):
+  - TurboQuant: a global transform by a dense random orthogonal matrix M, z = M u, O(d^2)
+    per vector; the inverse is M^T.  M is an input (drawn by the caller).
+  - RotorQuant: 3-D Clifford rotors.  Reading: channels 3b, 3b+1, 3b+2 form block b
+    (b < d // 3) and turn by the rotor of unit quaternion r_b, acting on the pure quaternion
+    (0, v) by the sandwich product r (0, v) r* of section 2.1; the page's d = 128 example
+    leaves a 2-D tail (42 blocks + 2 channels), which turns in its plane by an angle t
+    (the rotor of a plane); a 1-channel tail (d = 256: 85 blocks + 1) stays as it is.
 """
 from __future__ import annotations
 
@@ -76,3 +84,51 @@ def so4_inverse(z: np.ndarray, quat: np.ndarray) -> np.ndarray:
     blocks = z.reshape(z.shape[:-1] + (d // 4, 4))
     u = quat_mul(quat_conj(q[:, 0, :]), quat_mul(blocks, quat_conj(q[:, 1, :])))
     return u.reshape(z.shape)
+
+
+def dense_rotate(u: np.ndarray, m: np.ndarray) -> np.ndarray:
+    """z = M u for every vector of u [..., d] (M [d, d], orthogonal)."""
+    u = np.asarray(u, dtype=np.float64)
+    return u @ np.asarray(m, dtype=np.float64).T
+
+
+def dense_inverse(z: np.ndarray, m: np.ndarray) -> np.ndarray:
+    """u = M^T z (the inverse of an orthogonal M)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z @ np.asarray(m, dtype=np.float64)
+
+
+def rotor_split(d: int):
+    """(number of 3-D blocks, tail channels) of a head of d channels."""
+    return d // 3, d % 3
+
+
+def _rotor_apply(u: np.ndarray, rq: np.ndarray, tail_angle: float, inverse: bool) -> np.ndarray:
+    u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    nb, tail = rotor_split(d)
+    r = np.asarray(rq, dtype=np.float64)[:nb]
+    out = np.array(u, dtype=np.float64)
+    v = u[..., :3 * nb].reshape(u.shape[:-1] + (nb, 3))
+    pure = np.concatenate([np.zeros(v.shape[:-1] + (1,)), v], axis=-1)
+    left, right = (quat_conj(r), r) if inverse else (r, quat_conj(r))
+    w = quat_mul(left, quat_mul(pure, right))  # r (0, v) r*, or r* (0, v) r for the inverse
+    out[..., :3 * nb] = w[..., 1:].reshape(u.shape[:-1] + (3 * nb,))
+    if tail == 2:
+        t = -tail_angle if inverse else tail_angle
+        a, b = u[..., 3 * nb], u[..., 3 * nb + 1]
+        out[..., 3 * nb] = a * np.cos(t) - b * np.sin(t)
+        out[..., 3 * nb + 1] = a * np.sin(t) + b * np.cos(t)
+    return out
+
+
+def rotor_rotate(u: np.ndarray, rq: np.ndarray, tail_angle: float = 0.0) -> np.ndarray:
+    """RotorQuant's rotation: block b of 3 channels -> vector part of r_b (0, v_b) r_b*;
+    a 2-channel tail turned by ``tail_angle``.  ``rq`` is [d // 3][4] unit quaternions (w, x, y, z)."""
+    return _rotor_apply(u, rq, tail_angle, inverse=False)
+
+
+def rotor_inverse(z: np.ndarray, rq: np.ndarray, tail_angle: float = 0.0) -> np.ndarray:
+    """The inverse: r_b* (0, z_b) r_b per block, the tail turned back."""
+    return _rotor_apply(z, rq, tail_angle, inverse=True)
+

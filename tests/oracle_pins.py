@@ -899,4 +899,101 @@ def check_bit_allocation():
         assert np.all(np.diff(b[order]) >= 0)
 
 
+# --------------------------------------------------------------------------- #
+# baseline rotations: TurboQuant's dense orthogonal matrix, RotorQuant's 3-D rotors
+# --------------------------------------------------------------------------- #
+def check_dense_rotation():
+    """z = M u: with M = H/sqrt(d) it is the Walsh-Hadamard transform, with a permutation matrix
+    the gather, with a 2-D rotation the textbook turn; for a Haar-random M (scipy's ortho_group)
+    it keeps norms, and the inverse equals a linear solve of M u = z."""
+    from scipy.stats import ortho_group
+    rng = _rng(40)
+    for d in (128, 256):
+        u = rng.standard_normal((3, d))
+        h = rotations.hadamard(d) / np.sqrt(d)
+        assert np.allclose(rotations.dense_rotate(u, h), rotations.fwht(u), atol=1e-12)
+        perm = rng.permutation(d)
+        pm = np.zeros((d, d))
+        pm[np.arange(d), perm] = 1.0
+        assert np.array_equal(rotations.dense_rotate(u, pm), u[:, perm])
+        m = ortho_group.rvs(d, random_state=int(rng.integers(1 << 30)))
+        z = rotations.dense_rotate(u, m)
+        assert np.allclose(np.linalg.norm(z, axis=-1), np.linalg.norm(u, axis=-1), rtol=1e-12)
+        assert np.allclose(rotations.dense_inverse(z, m), np.linalg.solve(m, z.T).T, atol=1e-10)
+        assert np.allclose(rotations.dense_inverse(z, m), u, atol=1e-10)
+    t = 0.3
+    rot2 = np.array([[np.cos(t), -np.sin(t)], [np.sin(t), np.cos(t)]])
+    assert np.allclose(rotations.dense_rotate(np.array([1.0, 0.0]), rot2), [np.cos(t), np.sin(t)], atol=1e-15)
+
+
+def check_rotor_rotation():
+    """Each 3-channel block turns as scipy's Rotation of the same unit quaternion; the rotor about
+    z by a maps e_x to (cos a, sin a, 0); r and -r are one rotation; rotors compose as quaternion
+    products; d = 128 splits into 42 blocks and a 2-D tail turned by the tail angle, d = 256 into
+    85 blocks and one channel left as it is; the inverse undoes the rotation."""
+    rng = _rng(41)
+    assert rotations.rotor_split(128) == (42, 2) and rotations.rotor_split(256) == (85, 1)
+    for d in (128, 256):
+        nb, tail = rotations.rotor_split(d)
+        r = _unit(rng, nb)
+        u = rng.standard_normal((4, d))
+        ta = 0.7
+        z = rotations.rotor_rotate(u, r, ta)
+        for b in range(nb):
+            want = Rotation.from_quat([r[b, 1], r[b, 2], r[b, 3], r[b, 0]]).apply(u[:, 3 * b:3 * b + 3])
+            assert np.allclose(z[:, 3 * b:3 * b + 3], want, atol=1e-12)
+        if tail == 2:
+            a, c = u[:, -2], u[:, -1]
+            assert np.allclose(z[:, -2], a * np.cos(ta) - c * np.sin(ta), atol=1e-14)
+            assert np.allclose(z[:, -1], a * np.sin(ta) + c * np.cos(ta), atol=1e-14)
+        else:
+            assert np.array_equal(z[:, -1], u[:, -1])
+        assert np.allclose(np.linalg.norm(z, axis=-1), np.linalg.norm(u, axis=-1), rtol=1e-12)
+        assert np.allclose(rotations.rotor_inverse(z, r, ta), u, atol=1e-12)
+        assert np.allclose(rotations.rotor_rotate(u, -r, ta), z, atol=1e-12)
+        r2 = _unit(rng, nb)
+        both = rotations.rotor_rotate(rotations.rotor_rotate(u, r, 0.0), r2, 0.0)
+        assert np.allclose(both, rotations.rotor_rotate(u, rotations.quat_mul(r2, r), 0.0), atol=1e-12)
+    a = 0.9
+    rz = np.tile([np.cos(a / 2), 0.0, 0.0, np.sin(a / 2)], (42, 1))
+    e = np.zeros(128)
+    e[0], e[5] = 1.0, 2.0  # e_x of block 0, e_z of block 1
+    z = rotations.rotor_rotate(e, rz, 0.0)
+    assert np.allclose(z[:3], [np.cos(a), np.sin(a), 0.0], atol=1e-15)
+    assert np.allclose(z[3:6], [0.0, 0.0, 2.0], atol=1e-15)
+
+
+def check_pipeline_baseline_rotations():
+    """The codec with the dense and the rotor rotation: min-max round trip within the Parseval
+    bound of the group scales (any orthogonal rotation); Lloyd-Max codes are the nearest
+    centroids of the rotated direction (brute force) and the decoded direction rotates back onto
+    codebook points."""
+    from scipy.stats import ortho_group
+    rng = _rng(42)
+    d, g = 128, 32
+    m = ortho_group.rvs(d, random_state=7)
+    rq = _unit(rng, d // 3)
+    x = rng.standard_normal((2, 6, 2, d))
+    x[..., [3, 90]] *= 12
+    for kw in (dict(rot="dense", rot_matrix=m), dict(rot="rotor", rotor_quat=rq, rotor_tail=0.4)):
+        for bits in (2, 3):
+            p = codec.CodecParams(bits=bits, group_size=g, perm=rng.permutation(d), **kw)
+            out = codec.encode(x, p)
+            y = codec.decode(out, p, x.shape)
+            err = np.sqrt(np.sum((y - x) ** 2, axis=-1))
+            s = out["scale"].astype(np.float64)
+            assert np.all(err <= np.sqrt(np.sum(g * (s / 2) ** 2, axis=-1)) * (1 + 1e-9))
+        cb = lloyd.fit_gaussian(3, 1.0 / np.sqrt(d))
+        p = codec.CodecParams(bits=3, group_size=d, quant="lloyd", codebook=cb, **kw)
+        out = codec.encode(x, p)
+        rho = np.sqrt(np.sum(x * x, axis=-1))
+        un = x / (rho[..., None] + 1e-6)
+        zz = rotations.dense_rotate(un, m) if kw["rot"] == "dense" else rotations.rotor_rotate(un, rq, 0.4)
+        assert np.array_equal(np.argmin(np.abs(zz[..., None] - cb), axis=-1), out["q"])
+        y = codec.decode(out, p, x.shape)
+        back = y / out["norm"].astype(np.float64)[..., None]
+        w = rotations.dense_rotate(back, m) if kw["rot"] == "dense" else rotations.rotor_rotate(back, rq, 0.4)
+        assert np.min(np.abs(w[..., None] - cb), axis=-1).max() < 1e-12
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -258,7 +258,38 @@ def _attend_heads_interleaved(q, k, v, lengths, scale):
     return res
 
 
+_orig_rotor_rotate = rotations.rotor_rotate
+
+
+def _rotor_inverse_sandwich(u, rq, tail_angle=0.0):
+    # r* (0, v) r instead of r (0, v) r*
+    return rotations.rotor_inverse(u, rq, -tail_angle)
+
+
+def _rotor_tail_sign(u, rq, tail_angle=0.0):
+    return _orig_rotor_rotate(u, rq, -tail_angle)
+
+
+def _rotor_blocks_shifted(u, rq, tail_angle=0.0):
+    # blocks taken from channel 1 on (3b + 1 .. 3b + 3), channel 0 left alone
+    u = np.asarray(u, dtype=np.float64)
+    out = np.array(u)
+    nb = u.shape[-1] // 3
+    part = _orig_rotor_rotate(np.concatenate([u[..., 1:3 * nb + 1], np.zeros(u.shape[:-1] + (2,))], axis=-1)
+                              [..., :u.shape[-1]], rq, 0.0)
+    out[..., 1:3 * nb + 1] = part[..., :3 * nb]
+    return out
+
+
+def _dense_inverse_no_transpose(z, m):
+    return np.asarray(z, dtype=np.float64) @ np.asarray(m, dtype=np.float64).T
+
+
 MUTATIONS = {
+    "rotor_inverse_sandwich": (rotations, "rotor_rotate", _rotor_inverse_sandwich),
+    "rotor_tail_sign": (rotations, "rotor_rotate", _rotor_tail_sign),
+    "rotor_blocks_shifted": (rotations, "rotor_rotate", _rotor_blocks_shifted),
+    "dense_inverse_no_transpose": (rotations, "dense_inverse", _dense_inverse_no_transpose),
     "rope_negative_sine": (rope, "rope", _rope_neg_sine),
     "rope_half_split_pairs": (rope, "rope", _rope_half_split),
     "rope_theta_exponent": (rope, "thetas", _thetas_wrong_exponent),
