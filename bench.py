@@ -370,6 +370,96 @@ def dynamic_codebook_report(kvq, workloads, dev, stream):
     return res
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+
+
+def baseline_rotations_report(kvq, workloads, dev, stream, n_big=1 << 21):
+    """The rotations the IsoQuant page (section 1) compares -- its SO(4) blocks, the Walsh-Hadamard
+    transform, TurboQuant's dense random orthogonal matrix and RotorQuant's 3-D rotors -- in one
+    codec: norm separation + 3-bit Lloyd-Max for N(0, 1/128), fp32 input, d = 128.  Quality: SNR
+    of the round trip on the IsoQuant workload (8192 N(0,1) vectors).  Speed: encode and decode of
+    that 8192-vector batch (the batch of the page's benchmark), and of 2^21 vectors drawn the same
+    way, with GB/s and, for the matrix rotations (on the fp32 matrix cores), TFLOP/s of the
+    2 * 128 * 128 flops per vector against the 157.3 TFLOP/s fp32 matrix peak."""
+    import numpy as np
+    import torch
+
+    d = 128
+    wl = workloads.WORKLOADS["isoquant"]
+    c = wl.case("X")
+    h = workloads.host_workload("isoquant")
+    x_small = torch.from_numpy(np.ascontiguousarray(h["inputs"]["X"])).to(dev)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    x_big = torch.randn((1, n_big, 1, d), generator=gen, device=dev, dtype=torch.float32)
+    rng = np.random.default_rng(2024)
+    haar = torch.from_numpy(workloads.haar_orthogonal(d, rng)).to(dev)
+    rq, ta = workloads.rotor_quaternions(d, rng)
+    rotor = torch.from_numpy(kvq.rotor_matrix(rq, d, ta)).to(dev)
+    cb = kvq.lloyd_max_gaussian(3, 1.0 / np.sqrt(d))
+    kinds = {"so4 (IsoQuant)": dict(rot="so4", quat=h["quat"]), "fwht": dict(rot="fwht"),
+             "dense (TurboQuant)": dict(rot="dense", rot_matrix=haar),
+             "rotor (RotorQuant, as its block-diagonal matrix)": dict(rot="dense", rot_matrix=rotor)}
+    lw = workloads.WORKLOADS["llama2"]
+    lk = lw.case("K")
+    lh = workloads.host_workload("llama2")
+    x_out = torch.from_numpy(np.ascontiguousarray(lh["inputs"]["K"])).to(dev).float()
+    res = {"workload": "norm separation + 3-bit Lloyd-Max, fp32, d = 128; SNR on " + wl.title +
+                       " and on the Llama-2 layer's K (4 outlier channels x20; sink tokens left out)",
+           "big_vectors": n_big, "rotations": {}}
+    for label, kw in kinds.items():
+        entry = {}
+        for size, x in (("batch_8192", x_small), ("big", x_big)):
+            cfg = kvq.Config(shape=tuple(x.shape), dtype="f32", bits=3, quant="lloyd", codebook=cb, **kw)
+            pl = kvq.encode(x, cfg, stream=stream)
+            y = kvq.decode(pl, cfg, out_dtype="f32", stream=stream)
+            torch.cuda.synchronize()
+            if size == "batch_8192":
+                err = (y - x).double().pow(2).sum().item()
+                entry["snr_db"] = round(10 * np.log10(x.double().pow(2).sum().item() / err), 3)
+            n = int(x.numel() // d)
+            reps = 50 if size == "batch_8192" else 5
+            for kind in ("encode", "decode"):
+                with torch.cuda.stream(stream):
+                    for _ in range(2):
+                        kvq.encode(x, cfg, planes=pl, stream=stream) if kind == "encode" else \
+                            kvq.decode(pl, cfg, out_dtype="f32", out=y, stream=stream)
+                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    ev[0].record(stream)
+                    for _ in range(reps):
+                        if kind == "encode":
+                            kvq.encode(x, cfg, planes=pl, stream=stream)
+                        else:
+                            kvq.decode(pl, cfg, out_dtype="f32", out=y, stream=stream)
+                    ev[1].record(stream)
+                    stream.synchronize()
+                ms = ev[0].elapsed_time(ev[1]) / reps
+                nbytes = n * d * 4 + plane_bytes(pl)
+                e = {"us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+                if kw["rot"] == "dense":
+                    tf = 2.0 * d * d * n / (ms * 1e-3) / 1e12
+                    e["TFLOPs"] = round(tf, 2)
+                    e["mfma_f32_frac"] = round(tf / MFMA_F32_PEAK_TFLOPS, 4)
+                entry[f"{kind}_{size}"] = e
+            del pl, y
+        # quality where a few channels carry most of the energy: global mixing spreads them
+        cfg = kvq.Config(shape=tuple(x_out.shape), dtype="f32", bits=3, quant="lloyd", codebook=cb,
+                         n_sink=lk.n_sink, **kw)
+        pl = kvq.encode(x_out, cfg, stream=stream)
+        y = kvq.decode(pl, cfg, out_dtype="f32", stream=stream)
+        torch.cuda.synchronize()
+        keep = slice(lk.n_sink, None)
+        err = (y[:, keep] - x_out[:, keep]).double().pow(2).sum().item()
+        entry["snr_db_outlier_channels"] = round(10 * np.log10(x_out[:, keep].double().pow(2).sum().item() / err), 3)
+        del pl, y
+        res["rotations"][label] = entry
+        print(f"[bench] baseline {label}: SNR {entry['snr_db']} / {entry['snr_db_outlier_channels']} dB, "
+              f"encode {entry['encode_batch_8192']['us']} us "
+              f"/ 8192, big {entry['encode_big']['us']} us", file=sys.stderr, flush=True)
+    del x_big, x_out
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -624,6 +714,7 @@ def main():
         torch.cuda.empty_cache()
         others = time_other_configs(kvq, workloads, dev, stream)
         others["dynamic_codebook"] = dynamic_codebook_report(kvq, workloads, dev, stream)
+        others["baseline_rotations"] = baseline_rotations_report(kvq, workloads, dev, stream)
 
     out = {
         "metric": METRIC,

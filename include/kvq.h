@@ -104,8 +104,10 @@ typedef struct kvq_config {
   const uint8_t* chan_wide;   /* HOST [D], 0 or 1, exactly D/16 ones                       */
   const float* codebook_wide; /* HOST [2^(bits+1)] strictly ascending, finite              */
   /* KVQ_ROT_DENSE: DEVICE [D][D] float32 row-major, z_i = sum_j M[i][j] u_j; orthogonal (a
-   * precondition the host cannot check: decode applies the transpose).  The A/B baseline of
-   * a dense random rotation (IsoQuant page, section 1). */
+   * precondition the host cannot check: decode applies the transpose).  The baselines the
+   * IsoQuant page, section 1, compares against: a dense random rotation (TurboQuant), or
+   * 3-D rotors as a block-diagonal matrix (RotorQuant, kvq_rotor_matrix).  Codec (encode,
+   * decode): head_dim 128, no dynamic codebook; not in append or attention. */
   const float* rot_matrix;
 } kvq_config;
 
@@ -312,6 +314,19 @@ kvq_status kvq_allocate_bits(const double* entropy, int64_t heads, int32_t total
  * conditional-mean levels, iterated in double precision (IsoQuant page, section 3.1
  * names the Lloyd-Max quantizer; the fitting procedure is the textbook one). */
 kvq_status kvq_lloyd_max_gaussian(int32_t bits, double sigma, float* codebook_out);
+
+/* Host-only: RotorQuant's rotation (the 3-D Clifford rotors the IsoQuant page, section 1,
+ * compares against) as the matrix of a KVQ_ROT_DENSE rotation: the block-diagonal [D][D]
+ * float32 row-major matrix whose block b (rows and columns 3b .. 3b + 2, b < D / 3) maps v to
+ * the vector part of rq[b] (0, v) rq[b]* (the sandwich product of section 2.1, written out
+ * as the 3x3 matrix of the quaternion), whose 2-channel tail (D mod 3 = 2) turns in its plane
+ * by tail_angle, and whose 1-channel tail (D mod 3 = 1) is left as it is.
+ *   rq          HOST float32 [D / 3][4], (w, x, y, z), each of unit norm within 1e-4.
+ *   head_dim    128 or 256 (the dense codec takes 128).
+ *   out         HOST float32 [D][D], written whole; owned by the caller.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED (head_dim), KVQ_ERR_PARAM (a quaternion off unit
+ * norm or not finite, tail_angle not finite). */
+kvq_status kvq_rotor_matrix(const float* rq, int64_t head_dim, float tail_angle, float* out);
 
 /* Static description of a status code. */
 const char* kvq_status_string(kvq_status status);

@@ -27,7 +27,7 @@ __all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_noalloc",
            "channel_stats", "channel_stats_workspace_size", "outlier_perm", "detect_sinks", "rotated_moments",
            "dynamic_codebook", "attention_entropy", "allocate_bits", "encode_heads",
            "attend_workspace_size", "decode", "packed_sizes", "validate", "lloyd_max_gaussian",
-           "library_path", "abi_version", "DTYPES", "ROTATIONS", "QUANTIZERS", "EXPORTED_SYMBOLS"]
+           "rotor_matrix", "library_path", "abi_version", "DTYPES", "ROTATIONS", "QUANTIZERS", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvq.so")
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_
                     "kvq_decode", "kvq_lloyd_max_gaussian", "kvq_channel_stats_workspace_size", "kvq_channel_stats",
                     "kvq_outlier_perm", "kvq_detect_sinks", "kvq_rotated_moments", "kvq_dynamic_codebook",
                     "kvq_attention_entropy_workspace_size", "kvq_attention_entropy", "kvq_allocate_bits",
-                    "kvq_status_string", "kvq_last_error_message")
+                    "kvq_rotor_matrix", "kvq_status_string", "kvq_last_error_message")
 
 
 class _Config(ctypes.Structure):
@@ -134,6 +134,7 @@ def _load():
     lib.kvq_allocate_bits.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p]
     lib.kvq_lloyd_max_gaussian.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p]
+    lib.kvq_rotor_matrix.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_last_error_message.restype = ctypes.c_char_p
@@ -141,7 +142,7 @@ def _load():
                "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_channel_stats_workspace_size",
                "kvq_channel_stats", "kvq_outlier_perm", "kvq_detect_sinks", "kvq_rotated_moments",
                "kvq_dynamic_codebook", "kvq_attention_entropy_workspace_size", "kvq_attention_entropy",
-               "kvq_allocate_bits"):
+               "kvq_allocate_bits", "kvq_rotor_matrix"):
         getattr(lib, fn).restype = ctypes.c_int
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -500,3 +501,14 @@ def lloyd_max_gaussian(bits: int, sigma: float) -> np.ndarray:
     out = np.zeros(2 ** bits, dtype=np.float32)
     _check(_L().kvq_lloyd_max_gaussian(int(bits), float(sigma), out.ctypes.data))
     return out
+
+
+def rotor_matrix(rq, head_dim: int, tail_angle: float = 0.0) -> np.ndarray:
+    """RotorQuant's 3-D rotors as the [D, D] float32 matrix of a dense rotation (host)."""
+    rq = np.ascontiguousarray(rq, dtype=np.float32)
+    if rq.shape != (int(head_dim) // 3, 4):
+        raise ValueError(f"rq must be [{int(head_dim) // 3}, 4]")
+    out = np.zeros((int(head_dim), int(head_dim)), dtype=np.float32)
+    _check(_L().kvq_rotor_matrix(rq.ctypes.data, int(head_dim), float(tail_angle), out.ctypes.data))
+    return out
+

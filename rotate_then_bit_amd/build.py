@@ -26,7 +26,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-f
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
 
 # translation units: (source, extra defines)
-KERNEL_UNITS = [("kvq_kernels.hip", [f"-DKVQ_UNIT={i}"]) for i in range(20)]
+KERNEL_UNITS = [("kvq_kernels.hip", [f"-DKVQ_UNIT={i}"]) for i in range(22)]
 
 
 def _hipcc() -> str:

@@ -287,11 +287,20 @@ kvq_status kvq_packed_sizes(const kvq_config* cfg, size_t* codes, size_t* scale,
   return ok();
 }
 
+namespace {
+// the dense rotation's codec: head_dim 128, no dynamic codebook
+kvq_status check_dense(const kvq_config* cfg) {
+  if (cfg->head_dim != 128) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: head_dim 128 only");
+  if (cfg->chan_scale) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: no dynamic codebook");
+  return KVQ_OK;
+}
+}  // namespace
+
 kvq_status kvq_encode(const kvq_config* cfg, const void* x, const kvq_planes* out, void* stream) {
   Derived dv;
   kvq_status st = check_config(cfg, &dv);
   if (st != KVQ_OK) return st;
-  if (cfg->rot == KVQ_ROT_DENSE) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: not in the codec");
+  if (cfg->rot == KVQ_ROT_DENSE && (st = check_dense(cfg)) != KVQ_OK) return st;
   if ((st = check_planes(cfg, dv, out)) != KVQ_OK) return st;
   if (dv.n_vec == 0) return ok();
   if (!x) return fail(KVQ_ERR_NULL, "x is NULL");
@@ -308,16 +317,20 @@ kvq_status kvq_encode(const kvq_config* cfg, const void* x, const kvq_planes* ou
   plan_work(cfg, &a);
   const bool d128 = cfg->head_dim == 128;
   int err;
-  switch (cfg->dtype) {
-    case KVQ_F16:
-      err = (d128 ? kvq::launch_encode_f16_d128 : kvq::launch_encode_f16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
-      break;
-    case KVQ_BF16:
-      err = (d128 ? kvq::launch_encode_bf16_d128 : kvq::launch_encode_bf16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
-      break;
-    default:
-      err = (d128 ? kvq::launch_encode_f32_d128 : kvq::launch_encode_f32_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
-      break;
+  if (cfg->rot == KVQ_ROT_DENSE) {
+    err = kvq::launch_encode_dense(cfg->dtype, cfg->bits, cfg->quant, a, stream);
+  } else {
+    switch (cfg->dtype) {
+      case KVQ_F16:
+        err = (d128 ? kvq::launch_encode_f16_d128 : kvq::launch_encode_f16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+        break;
+      case KVQ_BF16:
+        err = (d128 ? kvq::launch_encode_bf16_d128 : kvq::launch_encode_bf16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+        break;
+      default:
+        err = (d128 ? kvq::launch_encode_f32_d128 : kvq::launch_encode_f32_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+        break;
+    }
   }
   if (err != 0) return fail(KVQ_ERR_DEVICE, "encode launch failed: %s", kvq::device_error_string(err));
   return ok();
@@ -328,7 +341,7 @@ kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* posit
   Derived dv;
   kvq_status st = check_config(cfg, &dv);  // cfg describes the cache: tokens = slots per row
   if (st != KVQ_OK) return st;
-  if (cfg->rot == KVQ_ROT_DENSE) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: not in the codec");
+  if (cfg->rot == KVQ_ROT_DENSE) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: no append (encode the batch)");
   if (!cache) return fail(KVQ_ERR_NULL, "cache planes is NULL");
   if (dv.n_vec == 0) return ok();
   if ((st = check_planes(cfg, dv, cache)) != KVQ_OK) return st;
@@ -381,7 +394,7 @@ kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int3
   Derived dv;
   kvq_status st = check_config(cfg, &dv);
   if (st != KVQ_OK) return st;
-  if (cfg->rot == KVQ_ROT_DENSE) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: not in the codec");
+  if (cfg->rot == KVQ_ROT_DENSE && (st = check_dense(cfg)) != KVQ_OK) return st;
   if (y_dtype < KVQ_F16 || y_dtype > KVQ_F32) return fail(KVQ_ERR_ROT, "unknown output dtype %d", y_dtype);
   if ((st = check_planes(cfg, dv, in)) != KVQ_OK) return st;
   if (dv.n_vec == 0) return ok();
@@ -399,16 +412,20 @@ kvq_status kvq_decode(const kvq_config* cfg, const kvq_planes* in, void* y, int3
   plan_work(cfg, &a);
   const bool d128 = cfg->head_dim == 128;
   int err;
-  switch (y_dtype) {
-    case KVQ_F16:
-      err = (d128 ? kvq::launch_decode_f16_d128 : kvq::launch_decode_f16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
-      break;
-    case KVQ_BF16:
-      err = (d128 ? kvq::launch_decode_bf16_d128 : kvq::launch_decode_bf16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
-      break;
-    default:
-      err = (d128 ? kvq::launch_decode_f32_d128 : kvq::launch_decode_f32_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
-      break;
+  if (cfg->rot == KVQ_ROT_DENSE) {
+    err = kvq::launch_decode_dense(y_dtype, cfg->bits, cfg->quant, a, stream);
+  } else {
+    switch (y_dtype) {
+      case KVQ_F16:
+        err = (d128 ? kvq::launch_decode_f16_d128 : kvq::launch_decode_f16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+        break;
+      case KVQ_BF16:
+        err = (d128 ? kvq::launch_decode_bf16_d128 : kvq::launch_decode_bf16_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+        break;
+      default:
+        err = (d128 ? kvq::launch_decode_f32_d128 : kvq::launch_decode_f32_d256)(cfg->bits, cfg->rot, cfg->quant, a, stream);
+        break;
+    }
   }
   if (err != 0) return fail(KVQ_ERR_DEVICE, "decode launch failed: %s", kvq::device_error_string(err));
   return ok();
@@ -926,3 +943,41 @@ const char* kvq_status_string(kvq_status s) {
 const char* kvq_last_error_message(void) { return g_last_error.c_str(); }
 
 }  // extern "C"
+
+kvq_status kvq_rotor_matrix(const float* rq, int64_t head_dim, float tail_angle, float* out) {
+  if (!rq || !out) return fail(KVQ_ERR_NULL, "rq or out is NULL");
+  if (head_dim != 128 && head_dim != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim %lld (supported: 128, 256)", (long long)head_dim);
+  if (!isfinite(tail_angle)) return fail(KVQ_ERR_PARAM, "tail_angle must be finite");
+  const int d = (int)head_dim, nb = d / 3;
+  for (int b = 0; b < nb; ++b) {
+    double n2 = 0.0;
+    for (int k = 0; k < 4; ++k) {
+      if (!isfinite(rq[4 * b + k])) return fail(KVQ_ERR_PARAM, "rq[%d] is not finite", b);
+      n2 += (double)rq[4 * b + k] * rq[4 * b + k];
+    }
+    if (fabs(sqrt(n2) - 1.0) > 1e-4) return fail(KVQ_ERR_PARAM, "rq[%d] is not a unit quaternion", b);
+  }
+  memset(out, 0, sizeof(float) * (size_t)d * (size_t)d);
+  for (int b = 0; b < nb; ++b) {
+    // r (0, v) r* for r = (w, x, y, z): the homogeneous 3x3 form (equal to |r|^2 times the
+    // rotation, so exact for the stored, nearly unit r)
+    const double w = rq[4 * b], x = rq[4 * b + 1], y = rq[4 * b + 2], z = rq[4 * b + 3];
+    const double m[3][3] = {{w * w + x * x - y * y - z * z, 2.0 * (x * y - w * z), 2.0 * (x * z + w * y)},
+                            {2.0 * (x * y + w * z), w * w - x * x + y * y - z * z, 2.0 * (y * z - w * x)},
+                            {2.0 * (x * z - w * y), 2.0 * (y * z + w * x), w * w - x * x - y * y + z * z}};
+    for (int i = 0; i < 3; ++i)
+      for (int j = 0; j < 3; ++j) out[(size_t)(3 * b + i) * d + 3 * b + j] = (float)m[i][j];
+  }
+  const int t0 = 3 * nb;
+  if (d - t0 == 2) {
+    const double c = cos((double)tail_angle), sn = sin((double)tail_angle);
+    out[(size_t)t0 * d + t0] = (float)c;
+    out[(size_t)t0 * d + t0 + 1] = (float)-sn;
+    out[(size_t)(t0 + 1) * d + t0] = (float)sn;
+    out[(size_t)(t0 + 1) * d + t0 + 1] = (float)c;
+  } else if (d - t0 == 1) {
+    out[(size_t)t0 * d + t0] = 1.0f;
+  }
+  return ok();
+}

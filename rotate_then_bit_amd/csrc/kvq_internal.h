@@ -234,6 +234,9 @@ KVQ_DECLARE_LAUNCH(launch_decode_bf16_d256)
 KVQ_DECLARE_LAUNCH(launch_decode_f32_d128)
 KVQ_DECLARE_LAUNCH(launch_decode_f32_d256)
 #undef KVQ_DECLARE_LAUNCH
+// The dense rotation (head_dim 128; dtype / out_dtype: DT_F16, DT_BF16, DT_F32), and its sink pass.
+int launch_encode_dense(int dtype, int bits, int quant, const CodecArgs& a, void* stream);
+int launch_decode_dense(int out_dtype, int bits, int quant, const CodecArgs& a, void* stream);
 const char* device_error_string(int err);
 
 }  // namespace kvq

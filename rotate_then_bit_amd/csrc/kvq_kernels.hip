@@ -599,6 +599,129 @@ __device__ __host__ inline size_t enc_wave_bytes(bool perm, bool rope, int trig_
 }
 
 // ---------------------------------------------------------------------------
+// quantization of a lane's 32 values (shared by the encoders)
+// ---------------------------------------------------------------------------
+// Norm separation of the Lloyd-Max path (IsoQuant page, section 3.1): rho = |v| over the
+// vector's LV lanes, with an exact power-of-two pre-scale by the largest |v_i| so that the sum
+// of squares neither underflows nor overflows; v becomes v / (rho + 1e-6).  Returns rho.
+template <int LV>
+__device__ __forceinline__ float norm_separate(float* v) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = vec_max<LV>(amax);
+  const int ex = (amax > 0.0f) ? __builtin_amdgcn_frexp_expf(amax) : 0;
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float w = __builtin_ldexpf(v[i], -ex);
+    ss = __builtin_fmaf(w, w, ss);
+  }
+  ss = vec_sum<LV>(ss);
+  const float rho = __builtin_ldexpf(__builtin_sqrtf(ss), ex);
+  const float inv = 1.0f / (rho + 1e-6f);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] *= inv;
+  return rho;
+}
+
+// Min-max quantization of a lane's 32 values whose true coefficients are A * v (for A < 0 min
+// and max swap).  A group covers 2^LB whole lanes (LB = log2 G - 5).  Returns the group's zero
+// (rounded down) and scale = (max - zero) / (2^b - 1) (rounded up) as fp16 bits, the same in
+// every lane of the group, and the codes q = rint((A v - zero) / scale), nearest-even.  RESID:
+// one residual step first makes the quotient correctly rounded (unrotated 16-bit data sit on
+// the zero/scale grid, so exact half-way quotients are common).
+template <int BITS, bool RESID>
+__device__ __forceinline__ void minmax_codes_lane(const float* v, float A, int LB, uint32_t& zb_out, uint32_t& sb_out,
+                                                  LaneCodes<BITS>& cw) {
+  float lo = fminf(fminf(v[0], v[1]), v[2]), hi = fmaxf(fmaxf(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int i = 3; i < 31; i += 2) {
+    lo = fminf(fminf(lo, v[i]), v[i + 1]);
+    hi = fmaxf(fmaxf(hi, v[i]), v[i + 1]);
+  }
+  lo = fminf(lo, v[31]);
+  hi = fmaxf(hi, v[31]);
+  float mn = (A > 0.0f) ? lo * A : hi * A;
+  float mx = (A > 0.0f) ? hi * A : lo * A;
+  if (LB >= 1) { mn = min_x1(mn); mx = max_x1(mx); }
+  if (LB >= 2) { mn = min_x2(mn); mx = max_x2(mx); }
+  if (LB >= 3) { mn = fminf(mn, swz_x4(mn)); mx = fmaxf(mx, swz_x4(mx)); }
+  // "+ 0.0f" turns a -0 (all-zero group, negated lanes) into +0
+  const uint32_t zb = f16_round_down(mn + 0.0f);
+  const float z = f16_value(zb);
+  constexpr float kInvLevels = 1.0f / (float)((1 << BITS) - 1);
+  const uint32_t sb = f16_round_up_nonneg((mx - z) * kInvLevels + 0.0f);
+  const float sc = f16_value(sb);
+  zb_out = zb;
+  sb_out = sb;
+  const float iv = (sc > 0.0f) ? __builtin_amdgcn_rcpf(sc) : 0.0f;
+  float tv[32];
+  if constexpr (RESID) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float d = __builtin_fmaf(v[i], A, -z);
+      const float t0 = d * iv;
+      tv[i] = (sc > 0.0f) ? __builtin_fmaf(__builtin_fmaf(-t0, sc, d), iv, t0) : 0.0f;
+    }
+  } else {
+    const float Ai = A * iv, c0 = -z * iv;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) tv[i] = __builtin_fmaf(v[i], Ai, c0);
+  }
+  if constexpr (BITS == 3) {
+    // q = rint(t) via 1.5 * 2^23: the sum rounds t to an integer in the low mantissa bits
+    // (bit pattern 0x4B400000 + q, since -eps <= t <= 2^b - 1 + eps)
+    constexpr float kMagic = 12582912.0f;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) cw.w[w] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t cq = __float_as_uint(tv[i] + kMagic) - 0x4B400000u;
+      const int bit = 3 * i, w = bit >> 5, sh = bit & 31;
+      cw.w[w] |= cq << sh;
+      if (sh > 29) cw.w[w + 1] |= cq >> (32 - sh);
+    }
+  } else {
+    // v_cvt_pk_u8_f32 (round to nearest even, clamped at 0) writes code k + ND j into byte j of
+    // dword D_k; the word is D_0 + D_1 << BITS + ... (each byte's code lands on its own field)
+    constexpr int PER = 32 / BITS;  // codes per word
+    constexpr int ND = PER / 4;     // dwords D_k per word
+#pragma unroll
+    for (int w = 0; w < BITS; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = ND - 1; k >= 0; --k) {
+        uint32_t d = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_cvt_pk_u8_f32(tv[PER * w + k + ND * j], j, d);
+        word = (word << BITS) + d;
+      }
+      cw.w[w] = word;
+    }
+  }
+}
+
+// Lloyd-Max codes of a lane's 32 values (true coefficients A * v): q = #{k : z > tau_k} against
+// the 2^b - 1 midpoints tau.
+template <int BITS>
+__device__ __forceinline__ void lloyd_codes_lane(const float* v, float A, const float* tau, LaneCodes<BITS>& cw) {
+  constexpr int NT = (1 << BITS) - 1;
+#pragma unroll
+  for (int w = 0; w < BITS; ++w) cw.w[w] = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float z = v[i] * A;
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < NT; ++k) c += (z > tau[k]) ? 1u : 0u;
+    const int bit = BITS * i, w = bit >> 5, sh = bit & 31;
+    cw.w[w] |= c << sh;
+    if (BITS == 3 && sh > 29) cw.w[w + 1] |= c >> (32 - sh);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // ENCODE
 // ---------------------------------------------------------------------------
 // RT / PT: RoPE / permutation off (0), on (1) or read from the arguments (-1).
@@ -849,24 +972,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
       }
     }
     if constexpr (QUANT == Q_LLOYD) {
-      // |u| (the permutation does not change it) with an exact power-of-two pre-scale by
-      // the largest |u_i|, so that the sum of squares neither underflows nor overflows
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      amax = vec_max<LV>(amax);
-      const int ex = (amax > 0.0f) ? __builtin_amdgcn_frexp_expf(amax) : 0;
-      float ss = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float w = __builtin_ldexpf(v[i], -ex);
-        ss = __builtin_fmaf(w, w, ss);
-      }
-      ss = vec_sum<LV>(ss);
-      const float rho = __builtin_ldexpf(__builtin_sqrtf(ss), ex);
-      const float inv = 1.0f / (rho + 1e-6f);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] *= inv;
+      // |u| (the permutation does not change it)
+      const float rho = norm_separate<LV>(v);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rho), make_buf_item(a.norm + vec0, (uint32_t)(4 * nvalid)),
                                             4u * (uint32_t)q, 0, 0);
     }
@@ -886,28 +993,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
     }
     LaneCodes<BITS> cw;
     if constexpr (QUANT == Q_MINMAX) {
-      // min/max of the lane's 32 values (one group covers 1, 2, 4 or 8 whole lanes); the
-      // true coefficients are A * v, so for A < 0 min and max swap
-      float lo = fminf(fminf(v[0], v[1]), v[2]), hi = fmaxf(fmaxf(v[0], v[1]), v[2]);
-#pragma unroll
-      for (int i = 3; i < 31; i += 2) {
-        lo = fminf(fminf(lo, v[i]), v[i + 1]);
-        hi = fmaxf(fmaxf(hi, v[i]), v[i + 1]);
-      }
-      lo = fminf(lo, v[31]);
-      hi = fmaxf(hi, v[31]);
-      float mn = (A > 0.0f) ? lo * A : hi * A;
-      float mx = (A > 0.0f) ? hi * A : lo * A;
-      if (LB >= 1) { mn = min_x1(mn); mx = max_x1(mx); }
-      if (LB >= 2) { mn = min_x2(mn); mx = max_x2(mx); }
-      if (LB >= 3) { mn = fminf(mn, swz_x4(mn)); mx = fmaxf(mx, swz_x4(mx)); }
-      // zero rounded down, scale = (max - zero)/(2^b - 1) rounded up, both to fp16;
-      // "+ 0.0f" turns a -0 (all-zero group, negated lanes) into +0
-      const uint32_t zb = f16_round_down(mn + 0.0f);
-      const float z = f16_value(zb);
-      constexpr float kInvLevels = 1.0f / (float)((1 << BITS) - 1);
-      const uint32_t sb = f16_round_up_nonneg((mx - z) * kInvLevels + 0.0f);
-      const float sc = f16_value(sb);
+      uint32_t zb, sb;
+      minmax_codes_lane<BITS, ROT == ROT_NONE>(v, A, LB, zb, sb, cw);
       {
         // every lane of a group holds the same values and stores them
         const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
@@ -915,76 +1002,17 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sb, make_buf_item(a.scale + vec0 * ngroups, gbytes), go, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)zb, make_buf_item(a.zero + vec0 * ngroups, gbytes), go, 0, 0);
       }
-      const float iv = (sc > 0.0f) ? __builtin_amdgcn_rcpf(sc) : 0.0f;
-      // q = rint(t), nearest-even, with t = (A v - zero) / scale for the 32 slots
-      float tv[32];
-      if constexpr (ROT == ROT_NONE) {
-        // q = rint(t): unrotated fp16/bf16 data sit on the same grid as zero/scale, so
-        // exact half-way quotients are common; one residual step makes d / scale
-        // correctly rounded before the integer rounding
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float d = __builtin_fmaf(v[i], A, -z);
-          const float t0 = d * iv;
-          tv[i] = (sc > 0.0f) ? __builtin_fmaf(__builtin_fmaf(-t0, sc, d), iv, t0) : 0.0f;
-        }
-      } else {
-        const float Ai = A * iv, c0 = -z * iv;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) tv[i] = __builtin_fmaf(v[i], Ai, c0);
-      }
-      if constexpr (BITS == 3) {
-        // q = rint(t) via 1.5 * 2^23: the sum rounds t to an integer in the low mantissa
-        // bits (bit pattern 0x4B400000 + q, since -eps <= t <= 2^b - 1 + eps)
-        constexpr float kMagic = 12582912.0f;
-#pragma unroll
-        for (int w = 0; w < 3; ++w) cw.w[w] = 0u;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const uint32_t cq = __float_as_uint(tv[i] + kMagic) - 0x4B400000u;
-          const int bit = 3 * i, w = bit >> 5, sh = bit & 31;
-          cw.w[w] |= cq << sh;
-          if (sh > 29) cw.w[w + 1] |= cq >> (32 - sh);
-        }
-      } else {
-        // v_cvt_pk_u8_f32 (round to nearest even, clamped at 0) writes code k + ND j into
-        // byte j of dword D_k; the word is D_0 + D_1 << BITS + ... (each byte's code
-        // lands on its own BITS-bit field)
-        constexpr int PER = 32 / BITS;  // codes per word
-        constexpr int ND = PER / 4;     // dwords D_k per word
-#pragma unroll
-        for (int w = 0; w < BITS; ++w) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int k = ND - 1; k >= 0; --k) {
-            uint32_t d = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_cvt_pk_u8_f32(tv[PER * w + k + ND * j], j, d);
-            word = (word << BITS) + d;
-          }
-          cw.w[w] = word;
-        }
-      }
     } else {
       // Lloyd-Max: q = #{k : z > tau_k}
       constexpr int NT = (1 << BITS) - 1;
       float tau[NT];
 #pragma unroll
       for (int i = 0; i < NT; ++i) tau[i] = 0.5f * (a.codebook[i] + a.codebook[i + 1]);
-#pragma unroll
-      for (int w = 0; w < BITS; ++w) cw.w[w] = 0u;
       if (!a.dyn) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float z = v[i] * A;
-          uint32_t c = 0;
-#pragma unroll
-          for (int k = 0; k < NT; ++k) c += (z > tau[k]) ? 1u : 0u;
-          const int bit = BITS * i, w = bit >> 5, sh = bit & 31;
-          cw.w[w] |= c << sh;
-          if (BITS == 3 && sh > 29) cw.w[w + 1] |= c >> (32 - sh);
-        }
+        lloyd_codes_lane<BITS>(v, A, tau, cw);
       } else {
+#pragma unroll
+        for (int w = 0; w < BITS; ++w) cw.w[w] = 0u;
         // dynamic codebook: channel j compares z_j / scale_j against the N(0,1) midpoints; a wide
         // channel against the 2^(b+1)-level codebook's, its top code bit going to the extra plane
         constexpr int NTW = (2 << BITS) - 1;
@@ -1494,6 +1522,215 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_sink_kernel(const 
         w.z = pack_bf16x2(v[8 * k + 4], v[8 * k + 5]);
         w.w = pack_bf16x2(v[8 * k + 6], v[8 * k + 7]);
         yp[k] = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// DENSE ROTATION (the baselines the IsoQuant page, section 1, compares against): z = M P u with
+// an orthogonal d x d matrix, d = 128, on the fp32 matrix cores
+// ---------------------------------------------------------------------------
+// A block of 8 waves holds the matrix in LDS with the permutation folded in: the encoder's
+// Q[i][perm[j]] = M[i][j] (Q u = M P u), the decoder's R[perm[j]][i] = M[i][j] (R z = P^T M^T z,
+// the output in the original channel order).  128 rows of 528 bytes, loaded once per block;
+// blocks then loop over items of 16 vectors, one wave per item.  Per item, every lane forms
+// its 32 channels of one vector as the encoder (or decoder) does, stages them in the wave's 16
+// LDS rows, and the wave computes Z^T = Q U^T with 256 v_mfma_f32_16x16x4f32: product (m, s)
+// multiplies rows 16 m .. 16 m + 15 of Q (A operand, lane (n16, g): row 16 m + n16) with the
+// 16 vectors (B operand, lane (n16, g): vector n16) over input channels 16 (s / 4) + 4 g + s % 4,
+// so each lane reads 4 consecutive floats of a row for 4 products.  Lane (n16, g) then holds
+// channels 16 m + 4 g .. + 3 of vector n16; they go back to LDS and are read in the codec's
+// lane layout (lane l of a vector: channels 32 l .. 32 l + 31).  fp32 products and sums: the
+// rotation is exact fp32 arithmetic up to the summation order.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kDenseWaves = 8;
+constexpr int kDensePitch = 128 * 4 + 16;                            // bytes per LDS row
+constexpr int kDenseLds = (128 + kDenseWaves * 16) * kDensePitch;  // 135168 bytes per block
+
+// the wave's 16 staged rows (U) times the block's matrix rows: acc[m] = rows 16 m .. of Z^T
+__device__ __forceinline__ void dense_product(uint32_t mat, uint32_t stage, int n16, int g, f32x4_t (&acc)[8]) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t col = 4u * (uint32_t)(16 * u + 4 * g);
+    const u32x4_t b4 = lds_ld4(stage + (uint32_t)(n16 * kDensePitch) + col);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const u32x4_t a4 = lds_ld4(mat + (uint32_t)((16 * m + n16) * kDensePitch) + col);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a4.x), __uint_as_float(b4.x), acc[m], 0, 0, 0);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a4.y), __uint_as_float(b4.y), acc[m], 0, 0, 0);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a4.z), __uint_as_float(b4.z), acc[m], 0, 0, 0);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a4.w), __uint_as_float(b4.w), acc[m], 0, 0, 0);
+    }
+  }
+}
+
+// A lane's 32 values through the matrix: staged as vector q's row (channels 32 l ..), rotated
+// by the wave, and read back in the same layout.
+__device__ __forceinline__ void dense_rotate_lane(float* v, uint32_t mat, uint32_t stage, int q, int l, int n16,
+                                                  int g) {
+  const uint32_t row = stage + (uint32_t)(q * kDensePitch + 128 * l);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    lds_st4(row + 16u * k, u32x4_t{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                                   __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])});
+  wave_lds_sync();
+  f32x4_t acc[8];
+  dense_product(mat, stage, n16, g, acc);
+  wave_lds_sync();  // every lane's reads of the staged rows are done
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    lds_st4(stage + (uint32_t)(n16 * kDensePitch) + 4u * (uint32_t)(16 * m + 4 * g),
+            u32x4_t{__float_as_uint(acc[m][0]), __float_as_uint(acc[m][1]), __float_as_uint(acc[m][2]),
+                    __float_as_uint(acc[m][3])});
+  wave_lds_sync();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4_t w = lds_ld4(row + 16u * k);
+    v[4 * k] = __uint_as_float(w.x);
+    v[4 * k + 1] = __uint_as_float(w.y);
+    v[4 * k + 2] = __uint_as_float(w.z);
+    v[4 * k + 3] = __uint_as_float(w.w);
+  }
+  wave_lds_sync();  // the rows are free for the next item
+}
+
+// The block's matrix into LDS with the permutation folded in: the encoder's Q[i][perm[j]] and
+// the decoder's R[perm[j]][i] both hold M[i][j].
+template <bool INVERSE>
+__device__ __forceinline__ void dense_load_matrix(const CodecArgs& a, uint32_t mat) {
+  for (int e = threadIdx.x; e < 128 * 128; e += blockDim.x) {
+    const int i = e >> 7, j = e & 127;  // M[i][j]
+    const int pj = a.use_perm ? a.perm[j] : j;
+    const uint32_t off = INVERSE ? (uint32_t)(pj * kDensePitch + 4 * i) : (uint32_t)(i * kDensePitch + 4 * pj);
+    lds_st(mat + off, a.rot_matrix[e]);
+  }
+}
+
+template <int DT, int BITS, int QUANT>
+__global__ void __launch_bounds__(64 * kDenseWaves) encode_dense_kernel(const CodecArgs a) {
+  constexpr int D = 128, LV = 4, CB = D * BITS / 8;
+  constexpr int ES = (DT == DT_F32) ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t s_dense[kDenseLds];
+  __shared__ double s_theta[D / 2];
+  const uint32_t mat = lds_addr(s_dense);
+  dense_load_matrix<false>(a, mat);
+  if (a.rope)
+    for (int i = threadIdx.x; i < D / 2; i += blockDim.x)
+      s_theta[i] = exp2(-(2.0 * (double)i / (double)D) * a.rope_log2_base);
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int q = lane >> 2, l = lane & 3, n16 = lane & 15, g = lane >> 4;
+  const uint32_t stage = mat + (uint32_t)((128 + 16 * wave) * kDensePitch);
+  const int64_t th = a.tokens * a.heads, n_vec = a.rows * th, n_items = (n_vec + 15) / 16;
+  const int LB = (QUANT == Q_MINMAX) ? a.group_log2 - 5 : 0;
+  const int64_t ngroups = (QUANT == Q_MINMAX) ? (D >> a.group_log2) : 0;
+  constexpr int NT = (1 << BITS) - 1;
+  float tau[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) tau[i] = (QUANT == Q_LLOYD) ? 0.5f * (a.codebook[i] + a.codebook[i + 1]) : 0.0f;
+  for (int64_t it = (int64_t)blockIdx.x * kDenseWaves + wave; it < n_items; it += (int64_t)gridDim.x * kDenseWaves) {
+    const int64_t vec0 = it * 16, nvalid = min((int64_t)16, n_vec - vec0);
+    const int64_t vec = min(vec0 + q, n_vec - 1);  // lanes past the end read the last vector; their stores drop
+    const int64_t r = vec / th, rem = vec - r * th, t = rem / a.heads, h = rem - t * a.heads;
+    RawRow<DT> raw;
+    load_row<DT>(raw, reinterpret_cast<const char*>(a.x) + (r * a.sr + t * a.st + h * a.sh + 32 * l) * ES);
+    float v[32];
+    widen_row<DT>(raw, v);
+    if (a.rope) {
+      const int64_t pos = a.pos_offset + t;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        float c, sn;
+        rope_cos_sin(pos, s_theta[16 * l + m], &c, &sn);
+        const float x0 = v[2 * m], x1 = v[2 * m + 1];
+        v[2 * m] = __builtin_fmaf(x0, c, -x1 * sn);
+        v[2 * m + 1] = __builtin_fmaf(x0, sn, x1 * c);
+      }
+    }
+    if constexpr (QUANT == Q_LLOYD) {
+      const float rho = norm_separate<LV>(v);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rho), make_buf_item(a.norm + vec0, (uint32_t)(4 * nvalid)),
+                                            4u * (uint32_t)q, 0, 0);
+    }
+    dense_rotate_lane(v, mat, stage, q, l, n16, g);
+    LaneCodes<BITS> cw;
+    if constexpr (QUANT == Q_MINMAX) {
+      uint32_t zb, sb;
+      minmax_codes_lane<BITS, false>(v, 1.0f, LB, zb, sb, cw);
+      const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
+      const uint32_t gbytes = (uint32_t)(2 * nvalid * ngroups);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sb, make_buf_item(a.scale + vec0 * ngroups, gbytes), go, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)zb, make_buf_item(a.zero + vec0 * ngroups, gbytes), go, 0, 0);
+    } else {
+      lloyd_codes_lane<BITS>(v, 1.0f, tau, cw);
+    }
+    store_lane_codes<BITS>(make_buf_item(a.codes + vec0 * CB, (uint32_t)(CB * nvalid)),
+                           (uint32_t)(q * CB + l * (4 * BITS)), cw);
+  }
+}
+
+template <int ODT, int BITS, int QUANT>
+__global__ void __launch_bounds__(64 * kDenseWaves) decode_dense_kernel(const CodecArgs a) {
+  constexpr int D = 128, CB = D * BITS / 8;
+  constexpr int OES = (ODT == DT_F32) ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t s_dense[kDenseLds];
+  __shared__ float s_cb[kMaxCodebook];
+  const uint32_t mat = lds_addr(s_dense);
+  dense_load_matrix<true>(a, mat);
+  if constexpr (QUANT == Q_LLOYD) {
+    if (threadIdx.x < (1 << BITS)) s_cb[threadIdx.x] = a.codebook[threadIdx.x];
+  }
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int q = lane >> 2, l = lane & 3, n16 = lane & 15, g = lane >> 4;
+  const uint32_t stage = mat + (uint32_t)((128 + 16 * wave) * kDensePitch);
+  const int64_t n_vec = a.rows * a.tokens * a.heads, n_items = (n_vec + 15) / 16;
+  const int LB = (QUANT == Q_MINMAX) ? a.group_log2 - 5 : 0;
+  const int64_t ngroups = (QUANT == Q_MINMAX) ? (D >> a.group_log2) : 0;
+  for (int64_t it = (int64_t)blockIdx.x * kDenseWaves + wave; it < n_items; it += (int64_t)gridDim.x * kDenseWaves) {
+    const int64_t vec0 = it * 16, nvalid = min((int64_t)16, n_vec - vec0);
+    LaneCodes<BITS> c;
+    load_lane_codes<BITS>(make_buf(a.codes + vec0 * CB, CB * nvalid), (uint32_t)(q * CB + l * (4 * BITS)), c);
+    float v[32];
+    if constexpr (QUANT == Q_MINMAX) {
+      const uint32_t go = 2u * (uint32_t)(q * ngroups + (l >> LB));
+      const int64_t gbytes = 2 * nvalid * ngroups;
+      const float sc = f16_value(__builtin_amdgcn_raw_buffer_load_b16(make_buf(a.scale + vec0 * ngroups, gbytes), go, 0, 0));
+      const float z = f16_value(__builtin_amdgcn_raw_buffer_load_b16(make_buf(a.zero + vec0 * ngroups, gbytes), go, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf((float)code_at<BITS>(c, i), sc, z);
+    } else {
+      // the norm scales the levels before the (linear) inverse rotation
+      const float rho = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(make_buf(a.norm + vec0, 4 * nvalid), 4u * (uint32_t)q, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = s_cb[code_at<BITS>(c, i)] * rho;
+    }
+    dense_rotate_lane(v, mat, stage, q, l, n16, g);
+    // the lane's 32 outputs of vector vec0 + q, channels 32 l ..: 64 or 128 contiguous bytes
+    const buf_t ob = make_buf_item(reinterpret_cast<char*>(a.y) + vec0 * D * OES, (uint32_t)(nvalid * D * OES));
+    const uint32_t off = (uint32_t)((q * D + 32 * l) * OES);
+    if constexpr (ODT == DT_F32) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                                                       __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])},
+                                               ob, off + 16u * k, 0, 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u32x4_t w;
+        if constexpr (ODT == DT_BF16) {
+          w = u32x4_t{pack_bf16x2(v[8 * k], v[8 * k + 1]), pack_bf16x2(v[8 * k + 2], v[8 * k + 3]),
+                      pack_bf16x2(v[8 * k + 4], v[8 * k + 5]), pack_bf16x2(v[8 * k + 6], v[8 * k + 7])};
+        } else {
+          w = u32x4_t{pack_f16x2(v[8 * k], v[8 * k + 1]), pack_f16x2(v[8 * k + 2], v[8 * k + 3]),
+                      pack_f16x2(v[8 * k + 4], v[8 * k + 5]), pack_f16x2(v[8 * k + 6], v[8 * k + 7])};
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(w, ob, off + 16u * k, 0, 0);
       }
     }
   }
@@ -3111,6 +3348,84 @@ int launch_attend_gen_d256_k3(int vb, int qg, const AttendArgs& a, void* s) { re
 #endif
 #if KVQ_UNIT == 19 || KVQ_UNIT == -1
 int launch_attend_gen_d256_k4(int vb, int qg, const AttendArgs& a, void* s) { return pick_attend_gen<256, 4>(vb, qg, a, s); }
+#endif
+
+#if KVQ_UNIT == 20 || KVQ_UNIT == 21 || KVQ_UNIT == -1
+namespace {
+// Grid of a dense-rotation pass: one block per CU (the matrix takes 132 KB of its LDS), fewer
+// when the tensor has fewer items than 8 per block; blocks stride over the items.
+inline unsigned dense_blocks(const CodecArgs& a) {
+  const int64_t n_items = (a.rows * a.tokens * a.heads + 15) / 16;
+  const int64_t nb = (n_items + kDenseWaves - 1) / kDenseWaves;
+  return (unsigned)(nb < 256 ? nb : 256);
+}
+}  // namespace
+#endif
+#if KVQ_UNIT == 20 || KVQ_UNIT == -1
+namespace {
+template <int DT, int BITS, int QUANT>
+int launch_enc_dense_t(const CodecArgs& a, hipStream_t s) {
+  const unsigned nb = dense_blocks(a);
+  if (nb == 0) return 0;
+  hipLaunchKernelGGL((encode_dense_kernel<DT, BITS, QUANT>), dim3(nb), dim3(64 * kDenseWaves), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  if (const unsigned ns = sink_blocks(a, Geo<128>::LV)) {
+    hipLaunchKernelGGL((encode_sink_kernel<DT, 128, BITS, QUANT>), dim3(ns), dim3(64 * kWavesPerBlock), 0, s, a);
+    return (int)hipGetLastError();
+  }
+  return 0;
+}
+template <int DT>
+int pick_enc_dense(int bits, int quant, const CodecArgs& a, hipStream_t s) {
+  if (quant == Q_MINMAX) {
+    if (bits == 2) return launch_enc_dense_t<DT, 2, Q_MINMAX>(a, s);
+    if (bits == 3) return launch_enc_dense_t<DT, 3, Q_MINMAX>(a, s);
+    return launch_enc_dense_t<DT, 4, Q_MINMAX>(a, s);
+  }
+  if (bits == 2) return launch_enc_dense_t<DT, 2, Q_LLOYD>(a, s);
+  if (bits == 3) return launch_enc_dense_t<DT, 3, Q_LLOYD>(a, s);
+  return launch_enc_dense_t<DT, 4, Q_LLOYD>(a, s);
+}
+}  // namespace
+int launch_encode_dense(int dtype, int bits, int quant, const CodecArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == DT_F16) return pick_enc_dense<DT_F16>(bits, quant, a, s);
+  if (dtype == DT_BF16) return pick_enc_dense<DT_BF16>(bits, quant, a, s);
+  return pick_enc_dense<DT_F32>(bits, quant, a, s);
+}
+#endif
+#if KVQ_UNIT == 21 || KVQ_UNIT == -1
+namespace {
+template <int ODT, int BITS, int QUANT>
+int launch_dec_dense_t(const CodecArgs& a, hipStream_t s) {
+  const unsigned nb = dense_blocks(a);
+  if (nb == 0) return 0;
+  hipLaunchKernelGGL((decode_dense_kernel<ODT, BITS, QUANT>), dim3(nb), dim3(64 * kDenseWaves), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  if (const unsigned ns = sink_blocks(a, Geo<128>::LV)) {
+    hipLaunchKernelGGL((decode_sink_kernel<ODT, 128>), dim3(ns), dim3(64 * kWavesPerBlock), 0, s, a);
+    return (int)hipGetLastError();
+  }
+  return 0;
+}
+template <int ODT>
+int pick_dec_dense(int bits, int quant, const CodecArgs& a, hipStream_t s) {
+  if (quant == Q_MINMAX) {
+    if (bits == 2) return launch_dec_dense_t<ODT, 2, Q_MINMAX>(a, s);
+    if (bits == 3) return launch_dec_dense_t<ODT, 3, Q_MINMAX>(a, s);
+    return launch_dec_dense_t<ODT, 4, Q_MINMAX>(a, s);
+  }
+  if (bits == 2) return launch_dec_dense_t<ODT, 2, Q_LLOYD>(a, s);
+  if (bits == 3) return launch_dec_dense_t<ODT, 3, Q_LLOYD>(a, s);
+  return launch_dec_dense_t<ODT, 4, Q_LLOYD>(a, s);
+}
+}  // namespace
+int launch_decode_dense(int out_dtype, int bits, int quant, const CodecArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (out_dtype == DT_F16) return pick_dec_dense<DT_F16>(bits, quant, a, s);
+  if (out_dtype == DT_BF16) return pick_dec_dense<DT_BF16>(bits, quant, a, s);
+  return pick_dec_dense<DT_F32>(bits, quant, a, s);
+}
 #endif
 
 #if KVQ_UNIT == 13 || KVQ_UNIT == -1

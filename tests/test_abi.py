@@ -357,3 +357,47 @@ def test_allocate_bits_host_matches_oracle():
         kvq.allocate_bits(np.ones(4), 17)
     with pytest.raises(kvq.KvqError):
         kvq.allocate_bits(np.array([1.0, -1.0]), 6)
+
+
+def test_rotor_matrix_host_matches_oracle():
+    """The host's block-diagonal matrix of the 3-D rotors applies the oracle's rotor rotation
+    (sandwich products per 3-channel block, the plane turn of a 2-channel tail, a 1-channel tail
+    left alone)."""
+    import workloads
+    from oracle import rotations
+    rng = np.random.default_rng(77)
+    for d in (128, 256):
+        rq, ta = workloads.rotor_quaternions(d, rng)
+        m = kvq.rotor_matrix(rq, d, ta)
+        u = rng.standard_normal((5, d))
+        want = rotations.rotor_rotate(u, rq.astype(np.float64), np.float64(np.float32(ta)))
+        assert np.allclose(u @ m.astype(np.float64).T, want, atol=2e-6), d
+        assert np.allclose(m.astype(np.float64) @ m.T.astype(np.float64), np.eye(d), atol=2e-6)
+    rq, ta = workloads.rotor_quaternions(128, rng)
+    for bad, status in ((dict(head_dim=64), 8), (dict(tail_angle=float("nan")), 6)):
+        kw = dict(head_dim=128, tail_angle=ta)
+        kw.update(bad)
+        with pytest.raises((kvq.KvqError, ValueError)) as e:
+            kvq.rotor_matrix(rq if kw["head_dim"] == 128 else rq[:21], kw["head_dim"], kw["tail_angle"])
+        if isinstance(e.value, kvq.KvqError):
+            assert e.value.status == status, bad
+    off = rq.copy()
+    off[3] *= 1.01
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.rotor_matrix(off, 128, ta)
+    assert e.value.status == 6
+
+
+def test_dense_rotation_refusals_on_the_host():
+    """The dense codec takes head_dim 128 without a dynamic codebook; append refuses it."""
+    lib = _lib_new_entry_points()
+    fake = 4096  # a pointer value the checks never dereference
+    for kw, status in ((dict(shape=(1, 4, 2, 256), group_size=32), 8),):
+        c = _cfg(rot="dense", **kw).c_struct()
+        c.rot_matrix = fake
+        pl = _planes()
+        assert lib.kvq_append(ctypes.byref(c), 4096, 4096, ctypes.byref(pl), None) == 8
+    c = _cfg(rot="dense").c_struct()
+    c.rot_matrix = fake
+    pl = _planes()
+    assert lib.kvq_append(ctypes.byref(c), 4096, 4096, ctypes.byref(pl), None) == 8

@@ -27,6 +27,8 @@ KVQ_STUB(launch_decode_f16_d128) KVQ_STUB(launch_decode_f16_d256) KVQ_STUB(launc
 KVQ_STUB(launch_decode_bf16_d256) KVQ_STUB(launch_decode_f32_d128) KVQ_STUB(launch_decode_f32_d256)
 const char* device_error_string(int) { return "host-only build: no device"; }
 int launch_attend(int, int, const AttendArgs&, void*) { return 98; }
+int launch_encode_dense(int, int, int, const CodecArgs&, void*) { return 98; }
+int launch_decode_dense(int, int, int, const CodecArgs&, void*) { return 98; }
 int launch_attend_gen_d128_k2(int, int, const AttendArgs&, void*) { return 98; }
 int launch_attend_gen_d128_k3(int, int, const AttendArgs&, void*) { return 98; }
 int launch_attend_gen_d128_k4(int, int, const AttendArgs&, void*) { return 98; }

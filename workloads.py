@@ -152,6 +152,22 @@ def permutation(head_dim: int, seed: int = SEED) -> np.ndarray:
     return np.random.default_rng(seed).permutation(head_dim).astype(np.uint16)
 
 
+def haar_orthogonal(d: int, rng: np.random.Generator) -> np.ndarray:
+    """[d, d] float32 orthogonal matrix drawn from the Haar measure: the Q factor of a d x d
+    standard normal matrix with the signs of R's diagonal moved into Q (a random draw the
+    dense-rotation baseline takes as its input)."""
+    g = rng.standard_normal((d, d))
+    qm, rm = np.linalg.qr(g)
+    return (qm * np.sign(np.diag(rm))[None, :]).astype(np.float32)
+
+
+def rotor_quaternions(d: int, rng: np.random.Generator):
+    """(rq [d // 3][4] float32 unit quaternions, tail angle) for the 3-D rotor baseline."""
+    g = rng.standard_normal((d // 3, 4))
+    rq = (g / np.linalg.norm(g, axis=1, keepdims=True)).astype(np.float32)
+    return rq, float(rng.uniform(-np.pi, np.pi))
+
+
 def unit_quaternions(n_blocks: int, rng: np.random.Generator) -> np.ndarray:
     """[n_blocks][2][4] float32: (qL, qR) per 4-D block, each (w, x, y, z) of unit norm.
 
