@@ -72,6 +72,14 @@ def parse_args():
                     help="skip the per-launch timings of the wide-head, Llama-2 layer, tiny and IsoQuant workloads")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain device copy of known size (for counter calibration)")
+    ap.add_argument("--only-other-configs", action="store_true",
+                    help="run only the other workloads' timings (wide-head cache with its attention, Llama-2 layer, "
+                         "tiny, IsoQuant, dynamic codebook, baseline rotations) and print them as one JSON line; "
+                         "for profiling those launches")
+    ap.add_argument("--other-keys", default=",".join(OTHER_CONFIGS),
+                    help="with --only-other-configs: the workloads to time (comma-separated)")
+    ap.add_argument("--no-other-reports", action="store_true",
+                    help="with --only-other-configs: skip the dynamic-codebook and baseline-rotation reports")
     return ap.parse_args()
 
 
@@ -210,7 +218,7 @@ REGIME = {"widehead": "hbm", "llama2": "cache-resident (76.5 MB per direction fi
           "tiny": "launch-bound (0.66 MB per direction)", "isoquant": "launch-bound (4.6 MB per direction)"}
 
 
-def time_other_configs(kvq, workloads, dev, stream):
+def time_other_configs(kvq, workloads, dev, stream, keys=None):
     """Per-launch times of the other workloads: encode, and decode to the input dtype, of each
     tensor; the wide-head cache at full size (drawn on the GPU), the others from the host."""
     import numpy as np
@@ -219,7 +227,7 @@ def time_other_configs(kvq, workloads, dev, stream):
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     res = {}
     kept = {}
-    for key in OTHER_CONFIGS:
+    for key in (keys if keys is not None else OTHER_CONFIGS):
         wl = workloads.WORKLOADS[key]
         if wl.device_generated:
             data = workloads.device_workload(key, device=dev)
@@ -484,6 +492,21 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.only_other_configs:
+        stream = torch.cuda.Stream(device=dev)  # default priority
+        keys = [k for k in args.other_keys.split(",") if k]
+        others = time_other_configs(kvq, workloads, dev, stream, keys=keys)
+        if not args.no_other_reports:
+            others["dynamic_codebook"] = dynamic_codebook_report(kvq, workloads, dev, stream)
+            others["baseline_rotations"] = baseline_rotations_report(kvq, workloads, dev, stream)
+        if args.calib_copy:
+            a = torch.empty(1 << 33, dtype=torch.uint8, device=dev)
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+            del a, b
+        print(json.dumps({"other_configs": others}), flush=True)
+        return
     wl = workloads.WORKLOADS[WORKLOAD]
     t0 = time.time()
     data = workloads.device_workload(WORKLOAD, device=dev)
@@ -623,7 +646,9 @@ def main():
     oa = torch.empty_like(qa)
     wsa = torch.empty(kvq.attend_workspace_size(cfgs["K"], q_heads), dtype=torch.uint8, device=dev)
     with torch.cuda.stream(stream):
-        for _ in range(10):
+        # after a pause the GPU needs about 20 ms of this load to reach its steady clock (measured:
+        # 0.59 ms for the first call after 2 s idle, 0.47 ms from about the 40th call on)
+        for _ in range(60):
             kvq.attend(qa, planes["K"], cfgs["K"], planes["V"], cfgs["V"], out=oa, workspace=wsa, stream=stream)
         stream.synchronize()
         a = torch.cuda.Event(enable_timing=True)
