@@ -610,7 +610,23 @@ def main():
         b.record(stream)
         stream.synchronize()
     copy_gbps = 2 * half * 3 / (a.elapsed_time(b) * 1e-3) / 1e9
-    del dst
+    # and torch's own write-only (fill) and read-only (sum) kernels over 8 GiB: what plain
+    # streaming kernels reach on this GPU, next to the 8 TB/s of the data sheet
+    big = torch.empty(data["inputs"]["K"].numel(), dtype=torch.bfloat16, device=dev)  # 8 GiB of its own
+    ceil = {}
+    with torch.cuda.stream(stream):
+        for name, fn in (("write_fill", lambda: big.fill_(0.5)), ("read_sum", lambda: big.sum(dtype=torch.float32))):
+            fn()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(3):
+                fn()
+            b.record(stream)
+            stream.synchronize()
+            ceil[name + "_GBps"] = round(big.numel() * big.element_size() * 3 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    ceil["copy_GBps"] = round(copy_gbps, 1)
+    del dst, big
 
     # context, outside the timed region: one decode step's cache update -- every row's new K
     # and V token (its first token's values, here) appended at a random position of the
@@ -765,6 +781,7 @@ def main():
         "compression_ratio": round(in_bytes["K"] / (pl_bytes["K"] - sink_bytes["K"]), 3),
         "kernels": kern,
         "copy_GBps_same_bytes": round(copy_gbps, 1),
+        "hbm_streaming_kernels": ceil,
         "attend": {"ms_per_step": round(attend_ms, 4), "rows": r0, "slots": t0_, "kv_heads": h0, "q_heads": q_heads,
                    "encoded_cache_bytes": attend_bytes,
                    "GBps": round(attend_bytes / (attend_ms * 1e-3) / 1e9, 1),

@@ -1109,14 +1109,21 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   extern __shared__ float s_stage[];
   __shared__ float s_mat[ROT == ROT_SO4 ? (D / 4) * 16 : 1];
   __shared__ float s_cb[kMaxCodebook];
+  // permutation: byte offset of channel perm[j] in a staging row (output type), for the scatter
+  __shared__ __attribute__((aligned(16))) uint16_t s_soff[PERM_ANY ? D : 8];
   // dynamic codebook: the wide codebook, each rotated channel's scale and wide-channel rank
   __shared__ float s_cbw[QUANT == Q_LLOYD ? 2 * kMaxCodebook : 1];
   __shared__ float s_csc[QUANT == Q_LLOYD ? D : 1];
   __shared__ uint8_t s_rank[QUANT == Q_LLOYD ? D : 1];
 
   const int tid = threadIdx.x;
+  constexpr int OES = (ODT == DT_F32) ? 4 : 2;
   if constexpr (ROT == ROT_SO4) {
     for (int b = tid; b < D / 4; b += blockDim.x) build_so4(&a.quat[8 * b], &s_mat[16 * b]);
+  }
+  if constexpr (PERM_ANY) {
+    if (PERM)
+      for (int j = tid; j < D; j += blockDim.x) s_soff[j] = (uint16_t)(OES * (uint32_t)a.perm[j]);
   }
   if constexpr (QUANT == Q_LLOYD) {
     if (tid < (1 << BITS)) s_cb[tid] = a.codebook[tid];
@@ -1140,7 +1147,6 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   const int q = lane / LV, l = lane % LV;
   const int64_t ncols = a.tokens * a.heads;
   constexpr int CB = D * BITS / 8;
-  constexpr int OES = (ODT == DT_F32) ? 4 : 2;
   const float norm_c = (ROT == ROT_FWHT) ? (float)(1.0 / __builtin_sqrt((double)D)) : 1.0f;
   const float sgn = (ROT == ROT_FWHT) ? lane_sign(l) : 1.0f;
   const int gb = a.group_log2;
@@ -1155,8 +1161,17 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   uint32_t saddr[PERM_ANY ? 32 : 1];
   if constexpr (PERM_ANY) {
     if (PERM) {
+      // the lane's 32 offsets (64 bytes of the block's table), two per word
 #pragma unroll
-      for (int i = 0; i < 32; ++i) saddr[i] = row_addr + (uint32_t)OES * (uint32_t)a.perm[32 * l + i];
+      for (int k = 0; k < 4; ++k) {
+        const u32x4_t w = lds_ld4(lds_addr(s_soff) + 64u * l + 16u * k);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          saddr[8 * k + 2 * e] = row_addr + (ws[e] & 0xffffu);
+          saddr[8 * k + 2 * e + 1] = row_addr + (ws[e] >> 16);
+        }
+      }
     }
   }
 
@@ -3099,7 +3114,7 @@ int launch_dec_t(const CodecArgs& a, hipStream_t s) {
   // tasks of 4 consecutive tiles of a row (a 16 KiB output run per wave at d = 128, bf16),
   // 8 with the permutation (whose scatter addresses each wave sets up once): the fastest
   // measured on MI355X at the Llama-3 cache shape
-  if (int e = plan_grid(b, true, PT != 0 ? 8 : 4, nb)) return e;
+  if (int e = plan_grid(b, true, PT != 0 ? 8 : 1, nb)) return e;
   hipLaunchKernelGGL((decode_kernel<ODT, D, BITS, ROT, QUANT, PT>), dim3(nb), dim3(64 * kWavesPerBlock), lds, s,
                      b);
   if (hipError_t e = hipGetLastError()) return (int)e;
