@@ -406,6 +406,7 @@ def baseline_rotations_report(kvq, workloads, dev, stream, n_big=1 << 21):
     cb = kvq.lloyd_max_gaussian(3, 1.0 / np.sqrt(d))
     kinds = {"so4 (IsoQuant)": dict(rot="so4", quat=h["quat"]), "fwht": dict(rot="fwht"),
              "dense (TurboQuant)": dict(rot="dense", rot_matrix=haar),
+             "rotor (RotorQuant)": dict(rot="rotor", rotor_quat=rq, rotor_tail=ta),
              "rotor (RotorQuant, as its block-diagonal matrix)": dict(rot="dense", rot_matrix=rotor)}
     lw = workloads.WORKLOADS["llama2"]
     lk = lw.case("K")

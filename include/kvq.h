@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 
 typedef enum kvq_status {
   KVQ_OK = 0,
@@ -68,7 +68,7 @@ typedef enum kvq_status {
 
 /* Element types (enum values are stored as int32_t in the structs below). */
 typedef enum kvq_dtype { KVQ_F16 = 0, KVQ_BF16 = 1, KVQ_F32 = 2 } kvq_dtype;
-typedef enum kvq_rot { KVQ_ROT_NONE = 0, KVQ_ROT_FWHT = 1, KVQ_ROT_SO4 = 2, KVQ_ROT_DENSE = 3 } kvq_rot;
+typedef enum kvq_rot { KVQ_ROT_NONE = 0, KVQ_ROT_FWHT = 1, KVQ_ROT_SO4 = 2, KVQ_ROT_DENSE = 3, KVQ_ROT_ROTOR = 4 } kvq_rot;
 typedef enum kvq_quant { KVQ_Q_MINMAX = 0, KVQ_Q_LLOYD = 1 } kvq_quant;
 
 typedef struct kvq_config {
@@ -109,6 +109,12 @@ typedef struct kvq_config {
    * 3-D rotors as a block-diagonal matrix (RotorQuant, kvq_rotor_matrix).  Codec (encode,
    * decode): head_dim 128, no dynamic codebook; not in append or attention. */
   const float* rot_matrix;
+  /* KVQ_ROT_ROTOR: RotorQuant's 3-D rotors (IsoQuant page, section 1), computed as rotors:
+   * channels 3b .. 3b + 2 (b < D / 3) turn by the sandwich product rotor_quat[b] (0, v)
+   * rotor_quat[b]* (section 2.1); a 2-channel tail (D mod 3 = 2) turns in its plane by
+   * rotor_tail radians; a 1-channel tail stays.  Codec (encode, decode) only. */
+  const float* rotor_quat;  /* HOST [D/3][4] (w, x, y, z), unit norm within 1e-4             */
+  double rotor_tail;        /* finite                                                       */
 } kvq_config;
 
 /* Packed planes, all DEVICE pointers, 16-byte aligned, contiguous, row-major:

@@ -32,9 +32,9 @@ __all__ = ["Config", "KvqError", "encode", "append", "attend", "attend_noalloc",
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
-ROTATIONS = {"none": 0, "fwht": 1, "so4": 2, "dense": 3}
+ROTATIONS = {"none": 0, "fwht": 1, "so4": 2, "dense": 3, "rotor": 4}
 QUANTIZERS = {"minmax": 0, "lloyd": 1}
 EXPORTED_SYMBOLS = ("kvq_abi_version", "kvq_validate", "kvq_packed_sizes", "kvq_encode", "kvq_append",
                     "kvq_attend_workspace_size", "kvq_attend", "kvq_attend_noalloc", "kvq_attend_noalloc_max_workspace",
@@ -70,6 +70,8 @@ class _Config(ctypes.Structure):
         ("chan_wide", ctypes.c_void_p),
         ("codebook_wide", ctypes.c_void_p),
         ("rot_matrix", ctypes.c_void_p),
+        ("rotor_quat", ctypes.c_void_p),
+        ("rotor_tail", ctypes.c_double),
     ]
 
 
@@ -192,6 +194,8 @@ class Config:
     chan_wide: Optional[np.ndarray] = None      # dynamic codebook: 0/1, D/16 ones
     codebook_wide: Optional[np.ndarray] = None  # dynamic codebook: 2^(bits+1) levels
     rot_matrix: Optional[object] = None         # dense rotation: float32 device tensor [D, D]
+    rotor_quat: Optional[np.ndarray] = None     # rotor rotation: [D // 3, 4] unit quaternions
+    rotor_tail: float = 0.0                     # rotor rotation: the 2-channel tail's angle
     strides: Optional[Sequence[int]] = None  # (stride_r, stride_t, stride_h) in elements
     _keep: list = field(default_factory=list, repr=False)
 
@@ -214,7 +218,8 @@ class Config:
         self._keep = []
         for name, arr, dt in (("perm", self.perm, np.uint16), ("quat", self.quat, np.float32),
                               ("codebook", self.codebook, np.float32), ("chan_scale", self.chan_scale, np.float32),
-                              ("chan_wide", self.chan_wide, np.uint8), ("codebook_wide", self.codebook_wide, np.float32)):
+                              ("chan_wide", self.chan_wide, np.uint8), ("codebook_wide", self.codebook_wide, np.float32),
+                              ("rotor_quat", self.rotor_quat, np.float32)):
             if arr is None:
                 setattr(c, name, None)
             else:
@@ -222,6 +227,7 @@ class Config:
                 self._keep.append(a)
                 setattr(c, name, a.ctypes.data)
         c.rot_matrix = None if self.rot_matrix is None else int(self.rot_matrix.data_ptr())
+        c.rotor_tail = float(self.rotor_tail)
         return c
 
 

@@ -64,7 +64,7 @@ kvq_status check_config(const kvq_config* cfg, Derived* dv) {
   if (cfg->abi_version != KVQ_ABI_VERSION)
     return fail(KVQ_ERR_ABI, "abi_version %d, library is %d", cfg->abi_version, KVQ_ABI_VERSION);
   if (cfg->dtype < KVQ_F16 || cfg->dtype > KVQ_F32) return fail(KVQ_ERR_ROT, "unknown dtype %d", cfg->dtype);
-  if (cfg->rot < KVQ_ROT_NONE || cfg->rot > KVQ_ROT_DENSE) return fail(KVQ_ERR_ROT, "unknown rotation %d", cfg->rot);
+  if (cfg->rot < KVQ_ROT_NONE || cfg->rot > KVQ_ROT_ROTOR) return fail(KVQ_ERR_ROT, "unknown rotation %d", cfg->rot);
   if (cfg->quant < KVQ_Q_MINMAX || cfg->quant > KVQ_Q_LLOYD)
     return fail(KVQ_ERR_ROT, "unknown quantizer %d", cfg->quant);
   if (cfg->rows < 0 || cfg->tokens < 0 || cfg->heads < 0 || cfg->head_dim < 0)
@@ -141,6 +141,19 @@ kvq_status check_config(const kvq_config* cfg, Derived* dv) {
         }
         if (fabs(sqrt(s) - 1.0) > 1e-4) return fail(KVQ_ERR_PARAM, "quaternion %lld is not unit", (long long)b);
       }
+  }
+  if (cfg->rot == KVQ_ROT_ROTOR) {
+    if (!cfg->rotor_quat) return fail(KVQ_ERR_NULL, "rotor_quat is required for the rotor rotation");
+    for (int64_t b = 0; b < d / 3; ++b) {
+      const float* q = cfg->rotor_quat + 4 * b;
+      double s = 0.0;
+      for (int i = 0; i < 4; ++i) {
+        if (!isfinite(q[i])) return fail(KVQ_ERR_PARAM, "rotor %lld is not finite", (long long)b);
+        s += (double)q[i] * q[i];
+      }
+      if (fabs(sqrt(s) - 1.0) > 1e-4) return fail(KVQ_ERR_PARAM, "rotor %lld is not unit", (long long)b);
+    }
+    if (!isfinite(cfg->rotor_tail)) return fail(KVQ_ERR_PARAM, "rotor_tail must be finite");
   }
   if (cfg->quant == KVQ_Q_LLOYD) {
     if (!cfg->codebook) return fail(KVQ_ERR_NULL, "codebook is required for Lloyd-Max");
@@ -249,6 +262,13 @@ void fill_args(const kvq_config* cfg, const Derived& dv, kvq::CodecArgs* a) {
   if (cfg->perm)
     for (int64_t i = 0; i < cfg->head_dim; ++i) a->perm[i] = (uint8_t)cfg->perm[i];
   if (cfg->rot == KVQ_ROT_SO4) memcpy(a->quat, cfg->quat, sizeof(float) * cfg->head_dim / 4 * 8);
+  if (cfg->rot == KVQ_ROT_ROTOR) {
+    // the kernels' rotor parameters: rotor b at quat[4 b], then the tail's (cos, sin)
+    const int64_t nb = cfg->head_dim / 3;
+    memcpy(a->quat, cfg->rotor_quat, sizeof(float) * 4 * nb);
+    a->quat[4 * nb] = (float)cos(cfg->rotor_tail);
+    a->quat[4 * nb + 1] = (float)sin(cfg->rotor_tail);
+  }
   if (cfg->quant == KVQ_Q_LLOYD) memcpy(a->codebook, cfg->codebook, sizeof(float) * (1 << cfg->bits));
   if (dv.extra_bytes) {
     a->dyn = 1;
@@ -341,7 +361,8 @@ kvq_status kvq_append(const kvq_config* cfg, const void* x, const int64_t* posit
   Derived dv;
   kvq_status st = check_config(cfg, &dv);  // cfg describes the cache: tokens = slots per row
   if (st != KVQ_OK) return st;
-  if (cfg->rot == KVQ_ROT_DENSE) return fail(KVQ_ERR_UNSUPPORTED, "dense rotation: no append (encode the batch)");
+  if (cfg->rot == KVQ_ROT_DENSE || cfg->rot == KVQ_ROT_ROTOR)
+    return fail(KVQ_ERR_UNSUPPORTED, "dense and rotor rotations: no append (encode the batch)");
   if (!cache) return fail(KVQ_ERR_NULL, "cache planes is NULL");
   if (dv.n_vec == 0) return ok();
   if ((st = check_planes(cfg, dv, cache)) != KVQ_OK) return st;
@@ -657,6 +678,7 @@ kvq_status kvq_rotated_moments(const kvq_config* cfg, const void* x, double* mom
   kvq_status st = check_config(cfg, &dv);
   if (st != KVQ_OK) return st;
   if (cfg->quant != KVQ_Q_LLOYD) return fail(KVQ_ERR_PARAM, "rotated moments belong to the Lloyd-Max path (quant)");
+  if (cfg->rot == KVQ_ROT_ROTOR) return fail(KVQ_ERR_UNSUPPORTED, "rotated moments: no rotor rotation");
   if (!moments) return fail(KVQ_ERR_NULL, "moments is NULL");
   if (reinterpret_cast<uintptr_t>(moments) & 7u) return fail(KVQ_ERR_ALIGN, "moments not 8-byte aligned");
   kvq::CalibArgs a;

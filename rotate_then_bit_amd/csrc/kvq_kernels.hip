@@ -39,7 +39,7 @@ namespace kvq {
 namespace {
 
 enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
-enum { ROT_NONE = 0, ROT_FWHT = 1, ROT_SO4 = 2, ROT_DENSE = 3 };
+enum { ROT_NONE = 0, ROT_FWHT = 1, ROT_SO4 = 2, ROT_DENSE = 3, ROT_ROTOR = 4 };
 enum { Q_MINMAX = 0, Q_LLOYD = 1 };
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -722,6 +722,88 @@ __device__ __forceinline__ void lloyd_codes_lane(const float* v, float A, const 
 }
 
 // ---------------------------------------------------------------------------
+// RotorQuant's 3-D rotors (the baseline of the IsoQuant page, section 1)
+// ---------------------------------------------------------------------------
+// Block b (channels 3b .. 3b + 2, b < D / 3) turns by the rotor of unit quaternion r_b, the
+// sandwich product r (0, v) r*, as its 3x3 matrix; a 2-channel tail turns by (cos t, sin t); a
+// 1-channel tail stays.  Table in LDS: 12 floats per block (rows of 3, each padded to 4), then
+// the tail's (cos t, sin t).  Built from CodecArgs.quat: r_b at quat[4 b], then (cos t, sin t).
+template <int D>
+__device__ void build_rotor_table(const float* rq, float* tab) {
+  constexpr int NB = D / 3;
+  for (int b = threadIdx.x; b <= NB; b += blockDim.x) {
+    float* m = tab + 12 * b;
+    if (b == NB) {
+      m[0] = rq[4 * NB];
+      m[1] = rq[4 * NB + 1];
+      continue;
+    }
+    const float w = rq[4 * b], x = rq[4 * b + 1], y = rq[4 * b + 2], z = rq[4 * b + 3];
+    // homogeneous form: equals r (0, v) r* for any r (|r|^2 times the rotation)
+    m[0] = w * w + x * x - y * y - z * z; m[1] = 2.0f * (x * y - w * z); m[2] = 2.0f * (x * z + w * y); m[3] = 0.0f;
+    m[4] = 2.0f * (x * y + w * z); m[5] = w * w - x * x + y * y - z * z; m[6] = 2.0f * (y * z - w * x); m[7] = 0.0f;
+    m[8] = 2.0f * (x * z - w * y); m[9] = 2.0f * (y * z + w * x); m[10] = w * w - x * x - y * y + z * z; m[11] = 0.0f;
+  }
+}
+
+// The rotation (INV: its inverse, the transposed blocks and the tail turned back) of a vector
+// held as 32 values per lane (lane l: channels 32 l ..), through the vector's LDS row of
+// contiguous floats: lane l turns blocks 11 l .. 11 l + 10 (channels 33 l ..) in place, one
+// block at a time (each lane reads and writes only its own channels there), the last lane also
+// the tail; then every lane reads its 32 channels back.  3-D blocks do not align with the
+// lanes' 32 channels, hence the row.
+template <int D, bool INV>
+__device__ __forceinline__ void rotor_lane(float* v, uint32_t row, int l, uint32_t tab) {
+  constexpr int LV = D / 32, NB = D / 3, TAIL = D % 3;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    lds_st4(row + 128u * l + 16u * k, u32x4_t{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                                             __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])});
+  wave_lds_sync();
+  const int nblk = min(11, NB - 11 * l);  // the lane's whole blocks
+  const uint32_t span = row + 132u * (uint32_t)l;
+  const uint32_t mtab = tab + 528u * (uint32_t)l;  // block 11 l
+#pragma unroll 1
+  for (int j = 0; j < nblk; ++j) {
+    const uint32_t p = span + 12u * (uint32_t)j, m = mtab + 48u * (uint32_t)j;
+    const float a0 = lds_ld(p), a1 = lds_ld(p + 4u), a2 = lds_ld(p + 8u);
+    const u32x4_t r0 = lds_ld4(m), r1 = lds_ld4(m + 16u), r2 = lds_ld4(m + 32u);
+    float z0, z1, z2;
+    if constexpr (!INV) {
+      z0 = __builtin_fmaf(__uint_as_float(r0.x), a0, __builtin_fmaf(__uint_as_float(r0.y), a1, __uint_as_float(r0.z) * a2));
+      z1 = __builtin_fmaf(__uint_as_float(r1.x), a0, __builtin_fmaf(__uint_as_float(r1.y), a1, __uint_as_float(r1.z) * a2));
+      z2 = __builtin_fmaf(__uint_as_float(r2.x), a0, __builtin_fmaf(__uint_as_float(r2.y), a1, __uint_as_float(r2.z) * a2));
+    } else {
+      z0 = __builtin_fmaf(__uint_as_float(r0.x), a0, __builtin_fmaf(__uint_as_float(r1.x), a1, __uint_as_float(r2.x) * a2));
+      z1 = __builtin_fmaf(__uint_as_float(r0.y), a0, __builtin_fmaf(__uint_as_float(r1.y), a1, __uint_as_float(r2.y) * a2));
+      z2 = __builtin_fmaf(__uint_as_float(r0.z), a0, __builtin_fmaf(__uint_as_float(r1.z), a1, __uint_as_float(r2.z) * a2));
+    }
+    lds_st(p, z0);
+    lds_st(p + 4u, z1);
+    lds_st(p + 8u, z2);
+  }
+  if constexpr (TAIL == 2) {
+    if (l == LV - 1) {
+      const uint32_t p = row + 4u * (3 * NB);
+      const float c = lds_ld(tab + 48u * NB), sn = INV ? -lds_ld(tab + 48u * NB + 4u) : lds_ld(tab + 48u * NB + 4u);
+      const float a0 = lds_ld(p), a1 = lds_ld(p + 4u);
+      lds_st(p, __builtin_fmaf(c, a0, -sn * a1));
+      lds_st(p + 4u, __builtin_fmaf(sn, a0, c * a1));
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4_t w = lds_ld4(row + 128u * l + 16u * k);
+    v[4 * k] = __uint_as_float(w.x);
+    v[4 * k + 1] = __uint_as_float(w.y);
+    v[4 * k + 2] = __uint_as_float(w.z);
+    v[4 * k + 3] = __uint_as_float(w.w);
+  }
+  wave_lds_sync();  // the row is free again
+}
+
+// ---------------------------------------------------------------------------
 // ENCODE
 // ---------------------------------------------------------------------------
 // RT / PT: RoPE / permutation off (0), on (1) or read from the arguments (-1).
@@ -739,6 +821,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   extern __shared__ float s_stage[];
   __shared__ double s_theta[ROPE_ANY ? D / 2 : 1];
   __shared__ float s_mat[ROT == ROT_SO4 ? (D / 4) * 16 : 1];
+  __shared__ __attribute__((aligned(16))) float s_rtab[ROT == ROT_ROTOR ? (D / 3 + 1) * 12 : 4];
   __shared__ __attribute__((aligned(16))) uint16_t s_goff[PERM_ANY ? D : 8];
   // dynamic codebook: 1 / scale and the wide-channel rank of each rotated channel
   __shared__ float s_cinv[QUANT == Q_LLOYD ? D : 1];
@@ -768,6 +851,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   if constexpr (ROT == ROT_SO4) {
     for (int b = tid; b < D / 4; b += blockDim.x) build_so4(&a.quat[8 * b], &s_mat[16 * b]);
   }
+  if constexpr (ROT == ROT_ROTOR) build_rotor_table<D>(a.quat, s_rtab);
   // block-shared parameters ready; the barrier also starts the block's four waves (adjacent
   // tiles) together, which measured about 2 % faster even where there are no parameters
   __syncthreads();
@@ -788,9 +872,11 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
   constexpr bool FUSED = (DT != DT_F32) && RT == 0 && PT == 0 && (QUANT == Q_MINMAX) && (ROT == ROT_FWHT);
 
   // per-wave staging: permutation rows, then the RoPE table
+  // (the rotor also stages each vector, in the permutation rows)
+  const bool STAGE = PERM || ROT == ROT_ROTOR;
   const uint32_t wave_addr =
-      lds_addr(s_stage) + (uint32_t)(wave * enc_wave_bytes<D>(PERM, ROPE, a.trig_rows));
-  const uint32_t trig_addr = wave_addr + enc_perm_bytes<D>(PERM);
+      lds_addr(s_stage) + (uint32_t)(wave * enc_wave_bytes<D>(STAGE, ROPE, a.trig_rows));
+  const uint32_t trig_addr = wave_addr + enc_perm_bytes<D>(STAGE);
   // permutation: this vector's LDS row and the lane's 32 gather addresses
   const uint32_t row_addr = wave_addr + (uint32_t)(q * enc_row<D>());
   uint32_t gaddr[PERM_ANY ? 32 : 1];
@@ -979,6 +1065,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) encode_kernel(const Codec
     }
     if constexpr (ROT == ROT_FWHT) {
       fwht_lane<LV, FUSED ? 2 : 0>(v, m1, m2, m4);
+    } else if constexpr (ROT == ROT_ROTOR) {
+      rotor_lane<D, false>(v, row_addr, l, lds_addr(s_rtab));
     } else if constexpr (ROT == ROT_SO4) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
@@ -1111,6 +1199,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   __shared__ float s_cb[kMaxCodebook];
   // permutation: byte offset of channel perm[j] in a staging row (output type), for the scatter
   __shared__ __attribute__((aligned(16))) uint16_t s_soff[PERM_ANY ? D : 8];
+  __shared__ __attribute__((aligned(16))) float s_rtab[ROT == ROT_ROTOR ? (D / 3 + 1) * 12 : 4];
   // dynamic codebook: the wide codebook, each rotated channel's scale and wide-channel rank
   __shared__ float s_cbw[QUANT == Q_LLOYD ? 2 * kMaxCodebook : 1];
   __shared__ float s_csc[QUANT == Q_LLOYD ? D : 1];
@@ -1125,6 +1214,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
     if (PERM)
       for (int j = tid; j < D; j += blockDim.x) s_soff[j] = (uint16_t)(OES * (uint32_t)a.perm[j]);
   }
+  if constexpr (ROT == ROT_ROTOR) build_rotor_table<D>(a.quat, s_rtab);
   if constexpr (QUANT == Q_LLOYD) {
     if (tid < (1 << BITS)) s_cb[tid] = a.codebook[tid];
     if (a.dyn) {
@@ -1156,7 +1246,10 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
   // staging rows: vector q's row; in the permuted case the lane scatters its 32 floats
   // to out[perm[j]], otherwise it writes its 32 outputs (in the output type) in order
   constexpr int ROWB = dec_row_bytes<D, ODT>();
-  const uint32_t wave_addr = lds_addr(s_stage) + (uint32_t)(wave * Geo<D>::VPW * ROWB);
+  // the rotor's float rows follow the wave's output rows
+  constexpr int RROW = D * 4 + 16, RBYTES = (ROT == ROT_ROTOR) ? Geo<D>::VPW * RROW : 0;
+  const uint32_t wave_addr = lds_addr(s_stage) + (uint32_t)(wave * (Geo<D>::VPW * ROWB + RBYTES));
+  const uint32_t rrow_addr = wave_addr + (uint32_t)(Geo<D>::VPW * ROWB + q * RROW);
   const uint32_t row_addr = wave_addr + (uint32_t)(q * ROWB);
   uint32_t saddr[PERM_ANY ? 32 : 1];
   if constexpr (PERM_ANY) {
@@ -1301,6 +1394,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(const Codec
         const float m1 = (l & 1) ? -1.0f : 1.0f, m2 = (l & 2) ? -1.0f : 1.0f, m4 = (l & 4) ? -1.0f : 1.0f;
         fwht_lane<LV>(v, m1, m2, m4);
         outscale = sgn * norm_c;
+      } else if constexpr (ROT == ROT_ROTOR) {
+        rotor_lane<D, true>(v, rrow_addr, l, lds_addr(s_rtab));
       } else if constexpr (ROT == ROT_SO4) {
         // inverse: M^T z (M orthogonal for unit quaternions)
 #pragma unroll
@@ -3091,7 +3186,8 @@ int launch_enc_t(const CodecArgs& a, hipStream_t s) {
   // Rows per task, the fastest measured on MI355X at the Llama-3 cache shape: with RoPE a
   // wave's cos/sin table serves 8 rows; with only a permutation its gather addresses
   // serve 2; otherwise one item per wave.
-  const size_t lds = (size_t)kWavesPerBlock * enc_wave_bytes<D>(a.use_perm != 0, a.rope != 0, b.trig_rows);
+  const size_t lds =
+      (size_t)kWavesPerBlock * enc_wave_bytes<D>(a.use_perm != 0 || ROT == ROT_ROTOR, a.rope != 0, b.trig_rows);
   unsigned nb = 0;
   if (int e = plan_grid(b, false, AP ? 1 : (a.rope ? 8 : (a.use_perm ? 2 : 1)), nb)) return e;
   hipLaunchKernelGGL((encode_kernel<DT, D, BITS, ROT, QUANT, RT, PT, GBT, AP>), dim3(nb), dim3(64 * kWavesPerBlock),
@@ -3108,7 +3204,8 @@ int launch_enc_t(const CodecArgs& a, hipStream_t s) {
 template <int ODT, int D, int BITS, int ROT, int QUANT, int PT>
 int launch_dec_t(const CodecArgs& a, hipStream_t s) {
   if (a.n_items == 0) return 0;
-  const size_t lds = (size_t)kWavesPerBlock * Geo<D>::VPW * dec_row_bytes<D, ODT>();
+  const size_t lds = (size_t)kWavesPerBlock * Geo<D>::VPW *
+                     (dec_row_bytes<D, ODT>() + (ROT == ROT_ROTOR ? D * 4 + 16 : 0));
   CodecArgs b = a;
   unsigned nb = 0;
   // one tile per wave (a 4 KiB output run at d = 128, bf16; measured 10 % faster than 4 tiles
@@ -3177,6 +3274,7 @@ int pick_rot(int rot, int quant, const CodecArgs& a, hipStream_t s) {
   switch (rot) {
     case ROT_NONE: return pick_quant<ENC, DT, D, BITS, ROT_NONE>(quant, a, s);
     case ROT_FWHT: return pick_quant<ENC, DT, D, BITS, ROT_FWHT>(quant, a, s);
+    case ROT_ROTOR: return pick_quant<ENC, DT, D, BITS, ROT_ROTOR>(quant, a, s);
     default: return pick_quant<ENC, DT, D, BITS, ROT_SO4>(quant, a, s);
   }
 }

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(kvq.library_path())
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert kvq.abi_version() == kvq.ABI_VERSION == 3
+    assert kvq.abi_version() == kvq.ABI_VERSION == 4
 
 
 def _cfg(**kw):
@@ -401,3 +401,26 @@ def test_dense_rotation_refusals_on_the_host():
     c.rot_matrix = fake
     pl = _planes()
     assert lib.kvq_append(ctypes.byref(c), 4096, 4096, ctypes.byref(pl), None) == 8
+
+
+def test_rotor_config_checks_on_the_host():
+    """The rotor rotation needs its unit quaternions and a finite tail angle; append, attention
+    and the rotated moments refuse it."""
+    import workloads
+    rq, ta = workloads.rotor_quaternions(128, np.random.default_rng(5))
+    base = dict(rot="rotor", rotor_quat=rq, rotor_tail=ta)
+    kvq.validate(_cfg(**base))
+    kvq.validate(_cfg(shape=(1, 4, 2, 256), group_size=32, rot="rotor",
+                      rotor_quat=workloads.rotor_quaternions(256, np.random.default_rng(6))[0]))
+    bad = rq.copy()
+    bad[7] *= 1.01
+    for kw, status in ((dict(rotor_quat=None), 1), (dict(rotor_quat=bad), 6), (dict(rotor_tail=float("inf")), 6)):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.validate(_cfg(**{**base, **kw}))
+        assert e.value.status == status, kw
+    lib = _lib_new_entry_points()
+    c = _cfg(**base).c_struct()
+    pl = _planes()
+    assert lib.kvq_append(ctypes.byref(c), 4096, 4096, ctypes.byref(pl), None) == 8
+    n = ctypes.c_size_t()
+    assert lib.kvq_attend_workspace_size(ctypes.byref(c), None, 8, ctypes.byref(n)) == 8

@@ -135,3 +135,58 @@ def test_dense_many_items_per_block():
             parity.compare_encode(g, ora, ps, xs.shape, f"dense many row {row} t0 {t0}")
             ref = oracle.decode(g, ps, xs.shape)
             parity.compare_decode(y[row:row + 1, sl].cpu().numpy(), ref, "f32", f"dense many decode row {row} t0 {t0}")
+
+
+# --------------------------------------------------------------------------- #
+# RotorQuant's rotors computed as rotors (KVQ_ROT_ROTOR): the codec's vector-ALU kernels
+# --------------------------------------------------------------------------- #
+def run_rotor_native(case, seed, out_dtypes=("f32",), label=""):
+    rng = np.random.default_rng(seed)
+    d = case.shape[-1]
+    data = workloads.synth_case(dataclasses.replace(case, rot="none"), seed)
+    rq, ta = workloads.rotor_quaternions(d, rng)
+    cb = gu.codebook_for(case)
+    say(f"[case] {label} rotor shape={case.shape} dtype={case.dtype} bits={case.bits} G={case.group_size} "
+        f"{case.quant} rope={case.rope} perm={case.use_perm} sink={case.n_sink} pos0={case.pos_offset}")
+    cfg = kvq.Config(shape=case.shape, dtype=case.dtype, bits=case.bits, group_size=case.group_size,
+                     quant=case.quant, rot="rotor", rope=case.rope, pos_offset=case.pos_offset, n_sink=case.n_sink,
+                     perm=data["perm"] if case.use_perm else None, codebook=cb, rotor_quat=rq, rotor_tail=ta)
+    planes = kvq.encode(gu.torch_input(data["input"], case.dtype), cfg)
+    torch.cuda.synchronize()
+    g = gu.planes_numpy(planes)
+    x64 = oracle.widen(data["input"], case.dtype)
+    p = dataclasses.replace(parity.params_for(case, data["perm"], None, cb), rot="rotor",
+                            rotor_quat=rq.astype(np.float64), rotor_tail=ta)
+    ora = oracle.encode(x64, p)
+    if case.n_sink:
+        ora["sink_f64"] = parity.sink_f64(x64, p)
+    rep = parity.compare_encode(g, ora, p, case.shape, label)
+    ref = oracle.decode(g, p, case.shape)
+    for od in out_dtypes:
+        y = kvq.decode(planes, cfg, out_dtype=od)
+        torch.cuda.synchronize()
+        yn = y.float().cpu().numpy() if od != "f32" else y.cpu().numpy()
+        parity.compare_decode(yn, ref, od, f"{label} decode->{od}")
+    return rep
+
+
+ROTOR_CASES = CASES + [
+    ("bf16", 2, "minmax", 32, True, True, 4, 0, (2, 37, 3, 256)),    # d = 256: 85 blocks and a 1-channel tail
+    ("f32", 3, "lloyd", 256, False, False, 0, 0, (1, 61, 2, 256)),
+    ("f16", 4, "minmax", 64, False, True, 2, 1, (2, 9, 5, 256)),
+]
+
+
+@pytest.mark.parametrize("dtype,bits,quant,g,rope,use_perm,n_sink,pos,shape", ROTOR_CASES)
+def test_rotor_native_small(dtype, bits, quant, g, rope, use_perm, n_sink, pos, shape):
+    seed = zlib.crc32(f"native/{dtype}/{bits}/{quant}/{g}/{shape}".encode()) % 100000
+    case = workloads.TensorCase(name="X", shape=shape, dtype=dtype, bits=bits, group_size=g, quant=quant,
+                                rot="rotor", rope=rope, n_sink=n_sink, use_perm=use_perm, pos_offset=pos)
+    run_rotor_native(case, seed, out_dtypes=("f32", "bf16"), label="rotor native")
+
+
+def test_rotor_native_isoquant_workload():
+    wl = workloads.WORKLOADS["isoquant"]
+    case = dataclasses.replace(wl.case("X"), rot="rotor")
+    rep = run_rotor_native(case, 4343, label="rotor native isoquant workload")
+    say(f"  {dict(rep)}")
