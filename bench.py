@@ -429,16 +429,17 @@ def baseline_rotations_report(kvq, workloads, dev, stream, n_big=1 << 21):
             reps = 50 if size == "batch_8192" else 5
             for kind in ("encode", "decode"):
                 with torch.cuda.stream(stream):
-                    for _ in range(2):
-                        kvq.encode(x, cfg, planes=pl, stream=stream) if kind == "encode" else \
-                            kvq.decode(pl, cfg, out_dtype="f32", out=y, stream=stream)
-                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    ev[0].record(stream)
-                    for _ in range(reps):
+                    def go():
                         if kind == "encode":
                             kvq.encode(x, cfg, planes=pl, stream=stream)
                         else:
                             kvq.decode(pl, cfg, out_dtype="f32", out=y, stream=stream)
+                    for _ in range(2):
+                        go()
+                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    ev[0].record(stream)
+                    for _ in range(reps):
+                        go()
                     ev[1].record(stream)
                     stream.synchronize()
                 ms = ev[0].elapsed_time(ev[1]) / reps

@@ -389,18 +389,25 @@ def test_rotor_matrix_host_matches_oracle():
 
 
 def test_dense_rotation_refusals_on_the_host():
-    """The dense codec takes head_dim 128 without a dynamic codebook; append refuses it."""
+    """The dense codec takes head_dim 128 without a dynamic codebook; append refuses it.  The
+    refusals come before any plane or input is touched (fake, never dereferenced pointers)."""
     lib = _lib_new_entry_points()
-    fake = 4096  # a pointer value the checks never dereference
-    for kw, status in ((dict(shape=(1, 4, 2, 256), group_size=32), 8),):
-        c = _cfg(rot="dense", **kw).c_struct()
-        c.rot_matrix = fake
-        pl = _planes()
-        assert lib.kvq_append(ctypes.byref(c), 4096, 4096, ctypes.byref(pl), None) == 8
+    lib.kvq_encode.argtypes = [ctypes.c_void_p] * 4
+    fake = 4096
+    pl = _planes()
+    c256 = _cfg(rot="dense", shape=(1, 4, 2, 256), group_size=32).c_struct()
+    c256.rot_matrix = fake
+    assert lib.kvq_encode(ctypes.byref(c256), fake, ctypes.byref(pl), None) == 8      # head_dim 256
     c = _cfg(rot="dense").c_struct()
     c.rot_matrix = fake
-    pl = _planes()
-    assert lib.kvq_append(ctypes.byref(c), 4096, 4096, ctypes.byref(pl), None) == 8
+    assert lib.kvq_append(ctypes.byref(c), fake, fake, ctypes.byref(pl), None) == 8   # no append
+    cb = np.linspace(-1, 1, 8).astype(np.float32)
+    dyn = _cfg(rot="dense", bits=3, quant="lloyd", codebook=cb, chan_scale=np.ones(128, np.float32),
+               chan_wide=(np.arange(128) % 16 == 0).astype(np.uint8),
+               codebook_wide=np.linspace(-1, 1, 16).astype(np.float32))
+    cd = dyn.c_struct()
+    cd.rot_matrix = fake
+    assert lib.kvq_encode(ctypes.byref(cd), fake, ctypes.byref(pl), None) == 8        # dynamic codebook
 
 
 def test_rotor_config_checks_on_the_host():
