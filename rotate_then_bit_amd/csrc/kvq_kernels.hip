@@ -186,6 +186,16 @@ __device__ __forceinline__ float add_x2(float v) {
   asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0" KVQ_QP2 : "+v"(v));
   return v;
 }
+// Sums over 8 and 16 lanes that finish what add_x1 and add_x2 began: the value is then equal
+// within each quad, so the partner across the half-row mirror (lane 7 - i of 8) or the row
+// mirror (15 - i of 16) holds what lane i ^ 4 or i ^ 8 holds, and every lane gets the same
+// sum in the same order as an xor butterfly.  DPP, without the LDS round trip of ds_swizzle.
+__device__ __forceinline__ float add_half_mirror(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float add_row_mirror(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
 
 // Sum / max over the LV lanes of a vector.
 template <int LV>
@@ -2021,7 +2031,7 @@ __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
         float part = __builtin_fmaf(ks, d, kz * sl[m]);  // q~ . (zero + code * scale) over 16 channels
         part = add_x1(part);
         part = add_x2(part);
-        part += swz_x4(part);
+        part = add_half_mirror(part);
         s[m] = valid ? part * a.scale : -INFINITY;
       }
       // online softmax: rescale the slot's sums when its maximum grows
@@ -2828,10 +2838,6 @@ __global__ void __launch_bounds__(256) attend_combine(const AttendArgs a) {
 // the positions below n_sink).  The same three passes in the rotated domain as above; the
 // scores and value sums run on the vector ALUs.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float swz_x8(float v) {
-  // ds_swizzle bit mode: and 0x1f, or 0, xor 8
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));
-}
 
 // Unnormalised Walsh-Hadamard transform (Sylvester order) of D values held by a wave as
 // u[k] = x[lane + 64 k]: index bits 6.. inside the lane, bits 0..5 across lanes.
@@ -3034,8 +3040,8 @@ __global__ void __launch_bounds__(256) attend_partial_gen(const AttendArgs a) {
         float part = __builtin_fmaf(ks, d, kz * sl[m]);  // q~ . (zero + code * scale) over 16 channels
         part = add_x1(part);
         part = add_x2(part);
-        part += swz_x4(part);
-        if constexpr (LPS == 16) part += swz_x8(part);
+        part = add_half_mirror(part);
+        if constexpr (LPS == 16) part = add_row_mirror(part);
         s[m] = valid ? part * a.scale : -INFINITY;
       }
       bool grow = false;
