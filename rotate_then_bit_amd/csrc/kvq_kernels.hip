@@ -1903,7 +1903,7 @@ __device__ __forceinline__ void fwht128_wave(float& v0, float& v1, int lane) {
 
 // rotated queries M P q: one wave per (row, query head); lane i holds channels i and i + 64
 __global__ void __launch_bounds__(256) attend_rotate_q(const AttendArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.q_heads) return;  // wave-uniform; no block barrier in this kernel
   const float* q = a.q + w * 128;
@@ -1928,7 +1928,7 @@ template <int BITS, int QG>
 __global__ void __launch_bounds__(256) attend_partial(const AttendArgs a) {
   // the rotated query slices live in LDS (read every step) instead of 16 * QG registers
   __shared__ __attribute__((aligned(16))) float s_qv[4][QG * 128];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
   const int64_t c = w % a.n_chunks, rh = w / a.n_chunks, h = rh % a.heads, r = rh / a.heads;
@@ -2773,7 +2773,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
 __global__ void __launch_bounds__(256) attend_combine(const AttendArgs a) {
   __shared__ float s_out[4][128];
   __shared__ float s_sc[4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.q_heads) return;  // wave-uniform; no block barrier in this kernel
   const int64_t r = w / a.q_heads, m = w % a.q_heads;
@@ -2867,7 +2867,7 @@ __device__ __forceinline__ void fwht_wave(float (&u)[D / 64], int lane) {
 template <int D>
 __global__ void __launch_bounds__(256) attend_rotate_q_gen(const AttendArgs a) {
   constexpr int K = D / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.q_heads) return;  // wave-uniform; no barrier in this kernel
   const float* q = a.q + w * D;
@@ -2950,7 +2950,7 @@ __global__ void __launch_bounds__(256) attend_partial_gen(const AttendArgs a) {
   constexpr int KCB = D * KB / 8, VCB = D * VB / 8;  // code bytes per vector
   constexpr int PS = D + 2;                          // floats per partial
   __shared__ __attribute__((aligned(16))) float s_qv[4][QG * D];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
   const int64_t c = w % a.n_chunks, rh = w / a.n_chunks, h = rh % a.heads, r = rh / a.heads;
@@ -2959,7 +2959,6 @@ __global__ void __launch_bounds__(256) attend_partial_gen(const AttendArgs a) {
   if (a.lengths) {
     const int64_t n = a.lengths[r];
     len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
-    len = (int64_t)__builtin_amdgcn_readfirstlane((int32_t)len);  // wave-uniform; tokens < 2^31 (host check)
   }
   const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.sink_slots);
   const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
@@ -3009,16 +3008,14 @@ __global__ void __launch_bounds__(256) attend_partial_gen(const AttendArgs a) {
     s.vz = a.v_zero[vec * vng + vg];
   };
 
-  // loads in flight: PF steps ahead.  Two steps measured 13 % faster than one at the wide-head
-  // cache (2 query heads per KV head); with 4 or 8 query heads the third slot's registers would
-  // cost a wave per SIMD.
-  constexpr int PF = QG <= 2 ? 2 : 1;
+  // loads in flight two steps ahead: measured 13 % faster than one at the wide-head cache, and
+  // the third slot's registers leave every instance at its occupancy
   if (t_begin < t_end) {
     Slot cur, nx1, nx2;
     load(t_begin, cur);
-    if (PF == 2 && t_begin + SPS < t_end) load(t_begin + SPS, nx1);
+    if (t_begin + SPS < t_end) load(t_begin + SPS, nx1);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += SPS) {
-      if (t0 + PF * SPS < t_end) load(t0 + PF * SPS, PF == 2 ? nx2 : nx1);  // wave-uniform
+      if (t0 + 2 * SPS < t_end) load(t0 + 2 * SPS, nx2);  // wave-uniform
       const bool valid = t0 + tk < t_end;
       float code[16];
       slot_code_floats<KB>(cur.k, l, code);
@@ -3074,7 +3071,7 @@ __global__ void __launch_bounds__(256) attend_partial_gen(const AttendArgs a) {
         for (int i = 0; i < 16; ++i) acc[m][i] = __builtin_fmaf(ps, code[i], acc[m][i]);
       }
       cur = nx1;
-      if constexpr (PF == 2) nx1 = nx2;
+      nx1 = nx2;
     }
   }
   // merge the wave's slots (lanes xor LPS, 2 LPS, ...) and write the chunk's partial
@@ -3110,7 +3107,7 @@ __global__ void __launch_bounds__(256) attend_combine_gen(const AttendArgs a) {
   constexpr int K = D / 64, PS = D + 2;
   __shared__ float s_out[4][D];
   __shared__ float s_sc[4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.q_heads) return;  // wave-uniform; no block barrier in this kernel
   const int64_t r = w / a.q_heads, m = w % a.q_heads;
@@ -3578,7 +3575,7 @@ template <int DT, int D>
 __global__ void __launch_bounds__(256) channel_stats_kernel(const CalibArgs a) {
   constexpr int NP = D / 128;  // channel pairs per lane
   constexpr int ES = (DT == DT_F32) ? 4 : 2;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.n_waves) return;  // wave-uniform; no block barrier in this kernel
   const int64_t nchunk = (a.tokens + a.tpw - 1) / a.tpw;
@@ -3670,7 +3667,7 @@ template <int DT, int D>
 __global__ void __launch_bounds__(256) token_norm_kernel(const CalibArgs a) {
   constexpr int ES = (DT == DT_F32) ? 4 : 2;
   constexpr int CPV = D * ES / 16;  // 16-byte pieces per vector
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.tokens) return;  // wave-uniform
   const int64_t r = w / a.tokens, t = w % a.tokens;
@@ -3778,7 +3775,7 @@ __global__ void __launch_bounds__(256) rotated_moments_kernel(const CalibArgs a)
   constexpr int ES = (DT == DT_F32) ? 4 : 2;
   __shared__ float s_mat[(D / 4) * 16];
   __shared__ float s_u[4][D];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (a.rot == ROT_SO4)
     for (int b = threadIdx.x; b < D / 4; b += blockDim.x) build_so4(&a.quat[8 * b], &s_mat[16 * b]);
   __syncthreads();
@@ -3911,7 +3908,7 @@ __global__ void __launch_bounds__(256) rotated_moments_kernel(const CalibArgs a)
 template <int D>
 __global__ void __launch_bounds__(256) entropy_rotate_q(const EntropyArgs a) {
   constexpr int K = D / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.q_heads) return;  // wave-uniform; no barrier in this kernel
   const float* q = a.q + w * D;
@@ -3981,7 +3978,7 @@ template <int D, int BITS, int QG>
 __global__ void __launch_bounds__(256) entropy_partial(const EntropyArgs a) {
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   __shared__ float s_q[4][QG * D];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
   const int64_t c = w % a.n_chunks, rh = w / a.n_chunks, h = rh % a.heads, r = rh / a.heads;
@@ -4069,7 +4066,7 @@ __global__ void __launch_bounds__(256) entropy_partial(const EntropyArgs a) {
 template <int D>
 __global__ void __launch_bounds__(256) entropy_combine(const EntropyArgs a) {
   constexpr int K = D / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.q_heads) return;  // wave-uniform; no barrier in this kernel
   const int64_t r = w / a.q_heads, m = w % a.q_heads;
