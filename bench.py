@@ -218,6 +218,22 @@ REGIME = {"widehead": "hbm", "llama2": "cache-resident (76.5 MB per direction fi
           "tiny": "launch-bound (0.66 MB per direction)", "isoquant": "launch-bound (4.6 MB per direction)"}
 
 
+def warm_up(go, stream, min_ms=30.0):
+    """Launch go() for about min_ms of GPU time before a timed run: after host-side set-up the
+    GPU clocks take some tens of milliseconds of load to come back up."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    go()
+    b.record(stream)
+    stream.synchronize()
+    n = max(3, min(2000, int(min_ms / max(a.elapsed_time(b), 1e-3))))
+    for _ in range(n):
+        go()
+    stream.synchronize()
+
+
 def time_other_configs(kvq, workloads, dev, stream, keys=None):
     """Per-launch times of the other workloads: encode, and decode to the input dtype, of each
     tensor; the wide-head cache at full size (drawn on the GPU), the others from the host."""
@@ -263,8 +279,7 @@ def time_other_configs(kvq, workloads, dev, stream, keys=None):
                     else:
                         kvq.decode(planes, cfg, out_dtype=c.dtype, out=y, stream=stream)
                 with torch.cuda.stream(stream):
-                    for _ in range(3):
-                        go()
+                    warm_up(go, stream)
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
@@ -307,8 +322,7 @@ def time_attend_general(kvq, kept, dev, stream, qg=2, reps=20):
     ws = torch.empty(kvq.attend_workspace_size(cfg_k, qg * h, cfg_v), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        for _ in range(3):
-            kvq.attend(q, pk, cfg_k, pv, cfg_v, out=out, workspace=ws, stream=stream)
+        warm_up(lambda: kvq.attend(q, pk, cfg_k, pv, cfg_v, out=out, workspace=ws, stream=stream), stream)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -434,8 +448,7 @@ def baseline_rotations_report(kvq, workloads, dev, stream, n_big=1 << 21):
                             kvq.encode(x, cfg, planes=pl, stream=stream)
                         else:
                             kvq.decode(pl, cfg, out_dtype="f32", out=y, stream=stream)
-                    for _ in range(2):
-                        go()
+                    warm_up(go, stream)
                     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                     ev[0].record(stream)
                     for _ in range(reps):
@@ -603,7 +616,7 @@ def main():
     src = data["inputs"]["K"].view(-1).view(torch.uint8)[:half]
     dst = torch.empty(half, dtype=torch.uint8, device=dev)
     with torch.cuda.stream(stream):
-        dst.copy_(src)
+        warm_up(lambda: dst.copy_(src), stream)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -618,7 +631,7 @@ def main():
     ceil = {}
     with torch.cuda.stream(stream):
         for name, fn in (("write_fill", lambda: big.fill_(0.5)), ("read_sum", lambda: big.sum(dtype=torch.float32))):
-            fn()
+            warm_up(fn, stream)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -695,9 +708,7 @@ def main():
     with torch.cuda.stream(stream):
         for name, fn in (("channel_stats", lambda: kvq.channel_stats(ksl, cal_cfg, workspace=ws_cal, stream=stream)),
                          ("detect_sinks", lambda: kvq.detect_sinks(ksl, cal_cfg, 8.0, stream=stream))):
-            for _ in range(2):
-                fn()
-            stream.synchronize()
+            warm_up(fn, stream)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
