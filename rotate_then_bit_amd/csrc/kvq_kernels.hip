@@ -2896,17 +2896,18 @@ struct SlotCodes {
   uint32_t w[BITS == 2 ? 1 : 2];
 };
 template <int BITS>
-__device__ __forceinline__ void load_slot_codes(const uint8_t* rec, int l, SlotCodes<BITS>& c) {
+__device__ __forceinline__ uint32_t slot_code_offset(int l) {  // the lane's first word in its record
+  return BITS == 2 ? 4u * (uint32_t)l : (BITS == 4 ? 8u * (uint32_t)l : (uint32_t)((6 * l) & ~3));
+}
+// the lane's words at byte off of the descriptor (reads past its end give zeros)
+template <int BITS>
+__device__ __forceinline__ void load_slot_codes(buf_t b, uint32_t off, SlotCodes<BITS>& c) {
   if constexpr (BITS == 2) {
-    c.w[0] = *reinterpret_cast<const uint32_t*>(rec + 4 * l);
-  } else if constexpr (BITS == 4) {
-    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(rec + 8 * l);
+    c.w[0] = __builtin_amdgcn_raw_buffer_load_b32(b, off, 0, 0);
+  } else {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(b, off, 0, 0);  // 4-byte aligned
     c.w[0] = v.x;
     c.w[1] = v.y;
-  } else {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + ((6 * l) & ~3));
-    c.w[0] = p[0];
-    c.w[1] = p[1];
   }
 }
 // codes to floats (for 3 bits the word pair is first shifted into place, see above)
@@ -2995,17 +2996,23 @@ __global__ void __launch_bounds__(256) attend_partial_gen(const AttendArgs a) {
     SlotCodes<VB> v;
     uint32_t ks, kz, vs, vz;  // fp16 bits of the lane's group scale and zero
   };
-  // the lane's slot of step t0 (clamped into the chunk for the loads; masked afterwards)
+  // The lane's slot of step t0, through descriptors based at (row r, slot t0, head h) that end
+  // with the record of (slot t_end - 1, head h): the per-step address arithmetic is scalar, the
+  // lane's offsets are fixed (below 8 slots * 32768 heads * 128 bytes: heads <= 32768 on the
+  // host), and lanes past the chunk's end read zeros (their slots are masked afterwards).
+  const int64_t vb = r * a.tokens * a.heads + h;  // vector (row r, slot 0, head h)
+  const uint32_t th = (uint32_t)tk * (uint32_t)a.heads;
+  const uint32_t kco = th * KCB + slot_code_offset<KB>(l), vco = th * VCB + slot_code_offset<VB>(l);
+  const uint32_t kso = 2u * (th * (uint32_t)kng + (uint32_t)kg), vso = 2u * (th * (uint32_t)vng + (uint32_t)vg);
   auto load = [&](int64_t t0, Slot& s) __attribute__((always_inline)) {
-    int64_t t = t0 + tk;
-    if (t >= t_end) t = t_end - 1;
-    const int64_t vec = (r * a.tokens + t) * a.heads + h;
-    load_slot_codes<KB>(a.k_codes + vec * KCB, l, s.k);
-    load_slot_codes<VB>(a.v_codes + vec * VCB, l, s.v);
-    s.ks = a.k_scale[vec * kng + kg];
-    s.kz = a.k_zero[vec * kng + kg];
-    s.vs = a.v_scale[vec * vng + vg];
-    s.vz = a.v_zero[vec * vng + vg];
+    const int64_t v0 = vb + t0 * a.heads;             // vector (row r, slot t0, head h)
+    const int64_t nv = (t_end - 1 - t0) * a.heads + 1;  // up to vector (row r, slot t_end - 1, head h)
+    load_slot_codes<KB>(make_buf(a.k_codes + v0 * KCB, nv * KCB), kco, s.k);
+    load_slot_codes<VB>(make_buf(a.v_codes + v0 * VCB, nv * VCB), vco, s.v);
+    s.ks = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.k_scale + v0 * kng, 2 * nv * kng), kso, 0, 0);
+    s.kz = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.k_zero + v0 * kng, 2 * nv * kng), kso, 0, 0);
+    s.vs = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.v_scale + v0 * vng, 2 * nv * vng), vso, 0, 0);
+    s.vz = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.v_zero + v0 * vng, 2 * nv * vng), vso, 0, 0);
   };
 
   // loads in flight two steps ahead: measured 13 % faster than one at the wide-head cache, and
