@@ -219,19 +219,22 @@ REGIME = {"widehead": "hbm", "llama2": "cache-resident (76.5 MB per direction fi
 
 
 def warm_up(go, stream, min_ms=30.0):
-    """Launch go() for about min_ms of GPU time before a timed run: after host-side set-up the
-    GPU clocks take some tens of milliseconds of load to come back up."""
+    """Launch go() for at least min_ms of GPU time before a timed run (batches of doubling size,
+    at most 4095 calls): after host-side set-up the GPU clocks take some tens of milliseconds of
+    load to come back up, and a first call (fresh memory, code loading) says little about the
+    rest."""
     import torch
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    go()
-    b.record(stream)
-    stream.synchronize()
-    n = max(3, min(2000, int(min_ms / max(a.elapsed_time(b), 1e-3))))
-    for _ in range(n):
-        go()
-    stream.synchronize()
+    total, k = 0.0, 1
+    while total < min_ms and k < 4096:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            go()
+        b.record(stream)
+        stream.synchronize()
+        total += a.elapsed_time(b)
+        k *= 2
 
 
 def time_other_configs(kvq, workloads, dev, stream, keys=None):
