@@ -3576,8 +3576,10 @@ int launch_decode_dense(int out_dtype, int bits, int quant, const CodecArgs& a, 
 namespace {
 // One wave per (row, run of tpw tokens).  Lane i owns the channel pairs (2i, 2i + 1) (and
 // (2i + 128, 2i + 129) at d = 256), so each load instruction of the wave covers one vector's
-// bytes contiguously, and the pair's cos/sin is computed once per token for all heads.  Sums
-// of |y| are float64 per lane; the per-wave sums go to the workspace.
+// bytes contiguously, and the pair's cos/sin is computed once per token for all heads.  A
+// token's heads are read in batches of 8 loads issued before any is used; each batch's |y|
+// are summed in float32 (8 terms) and added to float64 sums per lane; the per-wave sums go to
+// the workspace.
 template <int DT, int D>
 __global__ void __launch_bounds__(256) channel_stats_kernel(const CalibArgs a) {
   constexpr int NP = D / 128;  // channel pairs per lane
@@ -3606,33 +3608,52 @@ __global__ void __launch_bounds__(256) channel_stats_kernel(const CalibArgs a) {
       sn[k] = 0.0f;
       if (a.rope) rope_cos_sin(pos, theta[k], &c[k], &sn[k]);
     }
-    for (int64_t h = 0; h < a.heads; ++h) {
-      const char* v = base + (r * a.sr + t * a.st + h * a.sh) * ES;
+    const char* tb = base + (r * a.sr + t * a.st) * ES;
+    for (int64_t h0 = 0; h0 < a.heads; h0 += 8) {  // wave-uniform
+      constexpr int EW = (DT == DT_F32) ? 2 : 1;  // 32-bit words per channel pair
+      uint32_t wd[8][NP][EW];
 #pragma unroll
-      for (int k = 0; k < NP; ++k) {
-        const int i = lane + 64 * k;  // pair index
-        float x0, x1;
-        if constexpr (DT == DT_F32) {
-          const f32x2_t xx = *reinterpret_cast<const f32x2_t*>(v + 8 * i);
-          x0 = xx.x;
-          x1 = xx.y;
-        } else {
-          const uint32_t wd = *reinterpret_cast<const uint32_t*>(v + 4 * i);
-          if constexpr (DT == DT_BF16) {
-            x0 = __uint_as_float(wd << 16);
-            x1 = __uint_as_float(wd & 0xffff0000u);
+      for (int j = 0; j < 8; ++j) {
+        // heads past the last read as zeros (|y| = 0 adds nothing)
+        const buf_t hb = make_buf(tb + (h0 + j) * a.sh * ES, h0 + j < a.heads ? D * ES : 0);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const uint32_t off = (uint32_t)(lane + 64 * k) * (4u * EW);
+          if constexpr (EW == 2) {
+            const u32x2_t xx = __builtin_amdgcn_raw_buffer_load_b64(hb, off, 0, 0);
+            wd[j][k][0] = xx.x;
+            wd[j][k][EW - 1] = xx.y;
           } else {
-            x0 = f16_value(wd & 0xffffu);
-            x1 = f16_value(wd >> 16);
+            wd[j][k][0] = __builtin_amdgcn_raw_buffer_load_b32(hb, off, 0, 0);
           }
         }
-        float y0 = x0, y1 = x1;
-        if (a.rope) {
-          y0 = __builtin_fmaf(x0, c[k], -x1 * sn[k]);
-          y1 = __builtin_fmaf(x0, sn[k], x1 * c[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float x0, x1;
+          if constexpr (DT == DT_F32) {
+            x0 = __uint_as_float(wd[j][k][0]);
+            x1 = __uint_as_float(wd[j][k][EW - 1]);
+          } else if constexpr (DT == DT_BF16) {
+            x0 = __uint_as_float(wd[j][k][0] << 16);
+            x1 = __uint_as_float(wd[j][k][0] & 0xffff0000u);
+          } else {
+            x0 = f16_value(wd[j][k][0] & 0xffffu);
+            x1 = f16_value(wd[j][k][0] >> 16);
+          }
+          float y0 = x0, y1 = x1;
+          if (a.rope) {
+            y0 = __builtin_fmaf(x0, c[k], -x1 * sn[k]);
+            y1 = __builtin_fmaf(x0, sn[k], x1 * c[k]);
+          }
+          b0 += fabsf(y0);
+          b1 += fabsf(y1);
         }
-        s0[k] += (double)fabsf(y0);
-        s1[k] += (double)fabsf(y1);
+        s0[k] += (double)b0;
+        s1[k] += (double)b1;
       }
     }
   }
@@ -3705,7 +3726,10 @@ __global__ void __launch_bounds__(256) token_norm_kernel(const CalibArgs a) {
 // Per row: the lower median of the T token norms by an exact radix select on their bit
 // patterns (non-negative doubles order as unsigned integers), eight 8-bit digits from the top;
 // then the flags (norm > lambda * median), their count and one past the last flagged token.
-__global__ void __launch_bounds__(256) sink_select_kernel(const CalibArgs a) {
+// One block of kSelectThreads per row; each digit's bin is found by one wave (4 bins per lane,
+// an inclusive scan of the lane sums).
+constexpr int kSelectThreads = 1024;
+__global__ void __launch_bounds__(kSelectThreads) sink_select_kernel(const CalibArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ int64_t s_k;
   __shared__ int s_b;
@@ -3725,22 +3749,37 @@ __global__ void __launch_bounds__(256) sink_select_kernel(const CalibArgs a) {
   uint64_t prefix = 0, mask = 0;
   int64_t k = (T - 1) / 2;  // rank of the lower median among the values that match the prefix
   for (int d = 7; d >= 0; --d) {
-    hist[tid] = 0u;
+    if (tid < 256) hist[tid] = 0u;
     __syncthreads();
-    for (int64_t t = tid; t < T; t += 256) {
+    for (int64_t t = tid; t < T; t += kSelectThreads) {
       const uint64_t v = (uint64_t)__double_as_longlong(nr[t]);
       if ((v & mask) == prefix) atomicAdd(&hist[(v >> (8 * d)) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int64_t below = 0;
-      int b = 0;
-      for (; b < 255; ++b) {
-        if (below + (int64_t)hist[b] > k) break;
-        below += hist[b];
+    if (tid < 64) {
+      // lane L: bins 4L .. 4L + 3; the digit is the bin where the running count passes k
+      // (exactly one lane holds it: the matching values number more than k)
+      uint32_t hb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hb[e] = hist[4 * tid + e];
+      // counts stay below T < 2^31 (tokens * heads < 2^31 on the host)
+      const int own = (int)(hb[0] + hb[1] + hb[2] + hb[3]);
+      int incl = own;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int up = __shfl_up(incl, o);
+        if (tid >= o) incl += up;
       }
-      s_k = k - below;
-      s_b = b;
+      int64_t below = incl - own;
+      if (below <= k && k < incl) {
+        int e = 0;
+        for (; e < 3; ++e) {
+          if (below + (int64_t)hb[e] > k) break;
+          below += hb[e];
+        }
+        s_k = k - below;
+        s_b = 4 * tid + e;
+      }
     }
     __syncthreads();
     k = s_k;
@@ -3756,7 +3795,7 @@ __global__ void __launch_bounds__(256) sink_select_kernel(const CalibArgs a) {
   __syncthreads();
   const double thr = a.lambda * med;
   int cnt = 0, last = -1;
-  for (int64_t t = tid; t < T; t += 256) {
+  for (int64_t t = tid; t < T; t += kSelectThreads) {
     const bool f = nr[t] > thr;
     a.flags[r * T + t] = f ? 1 : 0;
     cnt += f ? 1 : 0;
@@ -4154,7 +4193,7 @@ int launch_sinks_t(const CalibArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((token_norm_kernel<DT, D>), dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, s, a);
     if (hipError_t e = hipGetLastError()) return (int)e;
   }
-  hipLaunchKernelGGL(sink_select_kernel, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(sink_select_kernel, dim3((unsigned)a.rows), dim3(kSelectThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 }  // namespace
