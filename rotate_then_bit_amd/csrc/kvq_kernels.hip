@@ -3125,11 +3125,14 @@ __global__ void __launch_bounds__(256) attend_combine_gen(const AttendArgs a) {
     len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
   }
   const float* pb = a.part + w * (int64_t)a.n_chunks * PS;
-  float M = -INFINITY;
-  for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, pb[c * PS + D]);
+  float M = -INFINITY;  // the chunks' maxima read by the lanes in parallel, then a wave maximum
+  for (int c = lane; c < a.n_chunks; c += 64) M = fmaxf(M, pb[c * PS + D]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
   float L = 0.0f, acc[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) acc[k] = 0.0f;
+#pragma unroll 4
   for (int c = 0; c < a.n_chunks; ++c) {
     const float mc = pb[c * PS + D];
     const float f = (mc == -INFINITY) ? 0.0f : __expf(mc - M);
@@ -4122,10 +4125,17 @@ __global__ void __launch_bounds__(256) entropy_combine(const EntropyArgs a) {
     const int64_t n = a.lengths[r];
     len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
   }
+  // lane i merges chunks i, i + 64, ...; then the lanes merge by a butterfly (the merge is
+  // symmetric in its two operands, so every lane ends with the same values)
   float M = -INFINITY, L = 0.0f, S = 0.0f;
-  for (int c = 0; c < a.n_chunks; ++c) {
+  for (int c = lane; c < a.n_chunks; c += 64) {
     const float* pb = a.part + (w * a.n_chunks + c) * 4;
     ent_merge(M, L, S, pb[0], pb[1], pb[2]);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float M2 = __shfl_xor(M, o), L2 = __shfl_xor(L, o), S2 = __shfl_xor(S, o);
+    ent_merge(M, L, S, M2, L2, S2);
   }
   const int nsk = (int)min((int64_t)a.n_sink, len);
   const float* qr = a.q + w * D;
