@@ -4027,6 +4027,7 @@ template <int D, int BITS, int QG>
 __global__ void __launch_bounds__(256) entropy_partial(const EntropyArgs a) {
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   __shared__ float s_q[4][QG * D];
+  __shared__ float s_qs[4][QG * (D / 32)];  // per query head and group: the sum of its channels
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + wave;
   if (w >= a.rows * a.heads * a.n_chunks) return;  // wave-uniform; no block barrier follows
@@ -4043,6 +4044,14 @@ __global__ void __launch_bounds__(256) entropy_partial(const EntropyArgs a) {
   for (int i = lane; i < QG * D; i += 64) sq[i] = src[i];
   wave_lds_sync();
   const int G = 1 << a.group_log2, ng = D >> a.group_log2;
+  // the group sums of the queries, once per wave (in channel order, as a slot's pass would)
+  for (int i = lane; i < QG * ng; i += 64) {
+    const int m = i / ng, g0 = (i % ng) * G;
+    float acc = 0.0f;
+    for (int j = 0; j < G; ++j) acc += sq[m * D + g0 + j];
+    s_qs[wave][i] = acc;
+  }
+  wave_lds_sync();
   float M[QG], L[QG], S[QG];
 #pragma unroll
   for (int m = 0; m < QG; ++m) {
@@ -4053,12 +4062,11 @@ __global__ void __launch_bounds__(256) entropy_partial(const EntropyArgs a) {
   for (int64_t t = t_begin + lane; t < t_end; t += 64) {
     const int64_t vec = (r * a.tokens + t) * a.heads + h;
     const uint32_t* cw = reinterpret_cast<const uint32_t*>(a.k_codes + vec * CB);
-    float dot[QG], qs[QG], sc[QG];
+    float dot[QG], sc[QG];
 #pragma unroll
     for (int m = 0; m < QG; ++m) {
       sc[m] = 0.0f;
       dot[m] = 0.0f;
-      qs[m] = 0.0f;
     }
     // blocks of 32 channels (BITS code words each; groups are whole blocks)
 #pragma unroll 1
@@ -4074,9 +4082,7 @@ __global__ void __launch_bounds__(256) entropy_partial(const EntropyArgs a) {
         const float cf = (float)(code & ((1u << BITS) - 1u));
 #pragma unroll
         for (int m = 0; m < QG; ++m) {
-          const float qv = sq[m * D + 32 * blk + i];
-          dot[m] = __builtin_fmaf(qv, cf, dot[m]);
-          qs[m] += qv;
+          dot[m] = __builtin_fmaf(sq[m * D + 32 * blk + i], cf, dot[m]);
         }
       }
       if ((((blk + 1) << 5) & (G - 1)) == 0) {  // the end of a group: q . (zero + code * scale)
@@ -4084,9 +4090,8 @@ __global__ void __launch_bounds__(256) entropy_partial(const EntropyArgs a) {
         const float gs = f16_value(a.k_scale[vec * ng + g]), gz = f16_value(a.k_zero[vec * ng + g]);
 #pragma unroll
         for (int m = 0; m < QG; ++m) {
-          sc[m] = __builtin_fmaf(gs, dot[m], __builtin_fmaf(gz, qs[m], sc[m]));
+          sc[m] = __builtin_fmaf(gs, dot[m], __builtin_fmaf(gz, s_qs[wave][m * ng + g], sc[m]));
           dot[m] = 0.0f;
-          qs[m] = 0.0f;
         }
       }
     }
