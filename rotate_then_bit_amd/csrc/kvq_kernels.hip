@@ -2492,22 +2492,25 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
 // The same pass with the 4 waves of a block on 4 consecutive KV heads of one (row, chunk), for
 // caches whose head count is a multiple of 4: the block loads each 64-slot window's code rows of
 // its 4 heads (128 contiguous bytes per slot and plane, whole 128-byte lines) and their scales
-// into LDS once, and each wave computes its head from there.  The loads run ahead in registers:
-// two windows for 2-bit codes (measured 1-2 % faster than one window of 128 slots at the Llama-3
-// cache), one for 4-bit codes (whose windows take twice the registers).  Rows of a code
+// into LDS once, and each wave computes its head from there.  The loads run one window ahead in
+// registers (at the Llama-3 cache, with the chunks below, 3 % faster than two windows ahead and
+// 2 % faster than one window of 128 slots: fewer bytes in flight stream faster here).  Rows of a code
 // window are padded to 136 bytes: the key reads (8 bytes, slot n16 of a block) and the value
-// reads (32-bit words, slots 4 g + j) then fall into distinct banks.
+// reads (32-bit words, slots 4 g + j) then fall into distinct banks.  Chunk c of a row takes
+// every n_chunks-th window from window c on (after the sink slots), so the blocks of a row
+// stream neighbouring windows at the same time (measured 1.7 % faster at the Llama-3 cache
+// than contiguous chunks of slots); the combine pass merges any split of the slots alike.
 // Per code width: code bytes per head and slot, slots per window, LDS bytes per slot row.
 template <int BITS> struct BlkGeo {
   static constexpr int CB = 16 * BITS;
   static constexpr int W = 64;
-  static constexpr int DEEP = BITS == 2 ? 2 : 1;  // windows in flight (registers): 2-bit, 2; 4-bit, 1
   static constexpr int ROWB = BITS == 2 ? 136 : 272;
 };
-// (at most 168 VGPRs: 3 waves per SIMD measured 9 % faster than 2 at 232)
+// (at most 168 VGPRs, 3 waves per SIMD: measured 9 % faster than 2 at 232 VGPRs; 4 waves at 128
+// VGPRs, with spills, measured 1 % slower)
 template <int BITS, int QG>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) attend_partial_mma_blk(const AttendArgs a) {
-  constexpr int CB = BlkGeo<BITS>::CB, WN = BlkGeo<BITS>::W, kRowB = BlkGeo<BITS>::ROWB, DEEP = BlkGeo<BITS>::DEEP;
+  constexpr int CB = BlkGeo<BITS>::CB, WN = BlkGeo<BITS>::W, kRowB = BlkGeo<BITS>::ROWB;
   __shared__ __attribute__((aligned(16))) uint8_t s_kc[WN * kRowB];
   __shared__ __attribute__((aligned(16))) uint8_t s_vc[WN * kRowB];
   __shared__ __attribute__((aligned(16))) uint16_t s_sr[4][WN][4];          // (k scale, k zero, v scale, v zero), slot, head
@@ -2525,8 +2528,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     const int64_t n = a.lengths[r];
     len = n < 0 ? 0 : (n > a.tokens ? a.tokens : n);
   }
-  const int64_t t_begin = max(c * (int64_t)a.chunk, (int64_t)a.n_sink);
-  const int64_t t_end = min((c + 1) * (int64_t)a.chunk, len);
+  const int64_t SW = a.n_chunks * (int64_t)WN;  // a chunk's windows: every n_chunks-th window of the row
+  const int64_t t_begin = (int64_t)a.n_sink + c * (int64_t)WN;
+  const int64_t t_end = len;
   const int n16 = lane & 15, g = lane >> 4;
   const int qm = n16 >> 2, qs = n16 & 3;
   uint32_t* const sn = &s_n[wave][0][0];
@@ -2582,7 +2586,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     u32x4_t kq[NU], vq[NU];
     u32x2_t sq[NS];
   };
-  WinRegs RA, RB;
+  WinRegs RA;
   auto load_win = [&](int64_t w0, WinRegs& R) __attribute__((always_inline)) {
     const int64_t vb = rb0 + w0 * a.heads;
     const int64_t n = min((int64_t)WN, t_end - w0);
@@ -2601,10 +2605,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
   };
   const uint32_t vsel = (n16 & 1) ? 0x07060302u : 0x05040100u;  // the lane's 16-bit half of two words
   const uint32_t dsel = (uint32_t)qs | ((uint32_t)qs + 4u) << 8;  // byte qs of two words -> bytes 0, 1
-  if (t_begin < t_end) {
-    load_win(t_begin, RA);
-    if constexpr (DEEP == 2) load_win(t_begin + WN, RB);
-  }
+  if (t_begin < t_end) load_win(t_begin, RA);
   auto window = [&](int64_t wt0, WinRegs& R) __attribute__((always_inline)) {
     const int nv = (int)min((int64_t)WN, t_end - wt0);
     __syncthreads();  // every wave is done with the previous window's LDS
@@ -2619,7 +2620,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
 #pragma unroll
     for (int e = 0; e < NS; ++e) *reinterpret_cast<u32x2_t*>(&s_sr[sp][NS * (tid & 63) + e][0]) = R.sq[e];
     __syncthreads();
-    load_win(wt0 + DEEP * WN, R);
+    load_win(wt0 + SW, R);  // the chunk's next window
     float vsm = 0.0f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) vsm = fmaxf(vsm, fabsf(f16_value(s_sr[2][lane + 64 * k][wave])));
@@ -2745,15 +2746,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
       }
     }
   };
-  if constexpr (DEEP == 2) {
-    for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += 2 * WN) {
-      window(wt0, RA);
-      if (wt0 + WN >= t_end) break;  // block-uniform
-      window(wt0 + WN, RB);
-    }
-  } else {
-    for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += WN) window(wt0, RA);
-  }
+  for (int64_t wt0 = t_begin; wt0 < t_end; wt0 += SW) window(wt0, RA);
   if (t_begin < t_end) flush(1.0f);
   Lf = row_sum16(Lf);
   Zf = row_sum16(Zf);
