@@ -3723,8 +3723,10 @@ __global__ void __launch_bounds__(256) token_norm_kernel(const CalibArgs a) {
 // patterns (non-negative doubles order as unsigned integers), eight 8-bit digits from the top;
 // then the flags (norm > lambda * median), their count and one past the last flagged token.
 // One block of kSelectThreads per row; each digit's bin is found by one wave (4 bins per lane,
-// an inclusive scan of the lane sums).
+// an inclusive scan of the lane sums).  Rows of up to kSelectHeld * kSelectThreads tokens are
+// read once into registers; longer rows are read again for every digit.
 constexpr int kSelectThreads = 1024;
+constexpr int kSelectHeld = 32;
 __global__ void __launch_bounds__(kSelectThreads) sink_select_kernel(const CalibArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ int64_t s_k;
@@ -3742,15 +3744,42 @@ __global__ void __launch_bounds__(kSelectThreads) sink_select_kernel(const Calib
     }
     return;  // block-uniform
   }
+  const bool held = T <= (int64_t)kSelectHeld * kSelectThreads;  // block-uniform
+  uint64_t hv[kSelectHeld];
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kSelectHeld; ++i) {
+      const int64_t t = tid + (int64_t)i * kSelectThreads;
+      hv[i] = t < T ? (uint64_t)__double_as_longlong(nr[t]) : 0u;
+    }
+  }
   uint64_t prefix = 0, mask = 0;
   int64_t k = (T - 1) / 2;  // rank of the lower median among the values that match the prefix
   for (int d = 7; d >= 0; --d) {
     if (tid < 256) hist[tid] = 0u;
     __syncthreads();
-    for (int64_t t = tid; t < T; t += kSelectThreads) {
-      const uint64_t v = (uint64_t)__double_as_longlong(nr[t]);
-      if ((v & mask) == prefix) atomicAdd(&hist[(v >> (8 * d)) & 255u], 1u);
+    // a thread's values fall into one bin over long runs in the top digits (the exponent), so it
+    // counts a run in a register and adds it with one atomic when the bin changes
+    uint32_t run_bin = 0u, run_n = 0u;
+    auto count = [&](uint64_t v) __attribute__((always_inline)) {
+      if ((v & mask) == prefix) {
+        const uint32_t b = (uint32_t)(v >> (8 * d)) & 255u;
+        if (b != run_bin) {
+          if (run_n) atomicAdd(&hist[run_bin], run_n);
+          run_bin = b;
+          run_n = 0u;
+        }
+        ++run_n;
+      }
+    };
+    if (held) {
+#pragma unroll
+      for (int i = 0; i < kSelectHeld; ++i)
+        if (tid + (int64_t)i * kSelectThreads < T) count(hv[i]);
+    } else {
+      for (int64_t t = tid; t < T; t += kSelectThreads) count((uint64_t)__double_as_longlong(nr[t]));
     }
+    if (run_n) atomicAdd(&hist[run_bin], run_n);
     __syncthreads();
     if (tid < 64) {
       // lane L: bins 4L .. 4L + 3; the digit is the bin where the running count passes k

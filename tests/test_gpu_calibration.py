@@ -124,7 +124,8 @@ def _check_sinks(x_raw, dtype, shape, lam, label, strides=None, xt=None):
 
 @pytest.mark.parametrize("shape,dtype", [((3, 101, 8, 128), "bf16"), ((2, 64, 3, 256), "f16"),
                                          ((2, 1, 2, 128), "f32"), ((1, 2, 4, 128), "bf16"),
-                                         ((4, 0, 8, 128), "bf16")])
+                                         ((4, 0, 8, 128), "bf16"),
+                                         ((1, 40000, 1, 128), "bf16")])  # rows longer than the register-held 32768
 def test_detect_sinks(shape, dtype):
     say(f"[case] detect_sinks {shape} {dtype}")
     case = _case(shape, dtype, False)
