@@ -2998,25 +2998,30 @@ __global__ void __launch_bounds__(256) attend_partial_gen(const AttendArgs a) {
   const uint32_t kco = th * KCB + slot_code_offset<KB>(l), vco = th * VCB + slot_code_offset<VB>(l);
   const uint32_t kso = 2u * (th * (uint32_t)kng + (uint32_t)kg), vso = 2u * (th * (uint32_t)vng + (uint32_t)vg);
   auto load = [&](int64_t t0, Slot& s) __attribute__((always_inline)) {
-    const int64_t v0 = vb + t0 * a.heads;             // vector (row r, slot t0, head h)
-    const int64_t nv = (t_end - 1 - t0) * a.heads + 1;  // up to vector (row r, slot t_end - 1, head h)
-    load_slot_codes<KB>(make_buf(a.k_codes + v0 * KCB, nv * KCB), kco, s.k);
-    load_slot_codes<VB>(make_buf(a.v_codes + v0 * VCB, nv * VCB), vco, s.v);
-    s.ks = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.k_scale + v0 * kng, 2 * nv * kng), kso, 0, 0);
-    s.kz = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.k_zero + v0 * kng, 2 * nv * kng), kso, 0, 0);
-    s.vs = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.v_scale + v0 * vng, 2 * nv * vng), vso, 0, 0);
-    s.vz = __builtin_amdgcn_raw_buffer_load_b16(make_buf(a.v_zero + v0 * vng, 2 * nv * vng), vso, 0, 0);
+    const int64_t v0 = vb + t0 * a.heads;  // vector (row r, slot t0, head h)
+    // vectors up to (row r, slot min(t_end - 1, t0 + SPS - 1), head h), none past the chunk's end,
+    // in 32-bit scalar arithmetic (slots < 2^31; at most SPS * heads vectors, below 2^18)
+    const int32_t rem = (int32_t)(t_end - 1 - t0);
+    const uint32_t nv = rem < 0 ? 0u : (uint32_t)min(rem, SPS - 1) * (uint32_t)a.heads + 1u;
+    load_slot_codes<KB>(make_buf_item(a.k_codes + v0 * KCB, nv * KCB), kco, s.k);
+    load_slot_codes<VB>(make_buf_item(a.v_codes + v0 * VCB, nv * VCB), vco, s.v);
+    const uint32_t kgb = 2u * nv * (uint32_t)kng, vgb = 2u * nv * (uint32_t)vng;
+    s.ks = __builtin_amdgcn_raw_buffer_load_b16(make_buf_item(a.k_scale + v0 * kng, kgb), kso, 0, 0);
+    s.kz = __builtin_amdgcn_raw_buffer_load_b16(make_buf_item(a.k_zero + v0 * kng, kgb), kso, 0, 0);
+    s.vs = __builtin_amdgcn_raw_buffer_load_b16(make_buf_item(a.v_scale + v0 * vng, vgb), vso, 0, 0);
+    s.vz = __builtin_amdgcn_raw_buffer_load_b16(make_buf_item(a.v_zero + v0 * vng, vgb), vso, 0, 0);
   };
 
   // loads in flight two steps ahead: measured 13 % faster than one at the wide-head cache, and
   // the third slot's registers leave every instance at its occupancy
+  const int32_t vlim = (int32_t)(t_end - tk);  // the lane's slot of step t0 exists iff t0 < vlim
   if (t_begin < t_end) {
     Slot cur, nx1, nx2;
     load(t_begin, cur);
     if (t_begin + SPS < t_end) load(t_begin + SPS, nx1);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += SPS) {
       if (t0 + 2 * SPS < t_end) load(t0 + 2 * SPS, nx2);  // wave-uniform
-      const bool valid = t0 + tk < t_end;
+      const bool valid = (int32_t)t0 < vlim;
       float code[16];
       slot_code_floats<KB>(cur.k, l, code);
       const float ks = f16_value(cur.ks), kz = f16_value(cur.kz);
