@@ -2800,14 +2800,27 @@ __global__ void __launch_bounds__(256) attend_combine(const AttendArgs a) {
   const float* qr = a.q + w * 128;
   const float q0 = qr[lane], q1 = qr[lane + 64];
   float Mp = M;
-  for (int t = 0; t < nsk; ++t) {
-    const uint16_t* kk = a.k_sink + ((r * a.n_sink + t) * a.heads + h) * 128;
-    float d = __builtin_fmaf(q0, f16_value(kk[lane]), q1 * f16_value(kk[lane + 64]));
+  // four sink slots at a time: their cross-lane sums interleave instead of queueing one after another
+  for (int t0 = 0; t0 < nsk; t0 += 4) {
+    float d[4];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) d += __shfl_xor(d, o);
-    const float st = d * a.scale;
-    if (lane == 0) s_sc[wave][t] = st;
-    Mp = fmaxf(Mp, st);
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + j < nsk ? t0 + j : t0;  // (a repeated slot past the end is not used)
+      const uint16_t* kk = a.k_sink + ((r * a.n_sink + t) * a.heads + h) * 128;
+      d[j] = __builtin_fmaf(q0, f16_value(kk[lane]), q1 * f16_value(kk[lane + 64]));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] += __shfl_xor(d[j], o);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (t0 + j < nsk) {
+        const float st = d[j] * a.scale;
+        if (lane == 0) s_sc[wave][t0 + j] = st;
+        Mp = fmaxf(Mp, st);
+      }
+    }
   }
   wave_lds_sync();
   const float f = (M == -INFINITY) ? 0.0f : __expf(M - Mp);
