@@ -2597,8 +2597,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     for (int k = 0; k < NU; ++k) {
       const uint32_t u = (uint32_t)(tid + 256 * k);  // slot u / UPS, bytes 16 (u % UPS) of the 4 heads' row
       const uint32_t off = (u / UPS) * sT + 16u * (u % UPS);
-      R.kq[k] = __builtin_amdgcn_raw_buffer_load_b128(bkc, off, 0, 0);
-      R.vq[k] = __builtin_amdgcn_raw_buffer_load_b128(bvc, off, 0, 0);
+      // each code line is read once, by this block: streamed (non-temporal, system scope), which
+      // measured 6-7 % faster than temporal loads at the Llama-3 cache; the scale records, half
+      // of whose lines the block of the other head quad reads, stay temporal
+      R.kq[k] = __builtin_amdgcn_raw_buffer_load_b128(bkc, off, 0, kNT | kSC1);
+      R.vq[k] = __builtin_amdgcn_raw_buffer_load_b128(bvc, off, 0, kNT | kSC1);
     }
 #pragma unroll
     for (int e = 0; e < NS; ++e) R.sq[e] = __builtin_amdgcn_raw_buffer_load_b64(bs, (uint32_t)(NS * (tid & 63) + e) * sH2, 0, 0);
