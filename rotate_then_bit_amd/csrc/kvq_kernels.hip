@@ -2191,12 +2191,11 @@ __device__ __forceinline__ void value_product(const uint32_t (&X)[4], const uint
 // and for the lane's key-product head g the factors of score = k_scale raw rs + k_zero zq
 // (log2 units).
 template <int QG, int BITS = 2>
-__device__ __forceinline__ void mma_query(const AttendArgs& a, int64_t r, int64_t h, int lane, i32x4_t (&qa)[2],
+__device__ __forceinline__ void mma_query(const AttendArgs& a, const float* qb, int lane, i32x4_t (&qa)[2],
                                           float& rs, float& zq) {
   const int n16 = lane & 15, g = lane >> 4, qm = n16 >> 2, qs = n16 & 3;
   constexpr float kLog2e = 1.4426950408889634f;
-  // per-head max |q~| and sum q~ of the rotated queries
-  const float* qb = a.qrot + (r * a.q_heads + h * QG) * 128;
+  // per-head max |q~| and sum q~ of the rotated queries qb[m * 128 + c] (m < QG)
   float qmx[4], qsum[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -2277,7 +2276,7 @@ __global__ void __launch_bounds__(256) attend_partial_mma(const AttendArgs a) {
   
   i32x4_t qa[2];
   float rs, zq;
-  mma_query<QG>(a, r, h, lane, qa, rs, zq);
+  mma_query<QG>(a, a.qrot + (r * a.q_heads + h * QG) * 128, lane, qa, rs, zq);
 
   i32x4_t cv[8];
   float fo[8];  // value product: channels 32 g + 8 qs + b of head qm, summed over the digits
@@ -2515,6 +2514,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
   __shared__ __attribute__((aligned(16))) uint8_t s_vc[WN * kRowB];
   __shared__ __attribute__((aligned(16))) uint16_t s_sr[4][WN][4];          // (k scale, k zero, v scale, v zero), slot, head
   __shared__ __attribute__((aligned(16))) uint32_t s_n[4][4][WN + kMmaPad];  // per wave: weight integers per head
+  __shared__ __attribute__((aligned(16))) float s_qr[4][QG * 128];             // per wave: its rotated queries
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t blk = blockIdx.x;
@@ -2536,9 +2536,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
   uint32_t* const sn = &s_n[wave][0][0];
   constexpr int SR = WN + kMmaPad;
 
+  // the wave's rotated queries M P q, computed here rather than by a pass of their own (the
+  // same arithmetic as attend_rotate_q), into the wave's LDS slice
+  {
+    float* qr = s_qr[wave];
+#pragma unroll
+    for (int m = 0; m < QG; ++m) {
+      const float* q = a.q + (r * a.q_heads + h * QG + m) * 128;
+      float z0 = q[a.use_perm_k ? a.perm_k[lane] : lane], z1 = q[a.use_perm_k ? a.perm_k[lane + 64] : lane + 64];
+      fwht128_wave(z0, z1, lane);
+      qr[m * 128 + lane] = z0 * kInvSqrt128;
+      qr[m * 128 + lane + 64] = z1 * kInvSqrt128;
+    }
+    wave_lds_sync();
+  }
   i32x4_t qa[2];
   float rs, zq;
-  mma_query<QG, BITS>(a, r, h, lane, qa, rs, zq);
+  mma_query<QG, BITS>(a, s_qr[wave], lane, qa, rs, zq);
 
   i32x4_t cv[8];
   float fo[8];
@@ -2593,6 +2607,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     const uint32_t cb = n > 0 ? (uint32_t)(n - 1) * sT + 4u * CB : 0u, sb = n > 0 ? (uint32_t)(n - 1) * sH2 + 8u : 0u;
     const buf_t bkc = make_buf(a.k_codes + vb * CB, cb), bvc = make_buf(a.v_codes + vb * CB, cb);
     const buf_t bs = make_buf(splane + vb, sb);
+    // the scales first: the key pass needs them first (measured 1 % faster than after the codes)
+#pragma unroll
+    for (int e = 0; e < NS; ++e) R.sq[e] = __builtin_amdgcn_raw_buffer_load_b64(bs, (uint32_t)(NS * (tid & 63) + e) * sH2, 0, 0);
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
       const uint32_t u = (uint32_t)(tid + 256 * k);  // slot u / UPS, bytes 16 (u % UPS) of the 4 heads' row
@@ -2603,8 +2620,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
       R.kq[k] = __builtin_amdgcn_raw_buffer_load_b128(bkc, off, 0, kNT | kSC1);
       R.vq[k] = __builtin_amdgcn_raw_buffer_load_b128(bvc, off, 0, kNT | kSC1);
     }
-#pragma unroll
-    for (int e = 0; e < NS; ++e) R.sq[e] = __builtin_amdgcn_raw_buffer_load_b64(bs, (uint32_t)(NS * (tid & 63) + e) * sH2, 0, 0);
   };
   const uint32_t vsel = (n16 & 1) ? 0x07060302u : 0x05040100u;  // the lane's 16-bit half of two words
   const uint32_t dsel = (uint32_t)qs | ((uint32_t)qs + 4u) << 8;  // byte qs of two words -> bytes 0, 1
@@ -3389,10 +3404,14 @@ int launch_attend_t(const AttendArgs& a, hipStream_t s) {
   const int64_t np = a.rows * a.heads * a.n_chunks;
   if (nq == 0) return 0;
   if ((np + 3) / 4 > 0x7fffffff || (nq + 3) / 4 > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(attend_rotate_q, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
-  if (hipError_t e = hipGetLastError()) return (int)e;
   const uintptr_t al4 = (uintptr_t)a.k_codes | (uintptr_t)a.v_codes | (uintptr_t)a.k_scale | (uintptr_t)a.k_zero |
                         (uintptr_t)a.v_scale | (uintptr_t)a.v_zero;
+  // the block-cooperative pass rotates its queries itself; the others read them from the workspace
+  const bool blk = a.group_log2 == 7 && a.heads % 4 == 0 && (al4 & 7) == 0 && (BITS == 4 || BITS == 2);
+  if (!blk) {
+    hipLaunchKernelGGL(attend_rotate_q, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError()) return (int)e;
+  }
   if (BITS == 4 && a.group_log2 == 7 && a.heads % 4 == 0 && (al4 & 7) == 0) {
     const int64_t nb = ((np + 3) / 4 + 15) / 16 * 16;  // whole groups of 16 blocks (XCD-aware order)
     if (nb > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
